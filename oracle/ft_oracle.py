@@ -1,0 +1,290 @@
+"""Plain fp64 CPU oracle of the FourTune W4A4G4 triple-branch linear.
+
+Test infrastructure only (see the package docstring).  Conventions:
+
+* bf16 tensors arrive as uint16 bit patterns (``bits``) and are decoded
+  exactly to float64.
+* A quantized matrix is described by its unpacked 4-bit codes ``codes``
+  (uint8 in 0..15, same shape as the input) and its scale grid
+  ``scales`` of shape [rows/16, cols/16].
+* Scale rules (the pages fix "scale from the block maximum" but not its
+  number format; both readings are implemented):
+    - "f32":  s = fl32(amax / 6), IEEE binary32 division (round to nearest
+      even); the element ratio is v = fl32(x / s).
+    - "pow2": s = 2^E with E the smallest integer such that 6 * 2^E >= amax,
+      clamped to [-127, 127] (the E8M0 scale byte is E + 127); the element
+      ratio is v = x * 2^-E, exact.  This is amax / 6 rounded up to a power
+      of two, so no element saturates.
+  A block whose maximum is zero gets s = 0 ("f32") or byte 0 ("pow2") and
+  all-zero codes.
+* E2M1 code = sign << 3 | exponent(2 bits, bias 1) << 1 | mantissa(1 bit);
+  magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Rounding is to the nearest
+  magnitude, ties to the code with mantissa bit 0, |v| > 6 saturates to 6,
+  and the sign bit is the sign bit of the input (so -0 gives code 8).
+* Packing: two codes per byte, the element with the even index in the low
+  nibble.  Row-major: element (i, j) in byte (i*cols + j) // 2.
+  Column-major: element (i, j) in byte (j*rows + i) // 2.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Tuple
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "f64_to_bf16_bits", "e2m1_decode", "e2m1_rne",
+    "block_amax", "scale_pow2_exponent", "scale_f32", "quantize_block16",
+    "pack_rm", "pack_cm", "unpack_rm", "dequantize", "scale_values",
+    "linear_fwd", "linear_bwd", "gelu", "gelu_grad", "svd_split_check",
+    "rel_frob", "BLOCK",
+]
+
+BLOCK = 16
+
+
+# --------------------------------------------------------------------------
+# bf16 <-> fp64
+# --------------------------------------------------------------------------
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns (bf16 is the top half of binary32)."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round fp64 values to bf16 with round-to-nearest-even (finite inputs).
+
+    Written as an explicit nearest-neighbour choice between the two bf16
+    values that bracket x: the truncation t (x rounded toward zero to 8
+    significant bits) and the next value away from zero; the tie goes to
+    the one whose last mantissa bit is 0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(np.abs(x))              # |x| = m * 2^e, m in [0.5, 1)
+    # bf16 keeps 8 significant bits for normal numbers (2^-126 and up) and
+    # a fixed quantum of 2^-133 below that.
+    q_exp = np.maximum(e - 8, -133)          # quantum (last-bit weight) exponent
+    q = np.ldexp(1.0, q_exp)
+    n = np.abs(x) / q                        # exact: power-of-two division
+    lo = np.floor(n)
+    frac = n - lo
+    up = (frac > 0.5) | ((frac == 0.5) & (np.fmod(lo, 2) == 1))
+    mag = (lo + up) * q
+    y = np.where(np.signbit(x), -mag, mag).astype(np.float32)
+    return (y.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# E2M1
+# --------------------------------------------------------------------------
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of 4-bit E2M1 codes from the format definition.
+
+    exponent field e (2 bits, bias 1), mantissa bit m:
+      e == 0: subnormal, magnitude m * 0.5
+      e >= 1: magnitude (1 + m/2) * 2^(e-1)
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e - 1.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+# magnitude thresholds of round-to-nearest-even on the E2M1 grid
+# 0 | 0.5 | 1 | 1.5 | 2 | 3 | 4 | 6 : a value moves to the next magnitude
+# when it passes the midpoint; on the midpoint it moves only if the next
+# code has mantissa bit 0 (codes 2, 4, 6), i.e. at 0.75, 1.75 and 3.5.
+_MID = [(0.25, False), (0.75, True), (1.25, False), (1.75, True),
+        (2.5, False), (3.5, True), (5.0, False)]
+
+
+def e2m1_rne(v) -> np.ndarray:
+    """Round fp64 ratios to E2M1 codes: nearest, ties to even, saturate at 6.
+
+    The sign bit of the code is the sign bit of ``v`` (-0 -> code 8).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    mag_code = np.zeros(v.shape, dtype=np.uint8)
+    for mid, inclusive in _MID:
+        mag_code += (a >= mid if inclusive else a > mid).astype(np.uint8)
+    return (np.signbit(v).astype(np.uint8) << 3) | mag_code
+
+
+# --------------------------------------------------------------------------
+# 16x16 block quantizer (sections 3.1 and 3.2)
+# --------------------------------------------------------------------------
+def _blocks(x: np.ndarray) -> np.ndarray:
+    r, c = x.shape
+    assert r % BLOCK == 0 and c % BLOCK == 0, "rows and cols must be multiples of 16"
+    return x.reshape(r // BLOCK, BLOCK, c // BLOCK, BLOCK)
+
+
+def block_amax(x: np.ndarray) -> np.ndarray:
+    """max |x| over each 16x16 block -> [rows/16, cols/16]."""
+    return np.abs(_blocks(x)).max(axis=(1, 3))
+
+
+def scale_pow2_exponent(amax) -> np.ndarray:
+    """E = min{e integer : 6 * 2^e >= amax}, clamped to [-127, 127] (E = -127 for amax 0).
+
+    6 * 2^e >= amax  <=>  e >= log2(amax / 6).  frexp gives amax/6 = f * 2^p
+    with f in [0.5, 1); the smallest such e is p - 1 when f == 0.5 (amax/6 a
+    power of two) and p otherwise.  amax/6 is computed in fp64; amax has at
+    most 8 significant bits, so the quotient is a power of two only when it
+    is exactly one.
+    """
+    a = np.asarray(amax, dtype=np.float64)
+    f, p = np.frexp(a / 6.0)
+    e = np.where(f == 0.5, p - 1, p).astype(np.int64)
+    e = np.where(a == 0.0, -127, e)
+    return np.clip(e, -127, 127)
+
+
+def scale_f32(amax) -> np.ndarray:
+    """s = fl32(amax / 6), IEEE binary32 division."""
+    a = np.asarray(amax, dtype=np.float64).astype(np.float32)
+    with np.errstate(all="ignore"):
+        return (a / np.float32(6.0)).astype(np.float32)
+
+
+def quantize_block16(bits, mode: str = "pow2") -> Tuple[np.ndarray, np.ndarray]:
+    """Q(.) of a bf16 matrix: unpacked codes [rows, cols] and the scale grid.
+
+    Returns (codes uint8, scales) where scales is uint8 E8M0 bytes
+    (mode "pow2") or float32 (mode "f32"), shape [rows/16, cols/16].
+    """
+    x = bf16_to_f64(bits)
+    rows, cols = x.shape
+    amax = block_amax(x)
+    xb = _blocks(x)
+    if mode == "pow2":
+        E = scale_pow2_exponent(amax)
+        v = xb * np.exp2(-E.astype(np.float64))[:, None, :, None]   # exact
+        scales = (E + 127).astype(np.uint8)
+    elif mode == "f32":
+        s = scale_f32(amax)
+        x32 = xb.astype(np.float32)                                  # exact (bf16 subset of f32)
+        with np.errstate(all="ignore"):
+            v32 = x32 / s[:, None, :, None]                          # IEEE binary32 division
+        # a block with amax == 0 has s == 0 and only (+-)0 elements: ratio (+-)0
+        zero_blk = (s == 0)[:, None, :, None] & np.ones_like(v32, dtype=bool)
+        v32 = np.where(zero_blk, x32 * np.float32(0.0), v32)
+        v = v32.astype(np.float64)
+        scales = s
+    else:
+        raise ValueError(mode)
+    codes = e2m1_rne(v).reshape(rows, cols)
+    return codes, scales
+
+
+def scale_values(scales, mode: str) -> np.ndarray:
+    """fp64 value of each block scale."""
+    if mode == "pow2":
+        return np.exp2(np.asarray(scales).astype(np.float64) - 127.0)
+    return np.asarray(scales, dtype=np.float32).astype(np.float64)
+
+
+def dequantize(codes, scales, mode: str) -> np.ndarray:
+    """Exact fp64 value of a block-quantized matrix: code value * block scale."""
+    vals = e2m1_decode(codes)
+    s = scale_values(scales, mode)
+    return vals * np.repeat(np.repeat(s, BLOCK, 0), BLOCK, 1)
+
+
+def pack_rm(codes) -> np.ndarray:
+    """Row-major packing: [rows, cols/2], even column in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_rm(packed, cols: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((p.shape[0], cols), np.uint8)
+    out[:, 0::2] = p & 15
+    out[:, 1::2] = p >> 4
+    return out
+
+
+def pack_cm(codes) -> np.ndarray:
+    """Column-major packing: [cols, rows/2]; byte (j, i/2) holds rows i, i+1 of column j."""
+    return pack_rm(np.asarray(codes, dtype=np.uint8).T)
+
+
+# --------------------------------------------------------------------------
+# Triple-branch linear (Eq. 2, Eq. 3, adapter gradients)
+# --------------------------------------------------------------------------
+def linear_fwd(Xhat, Rhat, X, L1, L2, A, B) -> np.ndarray:
+    """Eq. 2: Y = Q(X) Q(R)^T + X (L1 L2) + X (A B).
+
+    Xhat [M,K] and Rhat [N,K] are the dequantized Q(X), Q(R) (R in out x in
+    layout, so the backbone term is Xhat Rhat^T); X is the unquantized
+    input; L1 [K,rs], L2 [rs,N], A [K,r], B [r,N].  All fp64.
+    """
+    backbone = Xhat @ Rhat.T
+    stabilizer = X @ (L1 @ L2)
+    adapter = X @ (A @ B)
+    return backbone + stabilizer + adapter
+
+
+def linear_bwd(Ghat, Rhat, G, X, L1, L2, A, B) -> Dict[str, np.ndarray]:
+    """Eq. 3 and the adapter gradients of section 3.2.
+
+    dX = Q(G) Q(R) + G (L1 L2)^T + G (A B)^T   (Q(R) in out x in layout,
+         so GEMM_4bit(Q(G), Q(R)^T) of the paper's in x out layout is Ghat Rhat)
+    dB = (X A)^T G,   dA = X^T (G B^T).
+    Q is treated as the identity when differentiating (no gradient flows to
+    R, L1 or L2).
+    """
+    dX = Ghat @ Rhat + G @ (L1 @ L2).T + G @ (A @ B).T
+    dB = (X @ A).T @ G
+    dA = X.T @ (G @ B.T)
+    return {"dX": dX, "dA": dA, "dB": dB}
+
+
+def gelu(x) -> np.ndarray:
+    """GELU(x) = x * Phi(x), Phi the standard normal CDF (erf form)."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def gelu_grad(x) -> np.ndarray:
+    """d/dx [x Phi(x)] = Phi(x) + x phi(x)."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    Phi = 0.5 * (1.0 + erf(x / math.sqrt(2.0)))
+    phi = np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+    return Phi + x * phi
+
+
+def svd_split_check(W, R, L1, L2) -> Dict[str, float]:
+    """Checks of the offline split W ~= R + L1 L2 (Eq. 1) in fp64.
+
+    W, R in out x in layout [N,K]; L1 [K,rs], L2 [rs,N].  Returns the
+    relative reconstruction error of R + (L1 L2)^T and the Eckart-Young gap:
+    ||W - (L1 L2)^T||_F^2 compared with the sum of the discarded squared
+    singular values of W.
+    """
+    W = np.asarray(W, np.float64); R = np.asarray(R, np.float64)
+    Ls = (np.asarray(L1, np.float64) @ np.asarray(L2, np.float64)).T
+    rs = np.asarray(L1).shape[1]
+    sv = np.linalg.svd(W, compute_uv=False)
+    tail = float(np.sum(sv[rs:] ** 2))
+    resid = float(np.sum((W - Ls) ** 2))
+    return {
+        "recon_rel": float(np.linalg.norm(R + Ls - W) / np.linalg.norm(W)),
+        "resid_sq": resid,
+        "tail_sq": tail,
+        "top_sv": sv[: max(rs, 1)].tolist(),
+    }
+
+
+def rel_frob(a, b) -> float:
+    """||a - b||_F / ||b||_F (b is the reference)."""
+    a = np.asarray(a, np.float64); b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))

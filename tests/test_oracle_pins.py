@@ -1,0 +1,452 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks one oracle function against the format definition, a
+brute-force search in exact rational arithmetic, a closed form, an
+invariant or a special case that reduces to a textbook computation.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _all_finite_bf16():
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    expo = (b >> 7) & 0xFF
+    return b[expo != 0xFF]
+
+
+# ---------------------------------------------------------------- E2M1 decode
+def test_e2m1_decode_matches_published_table():
+    rows = _read_golden("e2m1_table.txt")
+    assert len(rows) == 16
+    for bits, val in rows:
+        code = int(bits, 2)
+        got = O.e2m1_decode(np.array([code]))[0]
+        assert got == float(val)
+        assert math.copysign(1.0, got) == math.copysign(1.0, float(val))
+
+
+# ---------------------------------------------------------------- RNE
+_GRID = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2),
+         Fraction(3), Fraction(4), Fraction(6)]
+
+
+def _rne_bruteforce(v: float) -> int:
+    """Nearest E2M1 magnitude by exact rational distance; ties to the even code."""
+    a = abs(Fraction(v))
+    if a > 6:
+        idx = 7
+    else:
+        d = [abs(a - g) for g in _GRID]
+        best = min(d)
+        cands = [i for i, di in enumerate(d) if di == best]
+        idx = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+    sign = 1 if math.copysign(1.0, v) < 0 else 0
+    return (sign << 3) | idx
+
+
+def test_rne_hand_worked_cases():
+    for v, bits in _read_golden("e2m1_rne_cases.txt"):
+        got = int(O.e2m1_rne(np.array([float(v)]))[0])
+        assert got == int(bits, 2), (v, got, bits)
+
+
+def test_rne_exhaustive_bf16_ratios():
+    """Every finite bf16 value, as a ratio, against exact-rational brute force."""
+    vals = O.bf16_to_f64(_all_finite_bf16())
+    got = O.e2m1_rne(vals)
+    # brute force on the distinct magnitudes, then apply sign
+    mags = np.unique(np.abs(vals))
+    table = {float(m): _rne_bruteforce(float(m)) for m in mags}
+    exp = np.array([table[abs(float(v))] | (8 if math.copysign(1, v) < 0 else 0)
+                    for v in vals], dtype=np.uint8)
+    assert np.array_equal(got, exp)
+
+
+def test_rne_fp32_neighbourhood_of_midpoints():
+    """fp32 ratios (the "f32" scale rule produces them) next to every midpoint."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.5, 1.0, 3.0],
+                    dtype=np.float32)
+    vals = []
+    for m in mids:
+        x = np.float32(m)
+        lo = x; hi = x
+        for _ in range(4):
+            vals += [lo, hi]
+            lo = np.nextafter(lo, np.float32(0)); hi = np.nextafter(hi, np.float32(10))
+    rng = np.random.default_rng(3)
+    vals += list(rng.uniform(0, 7, 3000).astype(np.float32))
+    vals = np.array(vals, dtype=np.float32).astype(np.float64)
+    vals = np.concatenate([vals, -vals])
+    got = O.e2m1_rne(vals)
+    exp = np.array([_rne_bruteforce(float(v)) for v in vals], dtype=np.uint8)
+    assert np.array_equal(got, exp)
+
+
+# ---------------------------------------------------------------- scales
+def _pow2_bruteforce(amax: Fraction) -> int:
+    """Smallest integer e with 6 * 2^e >= amax, clamped to [-127, 127], by bisection."""
+    if amax == 0:
+        return -127
+    lo, hi = -300, 300          # 6*2^lo < amax <= 6*2^hi
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if 6 * Fraction(2) ** mid >= amax:
+            hi = mid
+        else:
+            lo = mid
+    return max(-127, min(127, hi))
+
+
+def test_scale_pow2_exhaustive():
+    b = _all_finite_bf16()
+    b = b[b < 0x8000]                       # non-negative amax values
+    vals = O.bf16_to_f64(b)
+    got = O.scale_pow2_exponent(vals)
+    exp = np.array([_pow2_bruteforce(Fraction(float(v))) for v in vals])
+    assert np.array_equal(got, exp)
+    # no element of a block can saturate: amax * 2^-E <= 6, and E is minimal
+    nz = (vals > 0) & (exp > -127)
+    assert np.all(vals[nz] * np.exp2(-exp[nz]) <= 6.0)
+    assert np.all(vals[nz] * np.exp2(-(exp[nz] - 1.0)) > 6.0)
+
+
+def _fp32_round_exact(q: Fraction) -> np.float32:
+    """Correctly rounded binary32 of a positive rational, by checking neighbours."""
+    approx = np.float32(float(q))
+    cands = {approx, np.nextafter(approx, np.float32(np.inf)),
+             np.nextafter(approx, np.float32(0))}
+    cands = sorted(float(c) for c in cands)
+    best = None
+    for c in cands:
+        d = abs(Fraction(c) - q)
+        if best is None or d < best[0]:
+            best = (d, [c])
+        elif d == best[0]:
+            best[1].append(c)
+    if len(best[1]) == 1:
+        return np.float32(best[1][0])
+    for c in best[1]:           # tie: even mantissa (last bit of the binary32 pattern 0)
+        if int(np.float32(c).view(np.uint32)) % 2 == 0:
+            return np.float32(c)
+    raise AssertionError
+
+
+def test_scale_f32_exhaustive():
+    b = _all_finite_bf16()
+    b = b[b < 0x8000]
+    vals = O.bf16_to_f64(b)
+    got = O.scale_f32(vals)
+    exp = np.array([_fp32_round_exact(Fraction(float(v)) / 6) if v > 0 else np.float32(0)
+                    for v in vals], dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), exp.view(np.uint32))
+
+
+# ---------------------------------------------------------------- quantizer
+def _blocks_from_codes(rng, br, bc, mode):
+    """Blocks c * s with representable codes, each block holding a code of magnitude 4 or 6."""
+    codes = rng.integers(0, 16, size=(br * 16, bc * 16)).astype(np.uint8)
+    for i in range(br):
+        for j in range(bc):
+            codes[16 * i + rng.integers(16), 16 * j + rng.integers(16)] = rng.choice([6, 7, 14, 15])
+            if mode == "f32":
+                codes[16 * i + rng.integers(16), 16 * j + rng.integers(16)] = rng.choice([7, 15])
+    vals = O.e2m1_decode(codes)
+    if mode == "pow2":
+        E = rng.integers(-120, 120, size=(br, bc))
+        s = np.exp2(E.astype(np.float64))
+        scales = (E + 127).astype(np.uint8)
+    else:
+        # s = 1.25 * 2^k: 6 s and every c * s fit in bf16; fl32(6 s / 6) = s
+        k = rng.integers(-60, 60, size=(br, bc))
+        s = 1.25 * np.exp2(k.astype(np.float64))
+        scales = s.astype(np.float32)
+    x = vals * np.repeat(np.repeat(s, 16, 0), 16, 1)
+    bits = synth.f32_to_bf16_bits(x.astype(np.float32))
+    assert np.array_equal(O.bf16_to_f64(bits), x)   # exactly representable
+    return bits, codes, scales
+
+
+@pytest.mark.parametrize("mode", ["pow2", "f32"])
+def test_quantizer_roundtrip_of_representable_blocks(mode):
+    rng = np.random.default_rng(11)
+    bits, codes, scales = _blocks_from_codes(rng, 4, 6, mode)
+    got_codes, got_scales = O.quantize_block16(bits, mode)
+    # a zero code carries the sign of the zero it came from; compare values for those
+    nz = (codes & 7) != 0
+    assert np.array_equal(got_codes[nz], codes[nz])
+    assert np.all((got_codes[~nz] & 7) == 0)
+    if mode == "pow2":
+        assert np.array_equal(got_scales, scales)
+    else:
+        assert np.array_equal(got_scales.view(np.uint32), scales.view(np.uint32))
+    assert np.array_equal(O.dequantize(got_codes, got_scales, mode), O.bf16_to_f64(bits))
+
+
+@pytest.mark.parametrize("mode", ["pow2", "f32"])
+def test_quantizer_elementwise_bruteforce(mode):
+    """Small random tensor, every element re-derived by exact rational brute force."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((32, 48)) * np.exp2(rng.integers(-4, 4, (32, 48)))).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    codes, scales = O.quantize_block16(bits, mode)
+    xv = O.bf16_to_f64(bits)
+    for bi in range(2):
+        for bj in range(3):
+            blk = xv[16 * bi:16 * bi + 16, 16 * bj:16 * bj + 16]
+            amax = Fraction(float(np.abs(blk).max()))
+            if mode == "pow2":
+                E = _pow2_bruteforce(amax)
+                assert scales[bi, bj] == E + 127
+                ratio = lambda v: float(Fraction(v) / Fraction(2) ** E)
+            else:
+                s = _fp32_round_exact(amax / 6)
+                assert scales[bi, bj] == s
+                ratio = lambda v: float(_fp32_round_exact(abs(Fraction(v)) / Fraction(float(s)))) * \
+                    (1 if math.copysign(1, v) > 0 else -1) if v != 0 else v
+            for i in range(16):
+                for j in range(16):
+                    v = float(blk[i, j])
+                    exp = _rne_bruteforce(ratio(v))
+                    assert codes[16 * bi + i, 16 * bj + j] == exp
+
+
+@pytest.mark.parametrize("kind", ["zeros", "negzeros", "subnormal", "ties", "huge", "mixed"])
+@pytest.mark.parametrize("mode", ["pow2", "f32"])
+def test_quantizer_edge_invariants(kind, mode):
+    bits = synth.edge_tensor(kind, 64, 64)
+    codes, scales = O.quantize_block16(bits, mode)
+    x = O.bf16_to_f64(bits)
+    xhat = O.dequantize(codes, scales, mode)
+    # sign bit follows the input's sign bit
+    assert np.array_equal((codes >> 3).astype(bool), np.signbit(x))
+    # each element lands on one of the two grid neighbours of its ratio
+    s = np.repeat(np.repeat(O.scale_values(scales, mode), 16, 0), 16, 1)
+    with np.errstate(all="ignore"):
+        err = np.where(s > 0, np.abs(xhat - x) / np.where(s > 0, s, 1), 0.0)
+    # half a grid step is at most 1 (between 4 and 6); saturation is absent for pow2
+    assert np.all(err <= 1.0 + 1e-12)
+    if kind in ("zeros", "negzeros"):
+        assert np.all((codes & 7) == 0)
+        if mode == "pow2":
+            assert np.all(scales == 0)
+        else:
+            assert np.all(scales == 0)
+
+
+def test_transposition_invariance():
+    """The same 16x16 blocks serve Q(R) and Q(R)^T (section 3.2)."""
+    rng = np.random.default_rng(9)
+    for mode in ("pow2", "f32"):
+        bits = synth.f32_to_bf16_bits(rng.standard_t(3, (48, 80)).astype(np.float32))
+        c, s = O.quantize_block16(bits, mode)
+        ct, st = O.quantize_block16(np.ascontiguousarray(bits.T), mode)
+        assert np.array_equal(ct, c.T)
+        assert np.array_equal(np.asarray(st), np.asarray(s).T)
+        assert np.array_equal(O.pack_cm(c), O.pack_rm(ct))
+
+
+def test_packing_layout():
+    rng = np.random.default_rng(1)
+    c = rng.integers(0, 16, (16, 32)).astype(np.uint8)
+    rm = O.pack_rm(c)
+    cm = O.pack_cm(c)
+    flat_rm = np.zeros(16 * 32 // 2, np.uint8)
+    flat_cm = np.zeros(16 * 32 // 2, np.uint8)
+    for i in range(16):
+        for j in range(32):
+            idx = i * 32 + j
+            flat_rm[idx // 2] |= c[i, j] << (4 * (idx % 2))
+            idx = j * 16 + i
+            flat_cm[idx // 2] |= c[i, j] << (4 * (idx % 2))
+    assert np.array_equal(rm.reshape(-1), flat_rm)
+    assert np.array_equal(cm.reshape(-1), flat_cm)
+    assert np.array_equal(O.unpack_rm(rm, 32), c)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+def test_bf16_rounding_agrees_with_integer_rne():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.exp2(rng.integers(-140, 120, 200000)).astype(np.float32),
+        (np.arange(1, 5000, dtype=np.uint32) << 15 | 0x3F800000).view(np.float32),  # exact halfway cases
+    ])
+    x = x[np.isfinite(x)]
+    a = O.f64_to_bf16_bits(x.astype(np.float64))
+    b = synth.f32_to_bf16_bits(x)
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- linear algebra
+def _frac_mat(a):
+    return [[Fraction(float(v)) for v in row] for row in np.asarray(a)]
+
+
+def _frac_mm(a, b):
+    n, k, m = len(a), len(b), len(b[0])
+    return [[sum(a[i][t] * b[t][j] for t in range(k)) for j in range(m)] for i in range(n)]
+
+
+def _frac_T(a):
+    return [list(r) for r in zip(*a)]
+
+
+def _frac_add(a, b):
+    return [[x + y for x, y in zip(ra, rb)] for ra, rb in zip(a, b)]
+
+
+def _tiny_linear(M, K, N, rs, r, seed):
+    rng = np.random.default_rng(seed)
+    spec = synth.LinearSpec("tiny", M, K, N, rs, r)
+    d = synth.make_linear(spec, rng)
+    f = {k: O.bf16_to_f64(d[k]) for k in ("X", "W", "R", "L1", "L2", "A", "B", "G")}
+    xc, xs = O.quantize_block16(d["X"]); rc, rsc = O.quantize_block16(d["R"])
+    gc, gs = O.quantize_block16(d["G"])
+    f["Xhat"] = O.dequantize(xc, xs, "pow2")
+    f["Rhat"] = O.dequantize(rc, rsc, "pow2")
+    f["Ghat"] = O.dequantize(gc, gs, "pow2")
+    return f
+
+
+@pytest.mark.parametrize("shape", [(16, 16, 16, 2, 3), (32, 64, 48, 4, 4)])
+def test_linear_fwd_bwd_exact_rational(shape):
+    M, K, N, rs, r = shape
+    f = _tiny_linear(M, K, N, rs, r, 21)
+    Y = O.linear_fwd(f["Xhat"], f["Rhat"], f["X"], f["L1"], f["L2"], f["A"], f["B"])
+    g = O.linear_bwd(f["Ghat"], f["Rhat"], f["G"], f["X"], f["L1"], f["L2"], f["A"], f["B"])
+    F = {k: _frac_mat(v) for k, v in f.items()}
+    # Eq. 2 term by term in exact arithmetic, with R in out x in layout
+    Yq = _frac_mm(F["Xhat"], _frac_T(F["Rhat"]))
+    Ys = _frac_mm(F["X"], _frac_mm(F["L1"], F["L2"]))
+    Ya = _frac_mm(_frac_mm(F["X"], F["A"]), F["B"])
+    Yx = _frac_add(_frac_add(Yq, Ys), Ya)
+    dXq = _frac_mm(F["Ghat"], F["Rhat"])
+    dXs = _frac_mm(_frac_mm(F["G"], _frac_T(F["L2"])), _frac_T(F["L1"]))
+    dXa = _frac_mm(_frac_mm(F["G"], _frac_T(F["B"])), _frac_T(F["A"]))
+    dXx = _frac_add(_frac_add(dXq, dXs), dXa)
+    dBx = _frac_mm(_frac_T(_frac_mm(F["X"], F["A"])), F["G"])
+    dAx = _frac_mm(_frac_T(F["X"]), _frac_mm(F["G"], _frac_T(F["B"])))
+    for got, ex in ((Y, Yx), (g["dX"], dXx), (g["dB"], dBx), (g["dA"], dAx)):
+        ex = np.array([[float(v) for v in row] for row in ex])
+        assert O.rel_frob(got, ex) < 1e-14
+
+
+def test_linear_special_cases_reduce_to_plain_gemm():
+    """With Q-representable X, R, G the triple-branch layer is one dense layer
+    with weight W' = R + (L1 L2)^T + (A B)^T (out x in)."""
+    rng = np.random.default_rng(4)
+    M, K, N, rs, r = 48, 64, 32, 3, 5
+    def representable(rows, cols):
+        b, _, _ = _blocks_from_codes(rng, rows // 16, cols // 16, "pow2")
+        return b
+    X, R, G = representable(M, K), representable(N, K), representable(M, N)
+    Xf, Rf, Gf = (O.bf16_to_f64(t) for t in (X, R, G))
+    L1 = rng.standard_normal((K, rs)); L2 = rng.standard_normal((rs, N))
+    A = rng.standard_normal((K, r)); B = rng.standard_normal((r, N))
+    for t, f in ((X, Xf), (R, Rf), (G, Gf)):
+        c, s = O.quantize_block16(t)
+        assert np.array_equal(O.dequantize(c, s, "pow2"), f)
+    Wp = Rf + (L1 @ L2).T + (A @ B).T
+    Y = O.linear_fwd(Xf, Rf, Xf, L1, L2, A, B)
+    assert O.rel_frob(Y, Xf @ Wp.T) < 1e-14
+    g = O.linear_bwd(Gf, Rf, Gf, Xf, L1, L2, A, B)
+    assert O.rel_frob(g["dX"], Gf @ Wp) < 1e-14
+    # no low-rank branches: pure W4A4 GEMM; zero residual: pure low-rank layer
+    z = np.zeros
+    assert O.rel_frob(O.linear_fwd(Xf, Rf, Xf, z((K, 0)), z((0, N)), z((K, 0)), z((0, N))), Xf @ Rf.T) < 1e-15
+    Y0 = O.linear_fwd(Xf, z((N, K)), Xf, L1, L2, A, B)
+    assert O.rel_frob(Y0, Xf @ (L1 @ L2 + A @ B)) < 1e-14
+
+
+def test_adapter_gradients_finite_differences():
+    """dA, dB are the exact gradients of L = <G, Y(A, B)> (section 3.2)."""
+    rng = np.random.default_rng(8)
+    M, K, N, r = 32, 16, 24, 4
+    X = rng.standard_normal((M, K)); G = rng.standard_normal((M, N))
+    A = rng.standard_normal((K, r)); B = rng.standard_normal((r, N))
+    z = np.zeros
+    def loss(A_, B_):
+        Y = O.linear_fwd(z((M, K)), z((N, K)), X, z((K, 0)), z((0, N)), A_, B_)
+        return float(np.sum(G * Y))
+    g = O.linear_bwd(z((M, N)), z((N, K)), G, X, z((K, 0)), z((0, N)), A, B)
+    h = 1e-5
+    for name, P, grad in (("A", A, g["dA"]), ("B", B, g["dB"])):
+        fd = np.zeros_like(P)
+        for idx in np.ndindex(P.shape):
+            Pp = P.copy(); Pm = P.copy()
+            Pp[idx] += h; Pm[idx] -= h
+            args_p = (Pp, B) if name == "A" else (A, Pp)
+            args_m = (Pm, B) if name == "A" else (A, Pm)
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert O.rel_frob(grad, fd) < 1e-8
+
+
+def test_input_gradient_finite_differences_straight_through():
+    """dX of Eq. 3 equals d<G, Y>/dX when Q acts as identity and G is representable."""
+    rng = np.random.default_rng(12)
+    M, K, N, rs, r = 16, 32, 16, 2, 3
+    X = rng.standard_normal((M, K))
+    Rf = rng.standard_normal((N, K)); L1 = rng.standard_normal((K, rs)); L2 = rng.standard_normal((rs, N))
+    A = rng.standard_normal((K, r)); B = rng.standard_normal((r, N))
+    G = rng.standard_normal((M, N))
+    loss = lambda X_: float(np.sum(G * O.linear_fwd(X_, Rf, X_, L1, L2, A, B)))
+    g = O.linear_bwd(G, Rf, G, X, L1, L2, A, B)
+    h = 1e-5
+    fd = np.zeros_like(X)
+    for idx in np.ndindex(X.shape):
+        Xp = X.copy(); Xm = X.copy(); Xp[idx] += h; Xm[idx] -= h
+        fd[idx] = (loss(Xp) - loss(Xm)) / (2 * h)
+    assert O.rel_frob(g["dX"], fd) < 1e-8
+
+
+# ---------------------------------------------------------------- GELU
+def test_gelu_textbook_values_and_gradient():
+    for x, phi in _read_golden("normal_cdf.txt"):
+        x = float(x); phi = float(phi)
+        assert abs(O.gelu(np.array([x]))[0] - x * phi) < 1e-15
+    xs = np.linspace(-6, 6, 241)
+    h = 1e-6
+    fd = (O.gelu(xs + h) - O.gelu(xs - h)) / (2 * h)
+    assert np.max(np.abs(fd - O.gelu_grad(xs))) < 1e-8
+    # GELU(x) - GELU(-x) = x
+    assert np.max(np.abs(O.gelu(xs) - O.gelu(-xs) - xs)) < 1e-14
+
+
+# ---------------------------------------------------------------- SVD split (Eq. 1)
+@pytest.mark.parametrize("shape", [(64, 32, 4), (32, 96, 8)])
+def test_svd_split_reconstruction_and_eckart_young(shape):
+    N, K, rs = shape
+    rng = np.random.default_rng(17)
+    spec = synth.LinearSpec("split", 16, K, N, rs, 2, w_outlier_cols=2, w_outlier_mult=20.0)
+    d = synth.make_linear(spec, rng)
+    W = O.bf16_to_f64(d["W"]); R = O.bf16_to_f64(d["R"])
+    L1 = O.bf16_to_f64(d["L1"]); L2 = O.bf16_to_f64(d["L2"])
+    chk = O.svd_split_check(W, R, L1, L2)
+    # R is W - L1 L2 rounded to bf16: reconstruction within bf16 rounding of R
+    assert chk["recon_rel"] < 2 ** -8 * np.linalg.norm(R) / np.linalg.norm(W) + 1e-12
+    # Eckart-Young: the rank-rs part leaves the sum of the discarded sigma^2
+    # (up to the bf16 rounding of the factors)
+    assert abs(chk["resid_sq"] - chk["tail_sq"]) / chk["tail_sq"] < 2e-2
+    # an independent decomposition: eigenvalues of W^T W are sigma^2
+    ev = np.sort(np.linalg.eigvalsh(W.T @ W))[::-1][:rs]
+    assert np.allclose(ev, np.array(chk["top_sv"][:rs]) ** 2, rtol=1e-9)
+    # the stabilizer carries the outlier columns: the residual's peak is smaller
+    assert np.abs(R).max() < np.abs(W).max()
