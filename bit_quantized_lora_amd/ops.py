@@ -1,0 +1,127 @@
+"""Thin torch binding of the ft C ABI (argument marshalling only).
+
+Each function takes CUDA (HIP) tensors, allocates outputs with torch (device
+memory is torch's job here), passes raw pointers and the current stream to
+libft.so and raises ``FtError`` on a non-OK status.  No arithmetic of the
+method happens in Python.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+_MODES = {"pow2": _lib.FT_SCALE_POW2, "f32": _lib.FT_SCALE_F32}
+_OUT = {torch.float32: _lib.FT_OUT_F32, torch.bfloat16: _lib.FT_OUT_BF16}
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def quant_block16(x: torch.Tensor, mode: str = "pow2", rm: bool = True, cm: bool = False
+                  ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor], torch.Tensor]:
+    """Q(x) for a bf16 [rows, cols] matrix -> (codes_rm, codes_cm, scales)."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D matrix with unit column stride")
+    rows, cols = x.shape
+    dev = x.device
+    codes_rm = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if rm else None
+    codes_cm = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev) if cm else None
+    sdt = torch.uint8 if mode == "pow2" else torch.float32
+    scales = torch.empty((rows // 16, cols // 16), dtype=sdt, device=dev)
+    st = lib().ft_quant_block16(x.data_ptr(), rows, cols, x.stride(0), _MODES[mode],
+                                _ptr(codes_rm), _ptr(codes_cm), scales.data_ptr(), _stream(x))
+    check("ft_quant_block16", st)
+    return codes_rm, codes_cm, scales
+
+
+def lowrank_fused(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = [inp wa^T | inp wb^T] in fp32; wa [ra, Kin], wb [rb, Kin] bf16."""
+    _need(inp, torch.bfloat16, "inp")
+    M, Kin = inp.shape
+    ra, rb = wa.shape[0], wb.shape[0]
+    for w, n in ((wa, "wa"), (wb, "wb")):
+        _need(w, torch.bfloat16, n)
+        if w.dim() != 2 or w.shape[1] != Kin or not w.is_contiguous():
+            raise ValueError(f"{n} must be contiguous [rank, {Kin}]")
+    if out is None:
+        out = torch.empty((M, ra + rb), dtype=torch.float32, device=inp.device)
+    st = lib().ft_lowrank_fused(inp.data_ptr(), M, Kin, inp.stride(0), wa.data_ptr(), ra,
+                                wb.data_ptr(), rb, out.data_ptr(), _stream(inp))
+    check("ft_lowrank_fused", st)
+    return out
+
+
+def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
+               out_dtype=torch.float32, mode: str = "pow2", out: Optional[torch.Tensor] = None):
+    """Y = deq(Xq) deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B."""
+    rs, r = L2.shape[0], B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=T.device)
+    st = lib().ft_linear_fwd(M, N, K, _MODES[mode], xq_codes.data_ptr(), xq_scales.data_ptr(),
+                             rq_codes.data_ptr(), rq_scales.data_ptr(), T.data_ptr(),
+                             L2.data_ptr(), rs, B.data_ptr(), r, out.data_ptr(), _OUT[out.dtype],
+                             _stream(T))
+    check("ft_linear_fwd", st)
+    return out
+
+
+def linear_bwd_workspace(M: int, N: int, K: int, r: int) -> int:
+    return int(lib().ft_linear_bwd_workspace(M, N, K, r))
+
+
+def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales, V, L1t, At, X, G, T,
+               M: int, N: int, K: int, out_dtype=torch.float32, mode: str = "pow2",
+               workspace: Optional[torch.Tensor] = None, dX: Optional[torch.Tensor] = None):
+    """dX, dAt, dB of Eq. 3 and section 3.2 (see include/ft.h)."""
+    rs, r = L1t.shape[0], At.shape[0]
+    dev = V.device
+    if dX is None:
+        dX = torch.empty((M, K), dtype=out_dtype, device=dev)
+    dAt = torch.empty((r, K), dtype=torch.float32, device=dev)
+    dB = torch.empty((r, N), dtype=torch.float32, device=dev)
+    ws_bytes = linear_bwd_workspace(M, N, K, r)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    st = lib().ft_linear_bwd(M, N, K, _MODES[mode], gq_codes.data_ptr(), gq_scales.data_ptr(),
+                             rq_codes_cm.data_ptr(), rq_scales.data_ptr(), V.data_ptr(),
+                             L1t.data_ptr(), rs, At.data_ptr(), r, X.data_ptr(), G.data_ptr(),
+                             T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype], dAt.data_ptr(),
+                             dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(V))
+    check("ft_linear_bwd", st)
+    return dX, dAt, dB
+
+
+def gelu_fwd(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(y, torch.bfloat16, "y")
+    if out is None:
+        out = torch.empty_like(y)
+    st = lib().ft_gelu_fwd(y.data_ptr(), y.numel(), out.data_ptr(), _stream(y))
+    check("ft_gelu_fwd", st)
+    return out
+
+
+def gelu_bwd(y: torch.Tensor, dh: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _need(y, torch.bfloat16, "y"); _need(dh, torch.bfloat16, "dh")
+    if out is None:
+        out = torch.empty_like(y)
+    st = lib().ft_gelu_bwd(y.data_ptr(), dh.data_ptr(), y.numel(), out.data_ptr(), _stream(y))
+    check("ft_gelu_bwd", st)
+    return out

@@ -1,0 +1,160 @@
+/*
+ * ft.h -- C ABI of the W4A4G4 triple-branch quantized linear for MI355X (gfx950).
+ *
+ * Method: FourTune ("FourTune: Towards Fully 4-Bit Efficient Post-Training for
+ * Diffusion Models").  A frozen weight is split offline as W ~= R + L1 L2
+ * (section 3.1, Eq. 1).  The residual R, the activations X and the output
+ * gradient G = dL/dY are quantized in 16x16 blocks (4-bit E2M1 codes plus one
+ * scale per block; section 3.1 after Eq. 2, section 3.2, section 4.3 "Impact of
+ * Quantization Granularity") and multiplied in 4-bit; the stabilizer L1 L2 and
+ * the trainable LoRA factors A, B stay in bf16:
+ *
+ *   Y  = Q(X) Q(R)^T + X L1 L2 + X A B                       (Eq. 2)
+ *   dX = Q(G) Q(R)   + G (L1 L2)^T + G (A B)^T               (Eq. 3)
+ *   dB = (X A)^T G,   dA = X^T (G B^T)                        (section 3.2)
+ *
+ * Shapes: X [M x K] (tokens x in), R and W [N x K] (out x in), G and Y [M x N].
+ * The low-rank factors are stored rank-major, each factor's rank index being
+ * its row:  L1t = L1^T [rs x K], At = A^T [r x K], L2 [rs x N], B [r x N].
+ * Gradients come back in the same layout: dAt = (dA)^T [r x K], dB [r x N].
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are device pointers owned by the caller.  The library
+ *    allocates no device memory and keeps no pointer after a call returns.
+ *  - Work is enqueued asynchronously on the given stream; nothing synchronizes.
+ *  - Arguments are validated before anything is launched; on error nothing
+ *    is enqueued and the status says why.  The library never aborts.
+ *  - Matrices are row-major with the stated leading dimension (in elements).
+ *  - bf16 data is IEEE-754 binary32's upper half (torch.bfloat16).
+ *  - Results are deterministic: the same inputs give the same bits (no
+ *    floating-point atomics, fixed reduction orders).
+ *  - Pointers must be 16-byte aligned; leading dimensions must keep every
+ *    row 16-byte aligned (FT_EALIGN otherwise).
+ *  - Every matrix dimension must be a multiple of 16 (the quantization block;
+ *    FT_ESHAPE otherwise).  Zero-sized dimensions are accepted and enqueue
+ *    nothing.  Ranks: rs (stabilizer) and r (LoRA) are multiples of 16 with
+ *    0 <= rs + r <= 128.
+ */
+#ifndef FT_H_
+#define FT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FT_OK = 0,
+  FT_EINVAL = 1,   /* null pointer where one is required, unknown enum value */
+  FT_ESHAPE = 2,   /* a dimension not a multiple of 16, negative, or ranks out of range */
+  FT_EALIGN = 3,   /* pointer or leading dimension breaks 16-byte alignment */
+  FT_EHIP = 4,     /* a HIP launch failed (hipGetLastError after the launch) */
+  FT_ENOTSUP = 5,  /* valid request that this build does not implement */
+  FT_ESPACE = 6    /* workspace smaller than required */
+} ft_status;
+
+/* Block-scale rule of the quantizer (the pages fix "scale from the block
+ * maximum over 6", not its number format):
+ *  FT_SCALE_POW2: s = 2^E, E = min{e : 6 * 2^e >= amax}, clamped to
+ *                 [-127, 127]; stored as one E8M0 byte E + 127.  This is amax/6
+ *                 rounded up to the power-of-two scale format the gfx950
+ *                 block-scaled MFMA consumes; no element saturates.
+ *  FT_SCALE_F32:  s = fl32(amax / 6) stored as float; element ratio fl32(x / s).
+ * In both rules the element code is the round-to-nearest-even E2M1 value of
+ * the ratio, saturating at +-6, with the sign bit of x (so -0 -> code 8), and
+ * a block of zeros gets scale 0 (byte 0 or 0.0f) and zero codes. */
+typedef enum { FT_SCALE_POW2 = 0, FT_SCALE_F32 = 1 } ft_scale_mode;
+
+typedef enum { FT_OUT_F32 = 0, FT_OUT_BF16 = 1 } ft_out_dtype;
+
+/* ft_quant_block16 -- the 4-bit quantizer Q(.) (section 3.1: "applied offline
+ * for the residual weights R and dynamically for activations X"; section 3.2:
+ * 16x16 blocks whose scale serves both the matrix and its transpose).
+ *
+ *  x         bf16 [rows x cols], leading dimension ldx (>= cols).
+ *  codes_rm  out, may be NULL: row-major packed codes [rows x cols/2] bytes;
+ *            element (i, j) in byte i*cols/2 + j/2, even j in the low nibble.
+ *  codes_cm  out, may be NULL: column-major packed codes [cols x rows/2];
+ *            element (i, j) in byte j*rows/2 + i/2, even i in the low nibble.
+ *            (The codes of X^T: what the transposed GEMM of Eq. 3 reads.)
+ *  scales    out: [rows/16 x cols/16] row-major, uint8 E8M0 (POW2) or float (F32).
+ *  At least one of codes_rm, codes_cm must be non-NULL.  Input and outputs
+ *  must not overlap.  Codes and scales are bit-exact functions of x. */
+ft_status ft_quant_block16(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                           ft_scale_mode mode, uint8_t* codes_rm, uint8_t* codes_cm,
+                           void* scales, hipStream_t stream);
+
+/* ft_lowrank_fused -- the shared down-projection of the two low-rank branches
+ * (section 3.3 "LoRA Fusion": both branches read the same input, so one pass
+ * over it feeds both):
+ *
+ *   out[:, 0:ra]      = in . wa^T      (wa [ra x Kin], row-major, ld = Kin)
+ *   out[:, ra:ra+rb]  = in . wb^T      (wb [rb x Kin])
+ *
+ * forward:  in = X [M x K],  wa = L1t, wb = At  -> T = [X L1 | X A]
+ * backward: in = G [M x N],  wa = L2,  wb = B   -> V = [G L2^T | G B^T]
+ *  in   bf16 [M x Kin], leading dimension ld_in.
+ *  out  float [M x (ra+rb)], row-major, leading dimension ra+rb.
+ *  Products accumulate in fp32 from exact bf16 operands. */
+ft_status ft_lowrank_fused(const void* in, int64_t M, int64_t Kin, int64_t ld_in,
+                           const void* wa, int32_t ra, const void* wb, int32_t rb,
+                           float* out, hipStream_t stream);
+
+/* ft_linear_fwd -- Eq. 2 with the LoRA-fusion epilogue (section 3.3: the
+ * backbone GEMM and the up-projections are accumulated in one kernel):
+ *
+ *   Y = deq(Xq) deq(Rq)^T + T[:, 0:rs] L2 + T[:, rs:rs+r] B
+ *
+ *  xq_codes   row-major codes of X [M x K/2], xq_scales [M/16 x K/16]
+ *  rq_codes   row-major codes of R [N x K/2], rq_scales [N/16 x K/16]
+ *  T          float [M x (rs+r)] from ft_lowrank_fused(X, L1t, At)
+ *  L2 [rs x N], B [r x N] bf16
+ *  Y          [M x N] float or bf16 (round-to-nearest-even of the fp32 result).
+ * Only FT_SCALE_POW2 operands are supported by the GEMM (FT_ENOTSUP otherwise):
+ * the block-scaled MFMA applies power-of-two scales in hardware. */
+ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                        const uint8_t* xq_codes, const void* xq_scales,
+                        const uint8_t* rq_codes, const void* rq_scales,
+                        const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                        void* Y, ft_out_dtype ydt, hipStream_t stream);
+
+/* ft_linear_bwd -- Eq. 3 and the adapter gradients of section 3.2:
+ *
+ *   dX  = deq(Gq) deq(Rq) + V[:, 0:rs] L1t + V[:, rs:rs+r] At
+ *   dAt = V[:, rs:rs+r]^T X          ( = (X^T G B^T)^T )
+ *   dB  = T[:, rs:rs+r]^T G          ( = (X A)^T G )
+ *
+ *  gq_codes     row-major codes of G [M x N/2], gq_scales [M/16 x N/16]
+ *  rq_codes_cm  column-major codes of R [K x N/2] (ft_quant_block16 codes_cm of R)
+ *  rq_scales    [N/16 x K/16], the same scale grid the forward uses
+ *  V            float [M x (rs+r)] from ft_lowrank_fused(G, L2, B)
+ *  L1t [rs x K], At [r x K] bf16
+ *  X  bf16 [M x K], G bf16 [M x N] (unquantized), T float [M x (rs+r)] (forward)
+ *  dX [M x K] float or bf16; dAt float [r x K]; dB float [r x N]
+ *  workspace  device scratch of at least ft_linear_bwd_workspace(M, N, K, r)
+ *             bytes (partial sums of the reductions over M). */
+ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                        const uint8_t* gq_codes, const void* gq_scales,
+                        const uint8_t* rq_codes_cm, const void* rq_scales,
+                        const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                        const void* X, const void* G, const float* T,
+                        void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
+size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* GELU between the two linears of an MLP (section 3.3 "MLP Fusion" names the
+ * activation; the exact erf form x * Phi(x) is used).  h = GELU(y) in bf16;
+ * dy = GELU'(y) * dh in bf16.  y, dh, h, dy are bf16 [n] (n a multiple of 8). */
+ft_status ft_gelu_fwd(const void* y, int64_t n, void* h, hipStream_t stream);
+ft_status ft_gelu_bwd(const void* y, const void* dh, int64_t n, void* dy, hipStream_t stream);
+
+const char* ft_status_str(ft_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FT_H_ */
