@@ -245,20 +245,27 @@ def linear_bwd(Ghat, Rhat, G, X, L1, L2, A, B) -> Dict[str, np.ndarray]:
     return {"dX": dX, "dA": dA, "dB": dB}
 
 
+def _norm_cdf(x) -> np.ndarray:
+    """Standard normal CDF Phi(x) = erfc(-x / sqrt(2)) / 2.
+
+    The complementary-error-function form keeps full relative accuracy in the
+    lower tail, where 1 + erf(x / sqrt 2) cancels to zero (x below about -8).
+    """
+    from scipy.special import erfc
+    return 0.5 * erfc(-np.asarray(x, dtype=np.float64) / math.sqrt(2.0))
+
+
 def gelu(x) -> np.ndarray:
-    """GELU(x) = x * Phi(x), Phi the standard normal CDF (erf form)."""
-    from scipy.special import erf
+    """GELU(x) = x * Phi(x), Phi the standard normal CDF."""
     x = np.asarray(x, dtype=np.float64)
-    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+    return x * _norm_cdf(x)
 
 
 def gelu_grad(x) -> np.ndarray:
     """d/dx [x Phi(x)] = Phi(x) + x phi(x)."""
-    from scipy.special import erf
     x = np.asarray(x, dtype=np.float64)
-    Phi = 0.5 * (1.0 + erf(x / math.sqrt(2.0)))
     phi = np.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
-    return Phi + x * phi
+    return _norm_cdf(x) + x * phi
 
 
 def svd_split_check(W, R, L1, L2) -> Dict[str, float]:
