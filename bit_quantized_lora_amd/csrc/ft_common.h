@@ -42,4 +42,7 @@ __device__ __forceinline__ void split_bf16(float f, uint32_t& hi, uint32_t& lo) 
   lo = f32_to_bf16_rne(r);
 }
 
+// Zero n floats on the stream with a kernel (graph-capture friendly, no memset node).
+ft_status fill_zero_f32(float* p, int64_t n, hipStream_t s);
+
 }  // namespace ft

@@ -1,0 +1,101 @@
+// Entry points of the triple-branch linear: ft_linear_fwd (Eq. 2) and
+// ft_linear_bwd (Eq. 3 plus the adapter gradients of section 3.2).
+#include "ft_internal.h"
+
+namespace ft {
+namespace {
+
+bool ranks_ok(int rs, int r) { return rs >= 0 && r >= 0 && rs % 16 == 0 && r % 16 == 0 && rs + r <= 128; }
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+}  // namespace ft
+
+extern "C" ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                                   const uint8_t* xq_codes, const void* xq_scales,
+                                   const uint8_t* rq_codes, const void* rq_scales,
+                                   const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                                   void* Y, ft_out_dtype ydt, hipStream_t stream) {
+  using namespace ft;
+  if (mode != FT_SCALE_POW2 && mode != FT_SCALE_F32) return FT_EINVAL;
+  if (ydt != FT_OUT_F32 && ydt != FT_OUT_BF16) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  if (mode != FT_SCALE_POW2) return FT_ENOTSUP;
+  if (M == 0 || N == 0) return FT_OK;
+  const int rho = rs + r;
+  if (!Y || (K && (!xq_codes || !xq_scales || !rq_codes || !rq_scales)) || (rho && !T) ||
+      (rs && !L2) || (r && !B))
+    return FT_EINVAL;
+  if (!aligned16(Y) || (K && (!aligned16(xq_codes) || !aligned16(rq_codes))) || (rho && !aligned16(T)) ||
+      (rs && !aligned16(L2)) || (r && !aligned16(B)))
+    return FT_EALIGN;
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = xq_codes; g.lda = K / 2;
+  g.B = rq_codes; g.ldb = K / 2;
+  g.sA = static_cast<const uint8_t*>(xq_scales); g.sA_rs = K / 16;
+  g.sB = static_cast<const uint8_t*>(rq_scales); g.sB_ns = K / 16; g.sB_ks = 1;
+  g.P = T;
+  g.Wa = static_cast<const uint16_t*>(L2); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(B); g.rb = r;
+  g.C = Y; g.ldc = N;
+  return launch_gemm_w4a4(g, ydt == FT_OUT_BF16, stream);
+}
+
+extern "C" size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r) {
+  using namespace ft;
+  if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
+  return align256(lora_grad_workspace(M, K, r)) + align256(lora_grad_workspace(M, N, r));
+}
+
+extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                                   const uint8_t* gq_codes, const void* gq_scales,
+                                   const uint8_t* rq_codes_cm, const void* rq_scales,
+                                   const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                                   const void* X, const void* G, const float* T,
+                                   void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  using namespace ft;
+  if (mode != FT_SCALE_POW2 && mode != FT_SCALE_F32) return FT_EINVAL;
+  if (dxdt != FT_OUT_F32 && dxdt != FT_OUT_BF16) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  if (mode != FT_SCALE_POW2) return FT_ENOTSUP;
+  const int rho = rs + r;
+  const size_t need = ft_linear_bwd_workspace(M, N, K, r);
+  if (M && K && !dX) return FT_EINVAL;
+  if (M && N && K && (!gq_codes || !gq_scales || !rq_codes_cm || !rq_scales)) return FT_EINVAL;
+  if (M && rho && !V) return FT_EINVAL;
+  if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
+  if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
+  if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
+  const void* ptrs[] = {gq_codes, rq_codes_cm, V, L1t, At, X, G, T, dX, dAt, dB, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+
+  // dX = deq(Gq) deq(Rq) + V [L1^T; A^T]: GEMM over the output features N, with
+  // R's column-major codes as the B operand and R's scale grid read transposed.
+  if (M && K) {
+    GemmArgs g{};
+    g.M = M; g.N = K; g.K = N;
+    g.A = gq_codes; g.lda = N / 2;
+    g.B = rq_codes_cm; g.ldb = N / 2;
+    g.sA = static_cast<const uint8_t*>(gq_scales); g.sA_rs = N / 16;
+    g.sB = static_cast<const uint8_t*>(rq_scales); g.sB_ns = 1; g.sB_ks = K / 16;
+    g.P = V;
+    g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
+    g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
+    g.C = dX; g.ldc = K;
+    ft_status st = launch_gemm_w4a4(g, dxdt == FT_OUT_BF16, stream);
+    if (st != FT_OK) return st;
+  }
+  if (r) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const size_t wa = align256(lora_grad_workspace(M, K, r));
+    // dA^T = V[:, rs:]^T X ;  dB = T[:, rs:]^T G
+    ft_status st = launch_lora_grad(V, rho, rs, r, static_cast<const uint16_t*>(X), M, K, dAt, ws, stream);
+    if (st != FT_OK) return st;
+    st = launch_lora_grad(T, rho, rs, r, static_cast<const uint16_t*>(G), M, N, dB, ws + wa, stream);
+    if (st != FT_OK) return st;
+  }
+  return FT_OK;
+}

@@ -1,0 +1,180 @@
+// Adapter weight gradients of FourTune section 3.2 (reductions over tokens):
+//
+//   dA^T = V[:, rs:]^T X      (V[:, rs:] = G B^T from the backward down-projection)
+//   dB   = T[:, rs:]^T G      (T[:, rs:] = X A from the forward down-projection)
+//
+// Both are dW[j][c] = sum_m P[m][poff + j] Q[m][c] with a small fp32 P and a
+// large bf16 Q read once from HBM.  The MFMA needs runs of consecutive m in
+// both operands, so (1) a tiny pre-pass writes P's slice transposed and split
+// into bf16 hi + lo planes [r x M]; (2) each wave stages 64 x 32 tiles of Q in
+// its own LDS region transposed (so B fragments are single 16-byte reads) and
+// accumulates on bf16 MFMA 32x32x16; (3) the 4 waves of a workgroup, each owning
+// every 4th 64-row chunk of the workgroup's token range, are summed through LDS
+// in a fixed order, and token-range splits (for parallelism when the output is
+// narrow) are summed by a final pass in a fixed order: results are deterministic.
+#include "ft_internal.h"
+
+namespace ft {
+namespace {
+
+constexpr int LG_COLS = 32;
+constexpr int LG_CHUNK = 64;
+constexpr int LG_WAVES = 4;
+constexpr int LG_THREADS = LG_WAVES * 64;
+constexpr int QT_PITCH = LG_CHUNK + 8;       // bf16 elements per LDS row of Q^T
+constexpr int RED_PITCH = LG_COLS + 1;       // floats per LDS row of a partial
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int choose_splits(int64_t M, int64_t ncols) {
+  const int64_t strips = (ncols + LG_COLS - 1) / LG_COLS;
+  int64_t s = (512 + strips - 1) / strips;
+  const int64_t smax = M / 256 > 0 ? M / 256 : 1;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return (int)s;
+}
+
+// P[m][poff + j] -> hi/lo bf16 planes Pt[j][m]
+__global__ void split_transpose_kernel(const float* __restrict__ P, int64_t ldp, int poff, int r,
+                                       int64_t M, uint16_t* __restrict__ hi, uint16_t* __restrict__ lo) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M * r) return;
+  const int64_t m = idx / r;
+  const int j = (int)(idx % r);
+  uint32_t h, l;
+  split_bf16(P[m * ldp + poff + j], h, l);
+  hi[(int64_t)j * M + m] = (uint16_t)h;
+  lo[(int64_t)j * M + m] = (uint16_t)l;
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NRT>  // 32-row tiles over the adapter rank r (1..4)
+__global__ void __launch_bounds__(LG_THREADS)
+lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ Plo, int r,
+                 const uint16_t* __restrict__ Q, int64_t M, int64_t ncols, int64_t rows_per_split,
+                 float* __restrict__ out, int64_t out_split_stride) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_qt[LG_WAVES][LG_COLS * QT_PITCH];
+  __shared__ float s_red[LG_WAVES * 32 * RED_PITCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int64_t c0 = (int64_t)blockIdx.x * LG_COLS;
+  const int64_t ms = (int64_t)blockIdx.y * rows_per_split;
+  const int64_t me = min(M, ms + rows_per_split);
+  uint16_t* qt = s_qt[wave];
+
+  v16f acc[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) acc[t] = v16f{};
+
+  for (int64_t mb = ms + (int64_t)wave * LG_CHUNK; mb < me; mb += LG_WAVES * LG_CHUNK) {
+    // Q[mb : mb+64, c0 : c0+32] -> LDS transposed
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = lane + 64 * u, m = t >> 2, q = t & 3;
+      v4i v = {0, 0, 0, 0};
+      if (mb + m < me && c0 + 8 * q < ncols)
+        v = *reinterpret_cast<const v4i*>(Q + (mb + m) * ncols + c0 + 8 * q);
+      const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qt[(8 * q + e) * QT_PITCH + m] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+    wave_sync();
+#pragma unroll
+    for (int ks = 0; ks < LG_CHUNK / 16; ++ks) {
+      const int64_t m = mb + 16 * ks + 8 * lh;   // 8 consecutive tokens of this lane
+      const v8bf bq = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qt + l32 * QT_PITCH + 16 * ks + 8 * lh));
+#pragma unroll
+      for (int t = 0; t < NRT; ++t) {
+        const int j = 32 * t + l32;
+        v4i h = {0, 0, 0, 0}, l = {0, 0, 0, 0};
+        if (j < r && m < me) {   // M and the split bounds are multiples of 16
+          h = *reinterpret_cast<const v4i*>(Phi + (int64_t)j * M + m);
+          l = *reinterpret_cast<const v4i*>(Plo + (int64_t)j * M + m);
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, h), bq, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, l), bq, acc[t], 0, 0, 0);
+      }
+    }
+    wave_sync();
+  }
+
+  // sum the 4 wave partials in a fixed order and store this split's result
+  float* outs = out + (int64_t)blockIdx.y * out_split_stride;
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    float* mine = s_red + wave * 32 * RED_PITCH;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) mine[(8 * (rr >> 2) + 4 * lh + (rr & 3)) * RED_PITCH + l32] = acc[t][rr];
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < (32 * LG_COLS) / LG_THREADS; ++e) {
+      const int idx = e * LG_THREADS + threadIdx.x, row = idx >> 5, col = idx & 31;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < LG_WAVES; ++w) v += s_red[(w * 32 + row) * RED_PITCH + col];
+      const int j = 32 * t + row;
+      if (j < r && c0 + col < ncols) outs[(int64_t)j * ncols + c0 + col] = v;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ void sum_splits_kernel(const float* __restrict__ part, int splits, int64_t n, float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.0f;
+  for (int s = 0; s < splits; ++s) v += part[(int64_t)s * n + i];
+  out[i] = v;
+}
+
+}  // namespace
+
+size_t lora_grad_workspace(int64_t M, int64_t ncols, int r) {
+  if (r == 0 || M == 0 || ncols == 0) return 0;
+  const int S = choose_splits(M, ncols);
+  size_t b = 2 * align256((size_t)r * M * 2);
+  if (S > 1) b += align256((size_t)S * r * ncols * 4);
+  return b;
+}
+
+ft_status launch_lora_grad(const float* P, int64_t ldp, int poff, int r, const uint16_t* Q,
+                           int64_t M, int64_t ncols, float* dW, void* ws, hipStream_t s) {
+  if (r == 0 || ncols == 0) return FT_OK;
+  if (M == 0) return fill_zero_f32(dW, (int64_t)r * ncols, s);
+  const int S = choose_splits(M, ncols);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  uint16_t* hi = reinterpret_cast<uint16_t*>(w);
+  uint16_t* lo = reinterpret_cast<uint16_t*>(w + align256((size_t)r * M * 2));
+  float* part = S > 1 ? reinterpret_cast<float*>(w + 2 * align256((size_t)r * M * 2)) : dW;
+  const int64_t n = M * r;
+  hipLaunchKernelGGL(split_transpose_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P, ldp, poff, r, M, hi, lo);
+  if (launch_status() != FT_OK) return FT_EHIP;
+  // token range per split: a multiple of 64 rows
+  int64_t per = (M + S - 1) / S;
+  per = (per + LG_CHUNK - 1) / LG_CHUNK * LG_CHUNK;
+  const int S_used = (int)((M + per - 1) / per);
+  dim3 grid((unsigned)((ncols + LG_COLS - 1) / LG_COLS), (unsigned)S_used);
+  const int64_t stride = (int64_t)r * ncols;
+  const int nrt = (r + 31) / 32;
+  switch (nrt) {
+    case 1: hipLaunchKernelGGL(lora_grad_kernel<1>, grid, dim3(LG_THREADS), 0, s, hi, lo, r, Q, M, ncols, per, part, stride); break;
+    case 2: hipLaunchKernelGGL(lora_grad_kernel<2>, grid, dim3(LG_THREADS), 0, s, hi, lo, r, Q, M, ncols, per, part, stride); break;
+    case 3: hipLaunchKernelGGL(lora_grad_kernel<3>, grid, dim3(LG_THREADS), 0, s, hi, lo, r, Q, M, ncols, per, part, stride); break;
+    default: hipLaunchKernelGGL(lora_grad_kernel<4>, grid, dim3(LG_THREADS), 0, s, hi, lo, r, Q, M, ncols, per, part, stride); break;
+  }
+  if (launch_status() != FT_OK) return FT_EHIP;
+  if (S > 1) {
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((stride + 255) / 256)), dim3(256), 0, s, part, S_used, stride, dW);
+    return launch_status();
+  }
+  return FT_OK;
+}
+
+}  // namespace ft

@@ -1,0 +1,174 @@
+"""Parity of the HIP triple-branch linear (forward, backward, low-rank, GELU)
+against the fp64 CPU oracle.
+
+Contract tolerance: relative Frobenius error <= 2e-3 for Y, dX, dA, dB (fp32
+outputs).  A tighter precision budget (1e-4) is asserted as well: the 4-bit
+products are exact and accumulate in fp32, and the low-rank intermediates are
+carried as bf16 hi + lo pairs (16 significant bits), so anything above ~1e-5
+indicates a lost term rather than rounding.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_util import dev_bf16, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+BUDGET = 1e-4
+
+
+def _gpu_linear(d, out_dtype=None):
+    """Run quantize -> low-rank -> fwd and quantize -> low-rank -> bwd on the GPU."""
+    import torch
+    from bit_quantized_lora_amd import ops
+    out_dtype = out_dtype or torch.float32
+    X, R, G = dev_bf16(d["X"]), dev_bf16(d["R"]), dev_bf16(d["G"])
+    L1t = dev_bf16(np.ascontiguousarray(d["L1"].T))
+    At = dev_bf16(np.ascontiguousarray(d["A"].T))
+    L2, B = dev_bf16(d["L2"]), dev_bf16(d["B"])
+    M, K = d["X"].shape
+    N = d["R"].shape[0]
+    xq, _, xs = ops.quant_block16(X, rm=True, cm=False)
+    rq, rqc, rsc = ops.quant_block16(R, rm=True, cm=True)
+    T = ops.lowrank_fused(X, L1t, At)
+    Y = ops.linear_fwd(xq, xs, rq, rsc, T, L2, B, M, N, K, out_dtype=out_dtype)
+    gq, _, gs = ops.quant_block16(G, rm=True, cm=False)
+    V = ops.lowrank_fused(G, L2, B)
+    dX, dAt, dB = ops.linear_bwd(gq, gs, rqc, rsc, V, L1t, At, X, G, T, M, N, K, out_dtype=out_dtype)
+    return {"Y": Y, "dX": dX, "dA": dAt, "dB": dB, "T": T, "V": V}
+
+
+def _oracle_rows(d, rows):
+    """Oracle Y and dX restricted to `rows` (a union of 16-row strips), full dA, dB."""
+    f = {k: O.bf16_to_f64(d[k]) for k in ("X", "R", "L1", "L2", "A", "B", "G")}
+    rc, rsc = O.quantize_block16(d["R"])
+    Rhat = O.dequantize(rc, rsc, "pow2")
+    xc, xs = O.quantize_block16(d["X"][rows])
+    gc, gs = O.quantize_block16(d["G"][rows])
+    Xhat, Ghat = O.dequantize(xc, xs, "pow2"), O.dequantize(gc, gs, "pow2")
+    Y = O.linear_fwd(Xhat, Rhat, f["X"][rows], f["L1"], f["L2"], f["A"], f["B"])
+    g = O.linear_bwd(Ghat, Rhat, f["G"][rows], f["X"][rows], f["L1"], f["L2"], f["A"], f["B"])
+    # adapter gradients need every token
+    dB = (f["X"] @ f["A"]).T @ f["G"]
+    dA = f["X"].T @ (f["G"] @ f["B"].T)
+    return {"Y": Y, "dX": g["dX"], "dA": dA.T, "dB": dB}
+
+
+def _compare(gpu, ref, rows, label):
+    errs = {}
+    for k in ("Y", "dX", "dA", "dB"):
+        if ref[k].size == 0:
+            continue
+        got = host(gpu[k]).astype(np.float64)
+        if k in ("Y", "dX"):
+            got = got[rows]
+        errs[k] = O.rel_frob(got, ref[k])
+    say(f"[linear] {label} rel-Frobenius errors: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, e in errs.items():
+        assert e <= TOL, f"{label}: {k} error {e:.3e} above the 2e-3 contract"
+        assert e <= BUDGET, f"{label}: {k} error {e:.3e} above the fp32 precision budget"
+    return errs
+
+
+SMALL = [
+    # (M, K, N, rs, r): several 256-tiles, ragged tails, K % 32 == 16, rank edge cases
+    (256, 256, 256, 16, 16),
+    (144, 400, 272, 16, 16),
+    (528, 176, 48, 32, 0),
+    (48, 48, 48, 0, 16),
+    (80, 528, 304, 64, 64),
+    (16, 16, 16, 0, 0),
+    (272, 1040, 528, 32, 32),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_linear_small_and_ragged(shape):
+    require_gpu()
+    M, K, N, rs, r = shape
+    rng = np.random.default_rng(M * 7 + K * 3 + N)
+    spec = synth.LinearSpec("t", M, K, N, rs, r, x_outlier_count=min(4, K), x_outlier_mult=30.0,
+                            w_outlier_cols=min(2, K), w_outlier_mult=20.0)
+    d = synth.make_linear(spec, rng)
+    say(f"[linear] small {shape}")
+    gpu = _gpu_linear(d)
+    rows = np.arange(M)
+    _compare(gpu, _oracle_rows(d, rows), rows, f"small{shape}")
+
+
+def test_config1_full_and_bf16_and_determinism():
+    require_gpu()
+    import torch
+    d = synth.config_linears("c1")[0]
+    gpu = _gpu_linear(d)
+    rows = np.arange(d["X"].shape[0])
+    _compare(gpu, _oracle_rows(d, rows), rows, "c1")
+    # run twice: identical bits
+    again = _gpu_linear(d)
+    for k in ("Y", "dX", "dA", "dB", "T", "V"):
+        assert np.array_equal(host(gpu[k]).view(np.uint32), host(again[k]).view(np.uint32)), k
+    # bf16 outputs are the round-to-nearest-even of the fp32 outputs
+    gb = _gpu_linear(d, out_dtype=torch.bfloat16)
+    for k in ("Y", "dX"):
+        assert np.array_equal(host(gb[k]), synth.f32_to_bf16_bits(host(gpu[k]))), k
+
+
+def test_lowrank_matches_oracle_products():
+    require_gpu()
+    from bit_quantized_lora_amd import ops
+    for (M, K, ra, rb) in [(48, 400, 16, 16), (4608, 3072, 32, 16), (96, 12288, 64, 64), (32, 16, 0, 32)]:
+        rng = np.random.default_rng(M + K)
+        X = synth.f32_to_bf16_bits(synth.make_tensor(rng, (M, K), "t3"))
+        Wa = synth.f32_to_bf16_bits(synth.make_tensor(rng, (ra, K), "normal", 0.05))
+        Wb = synth.f32_to_bf16_bits(synth.make_tensor(rng, (rb, K), "normal", 0.01))
+        say(f"[lowrank] {M}x{K} ra={ra} rb={rb}")
+        out = host(ops.lowrank_fused(dev_bf16(X), dev_bf16(Wa), dev_bf16(Wb)))
+        Xf = O.bf16_to_f64(X)
+        ref = np.concatenate([Xf @ O.bf16_to_f64(Wa).T, Xf @ O.bf16_to_f64(Wb).T], axis=1)
+        assert O.rel_frob(out, ref) < 1e-5
+
+
+def test_gelu_matches_oracle():
+    require_gpu()
+    from bit_quantized_lora_amd import ops
+    rng = np.random.default_rng(3)
+    y = synth.f32_to_bf16_bits((rng.standard_normal(1 << 16) * 3).astype(np.float32))
+    dh = synth.f32_to_bf16_bits(rng.standard_normal(1 << 16).astype(np.float32))
+    h = host(ops.gelu_fwd(dev_bf16(y)))
+    dy = host(ops.gelu_bwd(dev_bf16(y), dev_bf16(dh)))
+    yv = O.bf16_to_f64(y)
+    ref_h = O.f64_to_bf16_bits(O.gelu(yv))
+    ref_dy = O.f64_to_bf16_bits(O.gelu_grad(yv) * O.bf16_to_f64(dh))
+    # fp32 math vs fp64: the bf16 results agree bit for bit except next to a
+    # rounding boundary (one bf16 ulp) and in the far negative tail where the
+    # value is below ~1e-30 and fp32 underflows (absolute error only)
+    for got, ref in ((h, ref_h), (dy, ref_dy)):
+        g, r = O.bf16_to_f64(got), O.bf16_to_f64(ref)
+        assert np.mean(got == ref) > 0.99
+        assert np.all(np.abs(g - r) <= 2.0 ** -7 * np.abs(r) + 1e-30)
+
+
+def _sample_strips(M, rng, n=6):
+    s = np.unique(np.concatenate([[0, M // 16 - 1], rng.integers(0, M // 16, n)]))
+    return np.concatenate([np.arange(16 * i, 16 * i + 16) for i in s])
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4"])
+def test_full_size_configs_sampled_rows(cfg):
+    """Full-size launches (as the benchmark runs them); Y and dX are checked on
+    sampled 16-row strips against the oracle, dA and dB in full."""
+    require_gpu()
+    for d in synth.config_linears(cfg):
+        spec = d["spec"]
+        if "X" not in d:  # second linear of a pair: a seeded stand-in input of the same shape
+            rng = np.random.default_rng(99)
+            d["X"] = synth.f32_to_bf16_bits(synth.make_tensor(rng, (spec.M, spec.K), "t3"))
+        say(f"[linear] full {spec.name} M={spec.M} K={spec.K} N={spec.N} rs={spec.rs} r={spec.r}")
+        gpu = _gpu_linear(d)
+        rows = _sample_strips(spec.M, np.random.default_rng(spec.M))
+        _compare(gpu, _oracle_rows(d, rows), rows, spec.name)
