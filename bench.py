@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A4G4 triple-branch linear on one MI355X.
+
+One step = the whole hot path of one linear, forward and backward, on the
+FLUX MLP-up shape X[4608 x 3072] -> Y[4608 x 12288] (stabilizer rank 32,
+LoRA rank 16, Student-t activations):
+
+  Q(X) -> T = X [L1 | A] -> Y = Q(X) Q(R)^T + T [L2; B]           (forward)
+  Q(G) -> V = G [L2; B]^T -> dX = Q(G) Q(R) + V [L1 | A]^T,
+                              dA = X^T V_A, dB = T_A^T G           (backward)
+
+Q(R) is prepared once (R is frozen) and is not part of the step.  Inputs are
+resident in HBM before timing starts.  `value` is 4*M*N*K (the fwd + dX 4-bit
+GEMM work; the low-rank FLOPs are not counted) divided by the step time.
+
+Prints one JSON line.  --gpus N with N > 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 (and MXFP6), published
+HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="token rows of the oracle sample")
+    ap.add_argument("--quant-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def make_inputs():
+    import synth
+    spec = synth.CONFIGS["c3"][0]          # the MLP-up linear of the MLP pair config
+    rng = np.random.default_rng(synth.CONFIG_SEED["c3"])
+    d = synth.make_linear(spec, rng)
+    return spec, d
+
+
+class Linear:
+    """Device buffers and the step of one triple-branch linear (all preallocated)."""
+
+    def __init__(self, spec, d):
+        import torch
+        from bit_quantized_lora_amd import ops
+        self.ops = ops
+        M, K, N, rs, r = spec.M, spec.K, spec.N, spec.rs, spec.r
+        self.M, self.K, self.N = M, K, N
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
+        self.X, self.G = dev_bf16(d["X"]), dev_bf16(d["G"])
+        self.L1t = dev_bf16(np.ascontiguousarray(d["L1"].T))
+        self.At = dev_bf16(np.ascontiguousarray(d["A"].T))
+        self.L2, self.B = dev_bf16(d["L2"]), dev_bf16(d["B"])
+        R = dev_bf16(d["R"])
+        # offline: Q(R) in both layouts (R is frozen)
+        self.rq, self.rqc, self.rs_, self.rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
+        del R
+        self.xq = (e((M, K // 2), u8), None, e((M // 16, K // 16), u8))
+        self.gq = (e((M, N // 2), u8), None, e((M // 16, N // 16), u8))
+        self.T, self.V = e((M, rs + r), f32), e((M, rs + r), f32)
+        self.Y, self.dX = e((M, N), bf), e((M, K), bf)
+        self.dAt, self.dB = e((r, K), f32), e((r, N), f32)
+        self.ws = e((max(ops.linear_bwd_workspace(M, N, K, r), 16),), u8)
+
+    def forward(self):
+        o = self.ops
+        o.quant_block16(self.X, out=self.xq)
+        o.lowrank_fused(self.X, self.L1t, self.At, out=self.T)
+        o.linear_fwd(self.xq[0], self.xq[2], self.rq, self.rs_, self.T, self.L2, self.B,
+                     self.M, self.N, self.K, out=self.Y)
+
+    def backward(self):
+        o = self.ops
+        o.quant_block16(self.G, out=self.gq)
+        o.lowrank_fused(self.G, self.L2, self.B, out=self.V)
+        o.linear_bwd(self.gq[0], self.gq[2], self.rqc, self.rsct, self.V, self.L1t, self.At,
+                     self.X, self.G, self.T, self.M, self.N, self.K, workspace=self.ws,
+                     dX=self.dX, dAt=self.dAt, dB=self.dB)
+
+    def step(self):
+        self.forward()
+        self.backward()
+
+
+def time_quantizer(reps):
+    """Standalone quantizer over the QKV-config X [18432 x 3072] and dY [18432 x 9216]
+    (both code layouts), rotating input copies that exceed the 256 MB MALL."""
+    import torch
+    from bit_quantized_lora_amd import ops
+    out = {}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1003)
+    for name, (rows, cols), ncopies in (("X", (18432, 3072), 3), ("dY", (18432, 9216), 2)):
+        xs = [torch.randn(rows, cols, device="cuda", dtype=torch.float32, generator=gen).to(torch.bfloat16)
+              for _ in range(ncopies)]
+        bufs = [ops.quant_block16(x, rm=True, cm=True) for x in xs]
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(3):
+            ops.quant_block16(xs[i % ncopies], rm=True, cm=True, out=bufs[i % ncopies])
+        e0.record(s)
+        for i in range(reps):
+            ops.quant_block16(xs[i % ncopies], rm=True, cm=True, out=bufs[i % ncopies])
+        e1.record(s)
+        e1.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / reps
+        elems = rows * cols
+        alg_bytes = elems * 2 + elems // 2 * 2 + elems // 256   # bf16 in, two code layouts, E8M0 scales
+        out[name] = {"shape": [rows, cols], "us": sec * 1e6, "GBps": alg_bytes / sec / 1e9,
+                     "bytes_per_elem": alg_bytes / elems}
+        del xs, bufs
+    return out
+
+
+def cpu_baseline(spec, d, rows):
+    """The oracle as it stands, on the first `rows` tokens of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    sl = slice(0, rows)
+    f = {k: O.bf16_to_f64(d[k]) for k in ("L1", "L2", "A", "B")}
+    rc, rsc = O.quantize_block16(d["R"])          # offline prep, outside the timed region
+    Rhat = O.dequantize(rc, rsc, "pow2")
+    t0 = time.perf_counter()
+    X = O.bf16_to_f64(d["X"][sl]); G = O.bf16_to_f64(d["G"][sl])
+    xc, xs = O.quantize_block16(d["X"][sl]); gc, gs = O.quantize_block16(d["G"][sl])
+    Xhat, Ghat = O.dequantize(xc, xs, "pow2"), O.dequantize(gc, gs, "pow2")
+    O.linear_fwd(Xhat, Rhat, X, f["L1"], f["L2"], f["A"], f["B"])
+    O.linear_bwd(Ghat, Rhat, G, X, f["L1"], f["L2"], f["A"], f["B"])
+    sec = time.perf_counter() - t0
+    flops = 4.0 * rows * spec.N * spec.K
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, fwd+bwd of the first {rows} of {spec.M} tokens "
+                      f"(K={spec.K}, N={spec.N}), Q(R) prepared outside the timing; {sec:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this build runs the hot path on one GPU only; "
+                                   "multi-GPU runs are not supported"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    spec, d = make_inputs()
+    lin = Linear(spec, d)
+    M, K, N = spec.M, spec.K, spec.N
+    s = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        lin.step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps; events around each forward GEMM launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(s)
+    o = lin.ops
+    for i in range(args.steps):
+        o.quant_block16(lin.X, out=lin.xq)
+        o.lowrank_fused(lin.X, lin.L1t, lin.At, out=lin.T)
+        ev[i][0].record(s)
+        o.linear_fwd(lin.xq[0], lin.xq[2], lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=lin.Y)
+        ev[i][1].record(s)
+        lin.backward()
+    t_end.record(s)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # per-phase breakdown from one extra (untimed-region) step
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    marks[0].record(s)
+    o.quant_block16(lin.X, out=lin.xq); marks[1].record(s)
+    o.lowrank_fused(lin.X, lin.L1t, lin.At, out=lin.T); marks[2].record(s)
+    o.linear_fwd(lin.xq[0], lin.xq[2], lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=lin.Y); marks[3].record(s)
+    o.quant_block16(lin.G, out=lin.gq); marks[4].record(s)
+    o.lowrank_fused(lin.G, lin.L2, lin.B, out=lin.V); marks[5].record(s)
+    o.linear_bwd(lin.gq[0], lin.gq[2], lin.rqc, lin.rsct, lin.V, lin.L1t, lin.At, lin.X, lin.G, lin.T,
+                 M, N, K, workspace=lin.ws, dX=lin.dX, dAt=lin.dAt, dB=lin.dB); marks[6].record(s)
+    torch.cuda.synchronize()
+    names = ["quant_X", "lowrank_X", "fwd_gemm", "quant_G", "lowrank_G", "bwd_gemm_and_adapter_grads"]
+    phases = {n: marks[i].elapsed_time(marks[i + 1]) * 1e3 for i, n in enumerate(names)}
+
+    quant = time_quantizer(args.quant_reps)
+    gemm_flops = 2.0 * M * N * K
+    achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
+    value = 4.0 * M * N * K / (ms_step / 1e3) / 1e12
+    rec = {
+        "metric": "W4A4G4 linear fwd+bwd TFLOPS & % FP4 peak at 4608x3072x12288; quant GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": "W4A4G4 triple-branch linear fwd+bwd, FLUX MLP-up shape",
+                   "M": M, "K": K, "N": N, "stabilizer_rank": spec.rs, "lora_rank": spec.r,
+                   "x_dist": "student-t df=3", "scale_rule": "pow2 (amax/6 rounded up to 2^E)",
+                   "gemm_scale_path": "S2 (one 16-K block per 32-K MFMA fragment)",
+                   "outputs": "bf16 Y and dX, fp32 dA and dB"},
+        "pct_fp4_peak_whole_linear": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
+        "roofline": {"kernel": "gemm_w4a4_kernel (forward)", "bound": "mfma",
+                     "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "per_launch_flops": gemm_flops, "avg_launch_us": round(gemm_ms * 1e3, 2)},
+        "phases_us": {k: round(v, 2) for k, v in phases.items()},
+        "quantizer": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                      for k, v in quant.items()},
+        "quant_GBps": round(quant["dY"]["GBps"], 1),
+        "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(spec, d, args.cpu_rows)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

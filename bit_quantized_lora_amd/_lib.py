@@ -19,7 +19,7 @@ FT_OUT_F32, FT_OUT_BF16 = 0, 1
 
 # name -> argtypes (restype is ft_status = int unless stated)
 _SIGS = {
-    "ft_quant_block16": [c_void_p, c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p],
+    "ft_quant_block16": [c_void_p, c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
     "ft_lowrank_fused": [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p],
     "ft_linear_fwd": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p],

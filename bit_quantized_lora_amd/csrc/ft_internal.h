@@ -7,21 +7,21 @@ namespace ft {
 
 // C[M x N] = deq(A)[M x K] deq(B)[N x K]^T + P[M x (ra+rb)] [Wa; Wb]
 // A, B: packed E2M1 codes, row pitch lda / ldb bytes, reduction index contiguous.
-// scale of A block (mb, kb) = sA[mb * sA_rs + kb]; of B block (nb, kb) = sB[nb * sB_ns + kb * sB_ks]
+// scale of A block (mb, kb) = sA[mb * sA_rs + kb]; of B block (nb, kb) = sB[nb * sB_rs + kb]
 // (E8M0 bytes).  Wa [ra x N], Wb [rb x N] bf16 (row pitch N); P fp32 [M x (ra+rb)].
 struct GemmArgs {
   int64_t M, N, K;
   const uint8_t* A; int64_t lda;
   const uint8_t* B; int64_t ldb;
   const uint8_t* sA; int64_t sA_rs;
-  const uint8_t* sB; int64_t sB_ns, sB_ks;
+  const uint8_t* sB; int64_t sB_rs;
   const float* P;
   const uint16_t* Wa; int ra;
   const uint16_t* Wb; int rb;
   void* C; int64_t ldc;
 };
 
-ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, hipStream_t s);
+ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s);
 
 // dW[j][c] = sum_m P[m][poff + j] Q[m][c] for j < r, c < ncols (reduction over M),
 // P fp32 with row pitch ldp, Q bf16 [M x ncols].  Needs lora_grad_workspace bytes.

@@ -3,162 +3,116 @@
 //   C[m][n] = sum_k deq(A)[m][k] deq(B)[n][k]  +  sum_j P[m][j] W[j][n]
 //
 // forward  (FourTune Eq. 2):  A = Q(X) [M x K], B = Q(R) [N x K], P = T, W = [L2; B]
-// backward (FourTune Eq. 3):  A = Q(G) [M x N], B = Q(R)^T via the column-major
-//                             codes [K x N], P = V, W = [L1^T; A^T]
-// Section 3.2 of the paper: the 16x16 blocks let the transposed product read the
-// same codes and scales "regardless of whether the access pattern is transposed";
-// here the backward pass reads R's column-major codes and the same scale grid
-// through a transposed index.  Section 3.3 "LoRA Fusion": the up-projections
-// are accumulated into the backbone GEMM's accumulators before the single store.
+// backward (FourTune Eq. 3):  A = Q(G) [M x N], B = Q(R)^T [K x N] (R's column-major
+//                             codes and transposed scale grid), P = V, W = [L1^T; A^T]
+// Section 3.2 of the paper: with 16x16 blocks the transposed product reads the
+// same codes and the same block scales, only laid out transposed, so Q(R) is
+// never dequantized or re-quantized.  Section 3.3 "LoRA Fusion": the
+// up-projections are accumulated into the backbone GEMM's accumulators before
+// the single store of C.
 //
 // How 16x16 scales reach the MFMA (scale path "S2"): gfx950's
 // v_mfma_scale_f32_32x32x64_f8f6f4 gives each lane 32 consecutive K values of
 // one row (or column) and ONE power-of-two (E8M0) scale for them.  A 16x16
 // block changes scale every 16 K, so each lane carries exactly one 16-K block
 // in the low half of its 32-slot fragment and zeros in the high half; the two
-// lane halves of the wave carry two different blocks.  The scale is applied by
-// the hardware exactly (power-of-two), so the result is the exact dequantized
-// product accumulated in fp32.  This uses half of each MFMA's K slots.
+// lane halves of the wave carry two different blocks.  The hardware applies the
+// power-of-two scales exactly, so the result is the exact dequantized product
+// accumulated in fp32.  Half of each MFMA's K slots carry data.
 //
 // Tiling: 256 x 256 output tile per workgroup, 4 waves in 2 x 2, each wave
-// 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane).
-// K advances 128 elements (64 bytes of codes per row, 8 blocks) per stage; the
-// codes are double-buffered in LDS with a 16-byte-chunk XOR swizzle so that
-// the fragment reads are conflict-free, and the per-stage 16 x 8 scale tiles
-// of both operands are staged alongside (transposed when B's grid is read
-// transposed).  Epilogue: W's 256-column slice is staged transposed in LDS;
-// P is split into bf16 hi + lo (hi + lo = P to 2^-16) and multiplied on bf16
-// MFMA 32x32x16, so the fp32 low-rank intermediate keeps ~16 significant bits.
+// 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane, in
+// AGPRs).  K advances 128 elements (64 code bytes per row, 8 blocks) per stage.
+//
+// Pipelined kernel (reduction length a multiple of 128): a 4-stage LDS ring
+// filled by buffer_load ... lds (global -> LDS without registers).  Each DMA
+// instruction writes 1 KiB = 16 tile rows contiguously; the 16-byte-chunk XOR
+// swizzle that keeps the fragment reads conflict-free is applied by choosing
+// which global chunk each lane fetches.  Out-of-range rows read as zero (buffer
+// range check).  One barrier per stage; each wave waits only for its own DMA of
+// the stage about to be consumed (explicit vmcnt), keeping 2 stages in flight.
+// Tiles are mapped XCD-aware: consecutive workgroups land on different XCDs, so
+// the linear id is re-grouped such that each XCD works on a compact block of
+// output tiles (shared A/B panels in that XCD's L2).
+//
+// Generic kernel (any multiple-of-16 reduction length): register-staged double
+// buffer with per-chunk bounds checks; used only when K % 128 != 0.
+//
+// Epilogue (both kernels): W's 256-column slice is staged transposed in LDS; P
+// is split into bf16 hi + lo (hi + lo = P to 2^-16 relative) and multiplied on
+// bf16 MFMA 32x32x16, so the fp32 low-rank intermediate keeps ~16 bits.
 #include "ft_common.h"
 #include "ft_internal.h"
 
 namespace ft {
 namespace {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int BM = 256, BN = 256;
 constexpr int BKB = 64;                         // code bytes per row per stage (128 K)
 constexpr int GT = 256;                         // threads
 constexpr int A_ST = BM * BKB, B_ST = BN * BKB;
-constexpr int SA_ST = (BM / 16) * 8, SB_ST = (BN / 16) * 8;
-constexpr int STAGE = A_ST + B_ST + SA_ST + SB_ST;
-constexpr int MAIN_LDS = 2 * STAGE;
+constexpr int S_ST = (BM / 16) * 8 + (BN / 16) * 8;   // A scales [16][8] then B scales [16][8]
+constexpr int STAGE = A_ST + B_ST + S_ST;
+constexpr int NS = 4;                           // pipeline depth (stages)
+constexpr int PIPE_LDS = NS * STAGE;
+constexpr int GEN_LDS = 2 * STAGE;
 constexpr int EPI_LDS = BN * (2 * 128 + 16);
-constexpr int GEMM_LDS = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int PIPE_SMEM = cmax(PIPE_LDS, EPI_LDS);
+constexpr int GEN_SMEM = cmax(GEN_LDS, EPI_LDS);
+constexpr uint32_t RSRC_FLAGS = 0x00020000u;   // raw buffer, 32-bit dword format (gfx9 family)
 
 __device__ __forceinline__ int swz(int row, int q) { return row * BKB + ((q ^ ((row >> 2) & 3)) << 4); }
 
-template <bool OUT_BF16>
-__global__ void __launch_bounds__(GT, 1) gemm_w4a4_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[GEMM_LDS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, lh = lane >> 5;
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt left at their maxima)
+#define FT_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt((((N) & 15) | (((N) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-  const int64_t tiles_m = (g.M + BM - 1) / BM;
-  const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int64_t nkt = (g.K + 127) / 128;
-  const int64_t Mb = g.M / 16, Nb = g.N / 16, Kb = g.K / 16;
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-  // ---- global -> register prefetch of one stage ----
-  v4i pa[4], pb[4];
-  uint8_t ps = 127;
-  auto gload = [&](int64_t kt) {
-    const int64_t k0 = kt * 128;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = it * GT + tid, row = c >> 2, q = c & 3;
-      const int64_t kel = k0 + 32 * q;
-      const int64_t am = m0 + row, bn = n0 + row;
-      v4i va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-      if (kel < g.K) {
-        const bool full = kel + 32 <= g.K;   // else exactly 16 K remain (K % 32 == 16)
-        if (am < g.M) {
-          const uint8_t* p = g.A + am * g.lda + kel / 2;
-          if (full) va = *reinterpret_cast<const v4i*>(p);
-          else { v2i h = *reinterpret_cast<const v2i*>(p); va = v4i{h.x, h.y, 0, 0}; }
-        }
-        if (bn < g.N) {
-          const uint8_t* p = g.B + bn * g.ldb + kel / 2;
-          if (full) vb = *reinterpret_cast<const v4i*>(p);
-          else { v2i h = *reinterpret_cast<const v2i*>(p); vb = v4i{h.x, h.y, 0, 0}; }
-        }
-      }
-      pa[it] = va; pb[it] = vb;
-    }
-    const int t = tid & 127, rb = t >> 3, kb = t & 7;
-    const int64_t gkb = kt * 8 + kb;
-    if (tid < 128) {
-      const int64_t grb = m0 / 16 + rb;
-      ps = (grb < Mb && gkb < Kb) ? g.sA[grb * g.sA_rs + gkb] : (uint8_t)127;
-    } else {
-      const int64_t gnb = n0 / 16 + rb;
-      ps = (gnb < Nb && gkb < Kb) ? g.sB[gnb * g.sB_ns + gkb * g.sB_ks] : (uint8_t)127;
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* As = smem + stage * STAGE;
-    uint8_t* Bs = As + A_ST;
-    uint8_t* Ss = Bs + B_ST;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = it * GT + tid, row = c >> 2, q = c & 3;
-      *reinterpret_cast<v4i*>(As + swz(row, q)) = pa[it];
-      *reinterpret_cast<v4i*>(Bs + swz(row, q)) = pb[it];
-    }
-    Ss[tid] = ps;   // [0,128): A scales [16 rb][8 kb]; [128,256): B scales
-  };
+using Acc = v16f[4][4];
 
-  v16f acc[4][4];
+// 64 MFMAs of one 128-K stage for this wave's 128 x 128 sub-tile.
+__device__ __forceinline__ void mfma_stage(Acc& acc, const uint8_t* st, int wm, int wn, int l32, int lh) {
+  const uint8_t* As = st;
+  const uint8_t* Bs = st + A_ST;
+  const uint8_t* SAs = st + A_ST + B_ST;
+  const uint8_t* SBs = SAs + (BM / 16) * 8;
+  v4i af[4][2], bf[4][2];
+  int sa[4], sb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-
-  if (nkt > 0) {
-    gload(0);
-    lstore(0);
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + 32 * i + l32;
+    af[i][0] = *reinterpret_cast<const v4i*>(As + swz(ra, 2 * lh));
+    af[i][1] = *reinterpret_cast<const v4i*>(As + swz(ra, 2 * lh + 1));
+    sa[i] = *reinterpret_cast<const int*>(SAs + (ra >> 4) * 8 + 4 * lh);
+    const int rbn = wn * 128 + 32 * i + l32;
+    bf[i][0] = *reinterpret_cast<const v4i*>(Bs + swz(rbn, 2 * lh));
+    bf[i][1] = *reinterpret_cast<const v4i*>(Bs + swz(rbn, 2 * lh + 1));
+    sb[i] = *reinterpret_cast<const int*>(SBs + (rbn >> 4) * 8 + 4 * lh);
   }
-  __syncthreads();
-
-  for (int64_t kt = 0; kt < nkt; ++kt) {
-    const int cur = (int)(kt & 1);
-    if (kt + 1 < nkt) gload(kt + 1);
-    const uint8_t* As = smem + cur * STAGE;
-    const uint8_t* Bs = As + A_ST;
-    const uint8_t* SAs = Bs + B_ST;
-    const uint8_t* SBs = SAs + SA_ST;
-    v4i af[4][2], bf[4][2];
-    int sa[4], sb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + 32 * i + l32;
-      af[i][0] = *reinterpret_cast<const v4i*>(As + swz(ra, 2 * lh));
-      af[i][1] = *reinterpret_cast<const v4i*>(As + swz(ra, 2 * lh + 1));
-      sa[i] = *reinterpret_cast<const int*>(SAs + (ra >> 4) * 8 + 4 * lh);
-      const int rbn = wn * 128 + 32 * i + l32;
-      bf[i][0] = *reinterpret_cast<const v4i*>(Bs + swz(rbn, 2 * lh));
-      bf[i][1] = *reinterpret_cast<const v4i*>(Bs + swz(rbn, 2 * lh + 1));
-      sb[i] = *reinterpret_cast<const int*>(SBs + (rbn >> 4) * 8 + 4 * lh);
-    }
+  // k-step KK: each lane's 16-K block (8 code bytes) = bytes [8KK, 8KK+8) of its 32-byte
+  // half row; the E8M0 scale of that block is byte KK of the scale dword (op_sel = KK).
 #define FT_KSTEP(KK)                                                                              \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                               \
-      const v8i aop = {af[i][(KK) >> 1][((KK) & 1) * 2], af[i][(KK) >> 1][((KK) & 1) * 2 + 1], 0, 0, 0, 0, 0, 0}; \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                             \
-        const v8i bop = {bf[j][(KK) >> 1][((KK) & 1) * 2], bf[j][(KK) >> 1][((KK) & 1) * 2 + 1], 0, 0, 0, 0, 0, 0}; \
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[i][j], 4, 4, KK, sa[i], KK, sb[j]); \
-      }                                                                                           \
-    }
-    FT_KSTEP(0)
-    FT_KSTEP(1)
-    FT_KSTEP(2)
-    FT_KSTEP(3)
-#undef FT_KSTEP
-    if (kt + 1 < nkt) lstore(cur ^ 1);
-    __syncthreads();
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
+    const v8i aop = {af[i][(KK) >> 1][((KK) & 1) * 2], af[i][(KK) >> 1][((KK) & 1) * 2 + 1], 0, 0, 0, 0, 0, 0}; \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                               \
+      const v8i bop = {bf[j][(KK) >> 1][((KK) & 1) * 2], bf[j][(KK) >> 1][((KK) & 1) * 2 + 1], 0, 0, 0, 0, 0, 0}; \
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[i][j], 4, 4, KK, sa[i], KK, sb[j]); \
+    }                                                                                             \
   }
+  FT_KSTEP(0)
+  FT_KSTEP(1)
+  FT_KSTEP(2)
+  FT_KSTEP(3)
+#undef FT_KSTEP
+}
 
-  // ---- epilogue: + P W (bf16 hi/lo split of P on bf16 MFMA) ----
+// + P W over the tile, then store C.  smem must be free (callers synchronize first).
+template <bool OUT_BF16>
+__device__ __forceinline__ void epilogue_and_store(Acc& acc, const GemmArgs& g, uint8_t* smem, int64_t m0,
+                                                   int64_t n0, int tid, int wm, int wn, int l32, int lh) {
   const int rho = g.ra + g.rb;
   if (rho > 0) {
     const int pitch = 2 * rho + 16;   // bytes per LDS row of W^T
@@ -210,8 +164,6 @@ __global__ void __launch_bounds__(GT, 1) gemm_w4a4_kernel(GemmArgs g) {
         }
     }
   }
-
-  // ---- store C ----
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -230,16 +182,223 @@ __global__ void __launch_bounds__(GT, 1) gemm_w4a4_kernel(GemmArgs g) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Pipelined kernel (K % 128 == 0)
+// ---------------------------------------------------------------------------------------
+constexpr int GROUP_M = 4;   // tile rows per raster group
+
+// TRANS_B: backward instantiation (B = Q(R)^T); same code, separate name in profiles.
+template <bool OUT_BF16, bool TRANS_B>
+__global__ void __launch_bounds__(GT, 1)
+gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[PIPE_SMEM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lh = lane >> 5;
+
+  // XCD-aware raster: hardware places workgroup b on XCD b % 8
+  const int b = blockIdx.x;
+  const int v = (b & 7) * per_xcd + (b >> 3);
+  if (v >= tiles_m * tiles_n) return;
+  const int grp = v / (GROUP_M * tiles_n);
+  const int first_m = grp * GROUP_M;
+  const int gm = min(GROUP_M, tiles_m - first_m);
+  const int in_grp = v - grp * GROUP_M * tiles_n;
+  const int64_t m0 = (int64_t)(first_m + in_grp % gm) * BM;
+  const int64_t n0 = (int64_t)(in_grp / gm) * BN;
+  const int nkt = (int)(g.K / 128);
+
+  // buffer resources for this tile; rows past M / N fall outside the range and read 0
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.A + m0 * g.lda), 0, (int)(min<int64_t>(BM, g.M - m0) * g.lda), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.B + n0 * g.ldb), 0, (int)(min<int64_t>(BN, g.N - n0) * g.ldb), RSRC_FLAGS);
+  // scale DMA: waves 0-1 fetch A's 16 x 8 scale bytes, waves 2-3 B's (16 dwords each)
+  const bool scale_b = wave >= 2;
+  const __amdgpu_buffer_rsrc_t rS = scale_b
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)(g.sB + (n0 / 16) * g.sB_rs), 0,
+                                          (int)(min<int64_t>(BN / 16, (g.N - n0) / 16) * g.sB_rs), RSRC_FLAGS)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)(g.sA + (m0 / 16) * g.sA_rs), 0,
+                                          (int)(min<int64_t>(BM / 16, (g.M - m0) / 16) * g.sA_rs), RSRC_FLAGS);
+  const int64_t s_rs = scale_b ? g.sB_rs : g.sA_rs;
+
+  // per-lane source offsets: DMA instruction j of this wave fills tile rows
+  // 64*wave + 16*j .. +16; lane l lands at physical chunk l & 3 of row (l >> 2)
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 64 * wave + 16 * j + (lane >> 2);
+    const int q = (lane & 3) ^ ((row >> 2) & 3);
+    offA[j] = (uint32_t)(row * g.lda + 16 * q);
+    offB[j] = (uint32_t)(row * g.ldb + 16 * q);
+  }
+  // lanes 0..15 of each wave: block row 8*(wave&1) + lane/2, blocks 4*(lane&1)..+3
+  const uint32_t offS = (uint32_t)((8 * (wave & 1) + (lane >> 1)) * s_rs + 4 * (lane & 1));
+  const int s_lds = A_ST + B_ST + 64 * wave;   // [0,128): A scales, [128,256): B scales
+
+  // every wave issues exactly 9 DMA instructions per stage
+  auto issue = [&](int stage, int kt) {
+    uint8_t* base = smem + stage * STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + (64 * wave + 16 * j) * BKB), 16,
+                                               offA[j] + (uint32_t)kt * BKB, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(base + A_ST + (64 * wave + 16 * j) * BKB), 16,
+                                               offB[j] + (uint32_t)kt * BKB, 0, 0, 0);
+    if (lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(base + s_lds), 4, offS + (uint32_t)kt * 8, 0, 0, 0);
+  };
+
+  Acc acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nkt) issue(s, s);
+
+  // steady state: stage kt is consumed while stages kt+1 .. kt+NS-1 are in flight.
+  // A wave's DMA of stage kt is complete once at most NS-2 later stages (9 DMAs
+  // each) are pending; the barrier then makes every wave's DMA visible and marks
+  // the buffer of stage kt-1 free for stage kt+NS-1.
+  int kt = 0;
+  for (; kt + NS - 1 < nkt; ++kt) {
+    compiler_fence();
+    FT_WAIT_VMCNT(9 * (NS - 2));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    issue((kt + NS - 1) % NS, kt + NS - 1);
+    mfma_stage(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
+  }
+  // drain: no more DMA to issue
+  for (; kt < nkt; ++kt) {
+    compiler_fence();
+    FT_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    mfma_stage(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
+  }
+  compiler_fence();
+  FT_WAIT_VMCNT(0);
+  __syncthreads();
+  epilogue_and_store<OUT_BF16>(acc, g, smem, m0, n0, tid, wm, wn, l32, lh);
+}
+
+// ---------------------------------------------------------------------------------------
+// Generic kernel (any K multiple of 16)
+// ---------------------------------------------------------------------------------------
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(GT, 1) gemm_w4a4_generic_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[GEN_SMEM];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lh = lane >> 5;
+
+  const int64_t tiles_m = (g.M + BM - 1) / BM;
+  const int64_t m0 = (blockIdx.x % tiles_m) * BM, n0 = (blockIdx.x / tiles_m) * BN;
+  const int64_t nkt = (g.K + 127) / 128;
+  const int64_t Mb = g.M / 16, Nb = g.N / 16, Kb = g.K / 16;
+
+  v4i pa[4], pb[4];
+  uint8_t ps = 127;
+  auto gload = [&](int64_t kt) {
+    const int64_t k0 = kt * 128;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int c = it * GT + tid, row = c >> 2, q = c & 3;
+      const int64_t kel = k0 + 32 * q;
+      const int64_t am = m0 + row, bn = n0 + row;
+      v4i va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
+      if (kel < g.K) {
+        const bool full = kel + 32 <= g.K;   // else exactly 16 K remain (K % 32 == 16)
+        if (am < g.M) {
+          const uint8_t* p = g.A + am * g.lda + kel / 2;
+          if (full) va = *reinterpret_cast<const v4i*>(p);
+          else { v2i h = *reinterpret_cast<const v2i*>(p); va = v4i{h.x, h.y, 0, 0}; }
+        }
+        if (bn < g.N) {
+          const uint8_t* p = g.B + bn * g.ldb + kel / 2;
+          if (full) vb = *reinterpret_cast<const v4i*>(p);
+          else { v2i h = *reinterpret_cast<const v2i*>(p); vb = v4i{h.x, h.y, 0, 0}; }
+        }
+      }
+      pa[it] = va; pb[it] = vb;
+    }
+    const int t = tid & 127, rb = t >> 3, kb = t & 7;
+    const int64_t gkb = kt * 8 + kb;
+    if (tid < 128) {
+      const int64_t grb = m0 / 16 + rb;
+      ps = (grb < Mb && gkb < Kb) ? g.sA[grb * g.sA_rs + gkb] : (uint8_t)127;
+    } else {
+      const int64_t gnb = n0 / 16 + rb;
+      ps = (gnb < Nb && gkb < Kb) ? g.sB[gnb * g.sB_rs + gkb] : (uint8_t)127;
+    }
+  };
+  auto lstore = [&](int stage) {
+    uint8_t* As = smem + stage * STAGE;
+    uint8_t* Bs = As + A_ST;
+    uint8_t* Ss = Bs + B_ST;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int c = it * GT + tid, row = c >> 2, q = c & 3;
+      *reinterpret_cast<v4i*>(As + swz(row, q)) = pa[it];
+      *reinterpret_cast<v4i*>(Bs + swz(row, q)) = pb[it];
+    }
+    Ss[tid] = ps;   // [0,128): A scales [16 rb][8 kb]; [128,256): B scales
+  };
+
+  Acc acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+  if (nkt > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int64_t kt = 0; kt < nkt; ++kt) {
+    const int cur = (int)(kt & 1);
+    if (kt + 1 < nkt) gload(kt + 1);
+    mfma_stage(acc, smem + cur * STAGE, wm, wn, l32, lh);
+    if (kt + 1 < nkt) lstore(cur ^ 1);
+    __syncthreads();
+  }
+  epilogue_and_store<OUT_BF16>(acc, g, smem, m0, n0, tid, wm, wn, l32, lh);
+}
+
 }  // namespace
 
-ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, hipStream_t s) {
+ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return FT_OK;
-  const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if (tiles >= (int64_t)1 << 31) return FT_ESHAPE;
-  if (out_bf16)
-    hipLaunchKernelGGL(gemm_w4a4_kernel<true>, dim3((unsigned)tiles), dim3(GT), 0, s, g);
-  else
-    hipLaunchKernelGGL(gemm_w4a4_kernel<false>, dim3((unsigned)tiles), dim3(GT), 0, s, g);
+  const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;
+  const dim3 block(GT);
+  const bool pipelined = g.K > 0 && g.K % 128 == 0 && BM * g.lda < ((int64_t)1 << 31) &&
+                         BN * g.ldb < ((int64_t)1 << 31);
+  if (pipelined) {
+    const int per_xcd = (int)((tiles + 7) / 8);
+    const dim3 grid((unsigned)(8 * per_xcd));
+    const int tm = (int)tiles_m, tn = (int)tiles_n;
+    if (out_bf16) {
+      if (trans_b) hipLaunchKernelGGL((gemm_w4a4_kernel<true, true>), grid, block, 0, s, g, tm, tn, per_xcd);
+      else hipLaunchKernelGGL((gemm_w4a4_kernel<true, false>), grid, block, 0, s, g, tm, tn, per_xcd);
+    } else {
+      if (trans_b) hipLaunchKernelGGL((gemm_w4a4_kernel<false, true>), grid, block, 0, s, g, tm, tn, per_xcd);
+      else hipLaunchKernelGGL((gemm_w4a4_kernel<false, false>), grid, block, 0, s, g, tm, tn, per_xcd);
+    }
+  } else {
+    const dim3 grid((unsigned)tiles);
+    if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g);
+  }
   return launch_status();
 }
 

@@ -34,12 +34,12 @@ extern "C" ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
   g.A = xq_codes; g.lda = K / 2;
   g.B = rq_codes; g.ldb = K / 2;
   g.sA = static_cast<const uint8_t*>(xq_scales); g.sA_rs = K / 16;
-  g.sB = static_cast<const uint8_t*>(rq_scales); g.sB_ns = K / 16; g.sB_ks = 1;
+  g.sB = static_cast<const uint8_t*>(rq_scales); g.sB_rs = K / 16;
   g.P = T;
   g.Wa = static_cast<const uint16_t*>(L2); g.ra = rs;
   g.Wb = static_cast<const uint16_t*>(B); g.rb = r;
   g.C = Y; g.ldc = N;
-  return launch_gemm_w4a4(g, ydt == FT_OUT_BF16, stream);
+  return launch_gemm_w4a4(g, ydt == FT_OUT_BF16, false, stream);
 }
 
 extern "C" size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r) {
@@ -50,7 +50,7 @@ extern "C" size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32
 
 extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
                                    const uint8_t* gq_codes, const void* gq_scales,
-                                   const uint8_t* rq_codes_cm, const void* rq_scales,
+                                   const uint8_t* rq_codes_cm, const void* rq_scales_cm,
                                    const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
                                    const void* X, const void* G, const float* T,
                                    void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
@@ -63,7 +63,7 @@ extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
   const int rho = rs + r;
   const size_t need = ft_linear_bwd_workspace(M, N, K, r);
   if (M && K && !dX) return FT_EINVAL;
-  if (M && N && K && (!gq_codes || !gq_scales || !rq_codes_cm || !rq_scales)) return FT_EINVAL;
+  if (M && N && K && (!gq_codes || !gq_scales || !rq_codes_cm || !rq_scales_cm)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
   if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
@@ -73,19 +73,19 @@ extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
     if (p && !aligned16(p)) return FT_EALIGN;
 
   // dX = deq(Gq) deq(Rq) + V [L1^T; A^T]: GEMM over the output features N, with
-  // R's column-major codes as the B operand and R's scale grid read transposed.
+  // R's column-major codes and transposed scale grid as the B operand.
   if (M && K) {
     GemmArgs g{};
     g.M = M; g.N = K; g.K = N;
     g.A = gq_codes; g.lda = N / 2;
     g.B = rq_codes_cm; g.ldb = N / 2;
     g.sA = static_cast<const uint8_t*>(gq_scales); g.sA_rs = N / 16;
-    g.sB = static_cast<const uint8_t*>(rq_scales); g.sB_ns = 1; g.sB_ks = K / 16;
+    g.sB = static_cast<const uint8_t*>(rq_scales_cm); g.sB_rs = N / 16;
     g.P = V;
     g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
     g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
     g.C = dX; g.ldc = K;
-    ft_status st = launch_gemm_w4a4(g, dxdt == FT_OUT_BF16, stream);
+    ft_status st = launch_gemm_w4a4(g, dxdt == FT_OUT_BF16, true, stream);
     if (st != FT_OK) return st;
   }
   if (r) {

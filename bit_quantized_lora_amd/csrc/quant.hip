@@ -68,7 +68,7 @@ template <bool POW2, bool WRITE_RM, bool WRITE_CM>
 __global__ void __launch_bounds__(QTHREADS)
 quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
                      uint8_t* __restrict__ codes_rm, uint8_t* __restrict__ codes_cm,
-                     void* __restrict__ scales) {
+                     void* __restrict__ scales, void* __restrict__ scales_cm) {
   __shared__ __attribute__((aligned(16))) uint8_t s_in[QT * IN_PITCH];
   __shared__ __attribute__((aligned(16))) uint8_t s_rm[WRITE_RM ? QT * RM_PITCH : 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_cm[WRITE_CM ? QT * CM_PITCH : 16];
@@ -125,6 +125,8 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
 #undef FT_CVT
       if (live && i == 0) {
         static_cast<uint8_t*>(scales)[(row0 / 16 + br) * (cols / 16) + col0 / 16 + bc] = (uint8_t)(E + 127);
+        if (scales_cm)
+          static_cast<uint8_t*>(scales_cm)[(col0 / 16 + bc) * (rows / 16) + row0 / 16 + br] = (uint8_t)(E + 127);
       }
     } else {
       const float amax = __builtin_bit_cast(float, m << 16);
@@ -143,6 +145,7 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
 #undef FT_CVT
       if (live && i == 0) {
         static_cast<float*>(scales)[(row0 / 16 + br) * (cols / 16) + col0 / 16 + bc] = s;
+        if (scales_cm) static_cast<float*>(scales_cm)[(col0 / 16 + bc) * (rows / 16) + row0 / 16 + br] = s;
       }
     }
     if constexpr (WRITE_RM) {
@@ -180,15 +183,15 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
 
 template <bool POW2>
 ft_status launch_quant(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* rm,
-                       uint8_t* cm, void* scales, hipStream_t s) {
+                       uint8_t* cm, void* scales, void* scales_cm, hipStream_t s) {
   dim3 grid((unsigned)((cols + QT - 1) / QT), (unsigned)((rows + QT - 1) / QT));
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   if (rm && cm)
-    hipLaunchKernelGGL((quant_block16_kernel<POW2, true, true>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales);
+    hipLaunchKernelGGL((quant_block16_kernel<POW2, true, true>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales, scales_cm);
   else if (rm)
-    hipLaunchKernelGGL((quant_block16_kernel<POW2, true, false>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales);
+    hipLaunchKernelGGL((quant_block16_kernel<POW2, true, false>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales, scales_cm);
   else
-    hipLaunchKernelGGL((quant_block16_kernel<POW2, false, true>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales);
+    hipLaunchKernelGGL((quant_block16_kernel<POW2, false, true>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales, scales_cm);
   return launch_status();
 }
 
@@ -197,18 +200,19 @@ ft_status launch_quant(const void* x, int64_t rows, int64_t cols, int64_t ldx, u
 
 extern "C" ft_status ft_quant_block16(const void* x, int64_t rows, int64_t cols, int64_t ldx,
                                       ft_scale_mode mode, uint8_t* codes_rm, uint8_t* codes_cm,
-                                      void* scales, hipStream_t stream) {
+                                      void* scales, void* scales_cm, hipStream_t stream) {
   using namespace ft;
   if (mode != FT_SCALE_POW2 && mode != FT_SCALE_F32) return FT_EINVAL;
   if (!mult16(rows) || !mult16(cols) || ldx < cols) return FT_ESHAPE;
   if (rows == 0 || cols == 0) return FT_OK;
   if (!x || !scales || (!codes_rm && !codes_cm)) return FT_EINVAL;
   if (!aligned16(x) || (ldx % 8) != 0) return FT_EALIGN;
-  if ((codes_rm && !aligned16(codes_rm)) || (codes_cm && !aligned16(codes_cm)) || !aligned16(scales))
+  if ((codes_rm && !aligned16(codes_rm)) || (codes_cm && !aligned16(codes_cm)) || !aligned16(scales) ||
+      (scales_cm && !aligned16(scales_cm)))
     return FT_EALIGN;
   if (rows / QT >= 65535) return FT_ESHAPE;
-  return mode == FT_SCALE_POW2 ? launch_quant<true>(x, rows, cols, ldx, codes_rm, codes_cm, scales, stream)
-                               : launch_quant<false>(x, rows, cols, ldx, codes_rm, codes_cm, scales, stream);
+  return mode == FT_SCALE_POW2 ? launch_quant<true>(x, rows, cols, ldx, codes_rm, codes_cm, scales, scales_cm, stream)
+                               : launch_quant<false>(x, rows, cols, ldx, codes_rm, codes_cm, scales, scales_cm, stream);
 }
 
 extern "C" const char* ft_status_str(ft_status s) {

@@ -33,21 +33,33 @@ def _need(t: torch.Tensor, dtype, name: str) -> None:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def quant_block16(x: torch.Tensor, mode: str = "pow2", rm: bool = True, cm: bool = False
-                  ) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor], torch.Tensor]:
-    """Q(x) for a bf16 [rows, cols] matrix -> (codes_rm, codes_cm, scales)."""
+def quant_block16(x: torch.Tensor, mode: str = "pow2", rm: bool = True, cm: bool = False,
+                  out: Optional[Tuple] = None, scales_cm: bool = False):
+    """Q(x) for a bf16 [rows, cols] matrix -> (codes_rm, codes_cm, scales), plus
+    the transposed scale grid as a fourth element when ``scales_cm`` is set.
+
+    ``out`` may supply preallocated (codes_rm, codes_cm, scales[, scales_cm]) buffers.
+    """
     _need(x, torch.bfloat16, "x")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D matrix with unit column stride")
     rows, cols = x.shape
     dev = x.device
-    codes_rm = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if rm else None
-    codes_cm = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev) if cm else None
     sdt = torch.uint8 if mode == "pow2" else torch.float32
-    scales = torch.empty((rows // 16, cols // 16), dtype=sdt, device=dev)
+    if out is not None:
+        codes_rm, codes_cm, scales = out[:3]
+        sc_cm = out[3] if len(out) > 3 else None
+    else:
+        codes_rm = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev) if rm else None
+        codes_cm = torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev) if cm else None
+        scales = torch.empty((rows // 16, cols // 16), dtype=sdt, device=dev)
+        sc_cm = torch.empty((cols // 16, rows // 16), dtype=sdt, device=dev) if scales_cm else None
     st = lib().ft_quant_block16(x.data_ptr(), rows, cols, x.stride(0), _MODES[mode],
-                                _ptr(codes_rm), _ptr(codes_cm), scales.data_ptr(), _stream(x))
+                                _ptr(codes_rm), _ptr(codes_cm), scales.data_ptr(), _ptr(sc_cm),
+                                _stream(x))
     check("ft_quant_block16", st)
+    if sc_cm is not None:
+        return codes_rm, codes_cm, scales, sc_cm
     return codes_rm, codes_cm, scales
 
 
@@ -87,21 +99,24 @@ def linear_bwd_workspace(M: int, N: int, K: int, r: int) -> int:
     return int(lib().ft_linear_bwd_workspace(M, N, K, r))
 
 
-def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales, V, L1t, At, X, G, T,
+def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G, T,
                M: int, N: int, K: int, out_dtype=torch.float32, mode: str = "pow2",
-               workspace: Optional[torch.Tensor] = None, dX: Optional[torch.Tensor] = None):
+               workspace: Optional[torch.Tensor] = None, dX: Optional[torch.Tensor] = None,
+               dAt: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None):
     """dX, dAt, dB of Eq. 3 and section 3.2 (see include/ft.h)."""
     rs, r = L1t.shape[0], At.shape[0]
     dev = V.device
     if dX is None:
         dX = torch.empty((M, K), dtype=out_dtype, device=dev)
-    dAt = torch.empty((r, K), dtype=torch.float32, device=dev)
-    dB = torch.empty((r, N), dtype=torch.float32, device=dev)
+    if dAt is None:
+        dAt = torch.empty((r, K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((r, N), dtype=torch.float32, device=dev)
     ws_bytes = linear_bwd_workspace(M, N, K, r)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
     st = lib().ft_linear_bwd(M, N, K, _MODES[mode], gq_codes.data_ptr(), gq_scales.data_ptr(),
-                             rq_codes_cm.data_ptr(), rq_scales.data_ptr(), V.data_ptr(),
+                             rq_codes_cm.data_ptr(), rq_scales_cm.data_ptr(), V.data_ptr(),
                              L1t.data_ptr(), rs, At.data_ptr(), r, X.data_ptr(), G.data_ptr(),
                              T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype], dAt.data_ptr(),
                              dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(V))

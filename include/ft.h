@@ -81,11 +81,13 @@ typedef enum { FT_OUT_F32 = 0, FT_OUT_BF16 = 1 } ft_out_dtype;
  *            element (i, j) in byte j*rows/2 + i/2, even i in the low nibble.
  *            (The codes of X^T: what the transposed GEMM of Eq. 3 reads.)
  *  scales    out: [rows/16 x cols/16] row-major, uint8 E8M0 (POW2) or float (F32).
+ *  scales_cm out, may be NULL: the same scale grid stored transposed,
+ *            [cols/16 x rows/16]; (codes_cm, scales_cm) is Q(x^T) in row-major form.
  *  At least one of codes_rm, codes_cm must be non-NULL.  Input and outputs
  *  must not overlap.  Codes and scales are bit-exact functions of x. */
 ft_status ft_quant_block16(const void* x, int64_t rows, int64_t cols, int64_t ldx,
                            ft_scale_mode mode, uint8_t* codes_rm, uint8_t* codes_cm,
-                           void* scales, hipStream_t stream);
+                           void* scales, void* scales_cm, hipStream_t stream);
 
 /* ft_lowrank_fused -- the shared down-projection of the two low-rank branches
  * (section 3.3 "LoRA Fusion": both branches read the same input, so one pass
@@ -129,7 +131,8 @@ ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
  *
  *  gq_codes     row-major codes of G [M x N/2], gq_scales [M/16 x N/16]
  *  rq_codes_cm  column-major codes of R [K x N/2] (ft_quant_block16 codes_cm of R)
- *  rq_scales    [N/16 x K/16], the same scale grid the forward uses
+ *  rq_scales_cm R's scale grid transposed, [K/16 x N/16] (ft_quant_block16
+ *               scales_cm of R): the forward's block scales, read transposed
  *  V            float [M x (rs+r)] from ft_lowrank_fused(G, L2, B)
  *  L1t [rs x K], At [r x K] bf16
  *  X  bf16 [M x K], G bf16 [M x N] (unquantized), T float [M x (rs+r)] (forward)
@@ -138,7 +141,7 @@ ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
  *             bytes (partial sums of the reductions over M). */
 ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
                         const uint8_t* gq_codes, const void* gq_scales,
-                        const uint8_t* rq_codes_cm, const void* rq_scales,
+                        const uint8_t* rq_codes_cm, const void* rq_scales_cm,
                         const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
                         const void* X, const void* G, const float* T,
                         void* dX, ft_out_dtype dxdt, float* dAt, float* dB,

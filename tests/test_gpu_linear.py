@@ -34,12 +34,12 @@ def _gpu_linear(d, out_dtype=None):
     M, K = d["X"].shape
     N = d["R"].shape[0]
     xq, _, xs = ops.quant_block16(X, rm=True, cm=False)
-    rq, rqc, rsc = ops.quant_block16(R, rm=True, cm=True)
+    rq, rqc, rsc, rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
     T = ops.lowrank_fused(X, L1t, At)
     Y = ops.linear_fwd(xq, xs, rq, rsc, T, L2, B, M, N, K, out_dtype=out_dtype)
     gq, _, gs = ops.quant_block16(G, rm=True, cm=False)
     V = ops.lowrank_fused(G, L2, B)
-    dX, dAt, dB = ops.linear_bwd(gq, gs, rqc, rsc, V, L1t, At, X, G, T, M, N, K, out_dtype=out_dtype)
+    dX, dAt, dB = ops.linear_bwd(gq, gs, rqc, rsct, V, L1t, At, X, G, T, M, N, K, out_dtype=out_dtype)
     return {"Y": Y, "dX": dX, "dA": dAt, "dB": dB, "T": T, "V": V}
 
 
@@ -84,6 +84,12 @@ SMALL = [
     (80, 528, 304, 64, 64),
     (16, 16, 16, 0, 0),
     (272, 1040, 528, 32, 32),
+    # reduction lengths that are multiples of 128 (pipelined GEMM path, fwd and bwd),
+    # with ragged M / N tiles and 1..9 pipeline stages
+    (272, 384, 512, 16, 16),
+    (48, 128, 128, 0, 16),
+    (528, 256, 640, 32, 32),
+    (304, 1152, 384, 16, 16),
 ]
 
 

@@ -13,9 +13,11 @@ def _check(bits, mode, label):
     from bit_quantized_lora_amd import ops
     say(f"[quant] {label} {bits.shape} mode={mode}")
     x = dev_bf16(bits)
-    rm, cm, sc = ops.quant_block16(x, mode=mode, rm=True, cm=True)
+    rm, cm, sc, sct = ops.quant_block16(x, mode=mode, rm=True, cm=True, scales_cm=True)
     codes, scales = O.quantize_block16(bits, mode)
     got_rm, got_cm, got_sc = host(rm), host(cm), host(sc)
+    # the transposed scale grid is the same grid, transposed (Q(x^T) = Q(x)^T)
+    assert np.array_equal(host(sct), got_sc.T), f"{label}: transposed scale grid differs"
     assert np.array_equal(got_rm, O.pack_rm(codes)), f"{label}: row-major codes differ"
     assert np.array_equal(got_cm, O.pack_cm(codes)), f"{label}: column-major codes differ"
     if mode == "pow2":
