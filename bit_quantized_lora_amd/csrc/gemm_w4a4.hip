@@ -20,9 +20,10 @@
 // power-of-two scales exactly, so the result is the exact dequantized product
 // accumulated in fp32.  Half of each MFMA's K slots carry data.
 //
-// Tiling: 256 x 256 output tile per workgroup, 4 waves in 2 x 2, each wave
-// 128 x 128 = 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per lane, in
-// AGPRs).  K advances 128 elements (64 code bytes per row, 8 blocks) per stage.
+// Tiling: 256 x 256 output tile per workgroup.  Pipelined kernel: 8 waves in
+// 4 x 2 (two per SIMD, so one wave's LDS or barrier wait overlaps the other's
+// MFMAs), each 64 x 128 = 2 x 4 MFMA tiles of 32 x 32.  Generic kernel: 4 waves
+// of 128 x 128.  K advances 128 elements (64 code bytes per row, 8 blocks) per stage.
 //
 // Pipelined kernel (reduction length a multiple of 128): a 4-stage LDS ring
 // filled by buffer_load ... lds (global -> LDS without registers).  Each DMA
@@ -48,17 +49,20 @@ namespace ft {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr int BM = 256, BN = 256;
 constexpr int BKB = 64;                         // code bytes per row per stage (128 K)
-constexpr int GT = 256;                         // threads
+constexpr int GT = 256;                         // threads, generic kernel (4 waves, 128 x 128 each)
+constexpr int PGT = 512;                        // threads, pipelined kernel (8 waves, 64 x 128 each)
 constexpr int A_ST = BM * BKB, B_ST = BN * BKB;
 constexpr int S_ST = (BM / 16) * 8 + (BN / 16) * 8;   // A scales [16][8] then B scales [16][8]
 constexpr int STAGE = A_ST + B_ST + S_ST;
 constexpr int NS = 4;                           // pipeline depth (stages)
 constexpr int PIPE_LDS = NS * STAGE;
 constexpr int GEN_LDS = 2 * STAGE;
-constexpr int EPI_LDS = BN * (2 * 128 + 16);
+constexpr int EPI_LDS = 64 * 544;               // W chunk of the epilogue (64 ranks)
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int PIPE_SMEM = cmax(PIPE_LDS, EPI_LDS);
 constexpr int GEN_SMEM = cmax(GEN_LDS, EPI_LDS);
@@ -71,22 +75,27 @@ __device__ __forceinline__ int swz(int row, int q) { return row * BKB + ((q ^ ((
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-using Acc = v16f[4][4];
+template <int TMI>
+using AccT = v16f[TMI][4];
 
-// 64 MFMAs of one 128-K stage for this wave's 128 x 128 sub-tile.
-__device__ __forceinline__ void mfma_stage(Acc& acc, const uint8_t* st, int wm, int wn, int l32, int lh) {
+// One 128-K stage for this wave's (32*TMI) x 128 sub-tile (16*TMI MFMAs per k-step).
+template <int TMI>
+__device__ __forceinline__ void mfma_stage(AccT<TMI>& acc, const uint8_t* st, int wm, int wn, int l32, int lh) {
   const uint8_t* As = st;
   const uint8_t* Bs = st + A_ST;
   const uint8_t* SAs = st + A_ST + B_ST;
   const uint8_t* SBs = SAs + (BM / 16) * 8;
-  v4i af[4][2], bf[4][2];
-  int sa[4], sb[4];
+  v4i af[TMI][2], bf[4][2];
+  int sa[TMI], sb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ra = wm * 128 + 32 * i + l32;
+  for (int i = 0; i < TMI; ++i) {
+    const int ra = wm * 32 * TMI + 32 * i + l32;
     af[i][0] = *reinterpret_cast<const v4i*>(As + swz(ra, 2 * lh));
     af[i][1] = *reinterpret_cast<const v4i*>(As + swz(ra, 2 * lh + 1));
     sa[i] = *reinterpret_cast<const int*>(SAs + (ra >> 4) * 8 + 4 * lh);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
     const int rbn = wn * 128 + 32 * i + l32;
     bf[i][0] = *reinterpret_cast<const v4i*>(Bs + swz(rbn, 2 * lh));
     bf[i][1] = *reinterpret_cast<const v4i*>(Bs + swz(rbn, 2 * lh + 1));
@@ -95,7 +104,7 @@ __device__ __forceinline__ void mfma_stage(Acc& acc, const uint8_t* st, int wm, 
   // k-step KK: each lane's 16-K block (8 code bytes) = bytes [8KK, 8KK+8) of its 32-byte
   // half row; the E8M0 scale of that block is byte KK of the scale dword (op_sel = KK).
 #define FT_KSTEP(KK)                                                                              \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                 \
+  _Pragma("unroll") for (int i = 0; i < TMI; ++i) {                                                 \
     const v8i aop = {af[i][(KK) >> 1][((KK) & 1) * 2], af[i][(KK) >> 1][((KK) & 1) * 2 + 1], 0, 0, 0, 0, 0, 0}; \
     _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                               \
       const v8i bop = {bf[j][(KK) >> 1][((KK) & 1) * 2], bf[j][(KK) >> 1][((KK) & 1) * 2 + 1], 0, 0, 0, 0, 0, 0}; \
@@ -110,68 +119,110 @@ __device__ __forceinline__ void mfma_stage(Acc& acc, const uint8_t* st, int wm, 
 }
 
 // + P W over the tile, then store C.  smem must be free (callers synchronize first).
-template <bool OUT_BF16>
-__device__ __forceinline__ void epilogue_and_store(Acc& acc, const GemmArgs& g, uint8_t* smem, int64_t m0,
-                                                   int64_t n0, int tid, int wm, int wn, int l32, int lh) {
+//
+// W rows (rank-major, [rho x N]) are copied to LDS with buffer_load ... lds, one
+// 512-byte row per DMA instruction at a 544-byte pitch (bank-conflict-free for the
+// transposed reads below).  The bf16 MFMA's B operand needs 8 consecutive ranks of
+// one output column per lane; two ds_read_b64_tr_b16 deliver them: within each
+// 16-lane group, result lane i, slot r receives element i % 4 of the 8 bytes that
+// source lane 4r + i/4 addressed, so source lanes point 4 columns wide into 4
+// consecutive rows.  P's rows for up to 64 ranks are fetched with all loads in
+// flight at once; ranks beyond 64 are processed in a second chunk.
+constexpr int W_PITCH = 544;
+constexpr int EPI_CHUNK = 64;
+
+template <bool OUT_BF16, int TMI, int NWAVES>
+__device__ __forceinline__ void epilogue_and_store(AccT<TMI>& acc, const GemmArgs& g, uint8_t* smem, int64_t m0,
+                                                   int64_t n0, int tid, int wave, int wm, int wn, int l32,
+                                                   int lh) {
+  const int lane = tid & 63;
   const int rho = g.ra + g.rb;
   if (rho > 0) {
-    const int pitch = 2 * rho + 16;   // bytes per LDS row of W^T
-    for (int c = tid; c < rho * (BN / 8); c += GT) {
-      const int j = c / (BN / 8), q = c % (BN / 8);
-      const int64_t n = n0 + 8 * q;
-      v4i v = {0, 0, 0, 0};
-      if (n < g.N) {
-        const uint16_t* wrow = j < g.ra ? g.Wa + (int64_t)j * g.N : g.Wb + (int64_t)(j - g.ra) * g.N;
-        v = *reinterpret_cast<const v4i*>(wrow + n);
-      }
-      const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(smem + (8 * q + e) * pitch + 2 * j) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-    }
-    __syncthreads();
-    for (int ks = 0; ks < rho / 16; ++ks) {
-      v8bf phi[4], plo[4], wf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = m0 + wm * 128 + 32 * i + l32;
-        const int col = 16 * ks + 8 * lh;
-        v4f p0 = {0, 0, 0, 0}, p1 = {0, 0, 0, 0};
-        if (row < g.M) {
-          p0 = *reinterpret_cast<const v4f*>(g.P + row * rho + col);
-          p1 = *reinterpret_cast<const v4f*>(g.P + row * rho + col + 4);
+    const __amdgpu_buffer_rsrc_t rWa =
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.Wa, 0, (int)((int64_t)g.ra * g.N * 2), RSRC_FLAGS);
+    const __amdgpu_buffer_rsrc_t rWb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.Wb, 0, (int)((int64_t)g.rb * g.N * 2), RSRC_FLAGS);
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);             // + 16 ks + 4 t
+    const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn*128 + 32 j
+    for (int jc = 0; jc < rho; jc += EPI_CHUNK) {
+      const int nr = min(EPI_CHUNK, rho - jc);                   // multiple of 16
+      // (a) W rows jc .. jc+nr-1 -> LDS (lanes 0..31: 16 bytes = 8 columns each)
+      for (int jr = wave; jr < nr; jr += NWAVES) {
+        const int j = jc + jr;
+        const bool in_a = j < g.ra;
+        const int jj = in_a ? j : j - g.ra;
+        const int64_t n = n0 + 8 * lane;
+        const uint32_t off = (lane < 32 && n < g.N) ? (uint32_t)(((int64_t)jj * g.N + n) * 2) : 0x80000000u;
+        if (lane < 32) {
+          if (in_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(rWa, (lds_void*)(smem + jr * W_PITCH), 16, off, 0, 0, 0);
+          else __builtin_amdgcn_raw_ptr_buffer_load_lds(rWb, (lds_void*)(smem + jr * W_PITCH), 16, off, 0, 0, 0);
         }
-        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        uint32_t h[8], l[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) split_bf16(pv[e], h[e], l[e]);
-        v4i hv = {(int)(h[0] | h[1] << 16), (int)(h[2] | h[3] << 16), (int)(h[4] | h[5] << 16), (int)(h[6] | h[7] << 16)};
-        v4i lv = {(int)(l[0] | l[1] << 16), (int)(l[2] | l[3] << 16), (int)(l[4] | l[5] << 16), (int)(l[6] | l[7] << 16)};
-        phi[i] = __builtin_bit_cast(v8bf, hv);
-        plo[i] = __builtin_bit_cast(v8bf, lv);
       }
+      // (b) P[rows][jc .. jc+nr) for this wave's 4 row tiles, every load in flight
+      v4f p[TMI][EPI_CHUNK / 16][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int nl = wn * 128 + 32 * j + l32;
-        wf[j] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(smem + nl * pitch + 2 * (16 * ks + 8 * lh)));
-      }
+      for (int i = 0; i < TMI; ++i) {
+        const int64_t row = m0 + wm * 32 * TMI + 32 * i + l32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi[i], wf[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo[i], wf[j], acc[i][j], 0, 0, 0);
+        for (int ks = 0; ks < EPI_CHUNK / 16; ++ks) {
+          p[i][ks][0] = p[i][ks][1] = v4f{0, 0, 0, 0};
+          if (16 * ks < nr && row < g.M) {
+            const float* src = g.P + row * rho + jc + 16 * ks + 8 * lh;
+            p[i][ks][0] = *reinterpret_cast<const v4f*>(src);
+            p[i][ks][1] = *reinterpret_cast<const v4f*>(src + 4);
+          }
         }
+      }
+      compiler_fence();
+      FT_WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      // (c) acc += (P_hi + P_lo) W on bf16 MFMA 32x32x16
+#pragma unroll
+      for (int ks = 0; ks < EPI_CHUNK / 16; ++ks) {
+        if (16 * ks < nr) {
+          v8bf wf[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint8_t* b0 = smem + (16 * ks + tr_row) * W_PITCH + 2 * (wn * 128 + 32 * j + tr_col);
+            const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0));
+            const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + 4 * W_PITCH));
+            const v2i l2 = __builtin_bit_cast(v2i, lo4), h2 = __builtin_bit_cast(v2i, hi4);
+            wf[j] = __builtin_bit_cast(v8bf, v4i{l2.x, l2.y, h2.x, h2.y});
+          }
+#pragma unroll
+          for (int i = 0; i < TMI; ++i) {
+            const float pv[8] = {p[i][ks][0].x, p[i][ks][0].y, p[i][ks][0].z, p[i][ks][0].w,
+                                 p[i][ks][1].x, p[i][ks][1].y, p[i][ks][1].z, p[i][ks][1].w};
+            uint32_t h[8], l[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) split_bf16(pv[e], h[e], l[e]);
+            const v8bf phi = __builtin_bit_cast(v8bf, v4i{(int)(h[0] | h[1] << 16), (int)(h[2] | h[3] << 16),
+                                                          (int)(h[4] | h[5] << 16), (int)(h[6] | h[7] << 16)});
+            const v8bf plo = __builtin_bit_cast(v8bf, v4i{(int)(l[0] | l[1] << 16), (int)(l[2] | l[3] << 16),
+                                                          (int)(l[4] | l[5] << 16), (int)(l[6] | l[7] << 16)});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi, wf[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo, wf[j], acc[i][j], 0, 0, 0);
+            }
+          }
+        }
+      }
+      compiler_fence();
+      __builtin_amdgcn_s_barrier();   // LDS free for the next chunk
+      compiler_fence();
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TMI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t col = n0 + wn * 128 + 32 * j + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int64_t row = m0 + wm * 32 * TMI + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
         if (row < g.M && col < g.N) {
           if constexpr (OUT_BF16)
             static_cast<uint16_t*>(g.C)[row * g.ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
@@ -189,12 +240,12 @@ constexpr int GROUP_M = 4;   // tile rows per raster group
 
 // TRANS_B: backward instantiation (B = Q(R)^T); same code, separate name in profiles.
 template <bool OUT_BF16, bool TRANS_B>
-__global__ void __launch_bounds__(GT, 1)
+__global__ void __launch_bounds__(PGT, 1)
 gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[PIPE_SMEM];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;                      // 4 x 2 waves of 64 x 128
   const int l32 = lane & 31, lh = lane >> 5;
 
   // XCD-aware raster: hardware places workgroup b on XCD b % 8
@@ -214,8 +265,8 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
       (void*)(g.A + m0 * g.lda), 0, (int)(min<int64_t>(BM, g.M - m0) * g.lda), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.B + n0 * g.ldb), 0, (int)(min<int64_t>(BN, g.N - n0) * g.ldb), RSRC_FLAGS);
-  // scale DMA: waves 0-1 fetch A's 16 x 8 scale bytes, waves 2-3 B's (16 dwords each)
-  const bool scale_b = wave >= 2;
+  // scale DMA: waves 0-3 fetch A's 16 x 8 scale bytes, waves 4-7 B's (8 dwords each)
+  const bool scale_b = wave >= 4;
   const __amdgpu_buffer_rsrc_t rS = scale_b
       ? __builtin_amdgcn_make_buffer_rsrc((void*)(g.sB + (n0 / 16) * g.sB_rs), 0,
                                           (int)(min<int64_t>(BN / 16, (g.N - n0) / 16) * g.sB_rs), RSRC_FLAGS)
@@ -224,37 +275,37 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   const int64_t s_rs = scale_b ? g.sB_rs : g.sA_rs;
 
   // per-lane source offsets: DMA instruction j of this wave fills tile rows
-  // 64*wave + 16*j .. +16; lane l lands at physical chunk l & 3 of row (l >> 2)
-  uint32_t offA[4], offB[4];
+  // 32*wave + 16*j .. +16; lane l lands at physical chunk l & 3 of row (l >> 2)
+  uint32_t offA[2], offB[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 64 * wave + 16 * j + (lane >> 2);
+  for (int j = 0; j < 2; ++j) {
+    const int row = 32 * wave + 16 * j + (lane >> 2);
     const int q = (lane & 3) ^ ((row >> 2) & 3);
     offA[j] = (uint32_t)(row * g.lda + 16 * q);
     offB[j] = (uint32_t)(row * g.ldb + 16 * q);
   }
-  // lanes 0..15 of each wave: block row 8*(wave&1) + lane/2, blocks 4*(lane&1)..+3
-  const uint32_t offS = (uint32_t)((8 * (wave & 1) + (lane >> 1)) * s_rs + 4 * (lane & 1));
-  const int s_lds = A_ST + B_ST + 64 * wave;   // [0,128): A scales, [128,256): B scales
+  // lanes 0..7 of each wave: block row 4*(wave&3) + lane/2, blocks 4*(lane&1)..+3
+  const uint32_t offS = (uint32_t)((4 * (wave & 3) + (lane >> 1)) * s_rs + 4 * (lane & 1));
+  const int s_lds = A_ST + B_ST + 32 * wave;   // [0,128): A scales, [128,256): B scales
 
-  // every wave issues exactly 9 DMA instructions per stage
+  // every wave issues exactly 5 DMA instructions per stage
   auto issue = [&](int stage, int kt) {
     uint8_t* base = smem + stage * STAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + (64 * wave + 16 * j) * BKB), 16,
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + (32 * wave + 16 * j) * BKB), 16,
                                                offA[j] + (uint32_t)kt * BKB, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(base + A_ST + (64 * wave + 16 * j) * BKB), 16,
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(base + A_ST + (32 * wave + 16 * j) * BKB), 16,
                                                offB[j] + (uint32_t)kt * BKB, 0, 0, 0);
-    if (lane < 16)
+    if (lane < 8)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(base + s_lds), 4, offS + (uint32_t)kt * 8, 0, 0, 0);
   };
 
-  Acc acc;
+  AccT<2> acc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
 
@@ -263,17 +314,17 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     if (s < nkt) issue(s, s);
 
   // steady state: stage kt is consumed while stages kt+1 .. kt+NS-1 are in flight.
-  // A wave's DMA of stage kt is complete once at most NS-2 later stages (9 DMAs
+  // A wave's DMA of stage kt is complete once at most NS-2 later stages (5 DMAs
   // each) are pending; the barrier then makes every wave's DMA visible and marks
   // the buffer of stage kt-1 free for stage kt+NS-1.
   int kt = 0;
   for (; kt + NS - 1 < nkt; ++kt) {
     compiler_fence();
-    FT_WAIT_VMCNT(9 * (NS - 2));
+    FT_WAIT_VMCNT(5 * (NS - 2));
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     issue((kt + NS - 1) % NS, kt + NS - 1);
-    mfma_stage(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
+    mfma_stage<2>(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
   }
   // drain: no more DMA to issue
   for (; kt < nkt; ++kt) {
@@ -281,12 +332,12 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     FT_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    mfma_stage(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
+    mfma_stage<2>(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
   }
   compiler_fence();
   FT_WAIT_VMCNT(0);
   __syncthreads();
-  epilogue_and_store<OUT_BF16>(acc, g, smem, m0, n0, tid, wm, wn, l32, lh);
+  epilogue_and_store<OUT_BF16, 2, 8>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -352,7 +403,7 @@ __global__ void __launch_bounds__(GT, 1) gemm_w4a4_generic_kernel(GemmArgs g) {
     Ss[tid] = ps;   // [0,128): A scales [16 rb][8 kb]; [128,256): B scales
   };
 
-  Acc acc;
+  AccT<4> acc;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -366,11 +417,11 @@ __global__ void __launch_bounds__(GT, 1) gemm_w4a4_generic_kernel(GemmArgs g) {
   for (int64_t kt = 0; kt < nkt; ++kt) {
     const int cur = (int)(kt & 1);
     if (kt + 1 < nkt) gload(kt + 1);
-    mfma_stage(acc, smem + cur * STAGE, wm, wn, l32, lh);
+    mfma_stage<4>(acc, smem + cur * STAGE, wm, wn, l32, lh);
     if (kt + 1 < nkt) lstore(cur ^ 1);
     __syncthreads();
   }
-  epilogue_and_store<OUT_BF16>(acc, g, smem, m0, n0, tid, wm, wn, l32, lh);
+  epilogue_and_store<OUT_BF16, 4, 4>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
 }
 
 }  // namespace
@@ -380,12 +431,11 @@ ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipSt
   const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;
-  const dim3 block(GT);
   const bool pipelined = g.K > 0 && g.K % 128 == 0 && BM * g.lda < ((int64_t)1 << 31) &&
                          BN * g.ldb < ((int64_t)1 << 31);
   if (pipelined) {
     const int per_xcd = (int)((tiles + 7) / 8);
-    const dim3 grid((unsigned)(8 * per_xcd));
+    const dim3 grid((unsigned)(8 * per_xcd)), block(PGT);
     const int tm = (int)tiles_m, tn = (int)tiles_n;
     if (out_bf16) {
       if (trans_b) hipLaunchKernelGGL((gemm_w4a4_kernel<true, true>), grid, block, 0, s, g, tm, tn, per_xcd);
@@ -395,7 +445,7 @@ ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipSt
       else hipLaunchKernelGGL((gemm_w4a4_kernel<false, false>), grid, block, 0, s, g, tm, tn, per_xcd);
     }
   } else {
-    const dim3 grid((unsigned)tiles);
+    const dim3 grid((unsigned)tiles), block(GT);
     if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g);
     else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g);
   }
