@@ -38,8 +38,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="token rows of the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the oracle sample (0: all)")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="oracle passes over the sample")
     ap.add_argument("--quant-reps", type=int, default=20)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run one plain 512 MiB device copy (counter calibration for profiles)")
     return ap.parse_args()
 
 
@@ -81,18 +84,19 @@ class Linear:
         self.Y, self.dX = e((M, N), bf), e((M, K), bf)
         self.dAt, self.dB = e((r, K), f32), e((r, N), f32)
         self.ws = e((max(ops.linear_bwd_workspace(M, N, K, r), 16),), u8)
+        self.ws_lr = e((max(ops.lowrank_workspace(M, K, rs + r), ops.lowrank_workspace(M, N, rs + r), 16),), u8)
 
     def forward(self):
         o = self.ops
         o.quant_block16(self.X, out=self.xq)
-        o.lowrank_fused(self.X, self.L1t, self.At, out=self.T)
+        o.lowrank_fused(self.X, self.L1t, self.At, out=self.T, workspace=self.ws_lr)
         o.linear_fwd(self.xq[0], self.xq[2], self.rq, self.rs_, self.T, self.L2, self.B,
                      self.M, self.N, self.K, out=self.Y)
 
     def backward(self):
         o = self.ops
         o.quant_block16(self.G, out=self.gq)
-        o.lowrank_fused(self.G, self.L2, self.B, out=self.V)
+        o.lowrank_fused(self.G, self.L2, self.B, out=self.V, workspace=self.ws_lr)
         o.linear_bwd(self.gq[0], self.gq[2], self.rqc, self.rsct, self.V, self.L1t, self.At,
                      self.X, self.G, self.T, self.M, self.N, self.K, workspace=self.ws,
                      dX=self.dX, dAt=self.dAt, dB=self.dB)
@@ -133,28 +137,59 @@ def time_quantizer(reps):
     return out
 
 
-def cpu_baseline(spec, d, rows):
-    """The oracle as it stands, on the first `rows` tokens of the same workload."""
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fwd_mlp_up.traffic.txt")
+GEMM_SRC = os.path.join(ROOT, "bit_quantized_lora_amd", "csrc", "gemm_w4a4.hip")
+
+
+def measured_traffic():
+    """HBM bytes per forward-GEMM launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE x calibration + WRITE_SIZE), or None if the kernel source changed since."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    if kv.get("gemm_source_sha256") != sha:
+        return None
+    return int(float(kv["hbm_bytes_per_launch"]))
+
+
+def calibration_copy():
+    import torch
+    src = torch.ones(256 << 20, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def cpu_baseline(spec, d, rows, reps):
+    """The oracle as it stands, `reps` passes over the first `rows` tokens of the same workload."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
+    rows = rows if 0 < rows <= spec.M else spec.M
     sl = slice(0, rows)
     f = {k: O.bf16_to_f64(d[k]) for k in ("L1", "L2", "A", "B")}
     rc, rsc = O.quantize_block16(d["R"])          # offline prep, outside the timed region
     Rhat = O.dequantize(rc, rsc, "pow2")
     t0 = time.perf_counter()
-    X = O.bf16_to_f64(d["X"][sl]); G = O.bf16_to_f64(d["G"][sl])
-    xc, xs = O.quantize_block16(d["X"][sl]); gc, gs = O.quantize_block16(d["G"][sl])
-    Xhat, Ghat = O.dequantize(xc, xs, "pow2"), O.dequantize(gc, gs, "pow2")
-    O.linear_fwd(Xhat, Rhat, X, f["L1"], f["L2"], f["A"], f["B"])
-    O.linear_bwd(Ghat, Rhat, G, X, f["L1"], f["L2"], f["A"], f["B"])
+    for _ in range(reps):
+        X = O.bf16_to_f64(d["X"][sl]); G = O.bf16_to_f64(d["G"][sl])
+        xc, xs = O.quantize_block16(d["X"][sl]); gc, gs = O.quantize_block16(d["G"][sl])
+        Xhat, Ghat = O.dequantize(xc, xs, "pow2"), O.dequantize(gc, gs, "pow2")
+        O.linear_fwd(Xhat, Rhat, X, f["L1"], f["L2"], f["A"], f["B"])
+        O.linear_bwd(Ghat, Rhat, G, X, f["L1"], f["L2"], f["A"], f["B"])
     sec = time.perf_counter() - t0
-    flops = 4.0 * rows * spec.N * spec.K
+    flops = 4.0 * rows * spec.N * spec.K * reps
     return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, fwd+bwd of the first {rows} of {spec.M} tokens "
+            "sample": f"fp64 numpy oracle, {reps} passes of fwd+bwd over {rows} of {spec.M} tokens "
                       f"(K={spec.K}, N={spec.N}), Q(R) prepared outside the timing; {sec:.2f} s"}
 
 
@@ -185,7 +220,7 @@ def main():
     o = lin.ops
     for i in range(args.steps):
         o.quant_block16(lin.X, out=lin.xq)
-        o.lowrank_fused(lin.X, lin.L1t, lin.At, out=lin.T)
+        o.lowrank_fused(lin.X, lin.L1t, lin.At, out=lin.T, workspace=lin.ws_lr)
         ev[i][0].record(s)
         o.linear_fwd(lin.xq[0], lin.xq[2], lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=lin.Y)
         ev[i][1].record(s)
@@ -199,10 +234,10 @@ def main():
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
     marks[0].record(s)
     o.quant_block16(lin.X, out=lin.xq); marks[1].record(s)
-    o.lowrank_fused(lin.X, lin.L1t, lin.At, out=lin.T); marks[2].record(s)
+    o.lowrank_fused(lin.X, lin.L1t, lin.At, out=lin.T, workspace=lin.ws_lr); marks[2].record(s)
     o.linear_fwd(lin.xq[0], lin.xq[2], lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=lin.Y); marks[3].record(s)
     o.quant_block16(lin.G, out=lin.gq); marks[4].record(s)
-    o.lowrank_fused(lin.G, lin.L2, lin.B, out=lin.V); marks[5].record(s)
+    o.lowrank_fused(lin.G, lin.L2, lin.B, out=lin.V, workspace=lin.ws_lr); marks[5].record(s)
     o.linear_bwd(lin.gq[0], lin.gq[2], lin.rqc, lin.rsct, lin.V, lin.L1t, lin.At, lin.X, lin.G, lin.T,
                  M, N, K, workspace=lin.ws, dX=lin.dX, dAt=lin.dAt, dB=lin.dB); marks[6].record(s)
     torch.cuda.synchronize()
@@ -210,6 +245,8 @@ def main():
     phases = {n: marks[i].elapsed_time(marks[i + 1]) * 1e3 for i, n in enumerate(names)}
 
     quant = time_quantizer(args.quant_reps)
+    if args.calibration_copy:
+        calibration_copy()
     gemm_flops = 2.0 * M * N * K
     achieved = gemm_flops / (gemm_ms / 1e3) / 1e12
     value = 4.0 * M * N * K / (ms_step / 1e3) / 1e12
@@ -234,7 +271,7 @@ def main():
         "pct_fp4_peak_whole_linear": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
         "roofline": {"kernel": "gemm_w4a4_kernel (forward)", "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                      "per_launch_flops": gemm_flops, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "phases_us": {k: round(v, 2) for k, v in phases.items()},
         "quantizer": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in v.items()}
@@ -243,7 +280,7 @@ def main():
         "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(spec, d, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(spec, d, args.cpu_rows, args.cpu_reps)
     print(json.dumps(rec))
 
 

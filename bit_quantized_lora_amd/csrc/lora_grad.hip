@@ -6,7 +6,7 @@
 // Both are dW[j][c] = sum_m P[m][poff + j] Q[m][c] with a small fp32 P and a
 // large bf16 Q read once from HBM.  The MFMA needs runs of consecutive m in
 // both operands, so (1) a tiny pre-pass writes P's slice transposed and split
-// into bf16 hi + lo planes [r x M]; (2) each wave stages 64 x 32 tiles of Q in
+// into bf16 hi + lo planes [r x M]; (2) each wave stages 64 x 64 tiles of Q in
 // its own LDS region transposed (so B fragments are single 16-byte reads) and
 // accumulates on bf16 MFMA 32x32x16; (3) the 4 waves of a workgroup, each owning
 // every 4th 64-row chunk of the workgroup's token range, are summed through LDS
@@ -17,12 +17,12 @@
 namespace ft {
 namespace {
 
-constexpr int LG_COLS = 32;
+constexpr int LG_COLS = 64;                  // output columns per workgroup (128-byte rows of Q)
 constexpr int LG_CHUNK = 64;
 constexpr int LG_WAVES = 4;
 constexpr int LG_THREADS = LG_WAVES * 64;
 constexpr int QT_PITCH = LG_CHUNK + 8;       // bf16 elements per LDS row of Q^T
-constexpr int RED_PITCH = LG_COLS + 1;       // floats per LDS row of a partial
+constexpr int RED_PITCH = 33;                // floats per LDS row of a 32 x 32 partial
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -69,15 +69,15 @@ lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ 
   const int64_t me = min(M, ms + rows_per_split);
   uint16_t* qt = s_qt[wave];
 
-  v16f acc[NRT];
+  v16f acc[NRT][2];
 #pragma unroll
-  for (int t = 0; t < NRT; ++t) acc[t] = v16f{};
+  for (int t = 0; t < NRT; ++t) acc[t][0] = acc[t][1] = v16f{};
 
   for (int64_t mb = ms + (int64_t)wave * LG_CHUNK; mb < me; mb += LG_WAVES * LG_CHUNK) {
-    // Q[mb : mb+64, c0 : c0+32] -> LDS transposed
+    // Q[mb : mb+64, c0 : c0+64] -> LDS transposed (Qt[c][m])
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = lane + 64 * u, m = t >> 2, q = t & 3;
+    for (int u = 0; u < 8; ++u) {
+      const int t = lane + 64 * u, m = t >> 3, q = t & 7;
       v4i v = {0, 0, 0, 0};
       if (mb + m < me && c0 + 8 * q < ncols)
         v = *reinterpret_cast<const v4i*>(Q + (mb + m) * ncols + c0 + 8 * q);
@@ -89,7 +89,10 @@ lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ 
 #pragma unroll
     for (int ks = 0; ks < LG_CHUNK / 16; ++ks) {
       const int64_t m = mb + 16 * ks + 8 * lh;   // 8 consecutive tokens of this lane
-      const v8bf bq = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qt + l32 * QT_PITCH + 16 * ks + 8 * lh));
+      v8bf bq[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        bq[ct] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qt + (32 * ct + l32) * QT_PITCH + 16 * ks + 8 * lh));
 #pragma unroll
       for (int t = 0; t < NRT; ++t) {
         const int j = 32 * t + l32;
@@ -98,8 +101,11 @@ lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ 
           h = *reinterpret_cast<const v4i*>(Phi + (int64_t)j * M + m);
           l = *reinterpret_cast<const v4i*>(Plo + (int64_t)j * M + m);
         }
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, h), bq, acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, l), bq, acc[t], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          acc[t][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, h), bq[ct], acc[t][ct], 0, 0, 0);
+          acc[t][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, l), bq[ct], acc[t][ct], 0, 0, 0);
+        }
       }
     }
     wave_sync();
@@ -108,22 +114,25 @@ lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ 
   // sum the 4 wave partials in a fixed order and store this split's result
   float* outs = out + (int64_t)blockIdx.y * out_split_stride;
 #pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    float* mine = s_red + wave * 32 * RED_PITCH;
+  for (int t = 0; t < NRT; ++t)
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) mine[(8 * (rr >> 2) + 4 * lh + (rr & 3)) * RED_PITCH + l32] = acc[t][rr];
-    __syncthreads();
+    for (int ct = 0; ct < 2; ++ct) {
+      float* mine = s_red + wave * 32 * RED_PITCH;
 #pragma unroll
-    for (int e = 0; e < (32 * LG_COLS) / LG_THREADS; ++e) {
-      const int idx = e * LG_THREADS + threadIdx.x, row = idx >> 5, col = idx & 31;
-      float v = 0.0f;
+      for (int rr = 0; rr < 16; ++rr) mine[(8 * (rr >> 2) + 4 * lh + (rr & 3)) * RED_PITCH + l32] = acc[t][ct][rr];
+      __syncthreads();
 #pragma unroll
-      for (int w = 0; w < LG_WAVES; ++w) v += s_red[(w * 32 + row) * RED_PITCH + col];
-      const int j = 32 * t + row;
-      if (j < r && c0 + col < ncols) outs[(int64_t)j * ncols + c0 + col] = v;
+      for (int e = 0; e < (32 * 32) / LG_THREADS; ++e) {
+        const int idx = e * LG_THREADS + threadIdx.x, row = idx >> 5, col = idx & 31;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < LG_WAVES; ++w) v += s_red[(w * 32 + row) * RED_PITCH + col];
+        const int j = 32 * t + row;
+        const int64_t cc = c0 + 32 * ct + col;
+        if (j < r && cc < ncols) outs[(int64_t)j * ncols + cc] = v;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
 }
 
 __global__ void sum_splits_kernel(const float* __restrict__ part, int splits, int64_t n, float* __restrict__ out) {

@@ -63,8 +63,13 @@ def quant_block16(x: torch.Tensor, mode: str = "pow2", rm: bool = True, cm: bool
     return codes_rm, codes_cm, scales
 
 
+def lowrank_workspace(M: int, Kin: int, rho: int) -> int:
+    return int(lib().ft_lowrank_workspace(M, Kin, rho))
+
+
 def lowrank_fused(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor,
-                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out = [inp wa^T | inp wb^T] in fp32; wa [ra, Kin], wb [rb, Kin] bf16."""
     _need(inp, torch.bfloat16, "inp")
     M, Kin = inp.shape
@@ -75,8 +80,12 @@ def lowrank_fused(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor,
             raise ValueError(f"{n} must be contiguous [rank, {Kin}]")
     if out is None:
         out = torch.empty((M, ra + rb), dtype=torch.float32, device=inp.device)
+    ws_bytes = lowrank_workspace(M, Kin, ra + rb)
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=inp.device)
     st = lib().ft_lowrank_fused(inp.data_ptr(), M, Kin, inp.stride(0), wa.data_ptr(), ra,
-                                wb.data_ptr(), rb, out.data_ptr(), _stream(inp))
+                                wb.data_ptr(), rb, out.data_ptr(), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0, _stream(inp))
     check("ft_lowrank_fused", st)
     return out
 

@@ -100,10 +100,15 @@ ft_status ft_quant_block16(const void* x, int64_t rows, int64_t cols, int64_t ld
  * backward: in = G [M x N],  wa = L2,  wb = B   -> V = [G L2^T | G B^T]
  *  in   bf16 [M x Kin], leading dimension ld_in.
  *  out  float [M x (ra+rb)], row-major, leading dimension ra+rb.
+ *  workspace  device scratch of at least ft_lowrank_workspace(M, Kin, ra+rb)
+ *             bytes (may be NULL when that is 0): partial sums of the split
+ *             reduction, added in a fixed order.
  *  Products accumulate in fp32 from exact bf16 operands. */
 ft_status ft_lowrank_fused(const void* in, int64_t M, int64_t Kin, int64_t ld_in,
                            const void* wa, int32_t ra, const void* wb, int32_t rb,
-                           float* out, hipStream_t stream);
+                           float* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+size_t ft_lowrank_workspace(int64_t M, int64_t Kin, int32_t rho);
 
 /* ft_linear_fwd -- Eq. 2 with the LoRA-fusion epilogue (section 3.3: the
  * backbone GEMM and the up-projections are accumulated in one kernel):

@@ -1,0 +1,96 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ft.h")
+
+
+def _lib():
+    from bit_quantized_lora_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        from bit_quantized_lora_amd import build
+        build.build()
+    return L
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:ft_status|size_t|const char\*)\s+(ft_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("ft_quant_block16", "ft_lowrank_fused", "ft_linear_fwd", "ft_linear_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    lib = L.lib()
+    missing = [n for n in _declared() if getattr(lib, n, None) is None]
+    assert not missing, missing
+    # the Python binding knows every declared function
+    assert set(_declared()) <= set(L._SIGS)
+
+
+def test_status_strings():
+    lib = _lib().lib()
+    for s in range(7):
+        assert lib.ft_status_str(s)
+    assert b"unknown" in lib.ft_status_str(99)
+
+
+def test_quant_argument_validation():
+    L = _lib(); lib = L.lib()
+    p = ctypes.c_void_p(16 * 1024)   # never dereferenced: validation fails or nothing launches
+    assert lib.ft_quant_block16(p, 15, 16, 16, 0, p, None, p, None, None) == L.FT_ESHAPE
+    assert lib.ft_quant_block16(p, 16, 16, 8, 0, p, None, p, None, None) == L.FT_ESHAPE      # ldx < cols
+    assert lib.ft_quant_block16(p, 16, 16, 16, 7, p, None, p, None, None) == L.FT_EINVAL     # bad mode
+    assert lib.ft_quant_block16(p, 16, 16, 16, 0, None, None, p, None, None) == L.FT_EINVAL  # no codes out
+    assert lib.ft_quant_block16(None, 16, 16, 16, 0, p, None, p, None, None) == L.FT_EINVAL
+    assert lib.ft_quant_block16(ctypes.c_void_p(16 * 1024 + 4), 16, 16, 16, 0, p, None, p, None, None) == L.FT_EALIGN
+    assert lib.ft_quant_block16(p, 16, 16, 20, 0, p, None, p, None, None) == L.FT_EALIGN    # row pitch
+    assert lib.ft_quant_block16(None, 0, 16, 16, 0, None, None, None, None, None) == L.FT_OK  # empty
+
+
+def test_lowrank_argument_validation():
+    L = _lib(); lib = L.lib()
+    p = ctypes.c_void_p(16 * 1024)
+    assert lib.ft_lowrank_fused(p, 16, 16, 16, p, 8, p, 16, p, None, 0, None) == L.FT_ESHAPE    # rank % 16
+    assert lib.ft_lowrank_fused(p, 16, 16, 16, p, 96, p, 48, p, None, 0, None) == L.FT_ESHAPE   # rho > 128
+    assert lib.ft_lowrank_fused(p, 17, 16, 16, p, 16, p, 16, p, None, 0, None) == L.FT_ESHAPE
+    assert lib.ft_lowrank_fused(p, 0, 16, 16, p, 16, p, 16, p, None, 0, None) == L.FT_OK         # empty
+    big_ws = lib.ft_lowrank_workspace(4608, 12288, 48)
+    assert big_ws > 0
+    assert lib.ft_lowrank_fused(p, 4608, 12288, 12288, p, 32, p, 16, p, None, 0, None) == L.FT_EINVAL
+    assert lib.ft_lowrank_fused(p, 4608, 12288, 12288, p, 32, p, 16, p, p, 16, None) == L.FT_ESPACE
+
+
+def test_linear_argument_validation():
+    L = _lib(); lib = L.lib()
+    p = ctypes.c_void_p(16 * 1024)
+    # f32 block scales: the 4-bit GEMM applies power-of-two scales only
+    assert lib.ft_linear_fwd(16, 16, 16, 1, p, p, p, p, p, p, 16, p, 16, p, 0, None) == L.FT_ENOTSUP
+    assert lib.ft_linear_fwd(16, 16, 24, 0, p, p, p, p, p, p, 16, p, 16, p, 0, None) == L.FT_ESHAPE
+    assert lib.ft_linear_fwd(16, 16, 16, 0, p, p, p, p, p, p, 16, p, 16, p, 5, None) == L.FT_EINVAL
+    assert lib.ft_linear_fwd(16, 16, 16, 0, None, p, p, p, p, p, 16, p, 16, p, 0, None) == L.FT_EINVAL
+    assert lib.ft_linear_fwd(0, 16, 16, 0, None, None, None, None, None, None, 16, None, 16, None, 0, None) == L.FT_OK
+    ws = lib.ft_linear_bwd_workspace(4608, 12288, 3072, 16)
+    assert ws > 0
+    args = [4608, 12288, 3072, 0, p, p, p, p, p, p, 32, p, 16, p, p, p, p, 0, p, p]
+    assert lib.ft_linear_bwd(*args, p, 16, None) == L.FT_ESPACE
+    assert lib.ft_linear_bwd(*args, None, 0, None) == L.FT_EINVAL
+
+
+def test_gelu_argument_validation():
+    L = _lib(); lib = L.lib()
+    p = ctypes.c_void_p(16 * 1024)
+    assert lib.ft_gelu_fwd(p, 12, p, None) == L.FT_ESHAPE
+    assert lib.ft_gelu_bwd(p, p, 12, p, None) == L.FT_ESHAPE
+    assert lib.ft_gelu_fwd(p, 0, p, None) == L.FT_OK
+    assert lib.ft_gelu_fwd(None, 16, p, None) == L.FT_EINVAL
