@@ -1,0 +1,159 @@
+"""Chained stacks on the GPU against the oracle's own chain, at full size.
+
+* MLP pair (Student-t activations): up 3072 -> 12288, GELU, down 12288 -> 3072,
+  M = 4608 tokens.
+* Double-stream block stack: image (M = 4096) and text (M = 512) streams, each
+  with qkv 3072 -> 9216 and proj 3072 -> 3072 on fresh seeded inputs and
+  up -> GELU -> down chained (attention and modulation are not part of the path).
+
+Where the GPU hands a bf16 tensor to the next layer (Y_up, h, dX_down, dY_up),
+the oracle rounds its fp64 value to bf16 at the same point and continues from
+that.  Final outputs are fp32 on the GPU and compared by relative Frobenius
+error against fp64 (contract 2e-3); the bf16 intermediates are compared with
+the oracle's bf16-rounded values.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from gpu_util import dev_bf16, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+_CACHE = {}
+
+
+def _config(cfg):
+    if cfg not in _CACHE:
+        _CACHE[cfg] = {d["spec"].name: d for d in synth.config_linears(cfg)}
+    return _CACHE[cfg]
+
+
+class GpuLayer:
+    """Device-side prepared layer: Q(R) in both layouts, rank-major factors."""
+
+    def __init__(self, d):
+        from bit_quantized_lora_amd import ops
+        self.ops = ops
+        self.N, self.K = d["R"].shape
+        R = dev_bf16(d["R"])
+        self.rq, self.rqc, self.rs, self.rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
+        self.L1t = dev_bf16(np.ascontiguousarray(d["L1"].T))
+        self.At = dev_bf16(np.ascontiguousarray(d["A"].T))
+        self.L2, self.B = dev_bf16(d["L2"]), dev_bf16(d["B"])
+
+    def fwd(self, X, out_dtype):
+        o = self.ops
+        M = X.shape[0]
+        xq, _, xs = o.quant_block16(X, rm=True, cm=False)
+        T = o.lowrank_fused(X, self.L1t, self.At)
+        Y = o.linear_fwd(xq, xs, self.rq, self.rs, T, self.L2, self.B, M, self.N, self.K, out_dtype=out_dtype)
+        return Y, T
+
+    def bwd(self, G, X, T, out_dtype):
+        o = self.ops
+        M = G.shape[0]
+        gq, _, gs = o.quant_block16(G, rm=True, cm=False)
+        V = o.lowrank_fused(G, self.L2, self.B)
+        dX, dAt, dB = o.linear_bwd(gq, gs, self.rqc, self.rsct, V, self.L1t, self.At, X, G, T,
+                                   M, self.N, self.K, out_dtype=out_dtype)
+        return dX, dAt, dB
+
+
+class OracleLayer:
+    def __init__(self, d):
+        rc, rsc = O.quantize_block16(d["R"])
+        self.Rhat = O.dequantize(rc, rsc, "pow2")
+        self.f = {k: O.bf16_to_f64(d[k]) for k in ("L1", "L2", "A", "B")}
+
+    def fwd(self, Xbits):
+        xc, xs = O.quantize_block16(Xbits)
+        f = self.f
+        return O.linear_fwd(O.dequantize(xc, xs, "pow2"), self.Rhat, O.bf16_to_f64(Xbits),
+                            f["L1"], f["L2"], f["A"], f["B"])
+
+    def bwd(self, Gbits, Xbits):
+        gc, gs = O.quantize_block16(Gbits)
+        f = self.f
+        g = O.linear_bwd(O.dequantize(gc, gs, "pow2"), self.Rhat, O.bf16_to_f64(Gbits),
+                         O.bf16_to_f64(Xbits), f["L1"], f["L2"], f["A"], f["B"])
+        g["dA"] = g["dA"].T  # compare in the rank-major layout of the ABI
+        return g
+
+
+def _check(label, got, ref, bf16=False):
+    g = O.bf16_to_f64(host(got)) if bf16 else host(got).astype(np.float64)
+    r = O.bf16_to_f64(ref) if bf16 else ref
+    e = O.rel_frob(g, r)
+    say(f"[chain] {label}: rel-Frobenius {e:.2e}")
+    assert e <= TOL, f"{label}: error {e:.3e} above 2e-3"
+    return e
+
+
+def _single(label, d):
+    """A standalone linear of the stack (fresh seeded input): fwd + bwd."""
+    import torch
+    say(f"[chain] {label} M={d['X'].shape[0]} K={d['R'].shape[1]} N={d['R'].shape[0]}")
+    L, Lo = GpuLayer(d), OracleLayer(d)
+    X, G = dev_bf16(d["X"]), dev_bf16(d["G"])
+    Y, T = L.fwd(X, torch.float32)
+    dX, dAt, dB = L.bwd(G, X, T, torch.float32)
+    _check(f"{label} Y", Y, Lo.fwd(d["X"]))
+    ref = Lo.bwd(d["G"], d["X"])
+    _check(f"{label} dX", dX, ref["dX"])
+    _check(f"{label} dA", dAt, ref["dA"])
+    _check(f"{label} dB", dB, ref["dB"])
+
+
+def _mlp_chain(label, up, down):
+    """up -> GELU -> down forward, then backward from down's seeded gradient."""
+    import torch
+    from bit_quantized_lora_amd import ops
+    M = up["X"].shape[0]
+    say(f"[chain] {label} MLP chain M={M}")
+    Lu, Ld = GpuLayer(up), GpuLayer(down)
+    X, G2 = dev_bf16(up["X"]), dev_bf16(down["G"])
+    Y1, T1 = Lu.fwd(X, torch.bfloat16)
+    h = ops.gelu_fwd(Y1)
+    Y2, T2 = Ld.fwd(h, torch.float32)
+    dh, dA2, dB2 = Ld.bwd(G2, h, T2, torch.bfloat16)
+    dY1 = ops.gelu_bwd(Y1, dh)
+    dX1, dA1, dB1 = Lu.bwd(dY1, X, T1, torch.float32)
+    torch.cuda.synchronize()
+
+    Lou, Lod = OracleLayer(up), OracleLayer(down)
+    y1 = O.f64_to_bf16_bits(Lou.fwd(up["X"]))
+    hb = O.f64_to_bf16_bits(O.gelu(O.bf16_to_f64(y1)))
+    y2 = Lod.fwd(hb)
+    gd = Lod.bwd(down["G"], hb)
+    dhb = O.f64_to_bf16_bits(gd["dX"])
+    dy1 = O.f64_to_bf16_bits(O.gelu_grad(O.bf16_to_f64(y1)) * O.bf16_to_f64(dhb))
+    gu = Lou.bwd(dy1, up["X"])
+
+    _check(f"{label} Y_up (bf16)", Y1, y1, bf16=True)
+    _check(f"{label} h = GELU(Y_up) (bf16)", h, hb, bf16=True)
+    _check(f"{label} Y_down", Y2, y2)
+    _check(f"{label} dX_down = dh (bf16)", dh, dhb, bf16=True)
+    _check(f"{label} dA_down", dA2, gd["dA"])
+    _check(f"{label} dB_down", dB2, gd["dB"])
+    _check(f"{label} dY_up (bf16)", dY1, dy1, bf16=True)
+    _check(f"{label} dX_up", dX1, gu["dX"])
+    _check(f"{label} dA_up", dA1, gu["dA"])
+    _check(f"{label} dB_up", dB1, gu["dB"])
+
+
+def test_mlp_pair_chain_full_size():
+    require_gpu()
+    c = _config("c3")
+    _mlp_chain("mlp-pair", c["c3-up"], c["c3-down"])
+
+
+@pytest.mark.parametrize("stream", ["txt", "img"])
+def test_block_stack_full_size(stream):
+    require_gpu()
+    c = _config("c5")
+    _single(f"c5-{stream}-qkv", c[f"c5-{stream}-qkv"])
+    _single(f"c5-{stream}-proj", c[f"c5-{stream}-proj"])
+    _mlp_chain(f"c5-{stream}", c[f"c5-{stream}-up"], c[f"c5-{stream}-down"])
