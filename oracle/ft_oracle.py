@@ -38,6 +38,7 @@ __all__ = [
     "pack_rm", "pack_cm", "unpack_rm", "dequantize", "scale_values",
     "linear_fwd", "linear_bwd", "gelu", "gelu_grad", "svd_split_check",
     "rel_frob", "BLOCK",
+    "e3m2_decode", "OP_GROUP", "operand_merge", "operand_values", "operand_shape",
 ]
 
 BLOCK = 16
@@ -212,6 +213,139 @@ def unpack_rm(packed, cols: int) -> np.ndarray:
 def pack_cm(codes) -> np.ndarray:
     """Column-major packing: [cols, rows/2]; byte (j, i/2) holds rows i, i+1 of column j."""
     return pack_rm(np.asarray(codes, dtype=np.uint8).T)
+
+
+# --------------------------------------------------------------------------
+# GEMM operand: the same Q(x), re-encoded with pairs of blocks merged
+# --------------------------------------------------------------------------
+# Not a step of the method: a value-preserving re-encoding of a quantized
+# matrix (pow2 scales) in which the two 16-column blocks of each 32-column
+# pair share one power-of-two scale, so that one 32-value, one-scale fragment
+# of a block-scaled matrix instruction carries both blocks.  Its only
+# contract is operand_values(operand_merge(codes, scales)) == dequantize(codes,
+# scales) exactly.  Elements are FP6 E3M2 (OCP Microscaling Formats v1.0,
+# section 5.3.2: 1 sign, 3 exponent bits with bias 3, 2 mantissa bits, no
+# Inf/NaN; magnitudes 0.0625 .. 28).
+#
+# Encoding of one pair (row block rb, blocks b1 = 2p, b2 = 2p + 1), with the
+# E8M0 bytes e1, e2 of the blocks:
+#  * a block whose codes are all +-0 takes its partner's byte (its scale does
+#    not matter); if both are, both take max(e1, e2);
+#  * d = |e1 - e2|, hi = max(e1, e2), u = min(d, 2, hi).  The pair is merged
+#    when d - u <= 3: both blocks then use the byte H = hi - u, and an element
+#    of block b becomes the E3M2 value e2m1(code) * 2^(e_b - H), a shift of
+#    +u for the larger block and u - d >= -3 for the other, always exact;
+#  * otherwise (d - u > 3) each block keeps its own byte and its values are
+#    the E2M1 values (shift 0).  Merged pairs have equal bytes, unmerged
+#    pairs different ones, which is how a consumer tells them apart.
+#  The sign bit of every element is the sign bit of its E2M1 code.
+#
+# Layout: the column index is padded to a multiple of OP_GROUP = 128 (4 pairs;
+# padding is all-zero codes with scale byte 0).  A row of the operand has
+# 96 bytes per group: the first 16 bytes of the 24-byte packed value of pairs
+# 0..3 of the group (64 bytes), then their last 8 bytes (32 bytes).  The
+# 24-byte value of a pair holds its 32 elements, element n (column 32p + n)
+# in bits 6n .. 6n+5, little-endian.  The scale grid is [rows/16, 8 * groups]
+# bytes: entries 2p and 2p + 1 of row block rb are the bytes of blocks b1, b2.
+OP_GROUP = 128
+
+
+def e3m2_decode(codes) -> np.ndarray:
+    """Value of 6-bit E3M2 codes from the format definition.
+
+    exponent field e (3 bits, bias 3), mantissa m (2 bits):
+      e == 0: subnormal, magnitude (m / 4) * 2^-2
+      e >= 1: magnitude (1 + m/4) * 2^(e-3)
+    """
+    c = np.asarray(codes).astype(np.int64)
+    sign = (c >> 5) & 1
+    e = (c >> 2) & 7
+    m = c & 3
+    mag = np.where(e == 0, (m / 4.0) * 0.25, (1.0 + m / 4.0) * np.exp2(e - 3.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+def _e3m2_code_of(mag) -> np.ndarray:
+    """The E3M2 magnitude code (0..31) whose value equals ``mag`` exactly."""
+    table = e3m2_decode(np.arange(32))
+    mag = np.asarray(mag, dtype=np.float64)
+    idx = np.searchsorted(table, mag)
+    idx = np.minimum(idx, 31)
+    if not np.all(table[idx] == mag):
+        raise ValueError("value not representable in E3M2")
+    return idx.astype(np.uint8)
+
+
+def operand_shape(rows: int, cols: int) -> Tuple[Tuple[int, int], Tuple[int, int]]:
+    """(operand bytes shape, operand scale grid shape) of a [rows, cols] matrix."""
+    g = -(-cols // OP_GROUP)
+    return (rows, 96 * g), (rows // BLOCK, 8 * g)
+
+
+def operand_merge(codes, scales) -> Tuple[np.ndarray, np.ndarray]:
+    """Pair-merged operand of a pow2-quantized matrix (codes [rows, cols], bytes)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    rows, cols = codes.shape
+    (_, obytes), (srows, scols) = operand_shape(rows, cols)
+    g = obytes // 96
+    P = 4 * g                                      # pairs per row (with padding)
+    cpad = np.zeros((rows, 32 * P), np.uint8)
+    cpad[:, :cols] = codes
+    epad = np.zeros((rows // BLOCK, 2 * P), np.int64)
+    epad[:, :cols // BLOCK] = scales
+    # zero blocks: every code of the block has magnitude 0
+    mag_blk = (cpad & 7).reshape(rows // BLOCK, BLOCK, 2 * P, BLOCK)
+    zero = ~mag_blk.any(axis=(1, 3))               # [rows/16, 2P]
+    e1, e2 = epad[:, 0::2], epad[:, 1::2]
+    z1, z2 = zero[:, 0::2], zero[:, 1::2]
+    both = z1 & z2
+    f1 = np.where(both, np.maximum(e1, e2), np.where(z1, e2, e1))
+    f2 = np.where(both, np.maximum(e1, e2), np.where(z2, e1, e2))
+    d = np.abs(f1 - f2)
+    hi = np.maximum(f1, f2)
+    u = np.minimum(np.minimum(d, 2), hi)
+    merged = (d - u) <= 3
+    H = hi - u
+    s1 = np.where(merged, H, e1)
+    s2 = np.where(merged, H, e2)
+    t1 = np.where(merged, f1 - H, 0)               # exponent shift of each block's values
+    t2 = np.where(merged, f2 - H, 0)
+    # element shifts [rows, 32P]
+    t = np.stack([t1, t2], axis=-1).reshape(rows // BLOCK, 2 * P)
+    t_el = np.repeat(np.repeat(t, BLOCK, axis=0), BLOCK, axis=1)
+    vals = np.abs(e2m1_decode(cpad)) * np.exp2(t_el.astype(np.float64))
+    c6 = _e3m2_code_of(vals) | ((cpad >> 3) << 5)
+    # pack 32 six-bit codes per pair into 24 little-endian bytes
+    c6 = c6.reshape(rows, P, 32)
+    bits = ((c6[..., None] >> np.arange(6, dtype=np.uint8)) & 1).reshape(rows, P, 192)
+    packed = np.packbits(bits, axis=-1, bitorder="little")          # [rows, P, 24]
+    op = np.zeros((rows, obytes), np.uint8)
+    for p in range(P):
+        grp, q = divmod(p, 4)
+        op[:, 96 * grp + 16 * q: 96 * grp + 16 * q + 16] = packed[:, p, :16]
+        op[:, 96 * grp + 64 + 8 * q: 96 * grp + 64 + 8 * q + 8] = packed[:, p, 16:]
+    osc = np.zeros((srows, scols), np.uint8)
+    osc[:, 0::2] = s1
+    osc[:, 1::2] = s2
+    return op, osc
+
+
+def operand_values(op, op_scales, rows: int, cols: int) -> np.ndarray:
+    """fp64 values [rows, 128 * groups] encoded by an operand (padding included)."""
+    op = np.asarray(op, dtype=np.uint8)
+    g = op.shape[1] // 96
+    P = 4 * g
+    packed = np.empty((rows, P, 24), np.uint8)
+    for p in range(P):
+        grp, q = divmod(p, 4)
+        packed[:, p, :16] = op[:, 96 * grp + 16 * q: 96 * grp + 16 * q + 16]
+        packed[:, p, 16:] = op[:, 96 * grp + 64 + 8 * q: 96 * grp + 64 + 8 * q + 8]
+    bits = np.unpackbits(packed, axis=-1, bitorder="little").reshape(rows, P, 32, 6)
+    c6 = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)      # [rows, P, 32]
+    v = e3m2_decode(c6).reshape(rows, 32 * P)
+    s = np.exp2(np.asarray(op_scales).astype(np.float64) - 127.0)  # [rows/16, 2P]
+    return v * np.repeat(np.repeat(s, BLOCK, 0), BLOCK, 1)
 
 
 # --------------------------------------------------------------------------

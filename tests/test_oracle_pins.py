@@ -451,3 +451,114 @@ def test_svd_split_reconstruction_and_eckart_young(shape):
     assert np.allclose(ev, np.array(chk["top_sv"][:rs]) ** 2, rtol=1e-9)
     # the stabilizer carries the outlier columns: the residual's peak is smaller
     assert np.abs(R).max() < np.abs(W).max()
+
+
+# --------------------------------------------------------------------------
+# pair-merged GEMM operand (a value-preserving re-encoding of Q(x))
+# --------------------------------------------------------------------------
+def test_e3m2_decode_matches_format_table():
+    rows = _read_golden("e3m2_table.txt")
+    assert len(rows) == 32
+    for code_s, val_s in rows:
+        c = int(code_s, 2)
+        assert O.e3m2_decode(c) == float(val_s)
+        assert O.e3m2_decode(c | 32) == -float(val_s) or float(val_s) == 0.0
+    assert np.signbit(O.e3m2_decode(32))
+
+
+def _operand_case(rng, rows, cols, exps):
+    """Random codes with the given scale bytes; a few all-zero blocks."""
+    codes = rng.integers(0, 16, size=(rows, cols), dtype=np.uint8)
+    scales = np.asarray(exps, dtype=np.uint8).reshape(rows // 16, cols // 16)
+    zero_blocks = rng.random(scales.shape) < 0.1
+    zb = np.repeat(np.repeat(zero_blocks, 16, 0), 16, 1)
+    codes = np.where(zb, codes & 8, codes).astype(np.uint8)   # keep signs, zero magnitudes
+    return codes, scales
+
+
+@pytest.mark.parametrize("cols", [16, 48, 112, 128, 144, 400, 528])
+def test_operand_decodes_to_the_dequantized_matrix(cols):
+    """The operand's values equal Q(x)'s dequantized values, every element, for
+    every exponent gap between the blocks of a pair (merged or not), zero
+    blocks, the smallest and largest scale bytes, and a ragged last group."""
+    rng = np.random.default_rng(cols)
+    rows = 64
+    nb = (rows // 16) * (cols // 16)
+    base = rng.integers(0, 255, size=nb)
+    gap = rng.integers(-9, 10, size=nb)
+    exps = np.clip(base + gap * (np.arange(nb) % 2), 0, 254)
+    exps[:3] = [0, 1, 254]
+    codes, scales = _operand_case(rng, rows, cols, exps)
+    op, osc = O.operand_merge(codes, scales)
+    (r, ob), (sr, sc) = O.operand_shape(rows, cols)
+    assert op.shape == (r, ob) and osc.shape == (sr, sc)
+    v = O.operand_values(op, osc, rows, cols)
+    assert np.array_equal(v[:, :cols], O.dequantize(codes, scales, "pow2"))
+    assert np.all(v[:, cols:] == 0)
+    # the sign of every element (zeros included) is the sign of its E2M1 code
+    sgn = np.signbit(v[:, :cols])
+    assert np.array_equal(sgn, (codes >> 3).astype(bool))
+
+
+def test_operand_merge_rule():
+    """Pairs of non-zero blocks merge (equal bytes) exactly when their gap fits the
+    E3M2 range: gap <= 5 when the larger byte is >= 2; unmerged pairs keep their
+    own bytes."""
+    rng = np.random.default_rng(5)
+    for e_hi in (0, 1, 2, 7, 127, 254):
+        for d in range(0, 9):
+            e_lo = e_hi - d
+            if e_lo < 0:
+                continue
+            codes = rng.integers(1, 8, size=(16, 32), dtype=np.uint8)   # no zero blocks
+            scales = np.array([[e_hi, e_lo]], np.uint8)
+            op, osc = O.operand_merge(codes, scales)
+            u = min(d, 2, e_hi)
+            if d - u <= 3:
+                assert osc[0, 0] == osc[0, 1] == e_hi - u, (e_hi, d)
+            else:
+                assert (osc[0, 0], osc[0, 1]) == (e_hi, e_lo), (e_hi, d)
+            assert np.array_equal(O.operand_values(op, osc, 16, 32)[:, :32],
+                                  O.dequantize(codes, scales, "pow2"))
+    # a zero block merges with anything, taking the partner's byte
+    codes = np.zeros((16, 32), np.uint8)
+    codes[:, 16:] = rng.integers(1, 8, size=(16, 16))
+    op, osc = O.operand_merge(codes, np.array([[3, 200]], np.uint8))
+    assert osc[0, 0] == osc[0, 1] == 200
+
+
+def test_operand_byte_layout():
+    """Hand-built case: positions of single elements in the packed bytes."""
+    codes = np.zeros((16, 160), np.uint8)
+    codes[0, 0] = 1       # 0.5  -> E3M2 0b01000
+    codes[0, 31] = 7      # 6.0  -> E3M2 0b10110
+    codes[0, 33] = 10     # -1.0 -> E3M2 0b101100 (sign bit 5)
+    codes[0, 128] = 2     # 1.0 in the second group, pair 4
+    scales = np.full((1, 10), 127, np.uint8)
+    op, osc = O.operand_merge(codes, scales)
+    assert op.shape == (16, 192) and osc.shape == (1, 16)
+    assert op[0, 0] == 0b01000                        # element 0: bits 0..5 of byte 0
+    assert op[0, 64 + 7] == (0b10110 << 2)            # element 31: bits 186..191 = byte 23
+    assert op[0, 16] == ((0b101100 << 6) & 0xFF)      # pair 1, element 1: bits 6..11
+    assert op[0, 17] == (0b101100 >> 2)
+    assert op[0, 96] == 0b01100                       # pair 4 = group 1, first chunk
+    assert np.count_nonzero(op) == 4                  # byte 16 holds only zero bits of it
+    assert np.all(osc[0, :10] == 127) and np.all(osc[0, 10:] == 0)
+    # shift: block bytes 127 and 125 (gap 2) merge at 125; the first block's values x4
+    codes2 = np.zeros((16, 32), np.uint8)
+    codes2[0, 0] = 7      # 6.0 * 2^0 -> shifted to 24.0 = E3M2 0b11110
+    codes2[0, 16] = 1     # 0.5 in the second block, unshifted
+    op2, osc2 = O.operand_merge(codes2, np.array([[127, 125]], np.uint8))
+    assert osc2[0, 0] == osc2[0, 1] == 125
+    assert op2[0, 0] == 0b11110
+    assert (int.from_bytes(bytes(op2[0, :16]), "little") >> 96) & 63 == 0b01000
+
+
+def test_operand_of_the_transpose():
+    """The operand of Q(x)^T (codes and scale grid transposed) decodes to the transposed values."""
+    rng = np.random.default_rng(8)
+    x = synth.f32_to_bf16_bits(synth.make_tensor(rng, (96, 160), "t3"))
+    codes, scales = O.quantize_block16(x)
+    op, osc = O.operand_merge(codes.T, scales.T)
+    v = O.operand_values(op, osc, 160, 96)
+    assert np.array_equal(v[:, :96], O.dequantize(codes, scales, "pow2").T)
