@@ -20,6 +20,9 @@ FT_OUT_F32, FT_OUT_BF16 = 0, 1
 # name -> argtypes (restype is ft_status = int unless stated)
 _SIGS = {
     "ft_quant_block16": [c_void_p, c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p],
+    "ft_quant_block16_op": [c_void_p, c_int64, c_int64, c_int64] + [c_void_p] * 9,
+    "ft_operand_bytes": [c_int64, c_int64],
+    "ft_operand_scale_bytes": [c_int64, c_int64],
     "ft_lowrank_fused": [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                          c_void_p, c_size_t, c_void_p],
     "ft_lowrank_workspace": [c_int64, c_int64, c_int32],
@@ -33,7 +36,8 @@ _SIGS = {
     "ft_gelu_bwd": [c_void_p, c_void_p, c_int64, c_void_p, c_void_p],
     "ft_status_str": [c_int32],
 }
-_RESTYPES = {"ft_linear_bwd_workspace": c_size_t, "ft_lowrank_workspace": c_size_t, "ft_status_str": c_char_p}
+_RESTYPES = {"ft_operand_bytes": c_size_t, "ft_operand_scale_bytes": c_size_t,
+             "ft_linear_bwd_workspace": c_size_t, "ft_lowrank_workspace": c_size_t, "ft_status_str": c_char_p}
 
 _lib = None
 

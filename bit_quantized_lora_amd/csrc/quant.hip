@@ -12,6 +12,19 @@
 // rounds to nearest-even and saturates, matching the oracle bit for bit), and
 // transposes the 16x16 nibble block across the 16 lanes for the column-major
 // codes.  Both code layouts are staged in LDS and written with coalesced stores.
+//
+// Optionally the same tile also writes the pair-merged GEMM operand of Q(x)
+// (along columns) and of Q(x)^T (along rows): a value-preserving re-encoding in
+// which the two 16-wide blocks of a 32-wide pair share one power-of-two scale,
+// so one 32-value fragment of the block-scaled MFMA carries both blocks.  The
+// elements become FP6 E3M2: a block with scale byte e_b is re-expressed at the
+// shared byte H as e2m1(code) * 2^(e_b - H) (shift in [-3, 2], always exact),
+// when the bytes are close enough (gap d with d - min(d, 2, hi) <= 3); otherwise
+// each block keeps its byte and its plain values.  An all-zero block takes its
+// partner's byte.  Codes are decoded with the hardware FP4 -> f32 convert at
+// scale 2^shift and re-encoded with the f32 -> FP6 (E3M2) convert, both exact
+// for these values.  The tile's 128 columns (rows) are exactly one 128-wide
+// operand group, so every byte of the operand, padding included, is written.
 #include "ft_common.h"
 
 namespace ft {
@@ -22,6 +35,15 @@ constexpr int QTHREADS = 256;
 constexpr int IN_PITCH = QT * 2 + 16;   // bytes per LDS input row (padded)
 constexpr int RM_PITCH = QT / 2 + 8;    // bytes per LDS row-major code row (padded)
 constexpr int CM_PITCH = QT / 2 + 8;    // bytes per LDS column-major code row (padded)
+constexpr int OP_GROUP_BYTES = 96;      // operand bytes per row per 128 reduction elements
+
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef unsigned v6u __attribute__((ext_vector_type(6)));
+
+struct QuantOut {
+  uint8_t* codes_rm; uint8_t* codes_cm; void* scales; void* scales_cm;
+  uint8_t* op_rm; uint8_t* op_rm_scales; uint8_t* op_cm; uint8_t* op_cm_scales;
+};
 
 // Exchange with the lane whose index differs in bit MASK (MASK < 16).
 template <int MASK>
@@ -64,14 +86,53 @@ __device__ __forceinline__ void transpose_nibbles16(uint32_t& w0, uint32_t& w1, 
 #undef FT_NIB_STEP
 }
 
-template <bool POW2, bool WRITE_RM, bool WRITE_CM>
+// One 32-element pair of a row: 16 bytes of E2M1 codes (elements 0..15 in bytes
+// 0..7 from block 1, 16..31 in bytes 8..15 from block 2), block scale bytes e1,
+// e2 and all-zero flags -> 6 dwords of E3M2 (element n in bits 6n..6n+5) and
+// the pair's scale bytes s1, s2 (equal when merged).
+__device__ __forceinline__ v6u merge_pair(const uint32_t (&w)[4], int e1, int e2, bool z1, bool z2, int& s1,
+                                          int& s2) {
+  int f1 = e1, f2 = e2;
+  if (z1 && z2) { f1 = f2 = max(e1, e2); }
+  else if (z1) { f1 = e2; }
+  else if (z2) { f2 = e1; }
+  const int d = abs(f1 - f2), hi = max(f1, f2);
+  const int u = min(min(d, 2), hi);
+  const bool merged = d - u <= 3;
+  const int H = hi - u;
+  s1 = merged ? H : e1;
+  s2 = merged ? H : e2;
+  const int t1 = merged ? f1 - H : 0, t2 = merged ? f2 - H : 0;     // in [-3, 2]
+  const float m1 = __builtin_bit_cast(float, (uint32_t)(t1 + 127) << 23);
+  const float m2 = __builtin_bit_cast(float, (uint32_t)(t2 + 127) << 23);
+  v16f ev, od;   // even / odd elements: the convert interleaves its two inputs
+#define FT_DEC(J, W, SEL, M)                                                   \
+  {                                                                            \
+    const v2f_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(W, M, SEL);        \
+    ev[J] = v.x;                                                               \
+    od[J] = v.y;                                                               \
+  }
+  FT_DEC(0, w[0], 0, m1) FT_DEC(1, w[0], 1, m1) FT_DEC(2, w[0], 2, m1) FT_DEC(3, w[0], 3, m1)
+  FT_DEC(4, w[1], 0, m1) FT_DEC(5, w[1], 1, m1) FT_DEC(6, w[1], 2, m1) FT_DEC(7, w[1], 3, m1)
+  FT_DEC(8, w[2], 0, m2) FT_DEC(9, w[2], 1, m2) FT_DEC(10, w[2], 2, m2) FT_DEC(11, w[2], 3, m2)
+  FT_DEC(12, w[3], 0, m2) FT_DEC(13, w[3], 1, m2) FT_DEC(14, w[3], 2, m2) FT_DEC(15, w[3], 3, m2)
+#undef FT_DEC
+  return __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, 1.0f);
+}
+
+template <bool POW2, bool WRITE_RM, bool WRITE_CM, bool OP_RM, bool OP_CM>
 __global__ void __launch_bounds__(QTHREADS)
-quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
-                     uint8_t* __restrict__ codes_rm, uint8_t* __restrict__ codes_cm,
-                     void* __restrict__ scales, void* __restrict__ scales_cm) {
+quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, QuantOut o) {
+  constexpr bool STAGE_RM = WRITE_RM || OP_RM, STAGE_CM = WRITE_CM || OP_CM, OPS = OP_RM || OP_CM;
   __shared__ __attribute__((aligned(16))) uint8_t s_in[QT * IN_PITCH];
-  __shared__ __attribute__((aligned(16))) uint8_t s_rm[WRITE_RM ? QT * RM_PITCH : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t s_cm[WRITE_CM ? QT * CM_PITCH : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_rm[STAGE_RM ? QT * RM_PITCH : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_cm[STAGE_CM ? QT * CM_PITCH : 16];
+  __shared__ uint8_t s_e[OPS ? 64 : 1];   // scale byte of each of the tile's 8 x 8 blocks
+  __shared__ uint8_t s_z[OPS ? 64 : 1];   // 1 when every code of the block is +-0
+  uint8_t* __restrict__ codes_rm = o.codes_rm;
+  uint8_t* __restrict__ codes_cm = o.codes_cm;
+  void* __restrict__ scales = o.scales;
+  void* __restrict__ scales_cm = o.scales_cm;
 
   const int tid = threadIdx.x;
   const int64_t row0 = (int64_t)blockIdx.y * QT;
@@ -124,9 +185,20 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
       FT_CVT(w1, 4, 0); FT_CVT(w1, 5, 1); FT_CVT(w1, 6, 2); FT_CVT(w1, 7, 3);
 #undef FT_CVT
       if (live && i == 0) {
-        static_cast<uint8_t*>(scales)[(row0 / 16 + br) * (cols / 16) + col0 / 16 + bc] = (uint8_t)(E + 127);
+        if (scales) static_cast<uint8_t*>(scales)[(row0 / 16 + br) * (cols / 16) + col0 / 16 + bc] = (uint8_t)(E + 127);
         if (scales_cm)
           static_cast<uint8_t*>(scales_cm)[(col0 / 16 + bc) * (rows / 16) + row0 / 16 + br] = (uint8_t)(E + 127);
+      }
+      if constexpr (OPS) {
+        uint32_t nz = (w0 | w1) & 0x77777777u;   // any non-zero magnitude in this row
+        nz |= xor_lane<8>(nz);
+        nz |= xor_lane<4>(nz);
+        nz |= xor_lane<2>(nz);
+        nz |= xor_lane<1>(nz);
+        if (i == 0) {
+          s_e[b] = (uint8_t)(E + 127);
+          s_z[b] = nz == 0 ? 1 : 0;
+        }
       }
     } else {
       const float amax = __builtin_bit_cast(float, m << 16);
@@ -148,10 +220,10 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
         if (scales_cm) static_cast<float*>(scales_cm)[(col0 / 16 + bc) * (rows / 16) + row0 / 16 + br] = s;
       }
     }
-    if constexpr (WRITE_RM) {
+    if constexpr (STAGE_RM) {
       *reinterpret_cast<v2i*>(s_rm + (br * 16 + i) * RM_PITCH + bc * 8) = v2i{(int)w0, (int)w1};
     }
-    if constexpr (WRITE_CM) {
+    if constexpr (STAGE_CM) {
       transpose_nibbles16(w0, w1, i);
       *reinterpret_cast<v2i*>(s_cm + (bc * 16 + i) * CM_PITCH + br * 8) = v2i{(int)w0, (int)w1};
     }
@@ -179,20 +251,88 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
             *reinterpret_cast<const v2i*>(s_cm + cl * CM_PITCH + q * 8);
     }
   }
+  // 4. pair-merged operands: item = (tile row or column, pair); 4 consecutive
+  //    lanes write one operand row's 96-byte group.
+  if constexpr (OP_RM) {
+    const int64_t pitch = (cols + QT - 1) / QT * OP_GROUP_BYTES;
+    const int64_t spitch = (cols + QT - 1) / QT * 8;
+#pragma unroll
+    for (int it = 0; it < (QT * 4) / QTHREADS; ++it) {
+      const int item = it * QTHREADS + tid, r = item >> 2, p = item & 3;
+      if (r < trows) {
+        const v2i c0 = *reinterpret_cast<const v2i*>(s_rm + r * RM_PITCH + 16 * p);
+        const v2i c1 = *reinterpret_cast<const v2i*>(s_rm + r * RM_PITCH + 16 * p + 8);
+        const uint32_t w[4] = {(uint32_t)c0.x, (uint32_t)c0.y, (uint32_t)c1.x, (uint32_t)c1.y};
+        const int b1 = (r >> 4) * 8 + 2 * p;
+        int s1, s2;
+        const v6u f = merge_pair(w, s_e[b1], s_e[b1 + 1], s_z[b1] != 0, s_z[b1 + 1] != 0, s1, s2);
+        uint8_t* dst = o.op_rm + (row0 + r) * pitch + blockIdx.x * OP_GROUP_BYTES;
+        *reinterpret_cast<v4i*>(dst + 16 * p) = v4i{(int)f[0], (int)f[1], (int)f[2], (int)f[3]};
+        *reinterpret_cast<v2i*>(dst + 64 + 8 * p) = v2i{(int)f[4], (int)f[5]};
+        if ((r & 15) == 0)
+          *reinterpret_cast<uint16_t*>(o.op_rm_scales + (row0 / 16 + (r >> 4)) * spitch + blockIdx.x * 8 + 2 * p) =
+              (uint16_t)(s1 | (s2 << 8));
+      }
+    }
+  }
+  if constexpr (OP_CM) {
+    const int64_t pitch = (rows + QT - 1) / QT * OP_GROUP_BYTES;
+    const int64_t spitch = (rows + QT - 1) / QT * 8;
+#pragma unroll
+    for (int it = 0; it < (QT * 4) / QTHREADS; ++it) {
+      const int item = it * QTHREADS + tid, cl = item >> 2, p = item & 3;
+      if (cl < tcols) {
+        const v2i c0 = *reinterpret_cast<const v2i*>(s_cm + cl * CM_PITCH + 16 * p);
+        const v2i c1 = *reinterpret_cast<const v2i*>(s_cm + cl * CM_PITCH + 16 * p + 8);
+        const uint32_t w[4] = {(uint32_t)c0.x, (uint32_t)c0.y, (uint32_t)c1.x, (uint32_t)c1.y};
+        const int b1 = (2 * p) * 8 + (cl >> 4), b2 = b1 + 8;
+        int s1, s2;
+        const v6u f = merge_pair(w, s_e[b1], s_e[b2], s_z[b1] != 0, s_z[b2] != 0, s1, s2);
+        uint8_t* dst = o.op_cm + (col0 + cl) * pitch + blockIdx.y * OP_GROUP_BYTES;
+        *reinterpret_cast<v4i*>(dst + 16 * p) = v4i{(int)f[0], (int)f[1], (int)f[2], (int)f[3]};
+        *reinterpret_cast<v2i*>(dst + 64 + 8 * p) = v2i{(int)f[4], (int)f[5]};
+        if ((cl & 15) == 0)
+          *reinterpret_cast<uint16_t*>(o.op_cm_scales + (col0 / 16 + (cl >> 4)) * spitch + blockIdx.y * 8 + 2 * p) =
+              (uint16_t)(s1 | (s2 << 8));
+      }
+    }
+  }
+}
+
+template <bool POW2, bool RM, bool CM, bool ORM, bool OCM>
+ft_status launch4(const void* x, int64_t rows, int64_t cols, int64_t ldx, const QuantOut& o, hipStream_t s) {
+  dim3 grid((unsigned)((cols + QT - 1) / QT), (unsigned)((rows + QT - 1) / QT));
+  hipLaunchKernelGGL((quant_block16_kernel<POW2, RM, CM, ORM, OCM>), grid, dim3(QTHREADS), 0, s,
+                     static_cast<const uint16_t*>(x), rows, cols, ldx, o);
+  return launch_status();
+}
+
+template <bool POW2, bool RM, bool CM>
+ft_status launch_ops(const void* x, int64_t rows, int64_t cols, int64_t ldx, const QuantOut& o, hipStream_t s) {
+  if constexpr (POW2) {
+    if (o.op_rm && o.op_cm) return launch4<POW2, RM, CM, true, true>(x, rows, cols, ldx, o, s);
+    if (o.op_rm) return launch4<POW2, RM, CM, true, false>(x, rows, cols, ldx, o, s);
+    if (o.op_cm) return launch4<POW2, RM, CM, false, true>(x, rows, cols, ldx, o, s);
+  }
+  if constexpr (RM || CM) return launch4<POW2, RM, CM, false, false>(x, rows, cols, ldx, o, s);
+  return FT_EINVAL;
 }
 
 template <bool POW2>
-ft_status launch_quant(const void* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* rm,
-                       uint8_t* cm, void* scales, void* scales_cm, hipStream_t s) {
-  dim3 grid((unsigned)((cols + QT - 1) / QT), (unsigned)((rows + QT - 1) / QT));
-  const uint16_t* xp = static_cast<const uint16_t*>(x);
-  if (rm && cm)
-    hipLaunchKernelGGL((quant_block16_kernel<POW2, true, true>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales, scales_cm);
-  else if (rm)
-    hipLaunchKernelGGL((quant_block16_kernel<POW2, true, false>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales, scales_cm);
-  else
-    hipLaunchKernelGGL((quant_block16_kernel<POW2, false, true>), grid, dim3(QTHREADS), 0, s, xp, rows, cols, ldx, rm, cm, scales, scales_cm);
-  return launch_status();
+ft_status launch_quant(const void* x, int64_t rows, int64_t cols, int64_t ldx, const QuantOut& o, hipStream_t s) {
+  if (o.codes_rm && o.codes_cm) return launch_ops<POW2, true, true>(x, rows, cols, ldx, o, s);
+  if (o.codes_rm) return launch_ops<POW2, true, false>(x, rows, cols, ldx, o, s);
+  if (o.codes_cm) return launch_ops<POW2, false, true>(x, rows, cols, ldx, o, s);
+  return launch_ops<POW2, false, false>(x, rows, cols, ldx, o, s);
+}
+
+ft_status validate(const void* x, int64_t rows, int64_t cols, int64_t ldx) {
+  if (!mult16(rows) || !mult16(cols) || ldx < cols) return FT_ESHAPE;
+  if (rows == 0 || cols == 0) return FT_OK;
+  if (!x) return FT_EINVAL;
+  if (!aligned16(x) || (ldx % 8) != 0) return FT_EALIGN;
+  if ((rows + QT - 1) / QT >= 65535) return FT_ESHAPE;
+  return FT_OK;
 }
 
 }  // namespace
@@ -203,16 +343,42 @@ extern "C" ft_status ft_quant_block16(const void* x, int64_t rows, int64_t cols,
                                       void* scales, void* scales_cm, hipStream_t stream) {
   using namespace ft;
   if (mode != FT_SCALE_POW2 && mode != FT_SCALE_F32) return FT_EINVAL;
-  if (!mult16(rows) || !mult16(cols) || ldx < cols) return FT_ESHAPE;
-  if (rows == 0 || cols == 0) return FT_OK;
-  if (!x || !scales || (!codes_rm && !codes_cm)) return FT_EINVAL;
-  if (!aligned16(x) || (ldx % 8) != 0) return FT_EALIGN;
+  ft_status st = validate(x, rows, cols, ldx);
+  if (st != FT_OK || rows == 0 || cols == 0) return st;
+  if (!scales || (!codes_rm && !codes_cm)) return FT_EINVAL;
   if ((codes_rm && !aligned16(codes_rm)) || (codes_cm && !aligned16(codes_cm)) || !aligned16(scales) ||
       (scales_cm && !aligned16(scales_cm)))
     return FT_EALIGN;
-  if (rows / QT >= 65535) return FT_ESHAPE;
-  return mode == FT_SCALE_POW2 ? launch_quant<true>(x, rows, cols, ldx, codes_rm, codes_cm, scales, scales_cm, stream)
-                               : launch_quant<false>(x, rows, cols, ldx, codes_rm, codes_cm, scales, scales_cm, stream);
+  const QuantOut o = {codes_rm, codes_cm, scales, scales_cm, nullptr, nullptr, nullptr, nullptr};
+  return mode == FT_SCALE_POW2 ? launch_quant<true>(x, rows, cols, ldx, o, stream)
+                               : launch_quant<false>(x, rows, cols, ldx, o, stream);
+}
+
+extern "C" size_t ft_operand_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return (size_t)rows * (size_t)((cols + 127) / 128) * 96;
+}
+
+extern "C" size_t ft_operand_scale_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  return (size_t)(rows / 16) * (size_t)((cols + 127) / 128) * 8;
+}
+
+extern "C" ft_status ft_quant_block16_op(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                         uint8_t* codes_rm, uint8_t* codes_cm, uint8_t* scales,
+                                         uint8_t* scales_cm, uint8_t* op_rm, uint8_t* op_rm_scales,
+                                         uint8_t* op_cm, uint8_t* op_cm_scales, hipStream_t stream) {
+  using namespace ft;
+  ft_status st = validate(x, rows, cols, ldx);
+  if (st != FT_OK || rows == 0 || cols == 0) return st;
+  if (!codes_rm && !codes_cm && !op_rm && !op_cm) return FT_EINVAL;
+  if ((op_rm && !op_rm_scales) || (op_cm && !op_cm_scales)) return FT_EINVAL;
+  if ((codes_rm || codes_cm) && !scales) return FT_EINVAL;
+  const void* ptrs[] = {codes_rm, codes_cm, scales, scales_cm, op_rm, op_rm_scales, op_cm, op_cm_scales};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  const QuantOut o = {codes_rm, codes_cm, scales, scales_cm, op_rm, op_rm_scales, op_cm, op_cm_scales};
+  return launch_quant<true>(x, rows, cols, ldx, o, stream);
 }
 
 extern "C" const char* ft_status_str(ft_status s) {

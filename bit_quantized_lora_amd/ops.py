@@ -63,6 +63,49 @@ def quant_block16(x: torch.Tensor, mode: str = "pow2", rm: bool = True, cm: bool
     return codes_rm, codes_cm, scales
 
 
+def operand_shapes(rows: int, cols: int):
+    """((rows, bytes per row), (rows/16, scale bytes per row)) of the operand of a [rows, cols] matrix."""
+    n = int(lib().ft_operand_bytes(rows, cols))
+    ns = int(lib().ft_operand_scale_bytes(rows, cols))
+    return (rows, n // rows if rows else 0), (rows // 16, ns // (rows // 16) if rows >= 16 else 0)
+
+
+def quant_block16_op(x: torch.Tensor, codes_rm: bool = False, codes_cm: bool = False, op_rm: bool = True,
+                     op_cm: bool = False, out: Optional[dict] = None) -> dict:
+    """Q(x) (power-of-two scales) -> dict with any of "codes_rm", "codes_cm", "scales",
+    "op_rm", "op_rm_scales" (the operand of x), "op_cm", "op_cm_scales" (of x^T).
+
+    ``out`` may supply preallocated buffers under the same keys."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D matrix with unit column stride")
+    rows, cols = x.shape
+    dev = x.device
+    u8 = torch.uint8
+    if out is None:
+        out = {}
+        if codes_rm:
+            out["codes_rm"] = torch.empty((rows, cols // 2), dtype=u8, device=dev)
+        if codes_cm:
+            out["codes_cm"] = torch.empty((cols, rows // 2), dtype=u8, device=dev)
+        if codes_rm or codes_cm:
+            out["scales"] = torch.empty((rows // 16, cols // 16), dtype=u8, device=dev)
+        if op_rm:
+            (a, b), (c, d) = operand_shapes(rows, cols)
+            out["op_rm"] = torch.empty((a, b), dtype=u8, device=dev)
+            out["op_rm_scales"] = torch.empty((c, d), dtype=u8, device=dev)
+        if op_cm:
+            (a, b), (c, d) = operand_shapes(cols, rows)
+            out["op_cm"] = torch.empty((a, b), dtype=u8, device=dev)
+            out["op_cm_scales"] = torch.empty((c, d), dtype=u8, device=dev)
+    g = lambda k: _ptr(out.get(k))
+    st = lib().ft_quant_block16_op(x.data_ptr(), rows, cols, x.stride(0), g("codes_rm"), g("codes_cm"),
+                                   g("scales"), g("scales_cm"), g("op_rm"), g("op_rm_scales"), g("op_cm"),
+                                   g("op_cm_scales"), _stream(x))
+    check("ft_quant_block16_op", st)
+    return out
+
+
 def lowrank_workspace(M: int, Kin: int, rho: int) -> int:
     return int(lib().ft_lowrank_workspace(M, Kin, rho))
 

@@ -89,6 +89,41 @@ ft_status ft_quant_block16(const void* x, int64_t rows, int64_t cols, int64_t ld
                            ft_scale_mode mode, uint8_t* codes_rm, uint8_t* codes_cm,
                            void* scales, void* scales_cm, hipStream_t stream);
 
+/* Pair-merged GEMM operand of a quantized matrix (FT_SCALE_POW2 only).
+ *
+ * Not a step of the method but a value-preserving re-encoding of Q(x) for
+ * gfx950's block-scaled MFMA, whose 32-value fragments take ONE power-of-two
+ * scale: the two 16-column blocks of each 32-column pair share a scale byte
+ * where their exponent gap allows it.  Elements are FP6 E3M2 (OCP MX v1.0):
+ * with block bytes e1, e2 (an all-zero block takes its partner's byte),
+ * d = |e1 - e2|, hi = max, u = min(d, 2, hi): if d - u <= 3 both blocks use
+ * byte H = hi - u and element values e2m1(code) * 2^(e_b - H) (exact);
+ * otherwise each block keeps its byte and its E2M1 values.  So merged pairs
+ * carry equal bytes and unmerged pairs different ones; dequantized values
+ * are identical to those of codes + scales.
+ *
+ * Layout of the operand of a [rows x cols] matrix (pairs along cols):
+ *  data    [rows][G * 96] bytes, G = ceil(cols / 128) groups of 4 pairs
+ *          (columns past cols are zero padding).  Per row and group: the first
+ *          16 bytes of each pair's 24-byte packed value (64 bytes), then the last
+ *          8 bytes of each (32 bytes).  The 24-byte value of a pair holds its 32
+ *          elements, element n in bits 6n .. 6n+5, little-endian.
+ *  scales  [rows/16][G * 8] bytes: entries 2p, 2p+1 are pair p's two bytes. */
+size_t ft_operand_bytes(int64_t rows, int64_t cols);
+size_t ft_operand_scale_bytes(int64_t rows, int64_t cols);
+
+/* ft_quant_block16_op -- Q(x) with FT_SCALE_POW2 (as ft_quant_block16), writing
+ * any subset of: E2M1 codes in either layout and the scale grid (as
+ * ft_quant_block16; scales required when codes are requested), the operand of
+ * x (op_rm + op_rm_scales, pairs along cols: the forward GEMM's layout) and the
+ * operand of x^T (op_cm + op_cm_scales, pairs along rows: what the transposed
+ * GEMM of Eq. 3 reads; sizes from ft_operand_bytes(cols, rows)).  Each operand
+ * needs its scale buffer.  All pointers 16-byte aligned; at least one output. */
+ft_status ft_quant_block16_op(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                              uint8_t* codes_rm, uint8_t* codes_cm, uint8_t* scales, uint8_t* scales_cm,
+                              uint8_t* op_rm, uint8_t* op_rm_scales, uint8_t* op_cm, uint8_t* op_cm_scales,
+                              hipStream_t stream);
+
 /* ft_lowrank_fused -- the shared down-projection of the two low-rank branches
  * (section 3.3 "LoRA Fusion": both branches read the same input, so one pass
  * over it feeds both):

@@ -76,3 +76,75 @@ def test_quant_full_size_config_tensors_sampled():
                 assert np.array_equal(got_rm[sl], O.pack_rm(codes))
                 assert np.array_equal(got_sc[s], scales[0])
                 assert np.array_equal(got_cm[:, 8 * s:8 * s + 8], O.pack_cm(codes))
+
+
+# --------------------------------------------------------------------------
+# pair-merged GEMM operands (bit-exact against the oracle's encoding)
+# --------------------------------------------------------------------------
+def _check_op(bits, label):
+    from bit_quantized_lora_amd import ops
+    say(f"[quant-op] {label} {bits.shape}")
+    x = dev_bf16(bits)
+    got = ops.quant_block16_op(x, codes_rm=True, codes_cm=True, op_rm=True, op_cm=True)
+    codes, scales = O.quantize_block16(bits, "pow2")
+    assert np.array_equal(host(got["codes_rm"]), O.pack_rm(codes)), f"{label}: codes_rm"
+    assert np.array_equal(host(got["codes_cm"]), O.pack_cm(codes)), f"{label}: codes_cm"
+    assert np.array_equal(host(got["scales"]), scales), f"{label}: scales"
+    op, osc = O.operand_merge(codes, scales)
+    assert np.array_equal(host(got["op_rm_scales"]), osc), f"{label}: op_rm scales"
+    assert np.array_equal(host(got["op_rm"]), op), f"{label}: op_rm bytes"
+    opt, osct = O.operand_merge(codes.T, scales.T)
+    assert np.array_equal(host(got["op_cm_scales"]), osct), f"{label}: op_cm scales"
+    assert np.array_equal(host(got["op_cm"]), opt), f"{label}: op_cm bytes"
+    # operand-only launches write the same bytes
+    only = ops.quant_block16_op(x, op_rm=True, op_cm=False)
+    assert np.array_equal(host(only["op_rm"]), op) and np.array_equal(host(only["op_rm_scales"]), osc)
+    only = ops.quant_block16_op(x, op_rm=False, op_cm=True)
+    assert np.array_equal(host(only["op_cm"]), opt) and np.array_equal(host(only["op_cm_scales"]), osct)
+
+
+@pytest.mark.parametrize("kind", ["zeros", "negzeros", "subnormal", "ties", "huge", "mixed"])
+def test_operand_edge_tensors(kind):
+    require_gpu()
+    _check_op(synth.edge_tensor(kind, 160, 272), f"edge:{kind}")
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (144, 400), (256, 128), (400, 144), (128, 528)])
+def test_operand_ragged_shapes(shape):
+    require_gpu()
+    rng = np.random.default_rng(shape[0] * 31 + shape[1])
+    _check_op(synth.f32_to_bf16_bits(synth.make_tensor(rng, shape, "t3")), f"ragged{shape}")
+
+
+def test_operand_outlier_channels_unmerged_pairs():
+    """Activation outlier channels (x50, x100) open exponent gaps past the merge
+    range: a mix of merged and unmerged pairs."""
+    require_gpu()
+    for cfg in ("c2", "c4"):
+        d = synth.config_linears(cfg, scale_m=256)[0]
+        codes, scales = O.quantize_block16(d["X"], "pow2")
+        _, osc = O.operand_merge(codes, scales)
+        assert np.any(osc[:, 0::2] != osc[:, 1::2]), "expected some unmerged pairs"
+        _check_op(d["X"], f"{cfg}:X")
+
+
+def test_operand_full_size_sampled():
+    """Full-size R of the MLP-up linear and G of the QKV config, one launch each;
+    sampled 16-row strips (operand of x) and 16-column strips (operand of x^T)."""
+    require_gpu()
+    from bit_quantized_lora_amd import ops
+    for cfg, name in (("c3", "R"), ("c4", "G")):
+        bits = synth.config_linears(cfg)[0][name]
+        rows, cols = bits.shape
+        say(f"[quant-op] full {cfg}:{name} {bits.shape}")
+        got = ops.quant_block16_op(dev_bf16(bits), op_rm=True, op_cm=True)
+        op_rm, sc_rm, op_cm, sc_cm = (host(got[k]) for k in ("op_rm", "op_rm_scales", "op_cm", "op_cm_scales"))
+        rng = np.random.default_rng(rows + cols)
+        for s in np.unique(np.concatenate([[0, rows // 16 - 1], rng.integers(0, rows // 16, 4)])):
+            c, sc = O.quantize_block16(bits[16 * s:16 * s + 16])
+            op, osc = O.operand_merge(c, sc)
+            assert np.array_equal(op_rm[16 * s:16 * s + 16], op) and np.array_equal(sc_rm[s], osc[0])
+        for s in np.unique(np.concatenate([[0, cols // 16 - 1], rng.integers(0, cols // 16, 4)])):
+            c, sc = O.quantize_block16(bits[:, 16 * s:16 * s + 16])
+            op, osc = O.operand_merge(c.T, sc.T)
+            assert np.array_equal(op_cm[16 * s:16 * s + 16], op) and np.array_equal(sc_cm[s], osc[0])
