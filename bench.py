@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the oracle sample (0: all)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle passes over the sample")
     ap.add_argument("--quant-reps", type=int, default=20)
+    ap.add_argument("--path", choices=["op", "codes"], default="op",
+                    help="GEMM operands: pair-merged FP6 operands (op) or E2M1 codes (codes)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (counter calibration for profiles)")
     return ap.parse_args()
@@ -60,12 +62,15 @@ def make_inputs():
 
 
 class Linear:
-    """Device buffers and the step of one triple-branch linear (all preallocated)."""
+    """Device buffers and the step of one triple-branch linear (all preallocated).
 
-    def __init__(self, spec, d):
+    path "op": the quantizer writes the pair-merged operands and the GEMMs read
+    them (a full 32-K fragment per MFMA); path "codes": E2M1 codes + scales."""
+
+    def __init__(self, spec, d, path="op"):
         import torch
         from bit_quantized_lora_amd import ops
-        self.ops = ops
+        self.ops, self.path = ops, path
         M, K, N, rs, r = spec.M, spec.K, spec.N, spec.rs, spec.r
         self.M, self.K, self.N = M, K, N
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
@@ -75,31 +80,69 @@ class Linear:
         self.At = dev_bf16(np.ascontiguousarray(d["A"].T))
         self.L2, self.B = dev_bf16(d["L2"]), dev_bf16(d["B"])
         R = dev_bf16(d["R"])
-        # offline: Q(R) in both layouts (R is frozen)
-        self.rq, self.rqc, self.rs_, self.rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
+        # offline: Q(R) (R is frozen)
+        if path == "op":
+            self.ro = ops.quant_block16_op(R, op_rm=True, op_cm=True)
+            (a, b), (c, dd) = ops.operand_shapes(M, K)
+            self.xo = {"op_rm": e((a, b), u8), "op_rm_scales": e((c, dd), u8)}
+            (a, b), (c, dd) = ops.operand_shapes(M, N)
+            self.go = {"op_rm": e((a, b), u8), "op_rm_scales": e((c, dd), u8)}
+        else:
+            self.rq, self.rqc, self.rs_, self.rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
+            self.xq = (e((M, K // 2), u8), None, e((M // 16, K // 16), u8))
+            self.gq = (e((M, N // 2), u8), None, e((M // 16, N // 16), u8))
         del R
-        self.xq = (e((M, K // 2), u8), None, e((M // 16, K // 16), u8))
-        self.gq = (e((M, N // 2), u8), None, e((M // 16, N // 16), u8))
         self.T, self.V = e((M, rs + r), f32), e((M, rs + r), f32)
         self.Y, self.dX = e((M, N), bf), e((M, K), bf)
         self.dAt, self.dB = e((r, K), f32), e((r, N), f32)
         self.ws = e((max(ops.linear_bwd_workspace(M, N, K, r), 16),), u8)
         self.ws_lr = e((max(ops.lowrank_workspace(M, K, rs + r), ops.lowrank_workspace(M, N, rs + r), 16),), u8)
 
+    def quant_x(self):
+        if self.path == "op":
+            self.ops.quant_block16_op(self.X, op_rm=True, out=self.xo)
+        else:
+            self.ops.quant_block16(self.X, out=self.xq)
+
+    def lowrank_x(self):
+        self.ops.lowrank_fused(self.X, self.L1t, self.At, out=self.T, workspace=self.ws_lr)
+
+    def gemm_fwd(self):
+        o, M, N, K = self.ops, self.M, self.N, self.K
+        if self.path == "op":
+            o.linear_fwd_op(self.xo["op_rm"], self.xo["op_rm_scales"], self.ro["op_rm"], self.ro["op_rm_scales"],
+                            self.T, self.L2, self.B, M, N, K, out=self.Y)
+        else:
+            o.linear_fwd(self.xq[0], self.xq[2], self.rq, self.rs_, self.T, self.L2, self.B, M, N, K, out=self.Y)
+
+    def quant_g(self):
+        if self.path == "op":
+            self.ops.quant_block16_op(self.G, op_rm=True, out=self.go)
+        else:
+            self.ops.quant_block16(self.G, out=self.gq)
+
+    def lowrank_g(self):
+        self.ops.lowrank_fused(self.G, self.L2, self.B, out=self.V, workspace=self.ws_lr)
+
+    def gemm_bwd_and_grads(self):
+        o, M, N, K = self.ops, self.M, self.N, self.K
+        if self.path == "op":
+            o.linear_bwd_op(self.go["op_rm"], self.go["op_rm_scales"], self.ro["op_cm"], self.ro["op_cm_scales"],
+                            self.V, self.L1t, self.At, self.X, self.G, self.T, M, N, K, workspace=self.ws,
+                            dX=self.dX, dAt=self.dAt, dB=self.dB)
+        else:
+            o.linear_bwd(self.gq[0], self.gq[2], self.rqc, self.rsct, self.V, self.L1t, self.At, self.X, self.G,
+                         self.T, M, N, K, workspace=self.ws, dX=self.dX, dAt=self.dAt, dB=self.dB)
+
     def forward(self):
-        o = self.ops
-        o.quant_block16(self.X, out=self.xq)
-        o.lowrank_fused(self.X, self.L1t, self.At, out=self.T, workspace=self.ws_lr)
-        o.linear_fwd(self.xq[0], self.xq[2], self.rq, self.rs_, self.T, self.L2, self.B,
-                     self.M, self.N, self.K, out=self.Y)
+        self.quant_x()
+        self.lowrank_x()
+        self.gemm_fwd()
 
     def backward(self):
-        o = self.ops
-        o.quant_block16(self.G, out=self.gq)
-        o.lowrank_fused(self.G, self.L2, self.B, out=self.V, workspace=self.ws_lr)
-        o.linear_bwd(self.gq[0], self.gq[2], self.rqc, self.rsct, self.V, self.L1t, self.At,
-                     self.X, self.G, self.T, self.M, self.N, self.K, workspace=self.ws,
-                     dX=self.dX, dAt=self.dAt, dB=self.dB)
+        self.quant_g()
+        self.lowrank_g()
+        self.gemm_bwd_and_grads()
 
     def step(self):
         self.forward()
@@ -204,7 +247,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     spec, d = make_inputs()
-    lin = Linear(spec, d)
+    lin = Linear(spec, d, args.path)
     M, K, N = spec.M, spec.K, spec.N
     s = torch.cuda.current_stream()
 
@@ -217,12 +260,11 @@ def main():
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(s)
-    o = lin.ops
     for i in range(args.steps):
-        o.quant_block16(lin.X, out=lin.xq)
-        o.lowrank_fused(lin.X, lin.L1t, lin.At, out=lin.T, workspace=lin.ws_lr)
+        lin.quant_x()
+        lin.lowrank_x()
         ev[i][0].record(s)
-        o.linear_fwd(lin.xq[0], lin.xq[2], lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=lin.Y)
+        lin.gemm_fwd()
         ev[i][1].record(s)
         lin.backward()
     t_end.record(s)
@@ -231,17 +273,14 @@ def main():
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
     # per-phase breakdown from one extra (untimed-region) step
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
-    marks[0].record(s)
-    o.quant_block16(lin.X, out=lin.xq); marks[1].record(s)
-    o.lowrank_fused(lin.X, lin.L1t, lin.At, out=lin.T, workspace=lin.ws_lr); marks[2].record(s)
-    o.linear_fwd(lin.xq[0], lin.xq[2], lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=lin.Y); marks[3].record(s)
-    o.quant_block16(lin.G, out=lin.gq); marks[4].record(s)
-    o.lowrank_fused(lin.G, lin.L2, lin.B, out=lin.V, workspace=lin.ws_lr); marks[5].record(s)
-    o.linear_bwd(lin.gq[0], lin.gq[2], lin.rqc, lin.rsct, lin.V, lin.L1t, lin.At, lin.X, lin.G, lin.T,
-                 M, N, K, workspace=lin.ws, dX=lin.dX, dAt=lin.dAt, dB=lin.dB); marks[6].record(s)
-    torch.cuda.synchronize()
     names = ["quant_X", "lowrank_X", "fwd_gemm", "quant_G", "lowrank_G", "bwd_gemm_and_adapter_grads"]
+    fns = [lin.quant_x, lin.lowrank_x, lin.gemm_fwd, lin.quant_g, lin.lowrank_g, lin.gemm_bwd_and_grads]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+    marks[0].record(s)
+    for i, f in enumerate(fns):
+        f()
+        marks[i + 1].record(s)
+    torch.cuda.synchronize()
     phases = {n: marks[i].elapsed_time(marks[i + 1]) * 1e3 for i, n in enumerate(names)}
 
     quant = time_quantizer(args.quant_reps)
@@ -266,10 +305,12 @@ def main():
         "config": {"workload": "W4A4G4 triple-branch linear fwd+bwd, FLUX MLP-up shape",
                    "M": M, "K": K, "N": N, "stabilizer_rank": spec.rs, "lora_rank": spec.r,
                    "x_dist": "student-t df=3", "scale_rule": "pow2 (amax/6 rounded up to 2^E)",
-                   "gemm_scale_path": "S2 (one 16-K block per 32-K MFMA fragment)",
+                   "gemm_operands": ("pair-merged FP6 E3M2 (two 16-K blocks per 32-K MFMA fragment)"
+                                     if args.path == "op" else "E2M1 codes (one 16-K block per 32-K fragment)"),
                    "outputs": "bf16 Y and dX, fp32 dA and dB"},
         "pct_fp4_peak_whole_linear": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
-        "roofline": {"kernel": "gemm_w4a4_kernel (forward)", "bound": "mfma",
+        "roofline": {"kernel": ("gemm_m6_kernel" if args.path == "op" else "gemm_w4a4_kernel") + " (forward)",
+                     "bound": "mfma",
                      "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                      "per_launch_flops": gemm_flops, "avg_launch_us": round(gemm_ms * 1e3, 2)},

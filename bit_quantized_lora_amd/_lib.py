@@ -32,6 +32,11 @@ _SIGS = {
                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_linear_bwd_workspace": [c_int64, c_int64, c_int64, c_int32],
+    "ft_linear_fwd_op": [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                         c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p],
+    "ft_linear_bwd_op": [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                         c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                         c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_gelu_fwd": [c_void_p, c_int64, c_void_p, c_void_p],
     "ft_gelu_bwd": [c_void_p, c_void_p, c_int64, c_void_p, c_void_p],
     "ft_status_str": [c_int32],

@@ -23,6 +23,12 @@ struct GemmArgs {
 
 ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s);
 
+// Same product from pair-merged FP6 operands (ft_quant_block16_op): A, B are
+// operand bytes with row pitch lda / ldb (= groups * 96), sA / sB the operand
+// scale grids with sA_rs / sB_rs = groups * 8 bytes per 16-row block.  K may be
+// any multiple of 16 (the operands are zero-padded to 128).
+ft_status launch_gemm_m6(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s);
+
 // dW[j][c] = sum_m P[m][poff + j] Q[m][c] for j < r, c < ncols (reduction over M),
 // P fp32 with row pitch ldp, Q bf16 [M x ncols].  Needs lora_grad_workspace bytes.
 size_t lora_grad_workspace(int64_t M, int64_t ncols, int r);

@@ -118,6 +118,29 @@ __device__ __forceinline__ void mfma_stage(AccT<TMI>& acc, const uint8_t* st, in
 #undef FT_KSTEP
 }
 
+// 4 x 4 transpose within each quad of lanes: on entry lane t of a quad holds
+// element (k, t) in v[k]; on exit it holds element (t, k) in v[k].  Two butterfly
+// stages over lane bits 0 and 1, each exchanging half of the values with DPP.
+__device__ __forceinline__ float dpp_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose4(float (&v)[4], int t) {
+  const bool b0 = t & 1, b1 = t & 2;
+#pragma unroll
+  for (int k = 0; k < 4; k += 2) {
+    const float r = dpp_xor1(b0 ? v[k] : v[k + 1]);
+    if (b0) v[k] = r; else v[k + 1] = r;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float r = dpp_xor2(b1 ? v[k] : v[k + 2]);
+    if (b1) v[k] = r; else v[k + 2] = r;
+  }
+}
+
 // + P W over the tile, then store C.  smem must be free (callers synchronize first).
 //
 // W rows (rank-major, [rho x N]) are copied to LDS with buffer_load ... lds, one
@@ -215,19 +238,29 @@ __device__ __forceinline__ void epilogue_and_store(AccT<TMI>& acc, const GemmArg
       compiler_fence();
     }
   }
+  // Store: each lane holds 4 consecutive rows of one column per group of 4
+  // accumulator values; a 4 x 4 transpose across the 4 lanes of a quad (DPP quad
+  // permutes) gives each lane one row of 4 consecutive columns, so the tile goes
+  // out in 8-byte (bf16) or 16-byte (fp32) stores: 4x fewer store instructions.
+  const int t4 = lane & 3;
 #pragma unroll
   for (int i = 0; i < TMI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + 32 * j + l32;
+      const int64_t col = n0 + wn * 128 + 32 * j + (l32 & ~3);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 32 * TMI + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+      for (int q = 0; q < 4; ++q) {
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        quad_transpose4(v, t4);
+        const int64_t row = m0 + wm * 32 * TMI + 32 * i + 8 * q + 4 * lh + t4;
         if (row < g.M && col < g.N) {
-          if constexpr (OUT_BF16)
-            static_cast<uint16_t*>(g.C)[row * g.ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-          else
-            static_cast<float*>(g.C)[row * g.ldc + col] = acc[i][j][r];
+          if constexpr (OUT_BF16) {
+            const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+            *reinterpret_cast<v2i*>(static_cast<uint16_t*>(g.C) + row * g.ldc + col) = v2i{(int)lo, (int)hi};
+          } else {
+            *reinterpret_cast<v4f*>(static_cast<float*>(g.C) + row * g.ldc + col) = v4f{v[0], v[1], v[2], v[3]};
+          }
         }
       }
     }
@@ -333,6 +366,197 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     __builtin_amdgcn_s_barrier();
     compiler_fence();
     mfma_stage<2>(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
+  }
+  compiler_fence();
+  FT_WAIT_VMCNT(0);
+  __syncthreads();
+  epilogue_and_store<OUT_BF16, 2, 8>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
+}
+
+// ---------------------------------------------------------------------------------------
+// Pair-merged operand kernel (scale path "S3"): full 32-K fragments
+// ---------------------------------------------------------------------------------------
+// Operands are the pair-merged FP6 (E3M2) re-encoding of the quantized matrices
+// (ft_quant_block16_op): per row and 128-K group, 64 bytes of pair heads (the
+// first 16 of each pair's 24 bytes, pairs 0..3) and 32 bytes of pair tails
+// (last 8 bytes, pairs 0, 2, 1, 3); pair scale bytes [rows/16][groups * 8].  A
+// lane of the 32x32x64 MFMA takes one whole pair of its row (32 K = 6 dwords) and
+// one scale byte when the pair is merged (equal bytes), so every K slot carries
+// data.  K-step ks of a stage covers pairs 2ks (lanes 0-31) and 2ks+1 (lanes
+// 32-63).  When any lane of a k-step holds an unmerged pair (unequal bytes: an
+// exponent gap too wide for E3M2), the wave takes that k-step as two MFMAs per
+// tile: A restricted to the first 16 K of each lane's pair (dwords 0-2) with
+// scale byte 0 of both operands, then to the last 16 K (dwords 3-5) with byte 1.
+// B needs no masking: the zeros of A remove the other half of its products, and
+// B's byte 0 / byte 1 are its two blocks' scales (equal when merged).
+//
+// Stage (128 K), per operand: three [256 rows][32 bytes] regions -- heads of
+// pairs 0-1, heads of pairs 2-3, tails (unit 0: pairs 0 and 2, unit 1: pairs 1
+// and 3) -- each row's two 16-byte units XOR-swizzled by row bits 2 and 3, so a
+// lane's reads of all three regions share one offset.  Then the pair scales
+// (A [16][8], B [16][8]).  3-stage LDS ring, 7 DMA instructions per wave per
+// stage (one per region and operand, plus scales), one barrier per stage.
+constexpr int M6_ROW = 32;                                // bytes per row of a region
+constexpr int M6_REG = BM * M6_ROW;                       // one region (8 KiB)
+constexpr int M6_OPB = 3 * M6_REG;                        // one operand's regions
+constexpr int M6_STAGE = 2 * M6_OPB + 256;
+constexpr int M6_NS = 3;
+constexpr int M6_DMAS = 7;                                // DMA instructions per wave per stage
+constexpr int M6_SMEM = cmax(M6_NS * M6_STAGE, EPI_LDS);
+
+// unit u (0, 1) of a region row, swizzled so 16 consecutive rows hit distinct banks
+__device__ __forceinline__ int tswz(int row, int u) {
+  return row * M6_ROW + ((u ^ ((row >> 2) & 1) ^ ((row >> 3) & 1)) << 4);
+}
+
+__device__ __forceinline__ bool unmerged(int s) { return ((s ^ (s >> 8)) & 0xff) != 0; }
+
+// aoff / boff: this lane's region offset for its first A / B row (rows of the
+// other tiles are 32 rows = 1 KiB further; swizzle bits are unchanged).
+__device__ __forceinline__ void mfma_stage_m6(AccT<2>& acc, const uint8_t* st, int aoff, int boff, int asc,
+                                              int bsc) {
+  const uint8_t* A = st;
+  const uint8_t* B = st + M6_OPB;
+  const uint8_t* S = st + 2 * M6_OPB;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    // this lane's pair: 16-byte head, 8-byte tail (contiguous registers), scale bytes (s1, s2)
+    v8i aop[2], bop[4];
+    int sA[2], sB[4];
+    bool split = false;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const v4i h = *reinterpret_cast<const v4i*>(A + ks * M6_REG + aoff + i * 32 * M6_ROW);
+      const v2i t = *reinterpret_cast<const v2i*>(A + 2 * M6_REG + aoff + i * 32 * M6_ROW + 8 * ks);
+      aop[i] = v8i{h.x, h.y, h.z, h.w, t.x, t.y, 0, 0};
+      sA[i] = (int)(*reinterpret_cast<const uint16_t*>(S + asc + 16 * i + 4 * ks));
+      split |= unmerged(sA[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4i h = *reinterpret_cast<const v4i*>(B + ks * M6_REG + boff + j * 32 * M6_ROW);
+      const v2i t = *reinterpret_cast<const v2i*>(B + 2 * M6_REG + boff + j * 32 * M6_ROW + 8 * ks);
+      bop[j] = v8i{h.x, h.y, h.z, h.w, t.x, t.y, 0, 0};
+      sB[j] = (int)(*reinterpret_cast<const uint16_t*>(S + 128 + bsc + 16 * j + 4 * ks));
+      split |= unmerged(sB[j]);
+    }
+    // merged k-step: one MFMA per tile over the whole pair.  Otherwise the same
+    // MFMAs take only the first 16 K of A (scale bytes 0), and a second round the
+    // last 16 K (scale bytes 1).
+    const bool two = __builtin_amdgcn_ballot_w64(split) != 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v8i a = aop[i];
+      if (two) a[3] = a[4] = a[5] = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[j], acc[i][j], 3, 3, 0, sA[i], 0, sB[j]);
+    }
+    if (two) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const v8i a = {0, 0, 0, aop[i][3], aop[i][4], aop[i][5], 0, 0};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop[j], acc[i][j], 3, 3, 1, sA[i], 1, sB[j]);
+      }
+    }
+  }
+}
+
+// A: operand of the left matrix [M x K]; B: operand of the right matrix [N x K];
+// lda / ldb = operand row pitch (groups * 96 bytes); sA_rs / sB_rs = groups * 8.
+template <bool OUT_BF16, bool TRANS_B>
+__global__ void __launch_bounds__(PGT, 1)
+gemm_m6_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[M6_SMEM];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lh = lane >> 5;
+
+  const int b = blockIdx.x;
+  const int v = (b & 7) * per_xcd + (b >> 3);
+  if (v >= tiles_m * tiles_n) return;
+  const int grp = v / (GROUP_M * tiles_n);
+  const int first_m = grp * GROUP_M;
+  const int gm = min(GROUP_M, tiles_m - first_m);
+  const int in_grp = v - grp * GROUP_M * tiles_n;
+  const int64_t m0 = (int64_t)(first_m + in_grp % gm) * BM;
+  const int64_t n0 = (int64_t)(in_grp / gm) * BN;
+  const int nkt = (int)((g.K + 127) / 128);
+
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.A + m0 * g.lda), 0, (int)(min<int64_t>(BM, g.M - m0) * g.lda), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.B + n0 * g.ldb), 0, (int)(min<int64_t>(BN, g.N - n0) * g.ldb), RSRC_FLAGS);
+  const bool scale_b = wave >= 4;
+  const __amdgpu_buffer_rsrc_t rS = scale_b
+      ? __builtin_amdgcn_make_buffer_rsrc((void*)(g.sB + (n0 / 16) * g.sB_rs), 0,
+                                          (int)(min<int64_t>(BN / 16, (g.N - n0) / 16) * g.sB_rs), RSRC_FLAGS)
+      : __builtin_amdgcn_make_buffer_rsrc((void*)(g.sA + (m0 / 16) * g.sA_rs), 0,
+                                          (int)(min<int64_t>(BM / 16, (g.M - m0) / 16) * g.sA_rs), RSRC_FLAGS);
+  const int64_t s_rs = scale_b ? g.sB_rs : g.sA_rs;
+
+  // DMA r of this wave fills rows 32*wave .. +32 of region r: lane l -> physical
+  // unit l & 1 of row l >> 1 (the swizzle picks which global unit it fetches)
+  uint32_t offA, offB;
+  {
+    const int row = 32 * wave + (lane >> 1);
+    const int u = (lane & 1) ^ ((row >> 2) & 1) ^ ((row >> 3) & 1);
+    offA = (uint32_t)(row * g.lda + 16 * u);
+    offB = (uint32_t)(row * g.ldb + 16 * u);
+  }
+  const uint32_t offS = (uint32_t)((4 * (wave & 3) + (lane >> 1)) * s_rs + 4 * (lane & 1));
+  const int s_lds = 2 * M6_OPB + 32 * wave;
+  // global byte of region r within a 96-byte group: heads 0-1 at 0, heads 2-3 at 32, tails at 64
+  auto issue = [&](int stage, int kt) {
+    uint8_t* base = smem + __builtin_amdgcn_readfirstlane(stage * M6_STAGE);
+    const uint32_t kofs = (uint32_t)kt * 96;
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + r * M6_REG + 32 * wave * M6_ROW), 16,
+                                               offA + kofs + 32 * r, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(base + M6_OPB + r * M6_REG + 32 * wave * M6_ROW), 16,
+                                               offB + kofs + 32 * r, 0, 0, 0);
+    if (lane < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(base + s_lds), 4, offS + (uint32_t)kt * 8, 0, 0, 0);
+  };
+  // fragment read offsets: A rows wm*64 + 32i + l32, B rows wn*128 + 32j + l32
+  const int aoff = tswz(wm * 64 + l32, lh), boff = tswz(wn * 128 + l32, lh);
+  const int asc = ((wm * 64 + l32) >> 4) * 8 + 2 * lh, bsc = ((wn * 128 + l32) >> 4) * 8 + 2 * lh;
+
+  AccT<2> acc;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+#pragma unroll
+  for (int s = 0; s < M6_NS - 1; ++s)
+    if (s < nkt) issue(s, s);
+
+  int kt = 0;
+  for (; kt + M6_NS - 1 < nkt; ++kt) {
+    compiler_fence();
+    FT_WAIT_VMCNT(M6_DMAS * (M6_NS - 2));
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    issue((kt + M6_NS - 1) % M6_NS, kt + M6_NS - 1);
+    // stage base as an opaque uniform value: keeps loop strength reduction from
+    // turning every fragment address into its own induction variable
+    const int cur = __builtin_amdgcn_readfirstlane((kt % M6_NS) * M6_STAGE);
+    mfma_stage_m6(acc, smem + cur, aoff, boff, asc, bsc);
+  }
+  for (; kt < nkt; ++kt) {
+    compiler_fence();
+    FT_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    const int cur = __builtin_amdgcn_readfirstlane((kt % M6_NS) * M6_STAGE);
+    mfma_stage_m6(acc, smem + cur, aoff, boff, asc, bsc);
   }
   compiler_fence();
   FT_WAIT_VMCNT(0);
@@ -448,6 +672,25 @@ ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipSt
     const dim3 grid((unsigned)tiles), block(GT);
     if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g);
     else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g);
+  }
+  return launch_status();
+}
+
+ft_status launch_gemm_m6(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s) {
+  if (g.M == 0 || g.N == 0) return FT_OK;
+  const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;
+  if (BM * g.lda >= ((int64_t)1 << 31) || BN * g.ldb >= ((int64_t)1 << 31)) return FT_ESHAPE;
+  const int per_xcd = (int)((tiles + 7) / 8);
+  const dim3 grid((unsigned)(8 * per_xcd)), block(PGT);
+  const int tm = (int)tiles_m, tn = (int)tiles_n;
+  if (out_bf16) {
+    if (trans_b) hipLaunchKernelGGL((gemm_m6_kernel<true, true>), grid, block, 0, s, g, tm, tn, per_xcd);
+    else hipLaunchKernelGGL((gemm_m6_kernel<true, false>), grid, block, 0, s, g, tm, tn, per_xcd);
+  } else {
+    if (trans_b) hipLaunchKernelGGL((gemm_m6_kernel<false, true>), grid, block, 0, s, g, tm, tn, per_xcd);
+    else hipLaunchKernelGGL((gemm_m6_kernel<false, false>), grid, block, 0, s, g, tm, tn, per_xcd);
   }
   return launch_status();
 }

@@ -1,5 +1,7 @@
 // Entry points of the triple-branch linear: ft_linear_fwd (Eq. 2) and
-// ft_linear_bwd (Eq. 3 plus the adapter gradients of section 3.2).
+// ft_linear_bwd (Eq. 3 plus the adapter gradients of section 3.2), taking the
+// 4-bit operands either as E2M1 codes + block scales or as the pair-merged
+// operands of ft_quant_block16_op (the _op variants).
 #include "ft_internal.h"
 
 namespace ft {
@@ -7,6 +9,11 @@ namespace {
 
 bool ranks_ok(int rs, int r) { return rs >= 0 && r >= 0 && rs % 16 == 0 && r % 16 == 0 && rs + r <= 128; }
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+int64_t op_groups(int64_t k) { return (k + 127) / 128; }
+
+// dA^T = V[:, rs:]^T X ;  dB = T[:, rs:]^T G  (reductions over the M tokens)
+ft_status adapter_grads(int64_t M, int64_t N, int64_t K, const float* V, int rs, int r, const void* X,
+                        const void* G, const float* T, float* dAt, float* dB, void* workspace, hipStream_t stream);
 
 }  // namespace
 }  // namespace ft
@@ -88,14 +95,88 @@ extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
     ft_status st = launch_gemm_w4a4(g, dxdt == FT_OUT_BF16, true, stream);
     if (st != FT_OK) return st;
   }
-  if (r) {
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const size_t wa = align256(lora_grad_workspace(M, K, r));
-    // dA^T = V[:, rs:]^T X ;  dB = T[:, rs:]^T G
-    ft_status st = launch_lora_grad(V, rho, rs, r, static_cast<const uint16_t*>(X), M, K, dAt, ws, stream);
-    if (st != FT_OK) return st;
-    st = launch_lora_grad(T, rho, rs, r, static_cast<const uint16_t*>(G), M, N, dB, ws + wa, stream);
+  return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
+}
+
+namespace ft {
+namespace {
+ft_status adapter_grads(int64_t M, int64_t N, int64_t K, const float* V, int rs, int r, const void* X,
+                        const void* G, const float* T, float* dAt, float* dB, void* workspace, hipStream_t stream) {
+  if (!r) return FT_OK;
+  const int rho = rs + r;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t wa = align256(lora_grad_workspace(M, K, r));
+  ft_status st = launch_lora_grad(V, rho, rs, r, static_cast<const uint16_t*>(X), M, K, dAt, ws, stream);
+  if (st != FT_OK) return st;
+  return launch_lora_grad(T, rho, rs, r, static_cast<const uint16_t*>(G), M, N, dB, ws + wa, stream);
+}
+}  // namespace
+}  // namespace ft
+
+extern "C" ft_status ft_linear_fwd_op(int64_t M, int64_t N, int64_t K, const uint8_t* x_op,
+                                      const uint8_t* x_op_scales, const uint8_t* r_op, const uint8_t* r_op_scales,
+                                      const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                                      void* Y, ft_out_dtype ydt, hipStream_t stream) {
+  using namespace ft;
+  if (ydt != FT_OUT_F32 && ydt != FT_OUT_BF16) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  if (M == 0 || N == 0) return FT_OK;
+  const int rho = rs + r;
+  if (!Y || (K && (!x_op || !x_op_scales || !r_op || !r_op_scales)) || (rho && !T) || (rs && !L2) || (r && !B))
+    return FT_EINVAL;
+  const void* ptrs[] = {Y, x_op, x_op_scales, r_op, r_op_scales, T, L2, B};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  const int64_t gk = op_groups(K);
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = x_op; g.lda = gk * 96;
+  g.B = r_op; g.ldb = gk * 96;
+  g.sA = x_op_scales; g.sA_rs = gk * 8;
+  g.sB = r_op_scales; g.sB_rs = gk * 8;
+  g.P = T;
+  g.Wa = static_cast<const uint16_t*>(L2); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(B); g.rb = r;
+  g.C = Y; g.ldc = N;
+  return launch_gemm_m6(g, ydt == FT_OUT_BF16, false, stream);
+}
+
+extern "C" ft_status ft_linear_bwd_op(int64_t M, int64_t N, int64_t K, const uint8_t* g_op,
+                                      const uint8_t* g_op_scales, const uint8_t* rt_op, const uint8_t* rt_op_scales,
+                                      const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                                      const void* X, const void* G, const float* T,
+                                      void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  using namespace ft;
+  if (dxdt != FT_OUT_F32 && dxdt != FT_OUT_BF16) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  const int rho = rs + r;
+  const size_t need = ft_linear_bwd_workspace(M, N, K, r);
+  if (M && K && !dX) return FT_EINVAL;
+  if (M && N && K && (!g_op || !g_op_scales || !rt_op || !rt_op_scales)) return FT_EINVAL;
+  if (M && rho && !V) return FT_EINVAL;
+  if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
+  if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
+  if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
+  const void* ptrs[] = {g_op, g_op_scales, rt_op, rt_op_scales, V, L1t, At, X, G, T, dX, dAt, dB, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  // dX = deq(Gq) deq(Rq) + V [L1^T; A^T]: reduction over the N output features;
+  // the right operand is R^T's operand (pairs along N)
+  if (M && K) {
+    const int64_t gn = op_groups(N);
+    GemmArgs g{};
+    g.M = M; g.N = K; g.K = N;
+    g.A = g_op; g.lda = gn * 96;
+    g.B = rt_op; g.ldb = gn * 96;
+    g.sA = g_op_scales; g.sA_rs = gn * 8;
+    g.sB = rt_op_scales; g.sB_rs = gn * 8;
+    g.P = V;
+    g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
+    g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
+    g.C = dX; g.ldc = K;
+    ft_status st = launch_gemm_m6(g, dxdt == FT_OUT_BF16, true, stream);
     if (st != FT_OK) return st;
   }
-  return FT_OK;
+  return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
 }

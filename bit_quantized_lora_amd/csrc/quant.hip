@@ -25,6 +25,8 @@
 // scale 2^shift and re-encoded with the f32 -> FP6 (E3M2) convert, both exact
 // for these values.  The tile's 128 columns (rows) are exactly one 128-wide
 // operand group, so every byte of the operand, padding included, is written.
+// Within a group the last 8 bytes of pairs 0..3 are stored in the order 0, 2,
+// 1, 3, so that one 16-byte read gives a GEMM lane both of its pairs' tails.
 #include "ft_common.h"
 
 namespace ft {
@@ -268,7 +270,7 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
         const v6u f = merge_pair(w, s_e[b1], s_e[b1 + 1], s_z[b1] != 0, s_z[b1 + 1] != 0, s1, s2);
         uint8_t* dst = o.op_rm + (row0 + r) * pitch + blockIdx.x * OP_GROUP_BYTES;
         *reinterpret_cast<v4i*>(dst + 16 * p) = v4i{(int)f[0], (int)f[1], (int)f[2], (int)f[3]};
-        *reinterpret_cast<v2i*>(dst + 64 + 8 * p) = v2i{(int)f[4], (int)f[5]};
+        *reinterpret_cast<v2i*>(dst + 64 + 8 * (2 * (p & 1) + (p >> 1))) = v2i{(int)f[4], (int)f[5]};
         if ((r & 15) == 0)
           *reinterpret_cast<uint16_t*>(o.op_rm_scales + (row0 / 16 + (r >> 4)) * spitch + blockIdx.x * 8 + 2 * p) =
               (uint16_t)(s1 | (s2 << 8));
@@ -290,7 +292,7 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
         const v6u f = merge_pair(w, s_e[b1], s_e[b2], s_z[b1] != 0, s_z[b2] != 0, s1, s2);
         uint8_t* dst = o.op_cm + (col0 + cl) * pitch + blockIdx.y * OP_GROUP_BYTES;
         *reinterpret_cast<v4i*>(dst + 16 * p) = v4i{(int)f[0], (int)f[1], (int)f[2], (int)f[3]};
-        *reinterpret_cast<v2i*>(dst + 64 + 8 * p) = v2i{(int)f[4], (int)f[5]};
+        *reinterpret_cast<v2i*>(dst + 64 + 8 * (2 * (p & 1) + (p >> 1))) = v2i{(int)f[4], (int)f[5]};
         if ((cl & 15) == 0)
           *reinterpret_cast<uint16_t*>(o.op_cm_scales + (col0 / 16 + (cl >> 4)) * spitch + blockIdx.y * 8 + 2 * p) =
               (uint16_t)(s1 | (s2 << 8));

@@ -176,6 +176,44 @@ def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G,
     return dX, dAt, dB
 
 
+def linear_fwd_op(x_op, x_op_scales, r_op, r_op_scales, T, L2, B, M: int, N: int, K: int,
+                  out_dtype=torch.float32, out: Optional[torch.Tensor] = None):
+    """Y of Eq. 2 from pair-merged operands (ft_quant_block16_op op_rm of X and of R)."""
+    rs, r = L2.shape[0], B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=T.device)
+    st = lib().ft_linear_fwd_op(M, N, K, x_op.data_ptr(), x_op_scales.data_ptr(), r_op.data_ptr(),
+                                r_op_scales.data_ptr(), T.data_ptr(), L2.data_ptr(), rs, B.data_ptr(), r,
+                                out.data_ptr(), _OUT[out.dtype], _stream(T))
+    check("ft_linear_fwd_op", st)
+    return out
+
+
+def linear_bwd_op(g_op, g_op_scales, rt_op, rt_op_scales, V, L1t, At, X, G, T, M: int, N: int, K: int,
+                  out_dtype=torch.float32, workspace: Optional[torch.Tensor] = None,
+                  dX: Optional[torch.Tensor] = None, dAt: Optional[torch.Tensor] = None,
+                  dB: Optional[torch.Tensor] = None):
+    """dX, dAt, dB of Eq. 3 from pair-merged operands (op_rm of G, op_cm of R)."""
+    rs, r = L1t.shape[0], At.shape[0]
+    dev = V.device
+    if dX is None:
+        dX = torch.empty((M, K), dtype=out_dtype, device=dev)
+    if dAt is None:
+        dAt = torch.empty((r, K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((r, N), dtype=torch.float32, device=dev)
+    ws_bytes = linear_bwd_workspace(M, N, K, r)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    st = lib().ft_linear_bwd_op(M, N, K, g_op.data_ptr(), g_op_scales.data_ptr(), rt_op.data_ptr(),
+                                rt_op_scales.data_ptr(), V.data_ptr(), L1t.data_ptr(), rs, At.data_ptr(), r,
+                                X.data_ptr(), G.data_ptr(), T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype],
+                                dAt.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream(V))
+    check("ft_linear_bwd_op", st)
+    return dX, dAt, dB
+
+
 def gelu_fwd(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     _need(y, torch.bfloat16, "y")
     if out is None:

@@ -105,9 +105,10 @@ ft_status ft_quant_block16(const void* x, int64_t rows, int64_t cols, int64_t ld
  * Layout of the operand of a [rows x cols] matrix (pairs along cols):
  *  data    [rows][G * 96] bytes, G = ceil(cols / 128) groups of 4 pairs
  *          (columns past cols are zero padding).  Per row and group: the first
- *          16 bytes of each pair's 24-byte packed value (64 bytes), then the last
- *          8 bytes of each (32 bytes).  The 24-byte value of a pair holds its 32
- *          elements, element n in bits 6n .. 6n+5, little-endian.
+ *          16 bytes of each pair's 24-byte packed value (64 bytes, pairs 0..3),
+ *          then the last 8 bytes of pairs 0, 2, 1, 3 in that order (32 bytes).
+ *          The 24-byte value of a pair holds its 32 elements, element n in bits
+ *          6n .. 6n+5, little-endian.
  *  scales  [rows/16][G * 8] bytes: entries 2p, 2p+1 are pair p's two bytes. */
 size_t ft_operand_bytes(int64_t rows, int64_t cols);
 size_t ft_operand_scale_bytes(int64_t rows, int64_t cols);
@@ -188,6 +189,29 @@ ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
                         void* workspace, size_t ws_bytes, hipStream_t stream);
 
 size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* ft_linear_fwd_op / ft_linear_bwd_op -- the same Eq. 2 and Eq. 3 (and adapter
+ * gradients) with the 4-bit operands given as pair-merged operands
+ * (ft_quant_block16_op), FT_SCALE_POW2 only.  Results equal those of
+ * ft_linear_fwd / ft_linear_bwd on the same Q(.) up to fp32 summation order:
+ * the operands carry exactly the same values, but every 32-K MFMA fragment is
+ * filled instead of half of it.
+ *
+ *  fwd:  x_op, x_op_scales   operand of X  [M x K] (op_rm of X)
+ *        r_op, r_op_scales   operand of R  [N x K] (op_rm of R)
+ *  bwd:  g_op, g_op_scales   operand of G  [M x N] (op_rm of G)
+ *        rt_op, rt_op_scales operand of R^T [K x N] (op_cm of R)
+ * Other arguments, layouts and the workspace are those of ft_linear_fwd / _bwd. */
+ft_status ft_linear_fwd_op(int64_t M, int64_t N, int64_t K, const uint8_t* x_op, const uint8_t* x_op_scales,
+                           const uint8_t* r_op, const uint8_t* r_op_scales,
+                           const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                           void* Y, ft_out_dtype ydt, hipStream_t stream);
+ft_status ft_linear_bwd_op(int64_t M, int64_t N, int64_t K, const uint8_t* g_op, const uint8_t* g_op_scales,
+                           const uint8_t* rt_op, const uint8_t* rt_op_scales,
+                           const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                           const void* X, const void* G, const float* T,
+                           void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* GELU between the two linears of an MLP (section 3.3 "MLP Fusion" names the
  * activation; the exact erf form x * Phi(x) is used).  h = GELU(y) in bf16;

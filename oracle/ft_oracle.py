@@ -243,11 +243,13 @@ def pack_cm(codes) -> np.ndarray:
 # Layout: the column index is padded to a multiple of OP_GROUP = 128 (4 pairs;
 # padding is all-zero codes with scale byte 0).  A row of the operand has
 # 96 bytes per group: the first 16 bytes of the 24-byte packed value of pairs
-# 0..3 of the group (64 bytes), then their last 8 bytes (32 bytes).  The
+# 0..3 of the group (64 bytes), then the last 8 bytes of pairs 0, 2, 1, 3 in
+# that order (32 bytes: a 16-byte unit per pair parity).  The
 # 24-byte value of a pair holds its 32 elements, element n (column 32p + n)
 # in bits 6n .. 6n+5, little-endian.  The scale grid is [rows/16, 8 * groups]
 # bytes: entries 2p and 2p + 1 of row block rb are the bytes of blocks b1, b2.
 OP_GROUP = 128
+_HPOS = (0, 2, 1, 3)   # slot of pair q's last 8 bytes among the group's four
 
 
 def e3m2_decode(codes) -> np.ndarray:
@@ -324,7 +326,8 @@ def operand_merge(codes, scales) -> Tuple[np.ndarray, np.ndarray]:
     for p in range(P):
         grp, q = divmod(p, 4)
         op[:, 96 * grp + 16 * q: 96 * grp + 16 * q + 16] = packed[:, p, :16]
-        op[:, 96 * grp + 64 + 8 * q: 96 * grp + 64 + 8 * q + 8] = packed[:, p, 16:]
+        h = 64 + 8 * _HPOS[q]
+        op[:, 96 * grp + h: 96 * grp + h + 8] = packed[:, p, 16:]
     osc = np.zeros((srows, scols), np.uint8)
     osc[:, 0::2] = s1
     osc[:, 1::2] = s2
@@ -340,7 +343,8 @@ def operand_values(op, op_scales, rows: int, cols: int) -> np.ndarray:
     for p in range(P):
         grp, q = divmod(p, 4)
         packed[:, p, :16] = op[:, 96 * grp + 16 * q: 96 * grp + 16 * q + 16]
-        packed[:, p, 16:] = op[:, 96 * grp + 64 + 8 * q: 96 * grp + 64 + 8 * q + 8]
+        h = 64 + 8 * _HPOS[q]
+        packed[:, p, 16:] = op[:, 96 * grp + h: 96 * grp + h + 8]
     bits = np.unpackbits(packed, axis=-1, bitorder="little").reshape(rows, P, 32, 6)
     c6 = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)      # [rows, P, 32]
     v = e3m2_decode(c6).reshape(rows, 32 * P)

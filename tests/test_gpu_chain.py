@@ -32,14 +32,14 @@ def _config(cfg):
 
 
 class GpuLayer:
-    """Device-side prepared layer: Q(R) in both layouts, rank-major factors."""
+    """Device-side prepared layer: Q(R)'s pair-merged operands (R and R^T),
+    rank-major factors; the GEMMs run on the pair-merged operand path."""
 
     def __init__(self, d):
         from bit_quantized_lora_amd import ops
         self.ops = ops
         self.N, self.K = d["R"].shape
-        R = dev_bf16(d["R"])
-        self.rq, self.rqc, self.rs, self.rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
+        self.ro = ops.quant_block16_op(dev_bf16(d["R"]), op_rm=True, op_cm=True)
         self.L1t = dev_bf16(np.ascontiguousarray(d["L1"].T))
         self.At = dev_bf16(np.ascontiguousarray(d["A"].T))
         self.L2, self.B = dev_bf16(d["L2"]), dev_bf16(d["B"])
@@ -47,18 +47,19 @@ class GpuLayer:
     def fwd(self, X, out_dtype):
         o = self.ops
         M = X.shape[0]
-        xq, _, xs = o.quant_block16(X, rm=True, cm=False)
+        xo = o.quant_block16_op(X, op_rm=True)
         T = o.lowrank_fused(X, self.L1t, self.At)
-        Y = o.linear_fwd(xq, xs, self.rq, self.rs, T, self.L2, self.B, M, self.N, self.K, out_dtype=out_dtype)
+        Y = o.linear_fwd_op(xo["op_rm"], xo["op_rm_scales"], self.ro["op_rm"], self.ro["op_rm_scales"], T, self.L2,
+                            self.B, M, self.N, self.K, out_dtype=out_dtype)
         return Y, T
 
     def bwd(self, G, X, T, out_dtype):
         o = self.ops
         M = G.shape[0]
-        gq, _, gs = o.quant_block16(G, rm=True, cm=False)
+        go = o.quant_block16_op(G, op_rm=True)
         V = o.lowrank_fused(G, self.L2, self.B)
-        dX, dAt, dB = o.linear_bwd(gq, gs, self.rqc, self.rsct, V, self.L1t, self.At, X, G, T,
-                                   M, self.N, self.K, out_dtype=out_dtype)
+        dX, dAt, dB = o.linear_bwd_op(go["op_rm"], go["op_rm_scales"], self.ro["op_cm"], self.ro["op_cm_scales"], V,
+                                      self.L1t, self.At, X, G, T, M, self.N, self.K, out_dtype=out_dtype)
         return dX, dAt, dB
 
 

@@ -22,8 +22,11 @@ TOL = 2e-3
 BUDGET = 1e-4
 
 
-def _gpu_linear(d, out_dtype=None):
-    """Run quantize -> low-rank -> fwd and quantize -> low-rank -> bwd on the GPU."""
+def _gpu_linear(d, out_dtype=None, path="codes"):
+    """Run quantize -> low-rank -> fwd and quantize -> low-rank -> bwd on the GPU.
+
+    path "codes": the GEMMs read E2M1 codes + block scales (one 16-K block per
+    32-K MFMA fragment); path "op": they read the pair-merged operands."""
     import torch
     from bit_quantized_lora_amd import ops
     out_dtype = out_dtype or torch.float32
@@ -33,13 +36,22 @@ def _gpu_linear(d, out_dtype=None):
     L2, B = dev_bf16(d["L2"]), dev_bf16(d["B"])
     M, K = d["X"].shape
     N = d["R"].shape[0]
-    xq, _, xs = ops.quant_block16(X, rm=True, cm=False)
-    rq, rqc, rsc, rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
     T = ops.lowrank_fused(X, L1t, At)
-    Y = ops.linear_fwd(xq, xs, rq, rsc, T, L2, B, M, N, K, out_dtype=out_dtype)
-    gq, _, gs = ops.quant_block16(G, rm=True, cm=False)
     V = ops.lowrank_fused(G, L2, B)
-    dX, dAt, dB = ops.linear_bwd(gq, gs, rqc, rsct, V, L1t, At, X, G, T, M, N, K, out_dtype=out_dtype)
+    if path == "codes":
+        xq, _, xs = ops.quant_block16(X, rm=True, cm=False)
+        rq, rqc, rsc, rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
+        Y = ops.linear_fwd(xq, xs, rq, rsc, T, L2, B, M, N, K, out_dtype=out_dtype)
+        gq, _, gs = ops.quant_block16(G, rm=True, cm=False)
+        dX, dAt, dB = ops.linear_bwd(gq, gs, rqc, rsct, V, L1t, At, X, G, T, M, N, K, out_dtype=out_dtype)
+    else:
+        xo = ops.quant_block16_op(X, op_rm=True)
+        ro = ops.quant_block16_op(R, op_rm=True, op_cm=True)
+        Y = ops.linear_fwd_op(xo["op_rm"], xo["op_rm_scales"], ro["op_rm"], ro["op_rm_scales"], T, L2, B,
+                              M, N, K, out_dtype=out_dtype)
+        go = ops.quant_block16_op(G, op_rm=True)
+        dX, dAt, dB = ops.linear_bwd_op(go["op_rm"], go["op_rm_scales"], ro["op_cm"], ro["op_cm_scales"], V, L1t,
+                                        At, X, G, T, M, N, K, out_dtype=out_dtype)
     return {"Y": Y, "dX": dX, "dA": dAt, "dB": dB, "T": T, "V": V}
 
 
@@ -93,18 +105,19 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("path", ["codes", "op"])
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
-def test_linear_small_and_ragged(shape):
+def test_linear_small_and_ragged(shape, path):
     require_gpu()
     M, K, N, rs, r = shape
     rng = np.random.default_rng(M * 7 + K * 3 + N)
     spec = synth.LinearSpec("t", M, K, N, rs, r, x_outlier_count=min(4, K), x_outlier_mult=30.0,
                             w_outlier_cols=min(2, K), w_outlier_mult=20.0)
     d = synth.make_linear(spec, rng)
-    say(f"[linear] small {shape}")
-    gpu = _gpu_linear(d)
+    say(f"[linear] small {shape} path={path}")
+    gpu = _gpu_linear(d, path=path)
     rows = np.arange(M)
-    _compare(gpu, _oracle_rows(d, rows), rows, f"small{shape}")
+    _compare(gpu, _oracle_rows(d, rows), rows, f"small{shape}/{path}")
 
 
 def test_config1_full_and_bf16_and_determinism():
@@ -164,8 +177,9 @@ def _sample_strips(M, rng, n=6):
     return np.concatenate([np.arange(16 * i, 16 * i + 16) for i in s])
 
 
+@pytest.mark.parametrize("path", ["codes", "op"])
 @pytest.mark.parametrize("cfg", ["c2", "c3", "c4"])
-def test_full_size_configs_sampled_rows(cfg):
+def test_full_size_configs_sampled_rows(cfg, path):
     """Full-size launches (as the benchmark runs them); Y and dX are checked on
     sampled 16-row strips against the oracle, dA and dB in full."""
     require_gpu()
@@ -174,7 +188,43 @@ def test_full_size_configs_sampled_rows(cfg):
         if "X" not in d:  # second linear of a pair: a seeded stand-in input of the same shape
             rng = np.random.default_rng(99)
             d["X"] = synth.f32_to_bf16_bits(synth.make_tensor(rng, (spec.M, spec.K), "t3"))
-        say(f"[linear] full {spec.name} M={spec.M} K={spec.K} N={spec.N} rs={spec.rs} r={spec.r}")
-        gpu = _gpu_linear(d)
+        say(f"[linear] full {spec.name} M={spec.M} K={spec.K} N={spec.N} rs={spec.rs} r={spec.r} path={path}")
+        gpu = _gpu_linear(d, path=path)
         rows = _sample_strips(spec.M, np.random.default_rng(spec.M))
-        _compare(gpu, _oracle_rows(d, rows), rows, spec.name)
+        _compare(gpu, _oracle_rows(d, rows), rows, f"{spec.name}/{path}")
+
+
+@pytest.mark.parametrize("shape", [(272, 384, 512), (304, 1040, 400)], ids=lambda s: "x".join(map(str, s)))
+def test_op_path_with_unmerged_pairs_in_both_operands(shape):
+    """Outlier columns x2000 in X and in W open exponent gaps beyond the E3M2
+    range in both GEMM operands (forward: X and R; backward: G and R^T), so
+    k-steps take the two-round MFMA path; results stay within the budget and
+    match the codes path."""
+    require_gpu()
+    import torch
+    M, K, N = shape
+    rng = np.random.default_rng(K + N)
+    spec = synth.LinearSpec("t", M, K, N, 16, 16, x_outlier_count=8, x_outlier_mult=2000.0,
+                            w_outlier_cols=8, w_outlier_mult=2000.0)
+    d = synth.make_linear(spec, rng)
+    # G with outlier output channels, so the backward's left operand is split too;
+    # R with outlier columns and rows (the stabilizer split absorbs W's outlier
+    # columns, so R is scaled directly: any bf16 R is a valid GEMM input)
+    G = synth.bf16_bits_to_f32(d["G"])
+    G[:, rng.choice(N, 8, replace=False)] *= np.float32(2000.0)
+    d["G"] = synth.f32_to_bf16_bits(G)
+    R = synth.bf16_bits_to_f32(d["R"])
+    R[:, rng.choice(K, 8, replace=False)] *= np.float32(2000.0)
+    R[rng.choice(N, 8, replace=False), :] *= np.float32(2000.0)
+    d["R"] = synth.f32_to_bf16_bits(R)
+    for name, bits in (("X", d["X"]), ("R", d["R"]), ("G", d["G"]), ("R^T", np.ascontiguousarray(d["R"].T))):
+        c, sc = O.quantize_block16(bits)
+        _, osc = O.operand_merge(c, sc)
+        assert np.any(osc[:, 0::2] != osc[:, 1::2]), f"{name}: expected unmerged pairs"
+    say(f"[linear] unmerged pairs {shape}")
+    gpu = _gpu_linear(d, path="op")
+    rows = np.arange(M)
+    _compare(gpu, _oracle_rows(d, rows), rows, f"unmerged{shape}")
+    ref = _gpu_linear(d, path="codes")
+    for k in ("Y", "dX", "dA", "dB"):
+        assert O.rel_frob(host(gpu[k]), host(ref[k]).astype(np.float64)) < 1e-5

@@ -538,11 +538,16 @@ def test_operand_byte_layout():
     op, osc = O.operand_merge(codes, scales)
     assert op.shape == (16, 192) and osc.shape == (1, 16)
     assert op[0, 0] == 0b01000                        # element 0: bits 0..5 of byte 0
-    assert op[0, 64 + 7] == (0b10110 << 2)            # element 31: bits 186..191 = byte 23
+    assert op[0, 64 + 7] == (0b10110 << 2)            # element 31: bits 186..191 = byte 23 (pair 0: slot 0)
     assert op[0, 16] == ((0b101100 << 6) & 0xFF)      # pair 1, element 1: bits 6..11
     assert op[0, 17] == (0b101100 >> 2)
     assert op[0, 96] == 0b01100                       # pair 4 = group 1, first chunk
     assert np.count_nonzero(op) == 4                  # byte 16 holds only zero bits of it
+    # pair 1's last 8 bytes sit in slot 2 (order 0, 2, 1, 3): element 31 of pair 1
+    c3 = np.zeros((16, 128), np.uint8)
+    c3[0, 63] = 7
+    op3, _ = O.operand_merge(c3, np.full((1, 8), 127, np.uint8))
+    assert op3[0, 64 + 16 + 7] == (0b10110 << 2) and np.count_nonzero(op3) == 1
     assert np.all(osc[0, :10] == 127) and np.all(osc[0, 10:] == 0)
     # shift: block bytes 127 and 125 (gap 2) merge at 125; the first block's values x4
     codes2 = np.zeros((16, 32), np.uint8)
