@@ -41,8 +41,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0, help="token rows of the oracle sample (0: all)")
     ap.add_argument("--cpu-reps", type=int, default=3, help="oracle passes over the sample")
     ap.add_argument("--quant-reps", type=int, default=20)
-    ap.add_argument("--path", choices=["op", "codes"], default="op",
-                    help="GEMM operands: pair-merged FP6 operands (op) or E2M1 codes (codes)")
+    ap.add_argument("--path", choices=["fused", "codes", "op"], default="fused",
+                    help="fused: one pass quantizes and down-projects X (and G), GEMMs read E2M1 codes; "
+                         "codes: separate quantizer and low-rank passes; op: pair-merged FP6 GEMM operands")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (counter calibration for profiles)")
     return ap.parse_args()
@@ -64,8 +65,10 @@ def make_inputs():
 class Linear:
     """Device buffers and the step of one triple-branch linear (all preallocated).
 
-    path "op": the quantizer writes the pair-merged operands and the GEMMs read
-    them (a full 32-K fragment per MFMA); path "codes": E2M1 codes + scales."""
+    path "fused": one pass over X (G) writes Q(X) (Q(G)) and T (V); the GEMMs
+    read E2M1 codes + scales.  path "codes": the same with separate quantizer and
+    low-rank passes.  path "op": the quantizer writes the pair-merged operands
+    and the GEMMs read them (a full 32-K fragment per MFMA)."""
 
     def __init__(self, spec, d, path="op"):
         import torch
@@ -97,6 +100,22 @@ class Linear:
         self.dAt, self.dB = e((r, K), f32), e((r, N), f32)
         self.ws = e((max(ops.linear_bwd_workspace(M, N, K, r), 16),), u8)
         self.ws_lr = e((max(ops.lowrank_workspace(M, K, rs + r), ops.lowrank_workspace(M, N, rs + r), 16),), u8)
+
+    def quant_lowrank_x(self):
+        if self.path == "fused":
+            self.ops.quant_lowrank(self.X, self.L1t, self.At, out=self.T, codes=self.xq[0], scales=self.xq[2],
+                                   workspace=self.ws_lr)
+        else:
+            self.quant_x()
+            self.lowrank_x()
+
+    def quant_lowrank_g(self):
+        if self.path == "fused":
+            self.ops.quant_lowrank(self.G, self.L2, self.B, out=self.V, codes=self.gq[0], scales=self.gq[2],
+                                   workspace=self.ws_lr)
+        else:
+            self.quant_g()
+            self.lowrank_g()
 
     def quant_x(self):
         if self.path == "op":
@@ -135,13 +154,11 @@ class Linear:
                          self.T, M, N, K, workspace=self.ws, dX=self.dX, dAt=self.dAt, dB=self.dB)
 
     def forward(self):
-        self.quant_x()
-        self.lowrank_x()
+        self.quant_lowrank_x()
         self.gemm_fwd()
 
     def backward(self):
-        self.quant_g()
-        self.lowrank_g()
+        self.quant_lowrank_g()
         self.gemm_bwd_and_grads()
 
     def step(self):
@@ -261,8 +278,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record(s)
     for i in range(args.steps):
-        lin.quant_x()
-        lin.lowrank_x()
+        lin.quant_lowrank_x()
         ev[i][0].record(s)
         lin.gemm_fwd()
         ev[i][1].record(s)
@@ -272,16 +288,20 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / args.steps
     gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    # per-phase breakdown from one extra (untimed-region) step
-    names = ["quant_X", "lowrank_X", "fwd_gemm", "quant_G", "lowrank_G", "bwd_gemm_and_adapter_grads"]
-    fns = [lin.quant_x, lin.lowrank_x, lin.gemm_fwd, lin.quant_g, lin.lowrank_g, lin.gemm_bwd_and_grads]
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
-    marks[0].record(s)
-    for i, f in enumerate(fns):
-        f()
-        marks[i + 1].record(s)
+    # per-phase breakdown: events between the phases over `steps` further steps,
+    # enqueued back to back so the GPU never waits for the host
+    names = ["quant_lowrank_X", "fwd_gemm", "quant_lowrank_G", "bwd_gemm_and_adapter_grads"]
+    fns = [lin.quant_lowrank_x, lin.gemm_fwd, lin.quant_lowrank_g, lin.gemm_bwd_and_grads]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
+    host_t0 = time.perf_counter()
+    for k in range(args.steps):
+        marks[k][0].record(s)
+        for i, f in enumerate(fns):
+            f()
+            marks[k][i + 1].record(s)
+    host_us = (time.perf_counter() - host_t0) / args.steps * 1e6
     torch.cuda.synchronize()
-    phases = {n: marks[i].elapsed_time(marks[i + 1]) * 1e3 for i, n in enumerate(names)}
+    phases = {n: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks])) * 1e3 for i, n in enumerate(names)}
 
     quant = time_quantizer(args.quant_reps)
     if args.calibration_copy:
@@ -307,6 +327,7 @@ def main():
                    "x_dist": "student-t df=3", "scale_rule": "pow2 (amax/6 rounded up to 2^E)",
                    "gemm_operands": ("pair-merged FP6 E3M2 (two 16-K blocks per 32-K MFMA fragment)"
                                      if args.path == "op" else "E2M1 codes (one 16-K block per 32-K fragment)"),
+                   "quantizer_and_lowrank": "one pass" if args.path == "fused" else "separate passes",
                    "outputs": "bf16 Y and dX, fp32 dA and dB"},
         "pct_fp4_peak_whole_linear": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
         "roofline": {"kernel": ("gemm_m6_kernel" if args.path == "op" else "gemm_w4a4_kernel") + " (forward)",
@@ -315,6 +336,7 @@ def main():
                      "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                      "per_launch_flops": gemm_flops, "avg_launch_us": round(gemm_ms * 1e3, 2)},
         "phases_us": {k: round(v, 2) for k, v in phases.items()},
+        "host_enqueue_us_per_step": round(host_us, 1),
         "quantizer": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in quant.items()},
         "quant_GBps": round(quant["dY"]["GBps"], 1),

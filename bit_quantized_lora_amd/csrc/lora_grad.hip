@@ -6,9 +6,11 @@
 // Both are dW[j][c] = sum_m P[m][poff + j] Q[m][c] with a small fp32 P and a
 // large bf16 Q read once from HBM.  The MFMA needs runs of consecutive m in
 // both operands, so (1) a tiny pre-pass writes P's slice transposed and split
-// into bf16 hi + lo planes [r x M]; (2) each wave stages 64 x 64 tiles of Q in
-// its own LDS region transposed (so B fragments are single 16-byte reads) and
-// accumulates on bf16 MFMA 32x32x16; (3) the 4 waves of a workgroup, each owning
+// into bf16 hi + lo planes [r x M]; (2) each wave stages 64 x 64 tiles of Q
+// row-major in its own LDS region (16-byte writes) and takes the MFMA's
+// token-major B fragments with transposing LDS reads (ds_read_b64_tr_b16: four
+// tokens of one column per read) and accumulates on bf16 MFMA 32x32x16; (3) the
+// 4 waves of a workgroup, each owning
 // every 4th 64-row chunk of the workgroup's token range, are summed through LDS
 // in a fixed order, and token-range splits (for parallelism when the output is
 // narrow) are summed by a final pass in a fixed order: results are deterministic.
@@ -21,7 +23,7 @@ constexpr int LG_COLS = 64;                  // output columns per workgroup (12
 constexpr int LG_CHUNK = 64;
 constexpr int LG_WAVES = 4;
 constexpr int LG_THREADS = LG_WAVES * 64;
-constexpr int QT_PITCH = LG_CHUNK + 8;       // bf16 elements per LDS row of Q^T
+constexpr int Q_PITCH = 2 * LG_COLS + 16;     // bytes per LDS row of a staged Q tile (conflict-free tr reads)
 constexpr int RED_PITCH = 33;                // floats per LDS row of a 32 x 32 partial
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -55,35 +57,41 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
 template <int NRT>  // 32-row tiles over the adapter rank r (1..4)
 __global__ void __launch_bounds__(LG_THREADS)
 lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ Plo, int r,
                  const uint16_t* __restrict__ Q, int64_t M, int64_t ncols, int64_t rows_per_split,
                  float* __restrict__ out, int64_t out_split_stride) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_qt[LG_WAVES][LG_COLS * QT_PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[LG_WAVES][LG_CHUNK * Q_PITCH];
   __shared__ float s_red[LG_WAVES * 32 * RED_PITCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, lh = lane >> 5;
   const int64_t c0 = (int64_t)blockIdx.x * LG_COLS;
   const int64_t ms = (int64_t)blockIdx.y * rows_per_split;
   const int64_t me = min(M, ms + rows_per_split);
-  uint16_t* qt = s_qt[wave];
+  uint8_t* qs = s_q[wave];
+  // transposing read: within each 16-lane group, source lane 4r + q points at
+  // row (token) 8 * (group >> 1) + r and columns 16 * (group & 1) + 4q .. +3
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);
+  const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);
 
   v16f acc[NRT][2];
 #pragma unroll
   for (int t = 0; t < NRT; ++t) acc[t][0] = acc[t][1] = v16f{};
 
   for (int64_t mb = ms + (int64_t)wave * LG_CHUNK; mb < me; mb += LG_WAVES * LG_CHUNK) {
-    // Q[mb : mb+64, c0 : c0+64] -> LDS transposed (Qt[c][m])
+    // Q[mb : mb+64, c0 : c0+64] -> LDS, row-major, 16-byte chunks
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = lane + 64 * u, m = t >> 3, q = t & 7;
       v4i v = {0, 0, 0, 0};
       if (mb + m < me && c0 + 8 * q < ncols)
         v = *reinterpret_cast<const v4i*>(Q + (mb + m) * ncols + c0 + 8 * q);
-      const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qt[(8 * q + e) * QT_PITCH + m] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      *reinterpret_cast<v4i*>(qs + m * Q_PITCH + 16 * q) = v;
     }
     wave_sync();
 #pragma unroll
@@ -91,8 +99,13 @@ lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ 
       const int64_t m = mb + 16 * ks + 8 * lh;   // 8 consecutive tokens of this lane
       v8bf bq[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        bq[ct] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qt + (32 * ct + l32) * QT_PITCH + 16 * ks + 8 * lh));
+      for (int ct = 0; ct < 2; ++ct) {
+        const uint8_t* b0 = qs + (16 * ks + tr_row) * Q_PITCH + 2 * (32 * ct + tr_col);
+        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0));
+        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + 4 * Q_PITCH));
+        const v2i l2 = __builtin_bit_cast(v2i, lo4), h2 = __builtin_bit_cast(v2i, hi4);
+        bq[ct] = __builtin_bit_cast(v8bf, v4i{l2.x, l2.y, h2.x, h2.y});
+      }
 #pragma unroll
       for (int t = 0; t < NRT; ++t) {
         const int j = 32 * t + l32;

@@ -14,6 +14,16 @@
 // run on bf16 MFMA 32x32x16 with fp32 accumulation.  Each split writes its
 // partial sums to the workspace and a second pass adds the splits in a fixed
 // order, so the result is deterministic.
+//
+// ft_quant_lowrank adds the 4-bit quantizer Q(in) (16x16 blocks, power-of-two
+// scales, row-major E2M1 codes) to the same pass: a 128-row x 128-column chunk
+// is exactly 8 x 8 quantization blocks, already in registers for the
+// down-projection, so the input is read from HBM once for both (the LoRA fusion
+// of FourTune section 3.3 extended to the quantizer, which reads the same input).
+// Lane (l32, lh) of wave w holds 8 values of row 32w + l32 in each 16-column
+// block s; a block is spread over the 16 lanes of one DPP row and the matching
+// 16 lanes of the other wave half, so its maximum is a 16-lane DPP reduction and
+// one permlane32 swap across the halves.
 #include "ft_common.h"
 
 namespace ft {
@@ -25,13 +35,42 @@ constexpr int LR_THREADS = 256;
 constexpr int LR_ROWS = 128;            // rows per workgroup (4 waves x 32)
 constexpr int LR_CHUNK = 128;           // reduction columns per chunk (8 MFMA k-steps)
 constexpr int LR_WROW = LR_CHUNK * 2;   // bytes per LDS weight row (256, swizzled, unpadded)
-constexpr int LR_WBUF = 128 * LR_WROW;  // one weight chunk (up to 128 ranks)
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
 #define FT_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8))
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ int wswz(int row, int q) { return row * LR_WROW + ((q ^ (row & 15)) << 4); }
+
+// 16-lane maximum inside each DPP row (quad xor 1, xor 2, half-row mirror, row mirror)
+__device__ __forceinline__ uint32_t dpp_max16(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with the
+// lower 32 lanes of its second; with both operands v, lane l ends up with
+// v[l mod 32] in the first result and v[32 + l mod 32] in the second.
+__device__ __forceinline__ uint32_t other_half_max(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+// the value of v in lane l ^ 32 (lh = l >> 5)
+__device__ __forceinline__ uint32_t from_other_half(uint32_t v, int lh) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return lh ? (uint32_t)r[0] : (uint32_t)r[1];
+}
+
+// E = min{e : 6 * 2^e >= a} clamped to [-127, 127] from the bf16 magnitude bits a.
+__device__ __forceinline__ int pow2_exp(uint32_t a) {
+  const int e = (int)(a >> 7);
+  if (e == 0) return -127;
+  const int E = (e - 127) - 2 + ((a & 0x7f) > 0x40 ? 1 : 0);
+  return E < -127 ? -127 : (E > 127 ? 127 : E);
+}
 
 int64_t chunks_per_split(int64_t M, int64_t Kin) {
   const int64_t nchunks = (Kin + LR_CHUNK - 1) / LR_CHUNK;
@@ -49,12 +88,14 @@ int64_t num_splits(int64_t M, int64_t Kin) {
   return (nchunks + cps - 1) / cps;
 }
 
-template <int NCT>  // number of 32-wide rank column tiles (1..4)
+template <int NCT, bool QUANT>  // NCT: 32-wide rank column tiles (0..4); QUANT: also write Q(in)
 __global__ void __launch_bounds__(LR_THREADS)
 lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t ld_in,
                const uint16_t* __restrict__ wa, int ra, const uint16_t* __restrict__ wb, int rb,
-               int64_t cps, float* __restrict__ out, int64_t out_split_stride) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_w[2 * LR_WBUF];
+               int64_t cps, float* __restrict__ out, int64_t out_split_stride,
+               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t s_w[];   // 2 buffers of rho rows
+  const int wbuf_bytes = (ra + rb) * LR_WROW;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rho = ra + rb;
@@ -83,7 +124,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       const bool in_a = 4 * i < ra;                   // ra is a multiple of 16: rows 4i..4i+3 share a matrix
       const int jj = in_a ? row : row - ra;
       const uint32_t off = col < Kin ? (uint32_t)(((int64_t)jj * Kin + col) * 2) : 0x80000000u;
-      uint8_t* dst = s_w + buf * LR_WBUF + 4 * i * LR_WROW;
+      uint8_t* dst = s_w + buf * wbuf_bytes + 4 * i * LR_WROW;
       if (in_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(rWa, (lds_void*)dst, 16, off, 0, 0, 0);
       else __builtin_amdgcn_raw_ptr_buffer_load_lds(rWb, (lds_void*)dst, 16, off, 0, 0, 0);
     }
@@ -96,7 +137,89 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
     }
   };
 
-  v16f acc[NCT];
+  // Codes and scales of a full chunk wait in registers and are stored after the
+  // next chunk's barrier: the wait at the top of each chunk covers every
+  // outstanding memory operation, so stores issued right before it would make
+  // every chunk wait for a write round trip.
+  struct Pending {
+    v4i o0, o1;
+    v2i s;
+    uint8_t* codes;
+    uint8_t* scales;
+    bool live;
+  } pend;
+  pend.live = false;
+  auto flush = [&]() {
+    if (QUANT && pend.live) {
+      *reinterpret_cast<v4i*>(pend.codes) = pend.o0;
+      *reinterpret_cast<v4i*>(pend.codes + 16) = pend.o1;
+      if (pend.scales) *reinterpret_cast<v2i*>(pend.scales) = pend.s;
+      pend.live = false;
+    }
+  };
+
+  // Q(in) of the chunk held in xa: one 16x16 block per (row half of the wave, s)
+  auto quantize_chunk = [&](const v4i (&x)[8], int64_t c) {
+    uint32_t cw[8];
+    int ex[8];
+    uint32_t mx[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t d[4] = {(uint32_t)x[s].x, (uint32_t)x[s].y, (uint32_t)x[s].z, (uint32_t)x[s].w};
+      uint32_t m = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = max(m, max(d[k] & 0x7fffu, (d[k] >> 16) & 0x7fffu));
+      mx[s] = other_half_max(dpp_max16(m));
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t d[4] = {(uint32_t)x[s].x, (uint32_t)x[s].y, (uint32_t)x[s].z, (uint32_t)x[s].w};
+      const int E = pow2_exp(mx[s]);
+      ex[s] = E;
+      const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);
+      uint32_t w = 0;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo_to_f32(d[0]), bf16hi_to_f32(d[0]), sc, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo_to_f32(d[1]), bf16hi_to_f32(d[1]), sc, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo_to_f32(d[2]), bf16hi_to_f32(d[2]), sc, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo_to_f32(d[3]), bf16hi_to_f32(d[3]), sc, 3);
+      cw[s] = w;   // codes of columns 16s + 8lh .. +8 of this lane's row
+    }
+    if (!arow_ok) return;
+    const int64_t k0 = c * LR_CHUNK;
+    uint8_t* crow = codes + arow * (Kin / 2) + k0 / 2;
+    uint8_t* srow = scales + (arow / 16) * (Kin / 16) + k0 / 16;
+    const bool sc_lane = lh == 0 && (l32 & 15) == 0;
+    if (k0 + LR_CHUNK <= Kin) {
+      // lane half 0 holds bytes [0, 32) of the row's 64 (blocks 0-3), half 1 bytes [32, 64);
+      // the stores are issued after the next chunk's barrier (see pend)
+      uint32_t r[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r[k] = from_other_half(lh ? cw[k] : cw[k + 4], lh);
+      if (lh == 0) {
+        pend.o0 = v4i{(int)cw[0], (int)r[0], (int)cw[1], (int)r[1]};
+        pend.o1 = v4i{(int)cw[2], (int)r[2], (int)cw[3], (int)r[3]};
+      } else {
+        pend.o0 = v4i{(int)r[0], (int)cw[4], (int)r[1], (int)cw[5]};
+        pend.o1 = v4i{(int)r[2], (int)cw[6], (int)r[3], (int)cw[7]};
+      }
+      pend.s = v2i{(int)((ex[0] + 127) | (ex[1] + 127) << 8 | (ex[2] + 127) << 16 | (uint32_t)(ex[3] + 127) << 24),
+                   (int)((ex[4] + 127) | (ex[5] + 127) << 8 | (ex[6] + 127) << 16 | (uint32_t)(ex[7] + 127) << 24)};
+      pend.codes = crow + 32 * lh;
+      pend.scales = sc_lane ? srow : nullptr;
+      pend.live = true;
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        if (k0 + 16 * s < Kin) *reinterpret_cast<uint32_t*>(crow + 8 * s + 4 * lh) = cw[s];
+      if (sc_lane) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (k0 + 16 * s < Kin) srow[s] = (uint8_t)(ex[s] + 127);
+      }
+    }
+  };
+
+  v16f acc[NCT > 0 ? NCT : 1];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct] = v16f{};
 
@@ -111,11 +234,13 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
     FT_WAIT_VMCNT0();                    // this wave's DMA and loads of chunk c are done
     __builtin_amdgcn_s_barrier();        // every wave's DMA landed; buffer buf^1 is free
     compiler_fence();
+    flush();
     if (c + 1 < c_end) {
       issue_w(buf ^ 1, c + 1);
       load_x(xb, c + 1);
     }
-    const uint8_t* wbuf = s_w + buf * LR_WBUF;
+    if constexpr (QUANT) quantize_chunk(xa, c);
+    const uint8_t* wbuf = s_w + buf * wbuf_bytes;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -130,6 +255,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
     for (int s = 0; s < 8; ++s) xa[s] = xb[s];
   }
 
+  flush();
   float* o = out + (int64_t)blockIdx.y * out_split_stride;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -160,43 +286,75 @@ extern "C" size_t ft_lowrank_workspace(int64_t M, int64_t Kin, int32_t rho) {
   return S > 1 ? (size_t)(S * M * rho * sizeof(float)) : 0;
 }
 
-extern "C" ft_status ft_lowrank_fused(const void* in, int64_t M, int64_t Kin, int64_t ld_in,
-                                      const void* wa, int32_t ra, const void* wb, int32_t rb,
-                                      float* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  using namespace ft;
+namespace ft {
+namespace {
+ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, const void* wa, int32_t ra,
+                       const void* wb, int32_t rb, float* out, uint8_t* codes, uint8_t* scales, void* workspace,
+                       size_t ws_bytes, hipStream_t stream) {
   if (!mult16(M) || !mult16(Kin) || ld_in < Kin) return FT_ESHAPE;
   if (ra < 0 || rb < 0 || (ra % 16) || (rb % 16) || ra + rb > 128) return FT_ESHAPE;
   const int rho = ra + rb;
-  if (M == 0 || rho == 0) return FT_OK;
-  if (!out || (ra && !wa) || (rb && !wb) || (Kin && !in)) return FT_EINVAL;
+  const bool quant = codes != nullptr;
+  if (M == 0 || (rho == 0 && !quant)) return FT_OK;
+  if ((rho && !out) || (ra && !wa) || (rb && !wb) || (Kin && !in) || (quant && !scales)) return FT_EINVAL;
   if ((Kin && !aligned16(in)) || (ld_in % 8) || (ra && !aligned16(wa)) || (rb && !aligned16(wb)) ||
-      !aligned16(out))
+      (rho && !aligned16(out)) || (quant && (!aligned16(codes) || !aligned16(scales))))
     return FT_EALIGN;
-  if (Kin == 0) return fill_zero_f32(out, M * rho, stream);  // empty reduction
+  if (Kin == 0) return rho ? fill_zero_f32(out, M * rho, stream) : FT_OK;  // empty reduction
   if ((int64_t)rho * Kin * 2 >= ((int64_t)1 << 31)) return FT_ESHAPE;
-  const size_t need = ft_lowrank_workspace(M, Kin, rho);
+  const size_t need = rho ? ft_lowrank_workspace(M, Kin, rho) : 0;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   if (need && !aligned16(workspace)) return FT_EALIGN;
   const int64_t cps = chunks_per_split(M, Kin);
   const int64_t S = num_splits(M, Kin);
-  float* dst = S > 1 ? static_cast<float*>(workspace) : out;
+  float* dst = (S > 1 && rho) ? static_cast<float*>(workspace) : out;
   dim3 grid((unsigned)((M + LR_ROWS - 1) / LR_ROWS), (unsigned)S);
   const uint16_t* ip = static_cast<const uint16_t*>(in);
   const uint16_t* a = static_cast<const uint16_t*>(wa);
   const uint16_t* b = static_cast<const uint16_t*>(wb);
   const int64_t stride = M * rho;
   const int nct = (rho + 31) / 32;
-  switch (nct) {
-    case 1: hipLaunchKernelGGL(lowrank_kernel<1>, grid, dim3(LR_THREADS), 0, stream, ip, M, Kin, ld_in, a, ra, b, rb, cps, dst, stride); break;
-    case 2: hipLaunchKernelGGL(lowrank_kernel<2>, grid, dim3(LR_THREADS), 0, stream, ip, M, Kin, ld_in, a, ra, b, rb, cps, dst, stride); break;
-    case 3: hipLaunchKernelGGL(lowrank_kernel<3>, grid, dim3(LR_THREADS), 0, stream, ip, M, Kin, ld_in, a, ra, b, rb, cps, dst, stride); break;
-    default: hipLaunchKernelGGL(lowrank_kernel<4>, grid, dim3(LR_THREADS), 0, stream, ip, M, Kin, ld_in, a, ra, b, rb, cps, dst, stride); break;
+#define FT_LR_LAUNCH(N, Q)                                                                                   \
+  hipLaunchKernelGGL((lowrank_kernel<N, Q>), grid, dim3(LR_THREADS), (size_t)(2 * rho * LR_WROW), stream, ip, M, Kin, ld_in, a, ra, b, rb, \
+                     cps, dst, stride, codes, scales)
+  if (quant) {
+    switch (nct) {
+      case 0: FT_LR_LAUNCH(0, true); break;
+      case 1: FT_LR_LAUNCH(1, true); break;
+      case 2: FT_LR_LAUNCH(2, true); break;
+      case 3: FT_LR_LAUNCH(3, true); break;
+      default: FT_LR_LAUNCH(4, true); break;
+    }
+  } else {
+    switch (nct) {
+      case 1: FT_LR_LAUNCH(1, false); break;
+      case 2: FT_LR_LAUNCH(2, false); break;
+      case 3: FT_LR_LAUNCH(3, false); break;
+      default: FT_LR_LAUNCH(4, false); break;
+    }
   }
+#undef FT_LR_LAUNCH
   if (launch_status() != FT_OK) return FT_EHIP;
-  if (S > 1) {
+  if (S > 1 && rho) {
     hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((stride + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float*>(workspace), S, stride, out);
     return launch_status();
   }
   return FT_OK;
+}
+}  // namespace
+}  // namespace ft
+
+extern "C" ft_status ft_lowrank_fused(const void* in, int64_t M, int64_t Kin, int64_t ld_in,
+                                      const void* wa, int32_t ra, const void* wb, int32_t rb,
+                                      float* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return ft::lowrank_impl(in, M, Kin, ld_in, wa, ra, wb, rb, out, nullptr, nullptr, workspace, ws_bytes, stream);
+}
+
+extern "C" ft_status ft_quant_lowrank(const void* in, int64_t M, int64_t Kin, int64_t ld_in,
+                                      const void* wa, int32_t ra, const void* wb, int32_t rb, float* out,
+                                      uint8_t* codes_rm, uint8_t* scales, void* workspace, size_t ws_bytes,
+                                      hipStream_t stream) {
+  if (!codes_rm) return FT_EINVAL;
+  return ft::lowrank_impl(in, M, Kin, ld_in, wa, ra, wb, rb, out, codes_rm, scales, workspace, ws_bytes, stream);
 }

@@ -133,6 +133,30 @@ def lowrank_fused(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor,
     return out
 
 
+def quant_lowrank(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """(out, codes_rm, scales): [inp wa^T | inp wb^T] and Q(inp) in one read of inp."""
+    _need(inp, torch.bfloat16, "inp")
+    M, Kin = inp.shape
+    ra, rb = wa.shape[0], wb.shape[0]
+    dev = inp.device
+    if out is None:
+        out = torch.empty((M, ra + rb), dtype=torch.float32, device=dev)
+    if codes is None:
+        codes = torch.empty((M, Kin // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M // 16, Kin // 16), dtype=torch.uint8, device=dev)
+    ws_bytes = lowrank_workspace(M, Kin, ra + rb)
+    if ws_bytes and (workspace is None or workspace.numel() < ws_bytes):
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    st = lib().ft_quant_lowrank(inp.data_ptr(), M, Kin, inp.stride(0), wa.data_ptr(), ra, wb.data_ptr(), rb,
+                                out.data_ptr(), codes.data_ptr(), scales.data_ptr(), _ptr(workspace),
+                                workspace.numel() if workspace is not None else 0, _stream(inp))
+    check("ft_quant_lowrank", st)
+    return out, codes, scales
+
+
 def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
                out_dtype=torch.float32, mode: str = "pow2", out: Optional[torch.Tensor] = None):
     """Y = deq(Xq) deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B."""

@@ -146,6 +146,17 @@ ft_status ft_lowrank_fused(const void* in, int64_t M, int64_t Kin, int64_t ld_in
 
 size_t ft_lowrank_workspace(int64_t M, int64_t Kin, int32_t rho);
 
+/* ft_quant_lowrank -- ft_lowrank_fused and the quantizer Q(in) (FT_SCALE_POW2,
+ * row-major codes) in one read of the input: the LoRA fusion of section 3.3
+ * extended to the quantizer, which reads the same activations (forward: X) or
+ * gradient (backward: G).  out / workspace as ft_lowrank_fused (out may be NULL
+ * when ra + rb == 0); codes_rm [M x Kin/2] and scales [M/16 x Kin/16] E8M0 bytes
+ * as ft_quant_block16's codes_rm and scales, bit for bit. */
+ft_status ft_quant_lowrank(const void* in, int64_t M, int64_t Kin, int64_t ld_in,
+                           const void* wa, int32_t ra, const void* wb, int32_t rb, float* out,
+                           uint8_t* codes_rm, uint8_t* scales, void* workspace, size_t ws_bytes,
+                           hipStream_t stream);
+
 /* ft_linear_fwd -- Eq. 2 with the LoRA-fusion epilogue (section 3.3: the
  * backbone GEMM and the up-projections are accumulated in one kernel):
  *

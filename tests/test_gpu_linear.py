@@ -152,6 +152,41 @@ def test_lowrank_matches_oracle_products():
         assert O.rel_frob(out, ref) < 1e-5
 
 
+@pytest.mark.parametrize("case", [(144, 400, 16, 16), (272, 128, 32, 16), (16, 16, 0, 16), (528, 1040, 64, 64),
+                                  (256, 384, 0, 0), (4608, 3072, 32, 16), (4608, 12288, 32, 16)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_quant_lowrank_one_pass(case):
+    """Q(in) and the down-projection from one read of the input: codes and scales
+    bit-exact with the oracle's quantizer, the projection bit-identical to
+    ft_lowrank_fused and within fp32 rounding of the oracle's product."""
+    require_gpu()
+    from bit_quantized_lora_amd import ops
+    M, K, ra, rb = case
+    rng = np.random.default_rng(M * 3 + K)
+    X = synth.f32_to_bf16_bits(synth.make_tensor(rng, (M, K), "t3"))
+    X[:, :16] = synth.f32_to_bf16_bits(synth.make_tensor(rng, (M, 16), "normal", 1e3))  # wide exponent range
+    Wa = synth.f32_to_bf16_bits(synth.make_tensor(rng, (ra, K), "normal", 0.05))
+    Wb = synth.f32_to_bf16_bits(synth.make_tensor(rng, (rb, K), "normal", 0.01))
+    say(f"[quant-lowrank] {M}x{K} ra={ra} rb={rb}")
+    x, wa, wb = dev_bf16(X), dev_bf16(Wa), dev_bf16(Wb)
+    out, codes, scales = ops.quant_lowrank(x, wa, wb)
+    rows = _sample_strips(M, rng) if M > 1024 else np.arange(M)
+    c_ref, s_ref = O.quantize_block16(X[rows] if M > 1024 else X, "pow2")
+    got_c, got_s = host(codes), host(scales)
+    if M > 1024:
+        strips = np.unique(rows // 16)
+        assert np.array_equal(got_c[rows], O.pack_rm(c_ref))
+        assert np.array_equal(got_s[strips], s_ref)
+    else:
+        assert np.array_equal(got_c, O.pack_rm(c_ref))
+        assert np.array_equal(got_s, s_ref)
+    if ra + rb:
+        assert np.array_equal(host(out), host(ops.lowrank_fused(x, wa, wb)))
+        Xf = O.bf16_to_f64(X[rows])
+        ref = np.concatenate([Xf @ O.bf16_to_f64(Wa).T, Xf @ O.bf16_to_f64(Wb).T], axis=1)
+        assert O.rel_frob(host(out)[rows], ref) < 1e-5
+
+
 def test_gelu_matches_oracle():
     require_gpu()
     from bit_quantized_lora_amd import ops
