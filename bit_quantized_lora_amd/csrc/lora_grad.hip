@@ -83,16 +83,28 @@ lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ 
 #pragma unroll
   for (int t = 0; t < NRT; ++t) acc[t][0] = acc[t][1] = v16f{};
 
-  for (int64_t mb = ms + (int64_t)wave * LG_CHUNK; mb < me; mb += LG_WAVES * LG_CHUNK) {
-    // Q[mb : mb+64, c0 : c0+64] -> LDS, row-major, 16-byte chunks
+  // Q[mb : mb+64, c0 : c0+64] in registers (lane: rows t >> 3 of 8 chunks of 16
+  // bytes); the next tile's loads are in flight while this one is consumed
+  auto load_q = [&](v4i (&v)[8], int64_t mb) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = lane + 64 * u, m = t >> 3, q = t & 7;
-      v4i v = {0, 0, 0, 0};
-      if (mb + m < me && c0 + 8 * q < ncols)
-        v = *reinterpret_cast<const v4i*>(Q + (mb + m) * ncols + c0 + 8 * q);
-      *reinterpret_cast<v4i*>(qs + m * Q_PITCH + 16 * q) = v;
+      v[u] = (mb + m < me && c0 + 8 * q < ncols) ? *reinterpret_cast<const v4i*>(Q + (mb + m) * ncols + c0 + 8 * q)
+                                               : v4i{0, 0, 0, 0};
     }
+  };
+  v4i qa[8], qb[8];
+  const int64_t mstep = LG_WAVES * LG_CHUNK;
+  int64_t mb = ms + (int64_t)wave * LG_CHUNK;
+  if (mb < me) load_q(qa, mb);
+  for (; mb < me; mb += mstep) {
+    // tile -> LDS, row-major, 16-byte chunks
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = lane + 64 * u, m = t >> 3, q = t & 7;
+      *reinterpret_cast<v4i*>(qs + m * Q_PITCH + 16 * q) = qa[u];
+    }
+    if (mb + mstep < me) load_q(qb, mb + mstep);
     wave_sync();
 #pragma unroll
     for (int ks = 0; ks < LG_CHUNK / 16; ++ks) {
@@ -122,6 +134,8 @@ lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ 
       }
     }
     wave_sync();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) qa[u] = qb[u];
   }
 
   // sum the 4 wave partials in a fixed order and store this split's result
