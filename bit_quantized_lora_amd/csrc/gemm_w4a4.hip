@@ -46,6 +46,39 @@
 #include "ft_internal.h"
 
 namespace ft {
+// (tile configurations have external linkage: kernels templated on an
+//  internal-linkage type get no host launch stub)
+constexpr int TC_BKB = 64;
+constexpr int tc_max(int a, int b) { return a > b ? a : b; }
+// Tile configurations: BM x BN per workgroup, 8 waves in WM x (8 / WM), each
+// wave (32*TMI) x (32*TNI).  The square 256 x 256 tile is the default; the
+// 192 x 384 tile (same operand bytes per FLOP) is taken when it fills the chip
+// in fewer partial rounds, e.g. 4608 x 12288 = 768 tiles = 3 full rounds on
+// 256 CUs where 256 x 256 gives 864 tiles = 3.4 rounds.
+template <int BM_, int BN_, int WM_, int TMI_, int NS_, int CHUNK_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 8 / WM_, TMI = TMI_;
+  static constexpr int TNI = BN_ / (8 / WM_) / 32;
+  static constexpr int NS = NS_, CHUNK = CHUNK_;
+  static constexpr int A_ST = BM * TC_BKB, B_ST = BN * TC_BKB;
+  static constexpr int SA_DW = BM / 16 * 2, SB_DW = BN / 16 * 2;      // scale dwords per stage
+  static constexpr int STAGE = A_ST + B_ST + (SA_DW + SB_DW) * 4;
+  static constexpr int N16 = (BM + BN) / 16;                          // 1-KiB DMAs per stage
+  static constexpr int NQ = (N16 + 7) / 8;                            // ... per wave, at most
+  // scale DMAs: waves [0, WA) fetch A's scale dwords, the others B's
+  static constexpr int WA = (8 * SA_DW + (SA_DW + SB_DW) / 2) / (SA_DW + SB_DW);
+  static constexpr int LA = (SA_DW + WA - 1) / WA, LB = (SB_DW + (8 - WA) - 1) / (8 - WA);
+  static constexpr int SMEM = tc_max(NS * STAGE, 64 * (2 * BN + 32));
+  static_assert(BM == WM * 32 * TMI && BN == WN * 32 * TNI, "tile shape");
+  static_assert(LA <= 64 && LB <= 64 && WA >= 1 && WA < 8, "scale DMA split");
+};
+using CfgSquare = TileCfg<256, 256, 4, 2, 4, 64>;
+using CfgWide = TileCfg<192, 384, 2, 3, 4, 32>;
+template <int I> struct CfgOf { using type = CfgSquare; };
+template <> struct CfgOf<1> { using type = CfgWide; };
+}  // namespace ft
+
+namespace ft {
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -62,7 +95,7 @@ constexpr int STAGE = A_ST + B_ST + S_ST;
 constexpr int NS = 4;                           // pipeline depth (stages)
 constexpr int PIPE_LDS = NS * STAGE;
 constexpr int GEN_LDS = 2 * STAGE;
-constexpr int EPI_LDS = 64 * 544;               // W chunk of the epilogue (64 ranks)
+constexpr int EPI_LDS = 64 * 544;               // W chunk of the epilogue (64 ranks, 256-wide tile)
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int PIPE_SMEM = cmax(PIPE_LDS, EPI_LDS);
 constexpr int GEN_SMEM = cmax(GEN_LDS, EPI_LDS);
@@ -75,18 +108,30 @@ __device__ __forceinline__ int swz(int row, int q) { return row * BKB + ((q ^ ((
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-template <int TMI>
-using AccT = v16f[TMI][4];
+// DMA helpers: the buffer-load-to-LDS builtin is called from these non-template
+// functions (called from a kernel templated on the tile configuration, it left
+// that kernel without a host launch stub).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
+}
 
-// One 128-K stage for this wave's (32*TMI) x 128 sub-tile (16*TMI MFMAs per k-step).
-template <int TMI>
-__device__ __forceinline__ void mfma_stage(AccT<TMI>& acc, const uint8_t* st, int wm, int wn, int l32, int lh) {
+template <int TMI, int TNI>
+using AccT = v16f[TMI][TNI];
+
+// One 128-K stage for this wave's (32*TMI) x (32*TNI) sub-tile of a BMc x BNc
+// workgroup tile (TMI*TNI MFMAs per k-step).  Stage layout: A codes [BMc][64],
+// B codes [BNc][64], A scales [BMc/16][8], B scales [BNc/16][8].
+template <int TMI, int TNI, int BMc, int BNc>
+__device__ __forceinline__ void mfma_stage(AccT<TMI, TNI>& acc, const uint8_t* st, int wm, int wn, int l32, int lh) {
   const uint8_t* As = st;
-  const uint8_t* Bs = st + A_ST;
-  const uint8_t* SAs = st + A_ST + B_ST;
-  const uint8_t* SBs = SAs + (BM / 16) * 8;
-  v4i af[TMI][2], bf[4][2];
-  int sa[TMI], sb[4];
+  const uint8_t* Bs = st + BMc * BKB;
+  const uint8_t* SAs = Bs + BNc * BKB;
+  const uint8_t* SBs = SAs + (BMc / 16) * 8;
+  v4i af[TMI][2], bf[TNI][2];
+  int sa[TMI], sb[TNI];
 #pragma unroll
   for (int i = 0; i < TMI; ++i) {
     const int ra = wm * 32 * TMI + 32 * i + l32;
@@ -95,8 +140,8 @@ __device__ __forceinline__ void mfma_stage(AccT<TMI>& acc, const uint8_t* st, in
     sa[i] = *reinterpret_cast<const int*>(SAs + (ra >> 4) * 8 + 4 * lh);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rbn = wn * 128 + 32 * i + l32;
+  for (int i = 0; i < TNI; ++i) {
+    const int rbn = wn * 32 * TNI + 32 * i + l32;
     bf[i][0] = *reinterpret_cast<const v4i*>(Bs + swz(rbn, 2 * lh));
     bf[i][1] = *reinterpret_cast<const v4i*>(Bs + swz(rbn, 2 * lh + 1));
     sb[i] = *reinterpret_cast<const int*>(SBs + (rbn >> 4) * 8 + 4 * lh);
@@ -106,7 +151,7 @@ __device__ __forceinline__ void mfma_stage(AccT<TMI>& acc, const uint8_t* st, in
 #define FT_KSTEP(KK)                                                                              \
   _Pragma("unroll") for (int i = 0; i < TMI; ++i) {                                                 \
     const v8i aop = {af[i][(KK) >> 1][((KK) & 1) * 2], af[i][(KK) >> 1][((KK) & 1) * 2 + 1], 0, 0, 0, 0, 0, 0}; \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                               \
+    _Pragma("unroll") for (int j = 0; j < TNI; ++j) {                                             \
       const v8i bop = {bf[j][(KK) >> 1][((KK) & 1) * 2], bf[j][(KK) >> 1][((KK) & 1) * 2 + 1], 0, 0, 0, 0, 0, 0}; \
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[i][j], 4, 4, KK, sa[i], KK, sb[j]); \
     }                                                                                             \
@@ -144,20 +189,21 @@ __device__ __forceinline__ void quad_transpose4(float (&v)[4], int t) {
 // + P W over the tile, then store C.  smem must be free (callers synchronize first).
 //
 // W rows (rank-major, [rho x N]) are copied to LDS with buffer_load ... lds, one
-// 512-byte row per DMA instruction at a 544-byte pitch (bank-conflict-free for the
-// transposed reads below).  The bf16 MFMA's B operand needs 8 consecutive ranks of
+// tile-wide row per DMA instruction at a pitch of row bytes + 32 (bank-conflict-free
+// for the transposed reads below).  The bf16 MFMA's B operand needs 8 consecutive ranks of
 // one output column per lane; two ds_read_b64_tr_b16 deliver them: within each
 // 16-lane group, result lane i, slot r receives element i % 4 of the 8 bytes that
 // source lane 4r + i/4 addressed, so source lanes point 4 columns wide into 4
 // consecutive rows.  P's rows for up to 64 ranks are fetched with all loads in
-// flight at once; ranks beyond 64 are processed in a second chunk.
-constexpr int W_PITCH = 544;
-constexpr int EPI_CHUNK = 64;
-
-template <bool OUT_BF16, int TMI, int NWAVES>
-__device__ __forceinline__ void epilogue_and_store(AccT<TMI>& acc, const GemmArgs& g, uint8_t* smem, int64_t m0,
-                                                   int64_t n0, int tid, int wave, int wm, int wn, int l32,
-                                                   int lh) {
+// flight at once; ranks beyond one chunk are processed in further passes.
+// BNc: tile width (W rows staged at a pitch of 2*BNc + 32 bytes); CHUNK: ranks
+// per pass (their P values are held in registers while the pass runs).
+template <bool OUT_BF16, int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
+__device__ __forceinline__ void epilogue_and_store(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
+                                                   int64_t m0, int64_t n0, int tid, int wave, int wm, int wn,
+                                                   int l32, int lh) {
+  constexpr int W_PITCH = 2 * BNc + 32;
+  constexpr int EPI_CHUNK = CHUNK;
   const int lane = tid & 63;
   const int rho = g.ra + g.rb;
   if (rho > 0) {
@@ -167,17 +213,17 @@ __device__ __forceinline__ void epilogue_and_store(AccT<TMI>& acc, const GemmArg
         __builtin_amdgcn_make_buffer_rsrc((void*)g.Wb, 0, (int)((int64_t)g.rb * g.N * 2), RSRC_FLAGS);
     const int g16 = lane >> 4, s16 = lane & 15;
     const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);             // + 16 ks + 4 t
-    const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn*128 + 32 j
+    const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn*32*TNI + 32 j
     for (int jc = 0; jc < rho; jc += EPI_CHUNK) {
       const int nr = min(EPI_CHUNK, rho - jc);                   // multiple of 16
-      // (a) W rows jc .. jc+nr-1 -> LDS (lanes 0..31: 16 bytes = 8 columns each)
+      // (a) W rows jc .. jc+nr-1 -> LDS (lanes 0 .. BNc/8-1: 16 bytes = 8 columns each)
       for (int jr = wave; jr < nr; jr += NWAVES) {
         const int j = jc + jr;
         const bool in_a = j < g.ra;
         const int jj = in_a ? j : j - g.ra;
         const int64_t n = n0 + 8 * lane;
-        const uint32_t off = (lane < 32 && n < g.N) ? (uint32_t)(((int64_t)jj * g.N + n) * 2) : 0x80000000u;
-        if (lane < 32) {
+        const uint32_t off = (lane < BNc / 8 && n < g.N) ? (uint32_t)(((int64_t)jj * g.N + n) * 2) : 0x80000000u;
+        if (lane < BNc / 8) {
           if (in_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(rWa, (lds_void*)(smem + jr * W_PITCH), 16, off, 0, 0, 0);
           else __builtin_amdgcn_raw_ptr_buffer_load_lds(rWb, (lds_void*)(smem + jr * W_PITCH), 16, off, 0, 0, 0);
         }
@@ -205,10 +251,10 @@ __device__ __forceinline__ void epilogue_and_store(AccT<TMI>& acc, const GemmArg
 #pragma unroll
       for (int ks = 0; ks < EPI_CHUNK / 16; ++ks) {
         if (16 * ks < nr) {
-          v8bf wf[4];
+          v8bf wf[TNI];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint8_t* b0 = smem + (16 * ks + tr_row) * W_PITCH + 2 * (wn * 128 + 32 * j + tr_col);
+          for (int j = 0; j < TNI; ++j) {
+            const uint8_t* b0 = smem + (16 * ks + tr_row) * W_PITCH + 2 * (wn * 32 * TNI + 32 * j + tr_col);
             const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0));
             const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + 4 * W_PITCH));
             const v2i l2 = __builtin_bit_cast(v2i, lo4), h2 = __builtin_bit_cast(v2i, hi4);
@@ -226,7 +272,7 @@ __device__ __forceinline__ void epilogue_and_store(AccT<TMI>& acc, const GemmArg
             const v8bf plo = __builtin_bit_cast(v8bf, v4i{(int)(l[0] | l[1] << 16), (int)(l[2] | l[3] << 16),
                                                           (int)(l[4] | l[5] << 16), (int)(l[6] | l[7] << 16)});
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < TNI; ++j) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi, wf[j], acc[i][j], 0, 0, 0);
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo, wf[j], acc[i][j], 0, 0, 0);
             }
@@ -246,8 +292,8 @@ __device__ __forceinline__ void epilogue_and_store(AccT<TMI>& acc, const GemmArg
 #pragma unroll
   for (int i = 0; i < TMI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + 32 * j + (l32 & ~3);
+    for (int j = 0; j < TNI; ++j) {
+      const int64_t col = n0 + wn * 32 * TNI + 32 * j + (l32 & ~3);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
@@ -271,14 +317,17 @@ __device__ __forceinline__ void epilogue_and_store(AccT<TMI>& acc, const GemmArg
 // ---------------------------------------------------------------------------------------
 constexpr int GROUP_M = 4;   // tile rows per raster group
 
+
 // TRANS_B: backward instantiation (B = Q(R)^T); same code, separate name in profiles.
-template <bool OUT_BF16, bool TRANS_B>
+template <bool OUT_BF16, bool TRANS_B, int CFG>   // CFG: 0 square tile, 1 wide tile
 __global__ void __launch_bounds__(PGT, 1)
 gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[PIPE_SMEM];
+  using C = typename CfgOf<CFG>::type;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
+  constexpr int BMc = C::BM, BNc = C::BN, NSc = C::NS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int wm = wave >> 1, wn = wave & 1;                      // 4 x 2 waves of 64 x 128
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int l32 = lane & 31, lh = lane >> 5;
 
   // XCD-aware raster: hardware places workgroup b on XCD b % 8
@@ -289,75 +338,80 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   const int first_m = grp * GROUP_M;
   const int gm = min(GROUP_M, tiles_m - first_m);
   const int in_grp = v - grp * GROUP_M * tiles_n;
-  const int64_t m0 = (int64_t)(first_m + in_grp % gm) * BM;
-  const int64_t n0 = (int64_t)(in_grp / gm) * BN;
+  const int64_t m0 = (int64_t)(first_m + in_grp % gm) * BMc;
+  const int64_t n0 = (int64_t)(in_grp / gm) * BNc;
   const int nkt = (int)(g.K / 128);
 
   // buffer resources for this tile; rows past M / N fall outside the range and read 0
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(g.A + m0 * g.lda), 0, (int)(min<int64_t>(BM, g.M - m0) * g.lda), RSRC_FLAGS);
+      (void*)(g.A + m0 * g.lda), 0, (int)(min<int64_t>(BMc, g.M - m0) * g.lda), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(g.B + n0 * g.ldb), 0, (int)(min<int64_t>(BN, g.N - n0) * g.ldb), RSRC_FLAGS);
-  // scale DMA: waves 0-3 fetch A's 16 x 8 scale bytes, waves 4-7 B's (8 dwords each)
-  const bool scale_b = wave >= 4;
+      (void*)(g.B + n0 * g.ldb), 0, (int)(min<int64_t>(BNc, g.N - n0) * g.ldb), RSRC_FLAGS);
+  const bool scale_b = wave >= C::WA;
   const __amdgpu_buffer_rsrc_t rS = scale_b
       ? __builtin_amdgcn_make_buffer_rsrc((void*)(g.sB + (n0 / 16) * g.sB_rs), 0,
-                                          (int)(min<int64_t>(BN / 16, (g.N - n0) / 16) * g.sB_rs), RSRC_FLAGS)
+                                          (int)(min<int64_t>(BNc / 16, (g.N - n0) / 16) * g.sB_rs), RSRC_FLAGS)
       : __builtin_amdgcn_make_buffer_rsrc((void*)(g.sA + (m0 / 16) * g.sA_rs), 0,
-                                          (int)(min<int64_t>(BM / 16, (g.M - m0) / 16) * g.sA_rs), RSRC_FLAGS);
+                                          (int)(min<int64_t>(BMc / 16, (g.M - m0) / 16) * g.sA_rs), RSRC_FLAGS);
   const int64_t s_rs = scale_b ? g.sB_rs : g.sA_rs;
 
-  // per-lane source offsets: DMA instruction j of this wave fills tile rows
-  // 32*wave + 16*j .. +16; lane l lands at physical chunk l & 3 of row (l >> 2)
-  uint32_t offA[2], offB[2];
+  // DMA instruction q (0 .. N16-1) of a stage fills 16 rows: A rows 16q .. for
+  // q < BM/16, else B rows; wave w issues q = w, w + 8, ...  Lane l lands at
+  // physical chunk l & 3 of row l >> 2 (the swizzle picks the global chunk).
+  const int nq = (C::N16 - wave + 7) / 8;                      // this wave's count (uniform)
+  uint32_t offq[C::NQ];
+  int ldsq[C::NQ];
+  bool isb[C::NQ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 32 * wave + 16 * j + (lane >> 2);
-    const int q = (lane & 3) ^ ((row >> 2) & 3);
-    offA[j] = (uint32_t)(row * g.lda + 16 * q);
-    offB[j] = (uint32_t)(row * g.ldb + 16 * q);
+  for (int u = 0; u < C::NQ; ++u) {
+    const int q = wave + 8 * u;
+    isb[u] = q >= BMc / 16;
+    const int r0 = isb[u] ? 16 * q - BMc : 16 * q;
+    const int row = r0 + (lane >> 2);
+    const int qc = (lane & 3) ^ ((row >> 2) & 3);
+    offq[u] = (uint32_t)(row * (isb[u] ? g.ldb : g.lda) + 16 * qc);
+    ldsq[u] = (isb[u] ? C::A_ST : 0) + r0 * BKB;
   }
-  // lanes 0..7 of each wave: block row 4*(wave&3) + lane/2, blocks 4*(lane&1)..+3
-  const uint32_t offS = (uint32_t)((4 * (wave & 3) + (lane >> 1)) * s_rs + 4 * (lane & 1));
-  const int s_lds = A_ST + B_ST + 32 * wave;   // [0,128): A scales, [128,256): B scales
+  // scale dwords: A's are [BM/16][2], B's [BN/16][2]; wave w of its group takes a
+  // contiguous run of LA (LB) of them, one per lane
+  const int sw = scale_b ? wave - C::WA : wave;
+  const int sl = scale_b ? C::LB : C::LA;
+  const int sd = sw * sl + lane;
+  const bool s_on = lane < sl && sd < (scale_b ? C::SB_DW : C::SA_DW);
+  const uint32_t offS = (uint32_t)((sd >> 1) * s_rs + 4 * (sd & 1));
+  const int s_lds = C::A_ST + C::B_ST + 4 * ((scale_b ? C::SA_DW : 0) + sw * sl);
 
-  // every wave issues exactly 5 DMA instructions per stage
   auto issue = [&](int stage, int kt) {
-    uint8_t* base = smem + stage * STAGE;
+    uint8_t* base = smem + stage * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + (32 * wave + 16 * j) * BKB), 16,
-                                               offA[j] + (uint32_t)kt * BKB, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(base + A_ST + (32 * wave + 16 * j) * BKB), 16,
-                                               offB[j] + (uint32_t)kt * BKB, 0, 0, 0);
-    if (lane < 8)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void*)(base + s_lds), 4, offS + (uint32_t)kt * 8, 0, 0, 0);
+    for (int u = 0; u < C::NQ; ++u)
+      if (u < nq) dma16(isb[u] ? rB : rA, base + ldsq[u], offq[u] + (uint32_t)kt * BKB);
+    if (s_on) dma4(rS, base + s_lds, offS + (uint32_t)kt * 8);
   };
 
-  AccT<2> acc;
+  AccT<C::TMI, C::TNI> acc;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::TMI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < C::TNI; ++j) acc[i][j] = v16f{};
 
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
+  for (int s = 0; s < NSc - 1; ++s)
     if (s < nkt) issue(s, s);
 
   // steady state: stage kt is consumed while stages kt+1 .. kt+NS-1 are in flight.
-  // A wave's DMA of stage kt is complete once at most NS-2 later stages (5 DMAs
-  // each) are pending; the barrier then makes every wave's DMA visible and marks
-  // the buffer of stage kt-1 free for stage kt+NS-1.
+  // A wave's DMA of stage kt is complete once at most NS-2 later stages (nq + 1
+  // DMAs each) are pending; the barrier then makes every wave's DMA visible and
+  // marks the buffer of stage kt-1 free for stage kt+NS-1.
   int kt = 0;
-  for (; kt + NS - 1 < nkt; ++kt) {
+  for (; kt + NSc - 1 < nkt; ++kt) {
     compiler_fence();
-    FT_WAIT_VMCNT(5 * (NS - 2));
+    if (nq == C::NQ) FT_WAIT_VMCNT((C::NQ + 1) * (NSc - 2));
+    else FT_WAIT_VMCNT(C::NQ * (NSc - 2));
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    issue((kt + NS - 1) % NS, kt + NS - 1);
-    mfma_stage<2>(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
+    issue((kt + NSc - 1) % NSc, kt + NSc - 1);
+    mfma_stage<C::TMI, C::TNI, BMc, BNc>(acc, smem + (kt % NSc) * C::STAGE, wm, wn, l32, lh);
   }
   // drain: no more DMA to issue
   for (; kt < nkt; ++kt) {
@@ -365,12 +419,12 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     FT_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    mfma_stage<2>(acc, smem + (kt % NS) * STAGE, wm, wn, l32, lh);
+    mfma_stage<C::TMI, C::TNI, BMc, BNc>(acc, smem + (kt % NSc) * C::STAGE, wm, wn, l32, lh);
   }
   compiler_fence();
   FT_WAIT_VMCNT(0);
   __syncthreads();
-  epilogue_and_store<OUT_BF16, 2, 8>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
+  epilogue_and_store<OUT_BF16, C::TMI, C::TNI, 8, BNc, C::CHUNK>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -413,7 +467,7 @@ __device__ __forceinline__ bool unmerged(int s) { return ((s ^ (s >> 8)) & 0xff)
 
 // aoff / boff: this lane's region offset for its first A / B row (rows of the
 // other tiles are 32 rows = 1 KiB further; swizzle bits are unchanged).
-__device__ __forceinline__ void mfma_stage_m6(AccT<2>& acc, const uint8_t* st, int aoff, int boff, int asc,
+__device__ __forceinline__ void mfma_stage_m6(AccT<2, 4>& acc, const uint8_t* st, int aoff, int boff, int asc,
                                               int bsc) {
   const uint8_t* A = st;
   const uint8_t* B = st + M6_OPB;
@@ -528,7 +582,7 @@ gemm_m6_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   const int aoff = tswz(wm * 64 + l32, lh), boff = tswz(wn * 128 + l32, lh);
   const int asc = ((wm * 64 + l32) >> 4) * 8 + 2 * lh, bsc = ((wn * 128 + l32) >> 4) * 8 + 2 * lh;
 
-  AccT<2> acc;
+  AccT<2, 4> acc;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -561,7 +615,7 @@ gemm_m6_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   compiler_fence();
   FT_WAIT_VMCNT(0);
   __syncthreads();
-  epilogue_and_store<OUT_BF16, 2, 8>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
+  epilogue_and_store<OUT_BF16, 2, 4, 8, 256, 64>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -627,7 +681,7 @@ __global__ void __launch_bounds__(GT, 1) gemm_w4a4_generic_kernel(GemmArgs g) {
     Ss[tid] = ps;   // [0,128): A scales [16 rb][8 kb]; [128,256): B scales
   };
 
-  AccT<4> acc;
+  AccT<4, 4> acc;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -641,12 +695,28 @@ __global__ void __launch_bounds__(GT, 1) gemm_w4a4_generic_kernel(GemmArgs g) {
   for (int64_t kt = 0; kt < nkt; ++kt) {
     const int cur = (int)(kt & 1);
     if (kt + 1 < nkt) gload(kt + 1);
-    mfma_stage<4>(acc, smem + cur * STAGE, wm, wn, l32, lh);
+    mfma_stage<4, 4, BM, BN>(acc, smem + cur * STAGE, wm, wn, l32, lh);
     if (kt + 1 < nkt) lstore(cur ^ 1);
     __syncthreads();
   }
-  epilogue_and_store<OUT_BF16, 4, 4>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
+  epilogue_and_store<OUT_BF16, 4, 4, 4, 256, 64>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
 }
+
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) ==
+                                                 hipSuccess && c > 0)
+      n = c;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+// fraction of workgroup slots busy over the launch (one workgroup per CU)
+double fill(int64_t tiles, int cus) { return (double)tiles / (double)(((tiles + cus - 1) / cus) * cus); }
 
 }  // namespace
 
@@ -655,24 +725,31 @@ ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipSt
   const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;
-  const bool pipelined = g.K > 0 && g.K % 128 == 0 && BM * g.lda < ((int64_t)1 << 31) &&
-                         BN * g.ldb < ((int64_t)1 << 31);
+  const bool pipelined = g.K > 0 && g.K % 128 == 0 && BN * g.lda < ((int64_t)1 << 31) &&
+                         CfgWide::BN * g.ldb < ((int64_t)1 << 31);
   if (pipelined) {
-    const int per_xcd = (int)((tiles + 7) / 8);
+    const int cus = num_cus();
+    const int64_t wide = ((g.M + CfgWide::BM - 1) / CfgWide::BM) * ((g.N + CfgWide::BN - 1) / CfgWide::BN);
+    const bool use_wide = fill(wide, cus) > fill(tiles, cus) + 0.02;
+    const int64_t tm = use_wide ? (g.M + CfgWide::BM - 1) / CfgWide::BM : tiles_m;
+    const int64_t tn = use_wide ? (g.N + CfgWide::BN - 1) / CfgWide::BN : tiles_n;
+    const int per_xcd = (int)((tm * tn + 7) / 8);
     const dim3 grid((unsigned)(8 * per_xcd)), block(PGT);
-    const int tm = (int)tiles_m, tn = (int)tiles_n;
-    if (out_bf16) {
-      if (trans_b) hipLaunchKernelGGL((gemm_w4a4_kernel<true, true>), grid, block, 0, s, g, tm, tn, per_xcd);
-      else hipLaunchKernelGGL((gemm_w4a4_kernel<true, false>), grid, block, 0, s, g, tm, tn, per_xcd);
+#define FT_GEMM_LAUNCH(OB, TB, C) \
+  hipLaunchKernelGGL((gemm_w4a4_kernel<OB, TB, C>), grid, block, 0, s, g, (int)tm, (int)tn, per_xcd)
+    if (use_wide) {
+      if (out_bf16) { if (trans_b) FT_GEMM_LAUNCH(true, true, 1); else FT_GEMM_LAUNCH(true, false, 1); }
+      else { if (trans_b) FT_GEMM_LAUNCH(false, true, 1); else FT_GEMM_LAUNCH(false, false, 1); }
     } else {
-      if (trans_b) hipLaunchKernelGGL((gemm_w4a4_kernel<false, true>), grid, block, 0, s, g, tm, tn, per_xcd);
-      else hipLaunchKernelGGL((gemm_w4a4_kernel<false, false>), grid, block, 0, s, g, tm, tn, per_xcd);
+      if (out_bf16) { if (trans_b) FT_GEMM_LAUNCH(true, true, 0); else FT_GEMM_LAUNCH(true, false, 0); }
+      else { if (trans_b) FT_GEMM_LAUNCH(false, true, 0); else FT_GEMM_LAUNCH(false, false, 0); }
     }
-  } else {
-    const dim3 grid((unsigned)tiles), block(GT);
-    if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g);
+#undef FT_GEMM_LAUNCH
+    return launch_status();
   }
+  const dim3 grid((unsigned)tiles), block(GT);
+  if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g);
+  else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g);
   return launch_status();
 }
 

@@ -229,6 +229,22 @@ def test_full_size_configs_sampled_rows(cfg, path):
         _compare(gpu, _oracle_rows(d, rows), rows, f"{spec.name}/{path}")
 
 
+@pytest.mark.parametrize("path", ["codes", "op"])
+def test_wide_tile_ragged_edges(path):
+    """A shape for which the 192 x 384 workgroup tile fills the chip better than
+    256 x 256 (so the forward GEMM takes it), with ragged last tiles in both M
+    and N; rows sampled across the tiles, including the last ones."""
+    require_gpu()
+    M, K, N = 4592, 384, 12272
+    rng = np.random.default_rng(4592)
+    spec = synth.LinearSpec("t", M, K, N, 16, 16, x_dist="t3")
+    d = synth.make_linear(spec, rng)
+    say(f"[linear] wide-tile ragged M={M} K={K} N={N} path={path}")
+    gpu = _gpu_linear(d, path=path)
+    rows = np.unique(np.concatenate([_sample_strips(M, rng, 10), np.arange(M - 48, M)]))
+    _compare(gpu, _oracle_rows(d, rows), rows, f"wide-tile/{path}")
+
+
 @pytest.mark.parametrize("shape", [(272, 384, 512), (304, 1040, 400)], ids=lambda s: "x".join(map(str, s)))
 def test_op_path_with_unmerged_pairs_in_both_operands(shape):
     """Outlier columns x2000 in X and in W open exponent gaps beyond the E3M2
