@@ -6,8 +6,9 @@
 // up, or fp32), element code = round-to-nearest-even E2M1 of x / scale.
 //
 // One workgroup quantizes a 128x128 tile: the bf16 tile is read once from HBM
-// with fully coalesced 16-byte loads into LDS; each lane then owns one 16-element
-// row segment of one 16x16 block (16 lanes per block), reduces the block maximum
+// straight into registers (each lane owns one 16-element row segment of one
+// 16x16 block per pass, 16 lanes per block; a wave's 4 blocks are adjacent, so
+// its loads cover 16 rows x 128 contiguous bytes), reduces the block maximum
 // across its 16 lanes, converts with the hardware scaled E2M1 convert (which
 // rounds to nearest-even and saturates, matching the oracle bit for bit), and
 // transposes the 16x16 nibble block across the 16 lanes for the column-major
@@ -34,7 +35,6 @@ namespace {
 
 constexpr int QT = 128;                 // tile edge (elements)
 constexpr int QTHREADS = 256;
-constexpr int IN_PITCH = QT * 2 + 16;   // bytes per LDS input row (padded)
 constexpr int RM_PITCH = QT / 2 + 8;    // bytes per LDS row-major code row (padded)
 constexpr int CM_PITCH = QT / 2 + 8;    // bytes per LDS column-major code row (padded)
 constexpr int OP_GROUP_BYTES = 96;      // operand bytes per row per 128 reduction elements
@@ -126,7 +126,6 @@ template <bool POW2, bool WRITE_RM, bool WRITE_CM, bool OP_RM, bool OP_CM>
 __global__ void __launch_bounds__(QTHREADS)
 quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, QuantOut o) {
   constexpr bool STAGE_RM = WRITE_RM || OP_RM, STAGE_CM = WRITE_CM || OP_CM, OPS = OP_RM || OP_CM;
-  __shared__ __attribute__((aligned(16))) uint8_t s_in[QT * IN_PITCH];
   __shared__ __attribute__((aligned(16))) uint8_t s_rm[STAGE_RM ? QT * RM_PITCH : 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_cm[STAGE_CM ? QT * CM_PITCH : 16];
   __shared__ uint8_t s_e[OPS ? 64 : 1];   // scale byte of each of the tile's 8 x 8 blocks
@@ -142,28 +141,32 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
   const int trows = (int)min<int64_t>(QT, rows - row0);   // multiple of 16
   const int tcols = (int)min<int64_t>(QT, cols - col0);   // multiple of 16
 
-  // 1. HBM -> LDS, 16-byte chunks; 16 lanes cover one 256-byte tile row.
-#pragma unroll
-  for (int it = 0; it < (QT * QT * 2 / 16) / QTHREADS; ++it) {
-    int c = it * QTHREADS + tid;
-    int r = c >> 4, q = c & 15;
-    v4i v = {0, 0, 0, 0};
-    if (r < trows && q * 8 < tcols)
-      v = *reinterpret_cast<const v4i*>(x + (row0 + r) * ldx + col0 + q * 8);
-    *reinterpret_cast<v4i*>(s_in + r * IN_PITCH + q * 16) = v;
-  }
-  __syncthreads();
-
-  // 2. one 16-element row segment of one block per lane, 4 segments per lane.
+  // 1. each lane owns one 16-element row segment of one block per pass, read
+  //    straight from HBM (two 16-byte loads; the 4 blocks of a wave are
+  //    horizontally adjacent, so a wave reads 16 rows x 128 contiguous bytes).
+  //    All 4 passes' loads are issued before any is used.
   const int i = tid & 15;              // row inside the block
+  constexpr int NPASS = (QT / 16) * (QT / 16) * 16 / QTHREADS;
+  v4i seg[NPASS][2];
 #pragma unroll
-  for (int it = 0; it < (QT / 16) * (QT / 16) * 16 / QTHREADS; ++it) {
+  for (int it = 0; it < NPASS; ++it) {
+    const int b = it * (QTHREADS / 16) + (tid >> 4);   // block index in the tile
+    const int br = b >> 3, bc = b & 7;                 // 8x8 blocks per tile
+    seg[it][0] = seg[it][1] = v4i{0, 0, 0, 0};
+    if (br * 16 < trows && bc * 16 < tcols) {
+      const uint16_t* src = x + (row0 + br * 16 + i) * ldx + col0 + bc * 16;
+      seg[it][0] = *reinterpret_cast<const v4i*>(src);
+      seg[it][1] = *reinterpret_cast<const v4i*>(src + 8);
+    }
+  }
+
+  // 2. per block: amax across its 16 lanes, scale, codes, layouts.
+#pragma unroll
+  for (int it = 0; it < NPASS; ++it) {
     const int b = it * (QTHREADS / 16) + (tid >> 4);   // block index in the tile
     const int br = b >> 3, bc = b & 7;                 // 8x8 blocks per tile
     const bool live = (br * 16 < trows) && (bc * 16 < tcols);  // uniform over the 16 lanes
-    const uint8_t* src = s_in + (br * 16 + i) * IN_PITCH + bc * 32;
-    v4i p0 = *reinterpret_cast<const v4i*>(src);
-    v4i p1 = *reinterpret_cast<const v4i*>(src + 16);
+    const v4i p0 = seg[it][0], p1 = seg[it][1];
     uint32_t d[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
                      (uint32_t)p1.x, (uint32_t)p1.y, (uint32_t)p1.z, (uint32_t)p1.w};
     // block maximum of |x| on the bf16 bit patterns (magnitude order = integer order)
