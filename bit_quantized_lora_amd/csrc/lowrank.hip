@@ -64,6 +64,20 @@ __device__ __forceinline__ uint32_t from_other_half(uint32_t v, int lh) {
   return lh ? (uint32_t)r[0] : (uint32_t)r[1];
 }
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+// largest magnitude (as bf16 bits; magnitude order = integer order) of 8 bf16
+// values: sign bits cleared, packed 16-bit maxima, then the two halves
+__device__ __forceinline__ uint32_t abs_max8(const v4i& v) {
+  const v2u16 a = __builtin_bit_cast(v2u16, (uint32_t)v.x & 0x7fff7fffu);
+  const v2u16 b = __builtin_bit_cast(v2u16, (uint32_t)v.y & 0x7fff7fffu);
+  const v2u16 c = __builtin_bit_cast(v2u16, (uint32_t)v.z & 0x7fff7fffu);
+  const v2u16 d = __builtin_bit_cast(v2u16, (uint32_t)v.w & 0x7fff7fffu);
+  const v2u16 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max((uint32_t)m.x, (uint32_t)m.y);
+}
+
 // E = min{e : 6 * 2^e >= a} clamped to [-127, 127] from the bf16 magnitude bits a.
 __device__ __forceinline__ int pow2_exp(uint32_t a) {
   const int e = (int)(a >> 7);
@@ -165,11 +179,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
     uint32_t mx[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint32_t d[4] = {(uint32_t)x[s].x, (uint32_t)x[s].y, (uint32_t)x[s].z, (uint32_t)x[s].w};
-      uint32_t m = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) m = max(m, max(d[k] & 0x7fffu, (d[k] >> 16) & 0x7fffu));
-      mx[s] = other_half_max(dpp_max16(m));
+      mx[s] = other_half_max(dpp_max16(abs_max8(x[s])));
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -178,10 +188,10 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       ex[s] = E;
       const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);
       uint32_t w = 0;
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo_to_f32(d[0]), bf16hi_to_f32(d[0]), sc, 0);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo_to_f32(d[1]), bf16hi_to_f32(d[1]), sc, 1);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo_to_f32(d[2]), bf16hi_to_f32(d[2]), sc, 2);
-      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, bf16lo_to_f32(d[3]), bf16hi_to_f32(d[3]), sc, 3);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[0]), sc, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[1]), sc, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[2]), sc, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(v2bf, d[3]), sc, 3);
       cw[s] = w;   // codes of columns 16s + 8lh .. +8 of this lane's row
     }
     if (!arow_ok) return;
@@ -223,12 +233,10 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct] = v16f{};
 
-  v4i xa[8], xb[8];
-  if (c_begin < c_end) {
-    issue_w(0, c_begin);
-    load_x(xa, c_begin);
-  }
-  for (int64_t c = c_begin; c < c_end; ++c) {
+  // one chunk: wait for its DMA and loads, free the other buffer, start the next
+  // chunk's loads into xn, then quantize and project xc (the two register sets
+  // alternate, so nothing is copied between chunks)
+  auto step = [&](v4i (&xc)[8], v4i (&xn)[8], int64_t c) {
     const int buf = (int)((c - c_begin) & 1);
     compiler_fence();
     FT_WAIT_VMCNT0();                    // this wave's DMA and loads of chunk c are done
@@ -237,9 +245,9 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
     flush();
     if (c + 1 < c_end) {
       issue_w(buf ^ 1, c + 1);
-      load_x(xb, c + 1);
+      load_x(xn, c + 1);
     }
-    if constexpr (QUANT) quantize_chunk(xa, c);
+    if constexpr (QUANT) quantize_chunk(xc, c);
     const uint8_t* wbuf = s_w + buf * wbuf_bytes;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -247,12 +255,19 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       for (int ct = 0; ct < NCT; ++ct) {
         const int j = 32 * ct + l32;
         const v4i b = j < rho ? *reinterpret_cast<const v4i*>(wbuf + wswz(j, 2 * s + lh)) : v4i{0, 0, 0, 0};
-        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xa[s]),
+        acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, xc[s]),
                                                           __builtin_bit_cast(v8bf, b), acc[ct], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) xa[s] = xb[s];
+  };
+  v4i xa[8], xb[8];
+  if (c_begin < c_end) {
+    issue_w(0, c_begin);
+    load_x(xa, c_begin);
+  }
+  for (int64_t c = c_begin; c < c_end; c += 2) {
+    step(xa, xb, c);
+    if (c + 1 < c_end) step(xb, xa, c + 1);
   }
 
   flush();

@@ -9,8 +9,8 @@
 // straight into registers (each lane owns one 16-element row segment of one
 // 16x16 block per pass, 16 lanes per block; a wave's 4 blocks are adjacent, so
 // its loads cover 16 rows x 128 contiguous bytes), reduces the block maximum
-// across its 16 lanes, converts with the hardware scaled E2M1 convert (which
-// rounds to nearest-even and saturates, matching the oracle bit for bit), and
+// across its 16 lanes, converts with the hardware scaled E2M1 convert from bf16
+// (which rounds to nearest-even and saturates, matching the oracle bit for bit), and
 // transposes the 16x16 nibble block across the 16 lanes for the column-major
 // codes.  Both code layouts are staged in LDS and written with coalesced stores.
 //
@@ -40,6 +40,8 @@ constexpr int CM_PITCH = QT / 2 + 8;    // bytes per LDS column-major code row (
 constexpr int OP_GROUP_BYTES = 96;      // operand bytes per row per 128 reduction elements
 
 typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 typedef unsigned v6u __attribute__((ext_vector_type(6)));
 
 struct QuantOut {
@@ -169,13 +171,12 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
     const v4i p0 = seg[it][0], p1 = seg[it][1];
     uint32_t d[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
                      (uint32_t)p1.x, (uint32_t)p1.y, (uint32_t)p1.z, (uint32_t)p1.w};
-    // block maximum of |x| on the bf16 bit patterns (magnitude order = integer order)
-    uint32_t m = 0;
+    // block maximum of |x| on the bf16 bit patterns (magnitude order = integer
+    // order): sign bits cleared, packed 16-bit maxima, then the two halves
+    v2u16 pm = __builtin_bit_cast(v2u16, d[0] & 0x7fff7fffu);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t lo = d[k] & 0x7fffu, hi = (d[k] >> 16) & 0x7fffu;
-      m = max(m, max(lo, hi));
-    }
+    for (int k = 1; k < 8; ++k) pm = __builtin_elementwise_max(pm, __builtin_bit_cast(v2u16, d[k] & 0x7fff7fffu));
+    uint32_t m = max((uint32_t)pm.x, (uint32_t)pm.y);
     m = max(m, xor_lane<8>(m));
     m = max(m, xor_lane<4>(m));
     m = max(m, xor_lane<2>(m));
@@ -185,7 +186,7 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
     if constexpr (POW2) {
       const int E = pow2_exponent(m);
       const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);  // 2^E as the E8M0 operand
-#define FT_CVT(W, K, SEL) W = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(W, bf16lo_to_f32(d[K]), bf16hi_to_f32(d[K]), sc, SEL)
+#define FT_CVT(W, K, SEL) W = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(W, __builtin_bit_cast(v2bf, d[K]), sc, SEL)
       FT_CVT(w0, 0, 0); FT_CVT(w0, 1, 1); FT_CVT(w0, 2, 2); FT_CVT(w0, 3, 3);
       FT_CVT(w1, 4, 0); FT_CVT(w1, 5, 1); FT_CVT(w1, 6, 2); FT_CVT(w1, 7, 3);
 #undef FT_CVT
