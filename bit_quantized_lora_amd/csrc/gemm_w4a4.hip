@@ -71,8 +71,10 @@ struct TileCfg {
   static constexpr int SMEM = tc_max(NS * STAGE, 64 * (2 * BN + 32));
   static_assert(BM == WM * 32 * TMI && BN == WN * 32 * TNI, "tile shape");
   static_assert(LA <= 64 && LB <= 64 && WA >= 1 && WA < 8, "scale DMA split");
+  static_assert(CHUNK_ * (2 * BN_ + 32) <= STAGE, "low-rank W chunk must fit one stage buffer");
 };
-using CfgSquare = TileCfg<256, 256, 4, 2, 4, 64>;
+// CHUNK: ranks per low-rank pass; its W rows (pitch 2 BN + 32 bytes) fit one stage buffer
+using CfgSquare = TileCfg<256, 256, 4, 2, 4, 48>;
 using CfgWide = TileCfg<192, 384, 2, 3, 4, 32>;
 template <int I> struct CfgOf { using type = CfgSquare; };
 template <> struct CfgOf<1> { using type = CfgWide; };
@@ -198,10 +200,10 @@ __device__ __forceinline__ void quad_transpose4(float (&v)[4], int t) {
 // flight at once; ranks beyond one chunk are processed in further passes.
 // BNc: tile width (W rows staged at a pitch of 2*BNc + 32 bytes); CHUNK: ranks
 // per pass (their P values are held in registers while the pass runs).
-template <bool OUT_BF16, int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
-__device__ __forceinline__ void epilogue_and_store(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
-                                                   int64_t m0, int64_t n0, int tid, int wave, int wm, int wn,
-                                                   int l32, int lh) {
+template <int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
+__device__ __forceinline__ void lowrank_into_acc(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
+                                                 int64_t m0, int64_t n0, int tid, int wave, int wm, int wn,
+                                                 int l32, int lh) {
   constexpr int W_PITCH = 2 * BNc + 32;
   constexpr int EPI_CHUNK = CHUNK;
   const int lane = tid & 63;
@@ -284,6 +286,11 @@ __device__ __forceinline__ void epilogue_and_store(AccT<TMI, TNI>& acc, const Ge
       compiler_fence();
     }
   }
+}
+
+template <bool OUT_BF16, int TMI, int TNI>
+__device__ __forceinline__ void store_acc(AccT<TMI, TNI>& acc, const GemmArgs& g, int64_t m0, int64_t n0, int lane,
+                                          int wm, int wn, int l32, int lh) {
   // Store: each lane holds 4 consecutive rows of one column per group of 4
   // accumulator values; a 4 x 4 transpose across the 4 lanes of a quad (DPP quad
   // permutes) gives each lane one row of 4 consecutive columns, so the tile goes
@@ -310,6 +317,14 @@ __device__ __forceinline__ void epilogue_and_store(AccT<TMI, TNI>& acc, const Ge
         }
       }
     }
+}
+
+template <bool OUT_BF16, int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
+__device__ __forceinline__ void epilogue_and_store(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
+                                                   int64_t m0, int64_t n0, int tid, int wave, int wm, int wn,
+                                                   int l32, int lh) {
+  lowrank_into_acc<TMI, TNI, NWAVES, BNc, CHUNK>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
+  store_acc<OUT_BF16, TMI, TNI>(acc, g, m0, n0, tid & 63, wm, wn, l32, lh);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -398,6 +413,11 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
 #pragma unroll
   for (int s = 0; s < NSc - 1; ++s)
     if (s < nkt) issue(s, s);
+  // the low-rank up-projection P W goes into the accumulators first, in the
+  // buffer of stage NS-1 (free until the first steady iteration): its W and P
+  // loads overlap the pipeline fill instead of trailing the main loop
+  lowrank_into_acc<C::TMI, C::TNI, 8, BNc, C::CHUNK>(acc, g, smem + (NSc - 1) * C::STAGE, m0, n0, tid, wave, wm,
+                                                     wn, l32, lh);
 
   // steady state: stage kt is consumed while stages kt+1 .. kt+NS-1 are in flight.
   // A wave's DMA of stage kt is complete once at most NS-2 later stages (nq + 1
@@ -421,10 +441,7 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     compiler_fence();
     mfma_stage<C::TMI, C::TNI, BMc, BNc>(acc, smem + (kt % NSc) * C::STAGE, wm, wn, l32, lh);
   }
-  compiler_fence();
-  FT_WAIT_VMCNT(0);
-  __syncthreads();
-  epilogue_and_store<OUT_BF16, C::TMI, C::TNI, 8, BNc, C::CHUNK>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
+  store_acc<OUT_BF16, C::TMI, C::TNI>(acc, g, m0, n0, lane, wm, wn, l32, lh);
 }
 
 // ---------------------------------------------------------------------------------------
