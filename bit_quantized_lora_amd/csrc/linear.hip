@@ -2,6 +2,8 @@
 // ft_linear_bwd (Eq. 3 plus the adapter gradients of section 3.2), taking the
 // 4-bit operands either as E2M1 codes + block scales or as the pair-merged
 // operands of ft_quant_block16_op (the _op variants).
+#include <mutex>
+
 #include "ft_internal.h"
 
 namespace ft {
@@ -14,6 +16,53 @@ int64_t op_groups(int64_t k) { return (k + 127) / 128; }
 // dA^T = V[:, rs:]^T X ;  dB = T[:, rs:]^T G  (reductions over the M tokens)
 ft_status adapter_grads(int64_t M, int64_t N, int64_t K, const float* V, int rs, int r, const void* X,
                         const void* G, const float* T, float* dAt, float* dB, void* workspace, hipStream_t stream);
+
+// The adapter gradients do not depend on the dX GEMM.  They run on a second
+// stream that forks from the caller's stream after the GEMM is enqueued and
+// joins it again before the call returns, so the memory-bound reductions use
+// the CUs the GEMM leaves idle (e.g. 216 tiles on 256 CUs) instead of
+// following it.  One side stream per device, created on first use (default
+// priority); the fork/join events are created per call, so concurrent calls on
+// different streams share nothing but the side stream's queue.
+hipStream_t side_stream() {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
+    streams[dev] = nullptr;
+  return streams[dev];
+}
+
+// enqueue `gemm` on `stream` and the adapter gradients concurrently beside it
+template <class F>
+ft_status gemm_with_adapter_grads(F gemm, int64_t M, int64_t N, int64_t K, const float* V, int rs, int r,
+                                  const void* X, const void* G, const float* T, float* dAt, float* dB,
+                                  void* workspace, hipStream_t stream) {
+  hipStream_t side = r ? side_stream() : nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  if (side && (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
+               hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess))
+    side = nullptr;
+  if (!side) {  // no side stream: one after the other on the caller's stream
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
+    ft_status st = gemm(stream);
+    if (st != FT_OK) return st;
+    return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
+  }
+  ft_status st = FT_OK;
+  if (hipEventRecord(fork, stream) != hipSuccess) st = FT_EHIP;
+  if (st == FT_OK) st = gemm(stream);
+  if (st == FT_OK && hipStreamWaitEvent(side, fork, 0) != hipSuccess) st = FT_EHIP;
+  if (st == FT_OK) st = adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, side);
+  if (st == FT_OK && hipEventRecord(join, side) != hipSuccess) st = FT_EHIP;
+  if (st == FT_OK && hipStreamWaitEvent(stream, join, 0) != hipSuccess) st = FT_EHIP;
+  (void)hipEventDestroy(fork);
+  (void)hipEventDestroy(join);
+  return st;
+}
 
 }  // namespace
 }  // namespace ft
@@ -81,21 +130,19 @@ extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
 
   // dX = deq(Gq) deq(Rq) + V [L1^T; A^T]: GEMM over the output features N, with
   // R's column-major codes and transposed scale grid as the B operand.
-  if (M && K) {
-    GemmArgs g{};
-    g.M = M; g.N = K; g.K = N;
-    g.A = gq_codes; g.lda = N / 2;
-    g.B = rq_codes_cm; g.ldb = N / 2;
-    g.sA = static_cast<const uint8_t*>(gq_scales); g.sA_rs = N / 16;
-    g.sB = static_cast<const uint8_t*>(rq_scales_cm); g.sB_rs = N / 16;
-    g.P = V;
-    g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
-    g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
-    g.C = dX; g.ldc = K;
-    ft_status st = launch_gemm_w4a4(g, dxdt == FT_OUT_BF16, true, stream);
-    if (st != FT_OK) return st;
-  }
-  return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
+  GemmArgs g{};
+  g.M = M; g.N = K; g.K = N;
+  g.A = gq_codes; g.lda = N / 2;
+  g.B = rq_codes_cm; g.ldb = N / 2;
+  g.sA = static_cast<const uint8_t*>(gq_scales); g.sA_rs = N / 16;
+  g.sB = static_cast<const uint8_t*>(rq_scales_cm); g.sB_rs = N / 16;
+  g.P = V;
+  g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
+  g.C = dX; g.ldc = K;
+  const bool out_bf16 = dxdt == FT_OUT_BF16;
+  auto gemm = [&](hipStream_t s) { return (M && K) ? launch_gemm_w4a4(g, out_bf16, true, s) : FT_OK; };
+  return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
 }
 
 namespace ft {
@@ -163,20 +210,18 @@ extern "C" ft_status ft_linear_bwd_op(int64_t M, int64_t N, int64_t K, const uin
     if (p && !aligned16(p)) return FT_EALIGN;
   // dX = deq(Gq) deq(Rq) + V [L1^T; A^T]: reduction over the N output features;
   // the right operand is R^T's operand (pairs along N)
-  if (M && K) {
-    const int64_t gn = op_groups(N);
-    GemmArgs g{};
-    g.M = M; g.N = K; g.K = N;
-    g.A = g_op; g.lda = gn * 96;
-    g.B = rt_op; g.ldb = gn * 96;
-    g.sA = g_op_scales; g.sA_rs = gn * 8;
-    g.sB = rt_op_scales; g.sB_rs = gn * 8;
-    g.P = V;
-    g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
-    g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
-    g.C = dX; g.ldc = K;
-    ft_status st = launch_gemm_m6(g, dxdt == FT_OUT_BF16, true, stream);
-    if (st != FT_OK) return st;
-  }
-  return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
+  const int64_t gn = op_groups(N);
+  GemmArgs g{};
+  g.M = M; g.N = K; g.K = N;
+  g.A = g_op; g.lda = gn * 96;
+  g.B = rt_op; g.ldb = gn * 96;
+  g.sA = g_op_scales; g.sA_rs = gn * 8;
+  g.sB = rt_op_scales; g.sB_rs = gn * 8;
+  g.P = V;
+  g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
+  g.C = dX; g.ldc = K;
+  const bool out_bf16 = dxdt == FT_OUT_BF16;
+  auto gemm = [&](hipStream_t s) { return (M && K) ? launch_gemm_m6(g, out_bf16, true, s) : FT_OK; };
+  return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
 }

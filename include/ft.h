@@ -22,6 +22,10 @@
  *  - All tensor pointers are device pointers owned by the caller.  The library
  *    allocates no device memory and keeps no pointer after a call returns.
  *  - Work is enqueued asynchronously on the given stream; nothing synchronizes.
+ *    The backward calls fork their adapter-gradient kernels onto a stream the
+ *    library keeps per device (created once, non-blocking, default priority)
+ *    and join it back with events before returning, so to the caller all
+ *    their work is ordered on the given stream as if it ran there.
  *  - Arguments are validated before anything is launched; on error nothing
  *    is enqueued and the status says why.  The library never aborts.
  *  - Matrices are row-major with the stated leading dimension (in elements).
