@@ -65,17 +65,28 @@ struct TileCfg {
   static constexpr int STAGE = A_ST + B_ST + (SA_DW + SB_DW) * 4;
   static constexpr int N16 = (BM + BN) / 16;                          // 1-KiB DMAs per stage
   static constexpr int NQ = (N16 + 7) / 8;                            // ... per wave, at most
-  // scale DMAs: waves [0, WA) fetch A's scale dwords, the others B's
-  static constexpr int WA = (8 * SA_DW + (SA_DW + SB_DW) / 2) / (SA_DW + SB_DW);
-  static constexpr int LA = (SA_DW + WA - 1) / WA, LB = (SB_DW + (8 - WA) - 1) / (8 - WA);
-  static constexpr int SMEM = tc_max(NS * STAGE, 64 * (2 * BN + 32));
+  // Scale DMAs go to the waves with one code DMA fewer (waves [FS, 8)), or to
+  // every wave when the code DMAs divide evenly, so that every wave issues the
+  // same number DPS of DMA instructions per stage (compile-time wait counts).
+  // Of the SW scale waves, the first WA fetch A's scale dwords, the others B's.
+  static constexpr int FS = N16 % 8, SW = 8 - FS;
+  static constexpr int DPS = FS ? NQ : NQ + 1;
+  static constexpr int WA_RAW = (SW * SA_DW + (SA_DW + SB_DW) / 2) / (SA_DW + SB_DW);
+  static constexpr int WA = WA_RAW < 1 ? 1 : (WA_RAW > SW - 1 ? SW - 1 : WA_RAW);
+  static constexpr int LA = (SA_DW + WA - 1) / WA, LB = (SB_DW + (SW - WA) - 1) / (SW - WA);
+  static constexpr int W_PITCH = 2 * BN + 32;                          // low-rank W rows in LDS
+  static constexpr int SMEM = tc_max(tc_max(NS * STAGE, (NS - 1) * STAGE + CHUNK * W_PITCH),
+                                     BM * (2 * BN + 64));                 // bf16 output tile image
   static_assert(BM == WM * 32 * TMI && BN == WN * 32 * TNI, "tile shape");
-  static_assert(LA <= 64 && LB <= 64 && WA >= 1 && WA < 8, "scale DMA split");
-  static_assert(CHUNK_ * (2 * BN_ + 32) <= STAGE, "low-rank W chunk must fit one stage buffer");
+  static_assert(SW >= 2 && LA <= 64 && LB <= 64, "scale DMA split");
+  // every scale wave has at least one dword to fetch
+  static_assert((WA - 1) * LA < SA_DW && (SW - WA - 1) * LB < SB_DW, "idle scale wave");
+  static_assert(SMEM <= 160 * 1024, "LDS");
 };
-// CHUNK: ranks per low-rank pass; its W rows (pitch 2 BN + 32 bytes) fit one stage buffer
+// CHUNK: ranks per low-rank pass; its W rows (pitch 2 BN + 32 bytes) go to the
+// last stage buffer (and the LDS beyond the ring where they need more)
 using CfgSquare = TileCfg<256, 256, 4, 2, 4, 48>;
-using CfgWide = TileCfg<192, 384, 2, 3, 4, 32>;
+using CfgWide = TileCfg<192, 384, 2, 3, 4, 48>;
 template <int I> struct CfgOf { using type = CfgSquare; };
 template <> struct CfgOf<1> { using type = CfgWide; };
 }  // namespace ft
@@ -115,6 +126,10 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // that kernel without a host launch stub).
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+// per-lane offset voff plus a wave-uniform offset soff (scalar operand)
+__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
@@ -165,6 +180,85 @@ __device__ __forceinline__ void mfma_stage(AccT<TMI, TNI>& acc, const uint8_t* s
 #undef FT_KSTEP
 }
 
+// The same stage split for software pipelining: part P holds k-steps 2P and 2P+1
+// (one 16-byte read per row tile and operand); the scale dwords cover all four.
+template <int TMI, int TNI>
+struct Part {
+  v4i a[TMI], b[TNI];
+};
+
+template <int TMI, int TNI, int BMc, int BNc>
+__device__ __forceinline__ void read_part(Part<TMI, TNI>& f, const uint8_t* st, int p, int wm, int wn, int l32,
+                                          int lh) {
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+    f.a[i] = *reinterpret_cast<const v4i*>(st + swz(wm * 32 * TMI + 32 * i + l32, 2 * lh + p));
+#pragma unroll
+  for (int j = 0; j < TNI; ++j)
+    f.b[j] = *reinterpret_cast<const v4i*>(st + BMc * BKB + swz(wn * 32 * TNI + 32 * j + l32, 2 * lh + p));
+}
+
+template <int TMI, int TNI, int BMc, int BNc>
+__device__ __forceinline__ void read_scales(int (&sa)[TMI], int (&sb)[TNI], const uint8_t* st, int wm, int wn,
+                                            int l32, int lh) {
+  const uint8_t* SAs = st + (BMc + BNc) * BKB;
+  const uint8_t* SBs = SAs + (BMc / 16) * 8;
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+    sa[i] = *reinterpret_cast<const int*>(SAs + ((wm * 32 * TMI + 32 * i + l32) >> 4) * 8 + 4 * lh);
+#pragma unroll
+  for (int j = 0; j < TNI; ++j)
+    sb[j] = *reinterpret_cast<const int*>(SBs + ((wn * 32 * TNI + 32 * j + l32) >> 4) * 8 + 4 * lh);
+}
+
+// k-step KK of a stage from its part (KK >> 1).  A 16-byte read holds the lane's
+// blocks of k-steps 2P (dwords 0-1) and 2P+1 (dwords 2-3).  A goes in whole; B
+// keeps only the k-step's block and zeros in the other half, so the products of
+// A's other block vanish (E2M1 has no infinities or NaNs: zero times any code is
+// zero).  Both operands take scale byte KK (op_sel): A's other block is never
+// scaled into the sum.  Only B needs a padded copy, one per column tile.
+template <int KK, int TMI, int TNI>
+__device__ __forceinline__ void mma_kstep(AccT<TMI, TNI>& acc, const Part<TMI, TNI>& f, const int (&sa)[TMI],
+                                          const int (&sb)[TNI]) {
+  const v4i z = {0, 0, 0, 0};
+  v8i bop[TNI];
+#pragma unroll
+  for (int j = 0; j < TNI; ++j) {
+    const v4i bv = f.b[j];
+    bop[j] = (KK & 1) ? __builtin_shufflevector(bv, z, 4, 4, 2, 3, 4, 4, 4, 4)
+                      : __builtin_shufflevector(bv, z, 0, 1, 4, 4, 4, 4, 4, 4);
+  }
+#pragma unroll
+  for (int i = 0; i < TMI; ++i) {
+    const v4i av = f.a[i];
+    const v8i aop = __builtin_shufflevector(av, z, 0, 1, 2, 3, 4, 4, 4, 4);
+#pragma unroll
+    for (int j = 0; j < TNI; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[j], acc[i][j], 4, 4, KK, sa[i], KK, sb[j]);
+  }
+}
+
+template <int P, int TMI, int TNI>
+__device__ __forceinline__ void mma_part(AccT<TMI, TNI>& acc, const Part<TMI, TNI>& f, const int (&sa)[TMI],
+                                         const int (&sb)[TNI]) {
+  mma_kstep<2 * P>(acc, f, sa, sb);
+  mma_kstep<2 * P + 1>(acc, f, sa, sb);
+}
+
+// An empty asm statement that reads the accumulators: the MFMAs producing them
+// are issued before it, so they cannot be sunk past a following wait or barrier.
+template <int TMI, int TNI>
+__device__ __forceinline__ void pin_acc(AccT<TMI, TNI>& acc) {
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < TNI; ++j) {
+#if defined(__HIP_DEVICE_COMPILE__)   // (the host pass has no VGPR constraint)
+      asm volatile("" ::"v"(acc[i][j]));
+#endif
+    }
+}
+
 // 4 x 4 transpose within each quad of lanes: on entry lane t of a quad holds
 // element (k, t) in v[k]; on exit it holds element (t, k) in v[k].  Two butterfly
 // stages over lane bits 0 and 1, each exchanging half of the values with DPP.
@@ -200,91 +294,108 @@ __device__ __forceinline__ void quad_transpose4(float (&v)[4], int t) {
 // flight at once; ranks beyond one chunk are processed in further passes.
 // BNc: tile width (W rows staged at a pitch of 2*BNc + 32 bytes); CHUNK: ranks
 // per pass (their P values are held in registers while the pass runs).
+template <int TMI, int CHUNK>
+using PRegs = v4f[TMI][CHUNK / 16][2];
+
+// Loads of chunk jc (ranks jc .. jc+nr-1, nr = min(CHUNK, rho - jc)): W rows to LDS
+// (lanes 0 .. BNc/8-1: 16 bytes = 8 columns each), this wave's P rows to registers.
+template <int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
+__device__ __forceinline__ void lowrank_load(PRegs<TMI, CHUNK>& p, const GemmArgs& g, uint8_t* smem, int jc,
+                                             int64_t m0, int64_t n0, int wave, int lane, int wm, int l32, int lh) {
+  constexpr int W_PITCH = 2 * BNc + 32;
+  const int rho = g.ra + g.rb;
+  const int nr = min(CHUNK, rho - jc);                           // multiple of 16
+  const __amdgpu_buffer_rsrc_t rWa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wa, 0, (int)((int64_t)g.ra * g.N * 2), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rWb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wb, 0, (int)((int64_t)g.rb * g.N * 2), RSRC_FLAGS);
+  for (int jr = wave; jr < nr; jr += NWAVES) {
+    const int j = jc + jr;
+    const bool in_a = j < g.ra;
+    const int jj = in_a ? j : j - g.ra;
+    const int64_t n = n0 + 8 * lane;
+    const uint32_t off = (lane < BNc / 8 && n < g.N) ? (uint32_t)(((int64_t)jj * g.N + n) * 2) : 0x80000000u;
+    if (lane < BNc / 8) {
+      if (in_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(rWa, (lds_void*)(smem + jr * W_PITCH), 16, off, 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rWb, (lds_void*)(smem + jr * W_PITCH), 16, off, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TMI; ++i) {
+    const int64_t row = m0 + wm * 32 * TMI + 32 * i + l32;
+#pragma unroll
+    for (int ks = 0; ks < CHUNK / 16; ++ks) {
+      p[i][ks][0] = p[i][ks][1] = v4f{0, 0, 0, 0};
+      if (16 * ks < nr && row < g.M) {
+        const float* src = g.P + row * rho + jc + 16 * ks + 8 * lh;
+        p[i][ks][0] = *reinterpret_cast<const v4f*>(src);
+        p[i][ks][1] = *reinterpret_cast<const v4f*>(src + 4);
+      }
+    }
+  }
+}
+
+// acc += (P_hi + P_lo) W for chunk jc on bf16 MFMA 32x32x16 (its loads complete
+// and visible to the workgroup)
+template <int TMI, int TNI, int BNc, int CHUNK>
+__device__ __forceinline__ void lowrank_mma(AccT<TMI, TNI>& acc, const PRegs<TMI, CHUNK>& p, const GemmArgs& g,
+                                            const uint8_t* smem, int jc, int lane, int wn) {
+  constexpr int W_PITCH = 2 * BNc + 32;
+  const int nr = min(CHUNK, g.ra + g.rb - jc);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);             // + 16 ks + 4 t
+  const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn*32*TNI + 32 j
+#pragma unroll
+  for (int ks = 0; ks < CHUNK / 16; ++ks) {
+    if (16 * ks < nr) {
+      v8bf wf[TNI];
+#pragma unroll
+      for (int j = 0; j < TNI; ++j) {
+        const uint8_t* b0 = smem + (16 * ks + tr_row) * W_PITCH + 2 * (wn * 32 * TNI + 32 * j + tr_col);
+        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0));
+        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + 4 * W_PITCH));
+        const v2i l2 = __builtin_bit_cast(v2i, lo4), h2 = __builtin_bit_cast(v2i, hi4);
+        wf[j] = __builtin_bit_cast(v8bf, v4i{l2.x, l2.y, h2.x, h2.y});
+      }
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) {
+        const float pv[8] = {p[i][ks][0].x, p[i][ks][0].y, p[i][ks][0].z, p[i][ks][0].w,
+                             p[i][ks][1].x, p[i][ks][1].y, p[i][ks][1].z, p[i][ks][1].w};
+        uint32_t h[8], l[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_bf16(pv[e], h[e], l[e]);
+        const v8bf phi = __builtin_bit_cast(v8bf, v4i{(int)(h[0] | h[1] << 16), (int)(h[2] | h[3] << 16),
+                                                      (int)(h[4] | h[5] << 16), (int)(h[6] | h[7] << 16)});
+        const v8bf plo = __builtin_bit_cast(v8bf, v4i{(int)(l[0] | l[1] << 16), (int)(l[2] | l[3] << 16),
+                                                      (int)(l[4] | l[5] << 16), (int)(l[6] | l[7] << 16)});
+#pragma unroll
+        for (int j = 0; j < TNI; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi, wf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo, wf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Chunks from jc0 on, each: loads, wait for all of this wave's memory operations,
+// barrier, MFMAs, barrier (LDS free for the next chunk).  smem must be free.
 template <int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
 __device__ __forceinline__ void lowrank_into_acc(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
                                                  int64_t m0, int64_t n0, int tid, int wave, int wm, int wn,
-                                                 int l32, int lh) {
-  constexpr int W_PITCH = 2 * BNc + 32;
-  constexpr int EPI_CHUNK = CHUNK;
+                                                 int l32, int lh, int jc0 = 0) {
   const int lane = tid & 63;
-  const int rho = g.ra + g.rb;
-  if (rho > 0) {
-    const __amdgpu_buffer_rsrc_t rWa =
-        __builtin_amdgcn_make_buffer_rsrc((void*)g.Wa, 0, (int)((int64_t)g.ra * g.N * 2), RSRC_FLAGS);
-    const __amdgpu_buffer_rsrc_t rWb =
-        __builtin_amdgcn_make_buffer_rsrc((void*)g.Wb, 0, (int)((int64_t)g.rb * g.N * 2), RSRC_FLAGS);
-    const int g16 = lane >> 4, s16 = lane & 15;
-    const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);             // + 16 ks + 4 t
-    const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn*32*TNI + 32 j
-    for (int jc = 0; jc < rho; jc += EPI_CHUNK) {
-      const int nr = min(EPI_CHUNK, rho - jc);                   // multiple of 16
-      // (a) W rows jc .. jc+nr-1 -> LDS (lanes 0 .. BNc/8-1: 16 bytes = 8 columns each)
-      for (int jr = wave; jr < nr; jr += NWAVES) {
-        const int j = jc + jr;
-        const bool in_a = j < g.ra;
-        const int jj = in_a ? j : j - g.ra;
-        const int64_t n = n0 + 8 * lane;
-        const uint32_t off = (lane < BNc / 8 && n < g.N) ? (uint32_t)(((int64_t)jj * g.N + n) * 2) : 0x80000000u;
-        if (lane < BNc / 8) {
-          if (in_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(rWa, (lds_void*)(smem + jr * W_PITCH), 16, off, 0, 0, 0);
-          else __builtin_amdgcn_raw_ptr_buffer_load_lds(rWb, (lds_void*)(smem + jr * W_PITCH), 16, off, 0, 0, 0);
-        }
-      }
-      // (b) P[rows][jc .. jc+nr) for this wave's 4 row tiles, every load in flight
-      v4f p[TMI][EPI_CHUNK / 16][2];
-#pragma unroll
-      for (int i = 0; i < TMI; ++i) {
-        const int64_t row = m0 + wm * 32 * TMI + 32 * i + l32;
-#pragma unroll
-        for (int ks = 0; ks < EPI_CHUNK / 16; ++ks) {
-          p[i][ks][0] = p[i][ks][1] = v4f{0, 0, 0, 0};
-          if (16 * ks < nr && row < g.M) {
-            const float* src = g.P + row * rho + jc + 16 * ks + 8 * lh;
-            p[i][ks][0] = *reinterpret_cast<const v4f*>(src);
-            p[i][ks][1] = *reinterpret_cast<const v4f*>(src + 4);
-          }
-        }
-      }
-      compiler_fence();
-      FT_WAIT_VMCNT(0);
-      __builtin_amdgcn_s_barrier();
-      compiler_fence();
-      // (c) acc += (P_hi + P_lo) W on bf16 MFMA 32x32x16
-#pragma unroll
-      for (int ks = 0; ks < EPI_CHUNK / 16; ++ks) {
-        if (16 * ks < nr) {
-          v8bf wf[TNI];
-#pragma unroll
-          for (int j = 0; j < TNI; ++j) {
-            const uint8_t* b0 = smem + (16 * ks + tr_row) * W_PITCH + 2 * (wn * 32 * TNI + 32 * j + tr_col);
-            const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0));
-            const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + 4 * W_PITCH));
-            const v2i l2 = __builtin_bit_cast(v2i, lo4), h2 = __builtin_bit_cast(v2i, hi4);
-            wf[j] = __builtin_bit_cast(v8bf, v4i{l2.x, l2.y, h2.x, h2.y});
-          }
-#pragma unroll
-          for (int i = 0; i < TMI; ++i) {
-            const float pv[8] = {p[i][ks][0].x, p[i][ks][0].y, p[i][ks][0].z, p[i][ks][0].w,
-                                 p[i][ks][1].x, p[i][ks][1].y, p[i][ks][1].z, p[i][ks][1].w};
-            uint32_t h[8], l[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) split_bf16(pv[e], h[e], l[e]);
-            const v8bf phi = __builtin_bit_cast(v8bf, v4i{(int)(h[0] | h[1] << 16), (int)(h[2] | h[3] << 16),
-                                                          (int)(h[4] | h[5] << 16), (int)(h[6] | h[7] << 16)});
-            const v8bf plo = __builtin_bit_cast(v8bf, v4i{(int)(l[0] | l[1] << 16), (int)(l[2] | l[3] << 16),
-                                                          (int)(l[4] | l[5] << 16), (int)(l[6] | l[7] << 16)});
-#pragma unroll
-            for (int j = 0; j < TNI; ++j) {
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi, wf[j], acc[i][j], 0, 0, 0);
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo, wf[j], acc[i][j], 0, 0, 0);
-            }
-          }
-        }
-      }
-      compiler_fence();
-      __builtin_amdgcn_s_barrier();   // LDS free for the next chunk
-      compiler_fence();
-    }
+  for (int jc = jc0; jc < g.ra + g.rb; jc += CHUNK) {
+    PRegs<TMI, CHUNK> p;
+    lowrank_load<TMI, TNI, NWAVES, BNc, CHUNK>(p, g, smem, jc, m0, n0, wave, lane, wm, l32, lh);
+    compiler_fence();
+    FT_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    lowrank_mma<TMI, TNI, BNc, CHUNK>(acc, p, g, smem, jc, lane, wn);
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
   }
 }
 
@@ -317,6 +428,45 @@ __device__ __forceinline__ void store_acc(AccT<TMI, TNI>& acc, const GemmArgs& g
         }
       }
     }
+}
+
+// bf16 store through LDS: the quad-transposed rows go to a row-major tile image
+// in LDS (pitch 2 BNc + 64 bytes, so the 8 rows of one write fall in different
+// banks), then the workgroup writes the tile with 16-byte stores, consecutive
+// lanes along a row: whole 128-byte lines instead of the 64-byte row pieces the
+// accumulator layout gives.  smem must be free (callers synchronize first).
+template <int TMI, int TNI, int NWAVES, int BMc, int BNc>
+__device__ __forceinline__ void store_acc_bf16_lds(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
+                                                   int64_t m0, int64_t n0, int tid, int wm, int wn, int l32,
+                                                   int lh) {
+  constexpr int PITCH = 2 * BNc + 64;
+  const int t4 = tid & 3;
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < TNI; ++j) {
+      const int col = wn * 32 * TNI + 32 * j + (l32 & ~3);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        quad_transpose4(v, t4);
+        const int row = wm * 32 * TMI + 32 * i + 8 * q + 4 * lh + t4;
+        const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<v2i*>(smem + row * PITCH + 2 * col) = v2i{(int)lo, (int)hi};
+      }
+    }
+  compiler_fence();
+  __syncthreads();
+  compiler_fence();
+  constexpr int CH = BNc / 8;                                   // 16-byte chunks per row
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+  for (int e = tid; e < BMc * CH; e += 64 * NWAVES) {
+    const int r = e / CH, c = e - (e / CH) * CH;
+    const int64_t row = m0 + r, col = n0 + 8 * c;
+    const v4i val = *reinterpret_cast<const v4i*>(smem + r * PITCH + 16 * c);
+    if (row < g.M && col < g.N) *reinterpret_cast<v4i*>(C + row * g.ldc + col) = val;
+  }
 }
 
 template <bool OUT_BF16, int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
@@ -362,7 +512,8 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
       (void*)(g.A + m0 * g.lda), 0, (int)(min<int64_t>(BMc, g.M - m0) * g.lda), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.B + n0 * g.ldb), 0, (int)(min<int64_t>(BNc, g.N - n0) * g.ldb), RSRC_FLAGS);
-  const bool scale_b = wave >= C::WA;
+  const bool scale_w = wave >= C::FS;                          // this wave fetches scale dwords
+  const bool scale_b = wave >= C::FS + C::WA;
   const __amdgpu_buffer_rsrc_t rS = scale_b
       ? __builtin_amdgcn_make_buffer_rsrc((void*)(g.sB + (n0 / 16) * g.sB_rs), 0,
                                           (int)(min<int64_t>(BNc / 16, (g.N - n0) / 16) * g.sB_rs), RSRC_FLAGS)
@@ -372,36 +523,39 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
 
   // DMA instruction q (0 .. N16-1) of a stage fills 16 rows: A rows 16q .. for
   // q < BM/16, else B rows; wave w issues q = w, w + 8, ...  Lane l lands at
-  // physical chunk l & 3 of row l >> 2 (the swizzle picks the global chunk).
+  // physical chunk l & 3 of row l >> 2 (the swizzle picks the global chunk; its
+  // row bits 2-3 are lane bits 4-5 since every DMA starts at a multiple of 16
+  // rows).  The lane's part of the offset is one register per operand; the
+  // row-block and stage parts are wave-uniform (scalar offset).
   const int nq = (C::N16 - wave + 7) / 8;                      // this wave's count (uniform)
-  uint32_t offq[C::NQ];
-  int ldsq[C::NQ];
-  bool isb[C::NQ];
-#pragma unroll
-  for (int u = 0; u < C::NQ; ++u) {
-    const int q = wave + 8 * u;
-    isb[u] = q >= BMc / 16;
-    const int r0 = isb[u] ? 16 * q - BMc : 16 * q;
-    const int row = r0 + (lane >> 2);
-    const int qc = (lane & 3) ^ ((row >> 2) & 3);
-    offq[u] = (uint32_t)(row * (isb[u] ? g.ldb : g.lda) + 16 * qc);
-    ldsq[u] = (isb[u] ? C::A_ST : 0) + r0 * BKB;
-  }
+  const uint32_t lane_chunk = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+  const uint32_t vA = (uint32_t)((lane >> 2) * g.lda) + lane_chunk;
+  const uint32_t vB = (uint32_t)((lane >> 2) * g.ldb) + lane_chunk;
   // scale dwords: A's are [BM/16][2], B's [BN/16][2]; wave w of its group takes a
   // contiguous run of LA (LB) of them, one per lane
-  const int sw = scale_b ? wave - C::WA : wave;
+  const int sw = scale_b ? wave - C::FS - C::WA : wave - C::FS;
   const int sl = scale_b ? C::LB : C::LA;
   const int sd = sw * sl + lane;
-  const bool s_on = lane < sl && sd < (scale_b ? C::SB_DW : C::SA_DW);
+  const bool s_on = scale_w && lane < sl && sd < (scale_b ? C::SB_DW : C::SA_DW);
   const uint32_t offS = (uint32_t)((sd >> 1) * s_rs + 4 * (sd & 1));
   const int s_lds = C::A_ST + C::B_ST + 4 * ((scale_b ? C::SA_DW : 0) + sw * sl);
 
   auto issue = [&](int stage, int kt) {
     uint8_t* base = smem + stage * C::STAGE;
 #pragma unroll
-    for (int u = 0; u < C::NQ; ++u)
-      if (u < nq) dma16(isb[u] ? rB : rA, base + ldsq[u], offq[u] + (uint32_t)kt * BKB);
-    if (s_on) dma4(rS, base + s_lds, offS + (uint32_t)kt * 8);
+    for (int u = 0; u < C::NQ; ++u) {
+      const int q = wave + 8 * u;
+      if (u < nq) {
+        const bool isb = q >= BMc / 16;
+        const int r0 = isb ? 16 * q - BMc : 16 * q;
+        const uint32_t soff = (uint32_t)(r0 * (isb ? g.ldb : g.lda)) + (uint32_t)kt * BKB;
+        dma16s(isb ? rB : rA, base + (isb ? C::A_ST : 0) + r0 * BKB, isb ? vB : vA,
+               __builtin_amdgcn_readfirstlane(soff));
+      }
+    }
+    if (scale_w) {   // wave-uniform: the instruction counts even where no lane is active
+      if (s_on) dma4(rS, base + s_lds, offS + (uint32_t)kt * 8);
+    }
   };
 
   AccT<C::TMI, C::TNI> acc;
@@ -410,38 +564,90 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
 #pragma unroll
     for (int j = 0; j < C::TNI; ++j) acc[i][j] = v16f{};
 
+  // The low-rank up-projection P W goes into the accumulators first, in the
+  // buffer of stage NS-1 (free until the first steady iteration).  The loads of
+  // its first chunk are issued ahead of the pipeline fill and awaited by count
+  // (the fill's DMAs, all younger, may stay in flight), so both overlap.
+  const int rho = g.ra + g.rb;
+  uint8_t* lr_smem = smem + (NSc - 1) * C::STAGE;
+  PRegs<C::TMI, C::CHUNK> pr;
+  if (rho > 0) lowrank_load<C::TMI, C::TNI, 8, BNc, C::CHUNK>(pr, g, lr_smem, 0, m0, n0, wave, lane, wm, l32, lh);
 #pragma unroll
   for (int s = 0; s < NSc - 1; ++s)
     if (s < nkt) issue(s, s);
-  // the low-rank up-projection P W goes into the accumulators first, in the
-  // buffer of stage NS-1 (free until the first steady iteration): its W and P
-  // loads overlap the pipeline fill instead of trailing the main loop
-  lowrank_into_acc<C::TMI, C::TNI, 8, BNc, C::CHUNK>(acc, g, smem + (NSc - 1) * C::STAGE, m0, n0, tid, wave, wm,
-                                                     wn, l32, lh);
+  if (rho > 0) {
+    compiler_fence();
+    if (nkt >= NSc - 1) FT_WAIT_VMCNT(C::DPS * (NSc - 1));
+    else if (nkt == 2) FT_WAIT_VMCNT(C::DPS * 2);
+    else if (nkt == 1) FT_WAIT_VMCNT(C::DPS);
+    else FT_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, pr, g, lr_smem, 0, lane, wn);
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    if (rho > C::CHUNK)
+      lowrank_into_acc<C::TMI, C::TNI, 8, BNc, C::CHUNK>(acc, g, lr_smem, m0, n0, tid, wave, wm, wn, l32, lh,
+                                                         C::CHUNK);
+  }
 
-  // steady state: stage kt is consumed while stages kt+1 .. kt+NS-1 are in flight.
-  // A wave's DMA of stage kt is complete once at most NS-2 later stages (nq + 1
-  // DMAs each) are pending; the barrier then makes every wave's DMA visible and
-  // marks the buffer of stage kt-1 free for stage kt+NS-1.
+  // Main loop, software-pipelined across the stage barrier.  Iteration kt reads
+  // part 1 of stage kt, runs part 0's MFMAs, then waits for its own DMA of stage
+  // kt+1 and meets the barrier (every wave's DMA of kt+1 visible; every wave done
+  // reading stage kt-1, whose buffer then takes stage kt+NS-1), reads part 0 of
+  // stage kt+1 and runs part 1's MFMAs: the LDS reads of one part are in flight
+  // while the MFMAs of the other execute, also across the barrier.  A DMA issued
+  // at iteration s-NS+1 is awaited at iteration s-1.  Scheduling barriers keep
+  // the compiler from moving the MFMAs across the wait and the barrier.
+  static_assert(NSc == 4, "the wait counts below assume a 4-stage ring");
+  Part<C::TMI, C::TNI> c0, p1;   // part 0 (current, then next stage's) and part 1
+  int sa[C::TMI], sb[C::TNI], na[C::TMI], nb[C::TNI];
+  // steady: stage kt+NS-1 exists, so after kt+1 one more stage (kt+2) is in flight
+  auto step = [&](int kt, bool steady) __attribute__((always_inline)) {
+    const uint8_t* st = smem + __builtin_amdgcn_readfirstlane((kt % NSc) * C::STAGE);
+    read_part<C::TMI, C::TNI, BMc, BNc>(p1, st, 1, wm, wn, l32, lh);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_part<0>(acc, c0, sa, sb);
+    pin_acc(acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if (steady || kt + 1 < nkt) {
+      compiler_fence();
+      if (steady || kt + 2 < nkt) FT_WAIT_VMCNT(C::DPS);
+      else FT_WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      if (steady) issue((kt + NSc - 1) % NSc, kt + NSc - 1);
+      const uint8_t* nx = smem + __builtin_amdgcn_readfirstlane(((kt + 1) % NSc) * C::STAGE);
+      read_part<C::TMI, C::TNI, BMc, BNc>(c0, nx, 0, wm, wn, l32, lh);
+      read_scales<C::TMI, C::TNI, BMc, BNc>(na, nb, nx, wm, wn, l32, lh);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma_part<1>(acc, p1, sa, sb);
+#pragma unroll
+    for (int i = 0; i < C::TMI; ++i) sa[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < C::TNI; ++j) sb[j] = nb[j];
+  };
+  compiler_fence();
+  if (nkt >= NSc - 1) FT_WAIT_VMCNT(C::DPS * (NSc - 2));
+  else FT_WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  read_part<C::TMI, C::TNI, BMc, BNc>(c0, smem, 0, wm, wn, l32, lh);
+  read_scales<C::TMI, C::TNI, BMc, BNc>(sa, sb, smem, wm, wn, l32, lh);
+  const int n_steady = max(0, nkt - (NSc - 1));
   int kt = 0;
-  for (; kt + NSc - 1 < nkt; ++kt) {
+  for (; kt < n_steady; ++kt) step(kt, true);
+  for (; kt < nkt; ++kt) step(kt, false);   // the last NS-1 stages: nothing more to fetch
+  if constexpr (OUT_BF16) {
     compiler_fence();
-    if (nq == C::NQ) FT_WAIT_VMCNT((C::NQ + 1) * (NSc - 2));
-    else FT_WAIT_VMCNT(C::NQ * (NSc - 2));
-    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_s_barrier();   // every wave done reading the last stage
     compiler_fence();
-    issue((kt + NSc - 1) % NSc, kt + NSc - 1);
-    mfma_stage<C::TMI, C::TNI, BMc, BNc>(acc, smem + (kt % NSc) * C::STAGE, wm, wn, l32, lh);
+    store_acc_bf16_lds<C::TMI, C::TNI, 8, BMc, BNc>(acc, g, smem, m0, n0, tid, wm, wn, l32, lh);
+  } else {
+    store_acc<OUT_BF16, C::TMI, C::TNI>(acc, g, m0, n0, lane, wm, wn, l32, lh);
   }
-  // drain: no more DMA to issue
-  for (; kt < nkt; ++kt) {
-    compiler_fence();
-    FT_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    mfma_stage<C::TMI, C::TNI, BMc, BNc>(acc, smem + (kt % NSc) * C::STAGE, wm, wn, l32, lh);
-  }
-  store_acc<OUT_BF16, C::TMI, C::TNI>(acc, g, m0, n0, lane, wm, wn, l32, lh);
 }
 
 // ---------------------------------------------------------------------------------------
