@@ -460,12 +460,20 @@ __device__ __forceinline__ void store_acc_bf16_lds(AccT<TMI, TNI>& acc, const Ge
   __syncthreads();
   compiler_fence();
   constexpr int CH = BNc / 8;                                   // 16-byte chunks per row
+  constexpr int PER = BMc * CH / (64 * NWAVES);                 // chunks per thread
+  static_assert(BMc * CH % (64 * NWAVES) == 0, "whole passes over the tile");
   uint16_t* C = static_cast<uint16_t*>(g.C);
-  for (int e = tid; e < BMc * CH; e += 64 * NWAVES) {
-    const int r = e / CH, c = e - (e / CH) * CH;
+  v4i val[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {   // all LDS reads first, then all stores
+    const int e = tid + 64 * NWAVES * it, r = e / CH, c = e - (e / CH) * CH;
+    val[it] = *reinterpret_cast<const v4i*>(smem + r * PITCH + 16 * c);
+  }
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int e = tid + 64 * NWAVES * it, r = e / CH, c = e - (e / CH) * CH;
     const int64_t row = m0 + r, col = n0 + 8 * c;
-    const v4i val = *reinterpret_cast<const v4i*>(smem + r * PITCH + 16 * c);
-    if (row < g.M && col < g.N) *reinterpret_cast<v4i*>(C + row * g.ldc + col) = val;
+    if (row < g.M && col < g.N) *reinterpret_cast<v4i*>(C + row * g.ldc + col) = val[it];
   }
 }
 
