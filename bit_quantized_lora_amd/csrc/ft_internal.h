@@ -21,7 +21,8 @@ struct GemmArgs {
   void* C; int64_t ldc;
 };
 
-ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s);
+// beside: other kernels run concurrently on the device (tile choice leaves them CUs)
+ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s, bool beside = false);
 
 // Same product from pair-merged FP6 operands (ft_quant_block16_op): A, B are
 // operand bytes with row pitch lda / ldb (= groups * 96), sA / sB the operand

@@ -951,7 +951,7 @@ double fill(int64_t tiles, int cus) { return (double)tiles / (double)(((tiles + 
 
 }  // namespace
 
-ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s) {
+ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s, bool beside) {
   if (g.M == 0 || g.N == 0) return FT_OK;
   const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
@@ -961,7 +961,11 @@ ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipSt
   if (pipelined) {
     const int cus = num_cus();
     const int64_t wide = ((g.M + CfgWide::BM - 1) / CfgWide::BM) * ((g.N + CfgWide::BN - 1) / CfgWide::BN);
-    const bool use_wide = fill(wide, cus) > fill(tiles, cus) + 0.02;
+    // Tile shape: the one that fills the CUs in fewer partial rounds; but when
+    // other kernels run beside the GEMM and both shapes take one round, the one
+    // with fewer tiles, which leaves those kernels more CUs.
+    const bool use_wide = (beside && wide <= cus && tiles <= cus) ? wide < tiles
+                                                                  : fill(wide, cus) > fill(tiles, cus) + 0.02;
     const int64_t tm = use_wide ? (g.M + CfgWide::BM - 1) / CfgWide::BM : tiles_m;
     const int64_t tn = use_wide ? (g.N + CfgWide::BN - 1) / CfgWide::BN : tiles_n;
     const int per_xcd = (int)((tm * tn + 7) / 8);

@@ -36,6 +36,7 @@ hipStream_t side_stream() {
 }
 
 // enqueue `gemm` on `stream` and the adapter gradients concurrently beside it
+// (gemm(stream, beside): beside tells it that other kernels share the device)
 template <class F>
 ft_status gemm_with_adapter_grads(F gemm, int64_t M, int64_t N, int64_t K, const float* V, int rs, int r,
                                   const void* X, const void* G, const float* T, float* dAt, float* dB,
@@ -48,13 +49,13 @@ ft_status gemm_with_adapter_grads(F gemm, int64_t M, int64_t N, int64_t K, const
   if (!side) {  // no side stream: one after the other on the caller's stream
     if (fork) (void)hipEventDestroy(fork);
     if (join) (void)hipEventDestroy(join);
-    ft_status st = gemm(stream);
+    ft_status st = gemm(stream, false);
     if (st != FT_OK) return st;
     return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
   }
   ft_status st = FT_OK;
   if (hipEventRecord(fork, stream) != hipSuccess) st = FT_EHIP;
-  if (st == FT_OK) st = gemm(stream);
+  if (st == FT_OK) st = gemm(stream, true);
   if (st == FT_OK && hipStreamWaitEvent(side, fork, 0) != hipSuccess) st = FT_EHIP;
   if (st == FT_OK) st = adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, side);
   if (st == FT_OK && hipEventRecord(join, side) != hipSuccess) st = FT_EHIP;
@@ -141,7 +142,9 @@ extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
   g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
   g.C = dX; g.ldc = K;
   const bool out_bf16 = dxdt == FT_OUT_BF16;
-  auto gemm = [&](hipStream_t s) { return (M && K) ? launch_gemm_w4a4(g, out_bf16, true, s) : FT_OK; };
+  auto gemm = [&](hipStream_t s, bool beside) {
+    return (M && K) ? launch_gemm_w4a4(g, out_bf16, true, s, beside) : FT_OK;
+  };
   return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
 }
 
@@ -222,6 +225,6 @@ extern "C" ft_status ft_linear_bwd_op(int64_t M, int64_t N, int64_t K, const uin
   g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
   g.C = dX; g.ldc = K;
   const bool out_bf16 = dxdt == FT_OUT_BF16;
-  auto gemm = [&](hipStream_t s) { return (M && K) ? launch_gemm_m6(g, out_bf16, true, s) : FT_OK; };
+  auto gemm = [&](hipStream_t s, bool) { return (M && K) ? launch_gemm_m6(g, out_bf16, true, s) : FT_OK; };
   return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
 }
