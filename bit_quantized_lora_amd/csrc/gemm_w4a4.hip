@@ -604,10 +604,11 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   // part 1 of stage kt, runs part 0's MFMAs, then waits for its own DMA of stage
   // kt+1 and meets the barrier (every wave's DMA of kt+1 visible; every wave done
   // reading stage kt-1, whose buffer then takes stage kt+NS-1), reads part 0 of
-  // stage kt+1 and runs part 1's MFMAs: the LDS reads of one part are in flight
-  // while the MFMAs of the other execute, also across the barrier.  A DMA issued
-  // at iteration s-NS+1 is awaited at iteration s-1.  Scheduling barriers keep
-  // the compiler from moving the MFMAs across the wait and the barrier.
+  // stage kt+1 and runs part 1's MFMAs, issuing the DMA of stage kt+NS-1 between
+  // its two k-steps: the LDS reads of one part are in flight while the MFMAs of
+  // the other execute, also across the barrier.  A DMA issued at iteration
+  // s-NS+1 is awaited at iteration s-1.  Scheduling barriers keep the compiler
+  // from moving the MFMAs across the wait, the barrier and the DMA issue.
   static_assert(NSc == 4, "the wait counts below assume a 4-stage ring");
   Part<C::TMI, C::TNI> c0, p1;   // part 0 (current, then next stage's) and part 1
   int sa[C::TMI], sb[C::TNI], na[C::TMI], nb[C::TNI];
@@ -625,13 +626,19 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
       else FT_WAIT_VMCNT(0);
       __builtin_amdgcn_s_barrier();
       compiler_fence();
-      if (steady) issue((kt + NSc - 1) % NSc, kt + NSc - 1);
       const uint8_t* nx = smem + __builtin_amdgcn_readfirstlane(((kt + 1) % NSc) * C::STAGE);
       read_part<C::TMI, C::TNI, BMc, BNc>(c0, nx, 0, wm, wn, l32, lh);
       read_scales<C::TMI, C::TNI, BMc, BNc>(na, nb, nx, wm, wn, l32, lh);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mma_part<1>(acc, p1, sa, sb);
+    mma_kstep<2>(acc, p1, sa, sb);
+    pin_acc(acc);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next DMA between part 1's two k-steps: its LDS writes then overlap
+    // MFMAs instead of the fragment reads just issued
+    if (steady) issue((kt + NSc - 1) % NSc, kt + NSc - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_kstep<3>(acc, p1, sa, sb);
 #pragma unroll
     for (int i = 0; i < C::TMI; ++i) sa[i] = na[i];
 #pragma unroll
