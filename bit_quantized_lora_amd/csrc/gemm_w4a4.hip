@@ -378,6 +378,92 @@ __device__ __forceinline__ void lowrank_mma(AccT<TMI, TNI>& acc, const PRegs<TMI
   }
 }
 
+// Low-rank term at the end of the main loop.  Its W and P tiles are fetched by
+// DMA during the last stages, into ring buffers those stages no longer need, so
+// their loads overlap the main loop's last MFMAs; the products follow the last
+// k-step.  (All ranks in one pass; W [rho x BNc] and P [BMc x rho] each fit one
+// stage buffer.)  LDS layouts, 16-byte chunks XOR-swizzled against bank
+// conflicts: W row j (pitch 2 BNc) keeps chunk c at position c ^ (2 (j & 3)), so
+// the 4 rows of a transposing read fall in distinct banks; P row r (rho / 4
+// chunks) keeps chunk c at r * (rho / 4) + (c ^ ((r >> 1) & 3)), so 8 consecutive
+// rows of a 16-byte read do.
+template <int NWAVES, int BNc>
+__device__ __forceinline__ void tail_issue_w(const GemmArgs& g, uint8_t* dst, int64_t n0, int wave, int lane) {
+  const int rho = g.ra + g.rb;
+  const __amdgpu_buffer_rsrc_t rWa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wa, 0, (int)((int64_t)g.ra * g.N * 2), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rWb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wb, 0, (int)((int64_t)g.rb * g.N * 2), RSRC_FLAGS);
+  for (int j = wave; j < rho; j += NWAVES) {
+    const bool in_a = j < g.ra;
+    const int jj = in_a ? j : j - g.ra;
+    const int c = lane ^ (2 * (j & 3));                          // chunk this lane fetches
+    const int64_t n = n0 + 8 * c;
+    const uint32_t off = (lane < BNc / 8 && n < g.N) ? (uint32_t)(((int64_t)jj * g.N + n) * 2) : 0x80000000u;
+    if (lane < BNc / 8) {
+      if (in_a) dma16(rWa, dst + j * 2 * BNc, off);
+      else dma16(rWb, dst + j * 2 * BNc, off);
+    }
+  }
+}
+
+template <int NWAVES, int BMc>
+__device__ __forceinline__ void tail_issue_p(const GemmArgs& g, uint8_t* dst, int64_t m0, int wave, int lane) {
+  const int rho = g.ra + g.rb, cpr = rho / 4;
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.P + m0 * rho), 0, (int)(min<int64_t>(BMc, g.M - m0) * rho * 4), RSRC_FLAGS);
+  const int nq = BMc * cpr / 64;                                 // 1-KiB DMAs (BMc * rho % 256 == 0)
+  for (int q = wave; q < nq; q += NWAVES) {
+    const int pos = 64 * q + lane, r = pos / cpr, cs = pos - (pos / cpr) * cpr;
+    const int c = cs ^ ((r >> 1) & 3);
+    dma16(rP, dst + 1024 * q, (uint32_t)((r * cpr + c) * 16));
+  }
+}
+
+// acc += (P_hi + P_lo) W from the tiles tail_issue_w / tail_issue_p staged
+template <int TMI, int TNI, int BNc, int CHUNK>
+__device__ __forceinline__ void tail_lowrank_mma(AccT<TMI, TNI>& acc, const GemmArgs& g, const uint8_t* wbuf,
+                                                 const uint8_t* pbuf, int lane, int wm, int wn, int l32, int lh) {
+  const int rho = g.ra + g.rb, cpr = rho / 4;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);             // + 16 ks (+ 4 for the second read)
+  const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn*32*TNI + 32 j
+#pragma unroll
+  for (int ks = 0; ks < CHUNK / 16; ++ks) {
+    if (16 * ks < rho) {
+      v8bf wf[TNI];
+#pragma unroll
+      for (int j = 0; j < TNI; ++j) {
+        const int row = 16 * ks + tr_row, col = wn * 32 * TNI + 32 * j + tr_col;
+        const uint8_t* b0 = wbuf + row * 2 * BNc + (((col >> 3) ^ (2 * (row & 3))) << 4) + 2 * (col & 7);
+        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0));
+        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + 4 * 2 * BNc));
+        const v2i l2 = __builtin_bit_cast(v2i, lo4), h2 = __builtin_bit_cast(v2i, hi4);
+        wf[j] = __builtin_bit_cast(v8bf, v4i{l2.x, l2.y, h2.x, h2.y});
+      }
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) {
+        const int r = wm * 32 * TMI + 32 * i + l32, c0 = 4 * ks + 2 * lh;
+        const v4f p0 = *reinterpret_cast<const v4f*>(pbuf + 16 * (r * cpr + (c0 ^ ((r >> 1) & 3))));
+        const v4f p1 = *reinterpret_cast<const v4f*>(pbuf + 16 * (r * cpr + ((c0 + 1) ^ ((r >> 1) & 3))));
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        uint32_t h[8], l[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_bf16(pv[e], h[e], l[e]);
+        const v8bf phi = __builtin_bit_cast(v8bf, v4i{(int)(h[0] | h[1] << 16), (int)(h[2] | h[3] << 16),
+                                                      (int)(h[4] | h[5] << 16), (int)(h[6] | h[7] << 16)});
+        const v8bf plo = __builtin_bit_cast(v8bf, v4i{(int)(l[0] | l[1] << 16), (int)(l[2] | l[3] << 16),
+                                                      (int)(l[4] | l[5] << 16), (int)(l[6] | l[7] << 16)});
+#pragma unroll
+        for (int j = 0; j < TNI; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi, wf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo, wf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
 // Chunks from jc0 on, each: loads, wait for all of this wave's memory operations,
 // barrier, MFMAs, barrier (LDS free for the next chunk).  smem must be free.
 template <int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
@@ -576,14 +662,19 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   // buffer of stage NS-1 (free until the first steady iteration).  The loads of
   // its first chunk are issued ahead of the pipeline fill and awaited by count
   // (the fill's DMAs, all younger, may stay in flight), so both overlap.
+  // (Or, when its tiles fit the ring buffers the last stages free, after the
+  // main loop: see tail_issue_w.)
   const int rho = g.ra + g.rb;
+  const bool tail_lr = rho > 0 && rho <= C::CHUNK && rho * 2 * BNc <= C::STAGE && BMc * rho * 4 <= C::STAGE &&
+                       nkt >= NSc && (BMc * rho) % 256 == 0;
   uint8_t* lr_smem = smem + (NSc - 1) * C::STAGE;
   PRegs<C::TMI, C::CHUNK> pr;
-  if (rho > 0) lowrank_load<C::TMI, C::TNI, 8, BNc, C::CHUNK>(pr, g, lr_smem, 0, m0, n0, wave, lane, wm, l32, lh);
+  if (rho > 0 && !tail_lr)
+    lowrank_load<C::TMI, C::TNI, 8, BNc, C::CHUNK>(pr, g, lr_smem, 0, m0, n0, wave, lane, wm, l32, lh);
 #pragma unroll
   for (int s = 0; s < NSc - 1; ++s)
     if (s < nkt) issue(s, s);
-  if (rho > 0) {
+  if (rho > 0 && !tail_lr) {
     compiler_fence();
     if (nkt >= NSc - 1) FT_WAIT_VMCNT(C::DPS * (NSc - 1));
     else if (nkt == 2) FT_WAIT_VMCNT(C::DPS * 2);
@@ -626,6 +717,10 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
       else FT_WAIT_VMCNT(0);
       __builtin_amdgcn_s_barrier();
       compiler_fence();
+      if (!steady && tail_lr) {   // from here on the buffer of stage kt-1 is free
+        if (kt == nkt - 3) tail_issue_w<8, BNc>(g, smem + ((nkt - 4) % NSc) * C::STAGE, n0, wave, lane);
+        else if (kt == nkt - 2) tail_issue_p<8, BMc>(g, smem + ((nkt - 3) % NSc) * C::STAGE, m0, wave, lane);
+      }
       const uint8_t* nx = smem + __builtin_amdgcn_readfirstlane(((kt + 1) % NSc) * C::STAGE);
       read_part<C::TMI, C::TNI, BMc, BNc>(c0, nx, 0, wm, wn, l32, lh);
       read_scales<C::TMI, C::TNI, BMc, BNc>(na, nb, nx, wm, wn, l32, lh);
@@ -655,6 +750,14 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   int kt = 0;
   for (; kt < n_steady; ++kt) step(kt, true);
   for (; kt < nkt; ++kt) step(kt, false);   // the last NS-1 stages: nothing more to fetch
+  if (tail_lr) {
+    compiler_fence();
+    FT_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    tail_lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, g, smem + ((nkt - 4) % NSc) * C::STAGE,
+                                                    smem + ((nkt - 3) % NSc) * C::STAGE, lane, wm, wn, l32, lh);
+  }
   if constexpr (OUT_BF16) {
     compiler_fence();
     __builtin_amdgcn_s_barrier();   // every wave done reading the last stage

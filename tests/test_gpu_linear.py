@@ -230,19 +230,22 @@ def test_full_size_configs_sampled_rows(cfg, path):
 
 
 @pytest.mark.parametrize("path", ["codes", "op"])
-def test_wide_tile_ragged_edges(path):
+@pytest.mark.parametrize("K,rs,r", [(384, 16, 16), (1024, 32, 16)], ids=["K384", "K1024"])
+def test_wide_tile_ragged_edges(path, K, rs, r):
     """A shape for which the 192 x 384 workgroup tile fills the chip better than
     256 x 256 (so the forward GEMM takes it), with ragged last tiles in both M
-    and N; rows sampled across the tiles, including the last ones."""
+    and N; rows sampled across the tiles, including the last ones.  K = 384
+    (3 stages) puts the fused low-rank term before the main loop, K = 1024
+    (8 stages) after it, from tiles fetched during the last stages."""
     require_gpu()
-    M, K, N = 4592, 384, 12272
-    rng = np.random.default_rng(4592)
-    spec = synth.LinearSpec("t", M, K, N, 16, 16, x_dist="t3")
+    M, N = 4592, 12272
+    rng = np.random.default_rng(4592 + K)
+    spec = synth.LinearSpec("t", M, K, N, rs, r, x_dist="t3")
     d = synth.make_linear(spec, rng)
-    say(f"[linear] wide-tile ragged M={M} K={K} N={N} path={path}")
+    say(f"[linear] wide-tile ragged M={M} K={K} N={N} rs={rs} r={r} path={path}")
     gpu = _gpu_linear(d, path=path)
     rows = np.unique(np.concatenate([_sample_strips(M, rng, 10), np.arange(M - 48, M)]))
-    _compare(gpu, _oracle_rows(d, rows), rows, f"wide-tile/{path}")
+    _compare(gpu, _oracle_rows(d, rows), rows, f"wide-tile/K{K}/{path}")
 
 
 @pytest.mark.parametrize("shape", [(272, 384, 512), (304, 1040, 400)], ids=lambda s: "x".join(map(str, s)))
