@@ -248,6 +248,21 @@ def test_wide_tile_ragged_edges(path, K, rs, r):
     _compare(gpu, _oracle_rows(d, rows), rows, f"wide-tile/K{K}/{path}")
 
 
+def test_square_tile_lowrank_after_main_loop():
+    """256 x 256 tiles with rs + r = 32 and 8 stages: the low-rank term's W and P
+    tiles fit the freed ring buffers, so it runs after the main loop; ragged last
+    tiles in M and N."""
+    require_gpu()
+    M, K, N = 528, 1024, 784
+    rng = np.random.default_rng(528)
+    spec = synth.LinearSpec("t", M, K, N, 16, 16, x_dist="t3")
+    d = synth.make_linear(spec, rng)
+    say(f"[linear] square-tile low-rank after the main loop M={M} K={K} N={N}")
+    gpu = _gpu_linear(d, path="codes")
+    rows = np.arange(M)
+    _compare(gpu, _oracle_rows(d, rows), rows, "square-tile/tail")
+
+
 @pytest.mark.parametrize("shape", [(272, 384, 512), (304, 1040, 400)], ids=lambda s: "x".join(map(str, s)))
 def test_op_path_with_unmerged_pairs_in_both_operands(shape):
     """Outlier columns x2000 in X and in W open exponent gaps beyond the E3M2
