@@ -121,7 +121,11 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
 
   const int64_t arow = row0 + 32 * wave + l32;
   const bool arow_ok = arow < M;
-  const uint16_t* aptr = in + (arow_ok ? arow : 0) * ld_in + 8 * lh;
+  // input rows of this workgroup through a buffer resource: a lane past M or past
+  // the reduction gets an out-of-range offset and reads zeros (no branches)
+  const __amdgpu_buffer_rsrc_t rIn = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(in + row0 * ld_in), 0, (int)(min<int64_t>(LR_ROWS, M - row0) * ld_in * 2), RSRC_FLAGS);
+  const uint32_t in_off = (uint32_t)(((32 * wave + l32) * ld_in + 8 * lh) * 2);
 
   const __amdgpu_buffer_rsrc_t rWa =
       __builtin_amdgcn_make_buffer_rsrc((void*)wa, 0, (int)((int64_t)ra * Kin * 2), RSRC_FLAGS);
@@ -147,7 +151,8 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int64_t k = c * LR_CHUNK + 16 * s;
-      a[s] = (arow_ok && k < Kin) ? *reinterpret_cast<const v4i*>(aptr + k) : v4i{0, 0, 0, 0};
+      const uint32_t off = (arow_ok && k < Kin) ? in_off + (uint32_t)(k * 2) : 0x80000000u;
+      a[s] = __builtin_amdgcn_raw_buffer_load_b128(rIn, off, 0, 0);
     }
   };
 
