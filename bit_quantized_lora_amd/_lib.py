@@ -30,6 +30,9 @@ _SIGS = {
                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_linear_fwd": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p],
+    "ft_linear_fwd_gelu": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                           c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                           c_void_p],
     "ft_linear_bwd": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],

@@ -19,10 +19,18 @@ struct GemmArgs {
   const uint16_t* Wa; int ra;
   const uint16_t* Wb; int rb;
   void* C; int64_t ldc;
+  // MLP fusion epilogue only: H = GELU(C) bf16 (pitch ldc), Q(H) codes row-major
+  // [M][N/2] and power-of-two scale bytes [M/16][N/16]
+  void* H; uint8_t* hq; uint8_t* hs;
 };
 
 // beside: other kernels run concurrently on the device (tile choice leaves them CUs)
 ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s, bool beside = false);
+
+// Forward GEMM (bf16 Y) with the MLP fusion epilogue: also H = GELU(Y) and Q(H)
+// (g.H, g.hq, g.hs).  FT_ENOTSUP when K is not a multiple of 128 (no pipelined
+// kernel for it); the caller then runs the separate kernels.
+ft_status launch_gemm_w4a4_gelu_quant(const GemmArgs& g, hipStream_t s);
 
 // Same product from pair-merged FP6 operands (ft_quant_block16_op): A, B are
 // operand bytes with row pitch lda / ldb (= groups * 96), sA / sB the operand

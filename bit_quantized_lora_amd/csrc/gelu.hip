@@ -1,20 +1,9 @@
-// GELU between the two linears of an MLP block (FourTune section 3.3 "MLP
-// Fusion" names the activation; the exact form x * Phi(x) with the error
-// function is used).  bf16 in, fp32 math, bf16 out (round to nearest even).
-#include "ft_common.h"
+// GELU between the two linears of an MLP block: bf16 in, fp32 math (gelu_f),
+// bf16 out (round to nearest even).
+#include "ft_device.h"
 
 namespace ft {
 namespace {
-
-// Phi(x) = erfc(-x / sqrt 2) / 2: no cancellation for negative x (1 + erf would lose
-// every significant bit of the small tail there).
-__device__ __forceinline__ float norm_cdf(float x) { return 0.5f * erfcf(-x * 0.70710678118654752f); }
-__device__ __forceinline__ float gelu_f(float x) { return x * norm_cdf(x); }
-__device__ __forceinline__ float gelu_grad_f(float x) {
-  const float cdf = norm_cdf(x);
-  const float pdf = 0.39894228040143268f * __expf(-0.5f * x * x);
-  return cdf + x * pdf;
-}
 
 __global__ void gelu_fwd_kernel(const v4i* __restrict__ y, int64_t n8, v4i* __restrict__ h) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

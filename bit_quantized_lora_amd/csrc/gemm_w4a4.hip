@@ -43,6 +43,7 @@
 // is split into bf16 hi + lo (hi + lo = P to 2^-16 relative) and multiplied on
 // bf16 MFMA 32x32x16, so the fp32 low-rank intermediate keeps ~16 bits.
 #include "ft_common.h"
+#include "ft_device.h"
 #include "ft_internal.h"
 
 namespace ft {
@@ -563,6 +564,99 @@ __device__ __forceinline__ void store_acc_bf16_lds(AccT<TMI, TNI>& acc, const Ge
   }
 }
 
+// MLP fusion epilogue (FourTune section 3.3 "MLP Fusion": the first linear's
+// GEMM carries the activation and the quantization of the next linear's input).
+// The tile of Y (bf16) goes through the LDS image as in store_acc_bf16_lds; each
+// thread stores its 16-byte pieces of Y, then h = GELU(Y) (fp32 math on the bf16
+// value, rounded to bf16) to H and back into the image; then Q(h) (16 x 16
+// blocks, power-of-two scales, E2M1 codes, the ft_quant_block16 rule) from the
+// image: 16 lanes per block, one block row per lane, the block maximum by DPP
+// within the 16 lanes.  Codes row-major [M][N/2], scales [M/16][N/16].
+template <int TMI, int TNI, int NWAVES, int BMc, int BNc>
+__device__ __forceinline__ void store_gelu_quant_lds(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
+                                                     int64_t m0, int64_t n0, int tid, int wm, int wn, int l32,
+                                                     int lh) {
+  constexpr int PITCH = 2 * BNc + 64;
+  const int t4 = tid & 3;
+#pragma unroll
+  for (int i = 0; i < TMI; ++i)
+#pragma unroll
+    for (int j = 0; j < TNI; ++j) {
+      const int col = wn * 32 * TNI + 32 * j + (l32 & ~3);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        quad_transpose4(v, t4);
+        const int row = wm * 32 * TMI + 32 * i + 8 * q + 4 * lh + t4;
+        const uint32_t lo = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+        *reinterpret_cast<v2i*>(smem + row * PITCH + 2 * col) = v2i{(int)lo, (int)hi};
+      }
+    }
+  compiler_fence();
+  __syncthreads();
+  compiler_fence();
+  constexpr int CH = BNc / 8;                                   // 16-byte chunks per row
+  constexpr int PER = BMc * CH / (64 * NWAVES);
+  static_assert(BMc * CH % (64 * NWAVES) == 0, "whole passes over the tile");
+  uint16_t* Y = static_cast<uint16_t*>(g.C);
+  uint16_t* H = static_cast<uint16_t*>(g.H);
+  v4i val[PER];
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int e = tid + 64 * NWAVES * it, r = e / CH, c = e - (e / CH) * CH;
+    val[it] = *reinterpret_cast<const v4i*>(smem + r * PITCH + 16 * c);
+  }
+#pragma unroll
+  for (int it = 0; it < PER; ++it) {
+    const int e = tid + 64 * NWAVES * it, r = e / CH, c = e - (e / CH) * CH;
+    const int64_t row = m0 + r, col = n0 + 8 * c;
+    const bool in = row < g.M && col < g.N;
+    if (in) *reinterpret_cast<v4i*>(Y + row * g.ldc + col) = val[it];
+    const uint32_t w[4] = {(uint32_t)val[it].x, (uint32_t)val[it].y, (uint32_t)val[it].z, (uint32_t)val[it].w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = f32_to_bf16_rne(gelu_f(bf16lo_to_f32(w[k]))) | (f32_to_bf16_rne(gelu_f(bf16hi_to_f32(w[k]))) << 16);
+    const v4i hv = {(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    if (in) *reinterpret_cast<v4i*>(H + row * g.ldc + col) = hv;
+    *reinterpret_cast<v4i*>(smem + r * PITCH + 16 * c) = hv;
+  }
+  compiler_fence();
+  __syncthreads();
+  compiler_fence();
+  constexpr int BC = BNc / 16, NBLK = (BMc / 16) * BC;          // blocks per tile
+  constexpr int GROUPS = 64 * NWAVES / 16;                      // 16-lane groups
+  const int grp = tid >> 4, li = tid & 15;
+#pragma unroll 1
+  for (int b = grp; b < NBLK; b += GROUPS) {                    // uniform within each 16-lane group
+    const int br = b / BC, bc = b - (b / BC) * BC, r = 16 * br + li;
+    const v4i x0 = *reinterpret_cast<const v4i*>(smem + r * PITCH + 32 * bc);
+    const v4i x1 = *reinterpret_cast<const v4i*>(smem + r * PITCH + 32 * bc + 16);
+    const uint32_t d[8] = {(uint32_t)x0.x, (uint32_t)x0.y, (uint32_t)x0.z, (uint32_t)x0.w,
+                           (uint32_t)x1.x, (uint32_t)x1.y, (uint32_t)x1.z, (uint32_t)x1.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = max(m, max(d[k] & 0x7fffu, (d[k] >> 16) & 0x7fffu));
+    const int E = pow2_exp_bf16(dpp_max16(m));
+    const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);
+    uint32_t c0 = 0, c1 = 0;   // byte k of c0 / c1: codes of values 2k, 2k+1 / 8+2k, 9+2k (low nibble first)
+#define FT_CVT2(K)                                                                          \
+    c0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c0, __builtin_bit_cast(v2bf, d[K]), sc, K); \
+    c1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c1, __builtin_bit_cast(v2bf, d[4 + K]), sc, K);
+    FT_CVT2(0)
+    FT_CVT2(1)
+    FT_CVT2(2)
+    FT_CVT2(3)
+#undef FT_CVT2
+    const int64_t row = m0 + r, col = n0 + 16 * bc;
+    if (row < g.M && col < g.N) {
+      *reinterpret_cast<v2i*>(g.hq + row * (g.N / 2) + col / 2) = v2i{(int)c0, (int)c1};
+      if (li == 0) g.hs[(row / 16) * (g.N / 16) + col / 16] = (uint8_t)(E + 127);
+    }
+  }
+}
+
 template <bool OUT_BF16, int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
 __device__ __forceinline__ void epilogue_and_store(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
                                                    int64_t m0, int64_t n0, int tid, int wave, int wm, int wn,
@@ -578,7 +672,8 @@ constexpr int GROUP_M = 4;   // tile rows per raster group
 
 
 // TRANS_B: backward instantiation (B = Q(R)^T); same code, separate name in profiles.
-template <bool OUT_BF16, bool TRANS_B, int CFG>   // CFG: 0 square tile, 1 wide tile
+// GELU_Q: MLP fusion epilogue (store_gelu_quant_lds; forward, bf16 Y)
+template <bool OUT_BF16, bool TRANS_B, int CFG, bool GELU_Q = false>   // CFG: 0 square tile, 1 wide tile
 __global__ void __launch_bounds__(PGT, 1)
 gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   using C = typename CfgOf<CFG>::type;
@@ -758,7 +853,13 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     tail_lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, g, smem + ((nkt - 4) % NSc) * C::STAGE,
                                                     smem + ((nkt - 3) % NSc) * C::STAGE, lane, wm, wn, l32, lh);
   }
-  if constexpr (OUT_BF16) {
+  if constexpr (GELU_Q) {
+    static_assert(OUT_BF16 && !TRANS_B, "MLP fusion epilogue: forward, bf16 output");
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();   // every wave done reading the last stage
+    compiler_fence();
+    store_gelu_quant_lds<C::TMI, C::TNI, 8, BMc, BNc>(acc, g, smem, m0, n0, tid, wm, wn, l32, lh);
+  } else if constexpr (OUT_BF16) {
     compiler_fence();
     __builtin_amdgcn_s_barrier();   // every wave done reading the last stage
     compiler_fence();
@@ -1095,6 +1196,28 @@ ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipSt
   const dim3 grid((unsigned)tiles), block(GT);
   if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g);
   else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g);
+  return launch_status();
+}
+
+ft_status launch_gemm_w4a4_gelu_quant(const GemmArgs& g, hipStream_t s) {
+  if (g.M == 0 || g.N == 0) return FT_OK;
+  const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;
+  const bool pipelined = g.K > 0 && g.K % 128 == 0 && BN * g.lda < ((int64_t)1 << 31) &&
+                         CfgWide::BN * g.ldb < ((int64_t)1 << 31);
+  if (!pipelined) return FT_ENOTSUP;
+  const int cus = num_cus();
+  const int64_t wide = ((g.M + CfgWide::BM - 1) / CfgWide::BM) * ((g.N + CfgWide::BN - 1) / CfgWide::BN);
+  const bool use_wide = fill(wide, cus) > fill(tiles, cus) + 0.02;
+  const int64_t tm = use_wide ? (g.M + CfgWide::BM - 1) / CfgWide::BM : tiles_m;
+  const int64_t tn = use_wide ? (g.N + CfgWide::BN - 1) / CfgWide::BN : tiles_n;
+  const int per_xcd = (int)((tm * tn + 7) / 8);
+  const dim3 grid((unsigned)(8 * per_xcd)), block(PGT);
+  if (use_wide)
+    hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 1, true>), grid, block, 0, s, g, (int)tm, (int)tn, per_xcd);
+  else
+    hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 0, true>), grid, block, 0, s, g, (int)tm, (int)tn, per_xcd);
   return launch_status();
 }
 

@@ -99,6 +99,44 @@ extern "C" ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
   return launch_gemm_w4a4(g, ydt == FT_OUT_BF16, false, stream);
 }
 
+extern "C" ft_status ft_linear_fwd_gelu(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                                        const uint8_t* xq_codes, const void* xq_scales,
+                                        const uint8_t* rq_codes, const void* rq_scales,
+                                        const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                                        void* Y, void* H, uint8_t* hq_codes, void* hq_scales, hipStream_t stream) {
+  using namespace ft;
+  if (mode != FT_SCALE_POW2 && mode != FT_SCALE_F32) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  if (mode != FT_SCALE_POW2) return FT_ENOTSUP;
+  if (M == 0 || N == 0) return FT_OK;
+  const int rho = rs + r;
+  if (!Y || !H || !hq_codes || !hq_scales || (K && (!xq_codes || !xq_scales || !rq_codes || !rq_scales)) ||
+      (rho && !T) || (rs && !L2) || (r && !B))
+    return FT_EINVAL;
+  if (!aligned16(Y) || !aligned16(H) || !aligned16(hq_codes) || !aligned16(hq_scales) ||
+      (K && (!aligned16(xq_codes) || !aligned16(rq_codes))) || (rho && !aligned16(T)) ||
+      (rs && !aligned16(L2)) || (r && !aligned16(B)))
+    return FT_EALIGN;
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = xq_codes; g.lda = K / 2;
+  g.B = rq_codes; g.ldb = K / 2;
+  g.sA = static_cast<const uint8_t*>(xq_scales); g.sA_rs = K / 16;
+  g.sB = static_cast<const uint8_t*>(rq_scales); g.sB_rs = K / 16;
+  g.P = T;
+  g.Wa = static_cast<const uint16_t*>(L2); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(B); g.rb = r;
+  g.C = Y; g.ldc = N;
+  g.H = H; g.hq = hq_codes; g.hs = static_cast<uint8_t*>(hq_scales);
+  const ft_status st = launch_gemm_w4a4_gelu_quant(g, stream);
+  if (st != FT_ENOTSUP) return st;
+  // no pipelined kernel for this K: the same three results from the separate kernels
+  ft_status s2 = launch_gemm_w4a4(g, true, false, stream);
+  if (s2 == FT_OK) s2 = ft_gelu_fwd(Y, M * N, H, stream);
+  if (s2 == FT_OK) s2 = ft_quant_block16(H, M, N, N, FT_SCALE_POW2, hq_codes, nullptr, hq_scales, nullptr, stream);
+  return s2;
+}
+
 extern "C" size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r) {
   using namespace ft;
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;

@@ -24,7 +24,7 @@
 // block s; a block is spread over the 16 lanes of one DPP row and the matching
 // 16 lanes of the other wave half, so its maximum is a 16-lane DPP reduction and
 // one permlane32 swap across the halves.
-#include "ft_common.h"
+#include "ft_device.h"
 
 namespace ft {
 namespace {
@@ -41,15 +41,6 @@ constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ int wswz(int row, int q) { return row * LR_WROW + ((q ^ (row & 15)) << 4); }
-
-// 16-lane maximum inside each DPP row (quad xor 1, xor 2, half-row mirror, row mirror)
-__device__ __forceinline__ uint32_t dpp_max16(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
-  return v;
-}
 
 // v_permlane32_swap exchanges the upper 32 lanes of its first operand with the
 // lower 32 lanes of its second; with both operands v, lane l ends up with
@@ -76,14 +67,6 @@ __device__ __forceinline__ uint32_t abs_max8(const v4i& v) {
   const v2u16 d = __builtin_bit_cast(v2u16, (uint32_t)v.w & 0x7fff7fffu);
   const v2u16 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
   return max((uint32_t)m.x, (uint32_t)m.y);
-}
-
-// E = min{e : 6 * 2^e >= a} clamped to [-127, 127] from the bf16 magnitude bits a.
-__device__ __forceinline__ int pow2_exp(uint32_t a) {
-  const int e = (int)(a >> 7);
-  if (e == 0) return -127;
-  const int E = (e - 127) - 2 + ((a & 0x7f) > 0x40 ? 1 : 0);
-  return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
 
 int64_t chunks_per_split(int64_t M, int64_t Kin) {
@@ -189,7 +172,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const uint32_t d[4] = {(uint32_t)x[s].x, (uint32_t)x[s].y, (uint32_t)x[s].z, (uint32_t)x[s].w};
-      const int E = pow2_exp(mx[s]);
+      const int E = pow2_exp_bf16(mx[s]);
       ex[s] = E;
       const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);
       uint32_t w = 0;

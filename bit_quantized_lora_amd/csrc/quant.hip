@@ -28,7 +28,7 @@
 // operand group, so every byte of the operand, padding included, is written.
 // Within a group the last 8 bytes of pairs 0..3 are stored in the order 0, 2,
 // 1, 3, so that one 16-byte read gives a GEMM lane both of its pairs' tails.
-#include "ft_common.h"
+#include "ft_device.h"
 
 namespace ft {
 namespace {
@@ -53,15 +53,6 @@ struct QuantOut {
 template <int MASK>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
   return (uint32_t)__shfl_xor((int)v, MASK, 64);
-}
-
-// E = min{e : 6 * 2^e >= a} clamped to [-127, 127], from the bf16 magnitude bits a.
-// a = 1.f * 2^q with 7-bit mantissa f: E = q - 2 when f <= 0.5 (1.f <= 1.5), else q - 1.
-__device__ __forceinline__ int pow2_exponent(uint32_t a) {
-  int e = (int)(a >> 7);
-  if (e == 0) return -127;  // zero or subnormal maximum: 6 * 2^-127 covers it
-  int E = (e - 127) - 2 + ((a & 0x7f) > 0x40 ? 1 : 0);
-  return E < -127 ? -127 : (E > 127 ? 127 : E);
 }
 
 // Transpose a 16x16 block of nibbles held one row per lane (64 bits: positions
@@ -184,7 +175,7 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
 
     uint32_t w0 = 0, w1 = 0;
     if constexpr (POW2) {
-      const int E = pow2_exponent(m);
+      const int E = pow2_exp_bf16(m);
       const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);  // 2^E as the E8M0 operand
 #define FT_CVT(W, K, SEL) W = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(W, __builtin_bit_cast(v2bf, d[K]), sc, SEL)
       FT_CVT(w0, 0, 0); FT_CVT(w0, 1, 1); FT_CVT(w0, 2, 2); FT_CVT(w0, 3, 3);

@@ -171,6 +171,25 @@ def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: in
     return out
 
 
+def linear_fwd_gelu(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
+                    mode: str = "pow2", out=None):
+    """First linear of an MLP with the fused epilogue: Y (bf16), H = GELU(Y) (bf16)
+    and Q(H) (row-major codes, scales); returns (Y, H, h_codes, h_scales)."""
+    rs, r = L2.shape[0], B.shape[0]
+    dev = T.device
+    if out is None:
+        out = (torch.empty((M, N), dtype=torch.bfloat16, device=dev), torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+               torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M // 16, N // 16), dtype=torch.uint8, device=dev))
+    Y, H, hc, hs = out
+    st = lib().ft_linear_fwd_gelu(M, N, K, _MODES[mode], xq_codes.data_ptr(), xq_scales.data_ptr(),
+                                  rq_codes.data_ptr(), rq_scales.data_ptr(), T.data_ptr(),
+                                  L2.data_ptr(), rs, B.data_ptr(), r, Y.data_ptr(), H.data_ptr(),
+                                  hc.data_ptr(), hs.data_ptr(), _stream(T))
+    check("ft_linear_fwd_gelu", st)
+    return Y, H, hc, hs
+
+
 def linear_bwd_workspace(M: int, N: int, K: int, r: int) -> int:
     return int(lib().ft_linear_bwd_workspace(M, N, K, r))
 

@@ -228,6 +228,28 @@ ft_status ft_linear_bwd_op(int64_t M, int64_t N, int64_t K, const uint8_t* g_op,
                            void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
                            void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ft_linear_fwd_gelu -- the first linear of an MLP block with the MLP fusion of
+ * section 3.3 ("MLP Fusion": the first linear's GEMM carries the activation and
+ * the quantization of the second linear's input, so the intermediate is not read
+ * back by separate kernels).  Eq. 2 as ft_linear_fwd with a bf16 Y, and from the
+ * same epilogue:
+ *
+ *   H  = GELU(Y)  (bf16; fp32 math on the bf16 Y, as ft_gelu_fwd)
+ *   Hq = Q(H)     (row-major codes and power-of-two scales, as ft_quant_block16)
+ *
+ *  Y, H        bf16 [M x N] (Y is kept for the GELU backward, H for the second
+ *              linear's adapter gradient dA)
+ *  hq_codes    row-major codes of H [M x N/2]; hq_scales [M/16 x N/16] E8M0 bytes
+ * All three equal, bit for bit, ft_linear_fwd (bf16) -> ft_gelu_fwd ->
+ * ft_quant_block16 (codes_rm, scales).  Operands and T, L2, B as ft_linear_fwd;
+ * FT_SCALE_POW2 only.  When K is not a multiple of 128 the three steps run as
+ * those separate kernels. */
+ft_status ft_linear_fwd_gelu(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                             const uint8_t* xq_codes, const void* xq_scales,
+                             const uint8_t* rq_codes, const void* rq_scales,
+                             const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                             void* Y, void* H, uint8_t* hq_codes, void* hq_scales, hipStream_t stream);
+
 /* GELU between the two linears of an MLP (section 3.3 "MLP Fusion" names the
  * activation; the exact erf form x * Phi(x) is used).  h = GELU(y) in bf16;
  * dy = GELU'(y) * dh in bf16.  y, dh, h, dy are bf16 [n] (n a multiple of 8). */

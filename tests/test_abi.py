@@ -87,6 +87,24 @@ def test_linear_argument_validation():
     assert lib.ft_linear_bwd(*args, None, 0, None) == L.FT_EINVAL
 
 
+def test_linear_fwd_gelu_argument_validation():
+    L = _lib(); lib = L.lib()
+    p = ctypes.c_void_p(16 * 1024)
+    ok = [16, 16, 16, 0, p, p, p, p, p, p, 16, p, 16, p, p, p, p, None]
+    bad_mode = list(ok); bad_mode[3] = 1
+    assert lib.ft_linear_fwd_gelu(*bad_mode) == L.FT_ENOTSUP                 # f32 scales
+    bad_k = list(ok); bad_k[2] = 24
+    assert lib.ft_linear_fwd_gelu(*bad_k) == L.FT_ESHAPE
+    no_h = list(ok); no_h[14] = None
+    assert lib.ft_linear_fwd_gelu(*no_h) == L.FT_EINVAL                      # H missing
+    no_codes = list(ok); no_codes[15] = None
+    assert lib.ft_linear_fwd_gelu(*no_codes) == L.FT_EINVAL
+    odd = list(ok); odd[16] = ctypes.c_void_p(16 * 1024 + 8)
+    assert lib.ft_linear_fwd_gelu(*odd) == L.FT_EALIGN
+    empty = [0, 16, 16, 0] + [None] * 6 + [16, None, 16, None, None, None, None, None]
+    assert lib.ft_linear_fwd_gelu(*empty) == L.FT_OK
+
+
 def test_gelu_argument_validation():
     L = _lib(); lib = L.lib()
     p = ctypes.c_void_p(16 * 1024)

@@ -39,7 +39,9 @@ class GpuLayer:
         from bit_quantized_lora_amd import ops
         self.ops = ops
         self.N, self.K = d["R"].shape
-        self.ro = ops.quant_block16_op(dev_bf16(d["R"]), op_rm=True, op_cm=True)
+        Rd = dev_bf16(d["R"])
+        self.ro = ops.quant_block16_op(Rd, op_rm=True, op_cm=True)
+        self.rq, _, self.rs = ops.quant_block16(Rd, rm=True, cm=False)
         self.L1t = dev_bf16(np.ascontiguousarray(d["L1"].T))
         self.At = dev_bf16(np.ascontiguousarray(d["A"].T))
         self.L2, self.B = dev_bf16(d["L2"]), dev_bf16(d["B"])
@@ -52,6 +54,24 @@ class GpuLayer:
         Y = o.linear_fwd_op(xo["op_rm"], xo["op_rm_scales"], self.ro["op_rm"], self.ro["op_rm_scales"], T, self.L2,
                             self.B, M, self.N, self.K, out_dtype=out_dtype)
         return Y, T
+
+    def fwd_codes_gelu(self, X):
+        """Forward on the E2M1-codes GEMM path with the MLP fusion epilogue:
+        (Y bf16, h bf16, Q(h) codes, Q(h) scales, T)."""
+        o = self.ops
+        M = X.shape[0]
+        xq, _, xs = o.quant_block16(X, rm=True, cm=False)
+        T = o.lowrank_fused(X, self.L1t, self.At)
+        Y, H, hc, hs = o.linear_fwd_gelu(xq, xs, self.rq, self.rs, T, self.L2, self.B, M, self.N, self.K)
+        return Y, H, hc, hs, T
+
+    def fwd_codes_given_q(self, X, xq, xs, out_dtype):
+        """Forward on the codes path from a Q(X) computed elsewhere."""
+        o = self.ops
+        M = X.shape[0]
+        T = o.lowrank_fused(X, self.L1t, self.At)
+        return o.linear_fwd(xq, xs, self.rq, self.rs, T, self.L2, self.B, M, self.N, self.K,
+                            out_dtype=out_dtype), T
 
     def bwd(self, G, X, T, out_dtype):
         o = self.ops
@@ -158,3 +178,80 @@ def test_block_stack_full_size(stream):
     _single(f"c5-{stream}-qkv", c[f"c5-{stream}-qkv"])
     _single(f"c5-{stream}-proj", c[f"c5-{stream}-proj"])
     _mlp_chain(f"c5-{stream}", c[f"c5-{stream}-up"], c[f"c5-{stream}-down"])
+
+
+def _fused_fc1_matches_separate(M, K, N, rs, r, seed):
+    """ft_linear_fwd_gelu against ft_linear_fwd -> ft_gelu_fwd -> ft_quant_block16,
+    bit for bit (Y, h, Q(h) codes and scales)."""
+    import torch
+    from bit_quantized_lora_amd import ops
+    rng = np.random.default_rng(seed)
+    spec = synth.LinearSpec("t", M, K, N, rs, r, x_dist="t3")
+    d = synth.make_linear(spec, rng)
+    say(f"[mlp-fusion] M={M} K={K} N={N} rs={rs} r={r}")
+    L = GpuLayer(d)
+    X = dev_bf16(d["X"])
+    Yf, Hf, hcf, hsf, T = L.fwd_codes_gelu(X)
+    xq, _, xs = ops.quant_block16(X, rm=True, cm=False)
+    Ys, _ = L.fwd_codes_given_q(X, xq, xs, torch.bfloat16)
+    Hs = ops.gelu_fwd(Ys)
+    hcs, _, hss = ops.quant_block16(Hs, rm=True, cm=False)
+    torch.cuda.synchronize()
+    for name, a, b in (("Y", Yf, Ys), ("h", Hf, Hs), ("Q(h) codes", hcf, hcs), ("Q(h) scales", hsf, hss)):
+        ha, hb = host(a.view(torch.int16) if a.dtype == torch.bfloat16 else a), \
+                 host(b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+        diff = int(np.count_nonzero(ha != hb))
+        say(f"[mlp-fusion]   {name}: {diff} of {ha.size} differ")
+        assert diff == 0, f"{name}: {diff} differing elements"
+
+
+@pytest.mark.parametrize("shape", [
+    (4608, 3072, 12288, 32, 16),   # MLP up at full size: wide tiles, low-rank after the main loop
+    (528, 1024, 784, 16, 16),      # square tiles, ragged N, low-rank after the main loop
+    (4592, 384, 12272, 16, 16),    # wide tiles, ragged M and N, low-rank before the main loop
+    (256, 272, 512, 16, 16),       # K % 128 != 0: the separate kernels
+], ids=lambda s: "x".join(map(str, s[:3])))
+def test_fused_fc1_epilogue_matches_separate_kernels(shape):
+    require_gpu()
+    M, K, N, rs, r = shape
+    _fused_fc1_matches_separate(M, K, N, rs, r, seed=M + K + N)
+
+
+def test_mlp_pair_chain_fused_fc1_full_size():
+    """The MLP pair with the fused first linear (codes GEMM path): the down layer
+    consumes Q(h) from the up layer's epilogue; every result against the oracle's
+    chain."""
+    require_gpu()
+    import torch
+    from bit_quantized_lora_amd import ops
+    c = _config("c3")
+    up, down = c["c3-up"], c["c3-down"]
+    say("[chain] mlp-pair fused FC1 (codes path)")
+    Lu, Ld = GpuLayer(up), GpuLayer(down)
+    X, G2 = dev_bf16(up["X"]), dev_bf16(down["G"])
+    Y1, h, hc, hs, T1 = Lu.fwd_codes_gelu(X)
+    Y2, T2 = Ld.fwd_codes_given_q(h, hc, hs, torch.float32)
+    dh, dA2, dB2 = Ld.bwd(G2, h, T2, torch.bfloat16)
+    dY1 = ops.gelu_bwd(Y1, dh)
+    dX1, dA1, dB1 = Lu.bwd(dY1, X, T1, torch.float32)
+    torch.cuda.synchronize()
+
+    Lou, Lod = OracleLayer(up), OracleLayer(down)
+    y1 = O.f64_to_bf16_bits(Lou.fwd(up["X"]))
+    hb = O.f64_to_bf16_bits(O.gelu(O.bf16_to_f64(y1)))
+    y2 = Lod.fwd(hb)
+    gd = Lod.bwd(down["G"], hb)
+    dhb = O.f64_to_bf16_bits(gd["dX"])
+    dy1 = O.f64_to_bf16_bits(O.gelu_grad(O.bf16_to_f64(y1)) * O.bf16_to_f64(dhb))
+    gu = Lou.bwd(dy1, up["X"])
+
+    _check("fused Y_up (bf16)", Y1, y1, bf16=True)
+    _check("fused h = GELU(Y_up) (bf16)", h, hb, bf16=True)
+    _check("fused Y_down", Y2, y2)
+    _check("fused dX_down = dh (bf16)", dh, dhb, bf16=True)
+    _check("fused dA_down", dA2, gd["dA"])
+    _check("fused dB_down", dB2, gd["dB"])
+    _check("fused dY_up (bf16)", dY1, dy1, bf16=True)
+    _check("fused dX_up", dX1, gu["dX"])
+    _check("fused dA_up", dA1, gu["dA"])
+    _check("fused dB_up", dB1, gu["dB"])
