@@ -197,6 +197,54 @@ def time_quantizer(reps):
     return out
 
 
+def time_mlp_fc1_fusion(lin, reps):
+    """The first linear of the MLP pair up to the second linear's inputs -- Y, h =
+    GELU(Y), Q(h) and T_down = h [L1_down | A_down] -- with the MLP fusion (GEMM
+    epilogue writes Y, h and Q(h); one low-rank pass over h) and with separate
+    kernels (GEMM, GELU, one quantize + low-rank pass over h).  Down factors are
+    seeded random bf16 of the MLP-down shape (rs 32, r 16)."""
+    import torch
+    from bit_quantized_lora_amd import ops
+    if lin.path == "op":
+        return None
+    M, N, K = lin.M, lin.N, lin.K
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1002)
+    wa = (0.02 * torch.randn(32, N, device="cuda", generator=gen)).to(torch.bfloat16)
+    wb = (0.01 * torch.randn(16, N, device="cuda", generator=gen)).to(torch.bfloat16)
+    bf, u8 = torch.bfloat16, torch.uint8
+    Y, H = torch.empty((M, N), dtype=bf, device="cuda"), torch.empty((M, N), dtype=bf, device="cuda")
+    hc, hs = torch.empty((M, N // 2), dtype=u8, device="cuda"), torch.empty((M // 16, N // 16), dtype=u8, device="cuda")
+    Td = torch.empty((M, 48), dtype=torch.float32, device="cuda")
+    ws = torch.empty((max(ops.lowrank_workspace(M, N, 48), 16),), dtype=u8, device="cuda")
+    xq, xs = lin.xq[0], lin.xq[2]
+
+    def fused():
+        ops.linear_fwd_gelu(xq, xs, lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=(Y, H, hc, hs))
+        ops.lowrank_fused(H, wa, wb, out=Td, workspace=ws)
+
+    def separate():
+        ops.linear_fwd(xq, xs, lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=Y)
+        ops.gelu_fwd(Y, out=H)
+        ops.quant_lowrank(H, wa, wb, out=Td, codes=hc, scales=hs, workspace=ws)
+
+    res = {}
+    s = torch.cuda.current_stream()
+    for name, fn in (("fused_us", fused), ("separate_us", separate)):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        e1.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    res["speedup"] = round(res["separate_us"] / res["fused_us"], 3)
+    return res
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fwd_mlp_up.traffic.txt")
 GEMM_SRC = os.path.join(ROOT, "bit_quantized_lora_amd", "csrc", "gemm_w4a4.hip")
 
@@ -317,6 +365,7 @@ def main():
     torch.cuda.synchronize()
     gemm_b2b_ms = g0.elapsed_time(g1) / args.steps
 
+    mlp_fusion = time_mlp_fc1_fusion(lin, args.steps)
     quant = time_quantizer(args.quant_reps)
     if args.calibration_copy:
         calibration_copy()
@@ -354,6 +403,7 @@ def main():
         "host_enqueue_us_per_step": round(host_us, 1),
         "quantizer": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in quant.items()},
+        "mlp_fc1_fusion_us": mlp_fusion,
         "quant_GBps": round(quant["dY"]["GBps"], 1),
         "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),
     }
