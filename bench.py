@@ -246,7 +246,7 @@ def time_mlp_fc1_fusion(lin, reps):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fwd_mlp_up.traffic.txt")
-GEMM_SRC = os.path.join(ROOT, "bit_quantized_lora_amd", "csrc", "gemm_w4a4.hip")
+GEMM_SRCS = [os.path.join(ROOT, "bit_quantized_lora_amd", "csrc", f) for f in ("gemm_w4a4.hip", "gemm_tile.h")]
 
 
 def measured_traffic():
@@ -260,7 +260,7 @@ def measured_traffic():
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    sha = hashlib.sha256(b"".join(open(p, "rb").read() for p in GEMM_SRCS)).hexdigest()
     if kv.get("gemm_source_sha256") != sha:
         return None
     return int(float(kv["hbm_bytes_per_launch"]))

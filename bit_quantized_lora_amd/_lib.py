@@ -42,6 +42,11 @@ _SIGS = {
     "ft_linear_bwd_op": [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
                          c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                          c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "ft_linear_fwd_a16": [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                          c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p],
+    "ft_linear_bwd_g16": [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                          c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
+                          c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_gelu_fwd": [c_void_p, c_int64, c_void_p, c_void_p],
     "ft_gelu_bwd": [c_void_p, c_void_p, c_int64, c_void_p, c_void_p],
     "ft_status_str": [c_int32],

@@ -32,6 +32,11 @@ ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipSt
 // kernel for it); the caller then runs the separate kernels.
 ft_status launch_gemm_w4a4_gelu_quant(const GemmArgs& g, hipStream_t s);
 
+// C[M x N] = A[M x K] deq(B)[N x K]^T + P [Wa; Wb] with a bf16 left operand:
+// g.A points to bf16 [M x K] with row pitch g.lda BYTES (g.sA unused); B, its
+// scales, P, W and C as for launch_gemm_w4a4.  K any multiple of 16.
+ft_status launch_gemm_a16(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s);
+
 // Same product from pair-merged FP6 operands (ft_quant_block16_op): A, B are
 // operand bytes with row pitch lda / ldb (= groups * 96), sA / sB the operand
 // scale grids with sA_rs / sB_rs = groups * 8 bytes per 16-row block.  K may be

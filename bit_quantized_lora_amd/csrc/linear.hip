@@ -266,3 +266,70 @@ extern "C" ft_status ft_linear_bwd_op(int64_t M, int64_t N, int64_t K, const uin
   auto gemm = [&](hipStream_t s, bool) { return (M && K) ? launch_gemm_m6(g, out_bf16, true, s) : FT_OK; };
   return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
 }
+
+// Precision variants (section 4.3 "Impact of Precision Configurations", Table 4):
+// the backbone GEMM with the unquantized bf16 activations (W4A16: Eq. 2 with X in
+// place of Q(X)) or output gradient (G16: Eq. 3 with G in place of Q(G)); R stays
+// quantized.  The low-rank branches and adapter gradients are those of the
+// W4A4G4 calls.
+extern "C" ft_status ft_linear_fwd_a16(int64_t M, int64_t N, int64_t K, const void* X,
+                                       const uint8_t* rq_codes, const void* rq_scales,
+                                       const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                                       void* Y, ft_out_dtype ydt, hipStream_t stream) {
+  using namespace ft;
+  if (ydt != FT_OUT_F32 && ydt != FT_OUT_BF16) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  if (M == 0 || N == 0) return FT_OK;
+  const int rho = rs + r;
+  if (!Y || (K && (!X || !rq_codes || !rq_scales)) || (rho && !T) || (rs && !L2) || (r && !B))
+    return FT_EINVAL;
+  const void* ptrs[] = {Y, X, rq_codes, rq_scales, T, L2, B};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = static_cast<const uint8_t*>(X); g.lda = 2 * K;
+  g.B = rq_codes; g.ldb = K / 2;
+  g.sB = static_cast<const uint8_t*>(rq_scales); g.sB_rs = K / 16;
+  g.P = T;
+  g.Wa = static_cast<const uint16_t*>(L2); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(B); g.rb = r;
+  g.C = Y; g.ldc = N;
+  return launch_gemm_a16(g, ydt == FT_OUT_BF16, false, stream);
+}
+
+extern "C" ft_status ft_linear_bwd_g16(int64_t M, int64_t N, int64_t K, const void* G,
+                                       const uint8_t* rq_codes_cm, const void* rq_scales_cm,
+                                       const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                                       const void* X, const float* T,
+                                       void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  using namespace ft;
+  if (dxdt != FT_OUT_F32 && dxdt != FT_OUT_BF16) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  const int rho = rs + r;
+  const size_t need = ft_linear_bwd_workspace(M, N, K, r);
+  if (M && K && !dX) return FT_EINVAL;
+  if (M && N && K && (!G || !rq_codes_cm || !rq_scales_cm)) return FT_EINVAL;
+  if (M && rho && !V) return FT_EINVAL;
+  if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
+  if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
+  if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
+  const void* ptrs[] = {G, rq_codes_cm, rq_scales_cm, V, L1t, At, X, T, dX, dAt, dB, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  // dX = G deq(Rq) + V [L1^T; A^T]: reduction over the N output features, R's
+  // column-major codes and transposed scale grid as the right operand
+  GemmArgs g{};
+  g.M = M; g.N = K; g.K = N;
+  g.A = static_cast<const uint8_t*>(G); g.lda = 2 * N;
+  g.B = rq_codes_cm; g.ldb = N / 2;
+  g.sB = static_cast<const uint8_t*>(rq_scales_cm); g.sB_rs = N / 16;
+  g.P = V;
+  g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
+  g.C = dX; g.ldc = K;
+  const bool out_bf16 = dxdt == FT_OUT_BF16;
+  auto gemm = [&](hipStream_t s, bool) { return (M && K) ? launch_gemm_a16(g, out_bf16, true, s) : FT_OK; };
+  return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
+}

@@ -257,6 +257,43 @@ def linear_bwd_op(g_op, g_op_scales, rt_op, rt_op_scales, V, L1t, At, X, G, T, M
     return dX, dAt, dB
 
 
+def linear_fwd_a16(X, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
+                   out_dtype=torch.float32, out: Optional[torch.Tensor] = None):
+    """W4A16 forward: Y = X deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B (X bf16, unquantized)."""
+    rs, r = L2.shape[0], B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    st = lib().ft_linear_fwd_a16(M, N, K, X.data_ptr(), rq_codes.data_ptr(), rq_scales.data_ptr(),
+                                 T.data_ptr(), L2.data_ptr(), rs, B.data_ptr(), r, out.data_ptr(),
+                                 _OUT[out.dtype], _stream(X))
+    check("ft_linear_fwd_a16", st)
+    return out
+
+
+def linear_bwd_g16(G, rq_codes_cm, rq_scales_cm, V, L1t, At, X, T, M: int, N: int, K: int,
+                   out_dtype=torch.float32, workspace: Optional[torch.Tensor] = None,
+                   dX: Optional[torch.Tensor] = None, dAt: Optional[torch.Tensor] = None,
+                   dB: Optional[torch.Tensor] = None):
+    """G16 backward: dX = G deq(Rq) + V [L1^T; A^T] (G bf16, unquantized) and dAt, dB."""
+    rs, r = L1t.shape[0], At.shape[0]
+    dev = G.device
+    if dX is None:
+        dX = torch.empty((M, K), dtype=out_dtype, device=dev)
+    if dAt is None:
+        dAt = torch.empty((r, K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((r, N), dtype=torch.float32, device=dev)
+    ws_bytes = linear_bwd_workspace(M, N, K, r)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    st = lib().ft_linear_bwd_g16(M, N, K, G.data_ptr(), rq_codes_cm.data_ptr(), rq_scales_cm.data_ptr(),
+                                 V.data_ptr(), L1t.data_ptr(), rs, At.data_ptr(), r, X.data_ptr(),
+                                 T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype], dAt.data_ptr(),
+                                 dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(G))
+    check("ft_linear_bwd_g16", st)
+    return dX, dAt, dB
+
+
 def gelu_fwd(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     _need(y, torch.bfloat16, "y")
     if out is None:

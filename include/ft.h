@@ -250,6 +250,36 @@ ft_status ft_linear_fwd_gelu(int64_t M, int64_t N, int64_t K, ft_scale_mode mode
                              const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
                              void* Y, void* H, uint8_t* hq_codes, void* hq_scales, hipStream_t stream);
 
+/* ft_linear_fwd_a16 / ft_linear_bwd_g16 -- the precision variants of section
+ * 4.3 ("Impact of Precision Configurations", Table 4).  W4A16 keeps the
+ * activations in bf16, G16 the output gradient; the weight residual stays
+ * quantized (same Q(R), same codes and block scales as the W4A4G4 calls), and
+ * the low-rank branches and adapter gradients are unchanged.  With ft_linear_fwd
+ * and ft_linear_bwd they make up the four settings of the table:
+ *   W4A4G4 = fwd + bwd,  W4A16G4 = fwd_a16 + bwd,
+ *   W4A4G16 = fwd + bwd_g16,  W4A16G16 = fwd_a16 + bwd_g16.
+ *
+ *   fwd_a16:  Y  = X deq(Rq)^T + T[:, 0:rs] L2 + T[:, rs:rs+r] B     (Eq. 2, X for Q(X))
+ *   bwd_g16:  dX = G deq(Rq)   + V[:, 0:rs] L1t + V[:, rs:rs+r] At   (Eq. 3, G for Q(G))
+ *             dAt = V[:, rs:rs+r]^T X,  dB = T[:, rs:rs+r]^T G
+ *
+ *  X  bf16 [M x K] (leading dimension K), G bf16 [M x N] (leading dimension N)
+ *  rq_codes, rq_scales         as ft_linear_fwd (FT_SCALE_POW2 bytes)
+ *  rq_codes_cm, rq_scales_cm   as ft_linear_bwd (FT_SCALE_POW2 bytes)
+ * All other arguments, layouts, the workspace and the stream behaviour are those
+ * of ft_linear_fwd / ft_linear_bwd.  The backbone product runs on bf16 matrix
+ * instructions with Q(R) dequantized exactly to bf16 and fp32 accumulation. */
+ft_status ft_linear_fwd_a16(int64_t M, int64_t N, int64_t K, const void* X,
+                            const uint8_t* rq_codes, const void* rq_scales,
+                            const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                            void* Y, ft_out_dtype ydt, hipStream_t stream);
+ft_status ft_linear_bwd_g16(int64_t M, int64_t N, int64_t K, const void* G,
+                            const uint8_t* rq_codes_cm, const void* rq_scales_cm,
+                            const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                            const void* X, const float* T,
+                            void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* GELU between the two linears of an MLP (section 3.3 "MLP Fusion" names the
  * activation; the exact erf form x * Phi(x) is used).  h = GELU(y) in bf16;
  * dy = GELU'(y) * dh in bf16.  y, dh, h, dy are bf16 [n] (n a multiple of 8). */

@@ -105,6 +105,37 @@ def test_linear_fwd_gelu_argument_validation():
     assert lib.ft_linear_fwd_gelu(*empty) == L.FT_OK
 
 
+def test_precision_variant_argument_validation():
+    L = _lib(); lib = L.lib()
+    p = ctypes.c_void_p(16 * 1024)
+    #      M   N   K   X  rq rs T  L2 rs  B  r   Y  ydt stream
+    fwd = [16, 16, 16, p, p, p, p, p, 16, p, 16, p, 0, None]
+    bad = list(fwd); bad[12] = 7
+    assert lib.ft_linear_fwd_a16(*bad) == L.FT_EINVAL                        # unknown output type
+    bad = list(fwd); bad[1] = 24
+    assert lib.ft_linear_fwd_a16(*bad) == L.FT_ESHAPE
+    bad = list(fwd); bad[8] = 128
+    assert lib.ft_linear_fwd_a16(*bad) == L.FT_ESHAPE                        # rs + r > 128
+    bad = list(fwd); bad[3] = None
+    assert lib.ft_linear_fwd_a16(*bad) == L.FT_EINVAL                        # X missing
+    bad = list(fwd); bad[3] = ctypes.c_void_p(16 * 1024 + 8)
+    assert lib.ft_linear_fwd_a16(*bad) == L.FT_EALIGN
+    assert lib.ft_linear_fwd_a16(0, 16, 16, None, None, None, None, None, 16, None, 16, None, 0, None) == L.FT_OK
+    ws = int(lib.ft_linear_bwd_workspace(16, 16, 16, 16))
+    #      M   N   K   G  rqc rsc V  L1t rs At r   X  T  dX dxdt dAt dB ws  bytes stream
+    bwd = [16, 16, 16, p, p, p, p, p, 16, p, 16, p, p, p, 0, p, p, p, ws, None]
+    bad = list(bwd); bad[18] = ws - 1
+    assert lib.ft_linear_bwd_g16(*bad) == L.FT_ESPACE
+    bad = list(bwd); bad[17] = None
+    assert lib.ft_linear_bwd_g16(*bad) == L.FT_EINVAL                        # workspace missing
+    bad = list(bwd); bad[3] = None
+    assert lib.ft_linear_bwd_g16(*bad) == L.FT_EINVAL                        # G missing
+    bad = list(bwd); bad[2] = 40
+    assert lib.ft_linear_bwd_g16(*bad) == L.FT_ESHAPE
+    bad = list(bwd); bad[13] = ctypes.c_void_p(16 * 1024 + 4)
+    assert lib.ft_linear_bwd_g16(*bad) == L.FT_EALIGN
+
+
 def test_gelu_argument_validation():
     L = _lib(); lib = L.lib()
     p = ctypes.c_void_p(16 * 1024)
