@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 (and MXFP6), published
 HBM_PEAK_GBPS = 8000.0         # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
 
 def parse():
@@ -245,6 +246,68 @@ def time_mlp_fc1_fusion(lin, reps):
     return res
 
 
+def time_precision_variants(lin, reps):
+    """The precision settings of the paper's Table 4 on the same linear: the bf16
+    x E2M1 GEMMs (W4A16 forward: X unquantized; G16 backward: G unquantized)
+    against the 4-bit ones, each launched back to back, and the whole fwd+bwd
+    step of each setting (an A16 / G16 side skips its quantizer but keeps the
+    low-rank pass)."""
+    import torch
+    from bit_quantized_lora_amd import ops
+    if lin.path == "op":
+        return None
+    M, N, K = lin.M, lin.N, lin.K
+    Yv, dXv = torch.empty_like(lin.Y), torch.empty_like(lin.dX)
+    dAt, dB = torch.empty_like(lin.dAt), torch.empty_like(lin.dB)
+
+    def fwd_a16():
+        ops.linear_fwd_a16(lin.X, lin.rq, lin.rs_, lin.T, lin.L2, lin.B, M, N, K, out=Yv)
+
+    def bwd_g16():
+        ops.linear_bwd_g16(lin.G, lin.rqc, lin.rsct, lin.V, lin.L1t, lin.At, lin.X, lin.T, M, N, K,
+                           workspace=lin.ws, dX=dXv, dAt=dAt, dB=dB)
+
+    def step(a16, g16):
+        def run():
+            if a16:
+                lin.lowrank_x()
+                fwd_a16()
+            else:
+                lin.forward()
+            if g16:
+                lin.lowrank_g()
+                bwd_g16()
+            else:
+                lin.backward()
+        return run
+
+    s = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    flops = 2.0 * M * N * K
+    res = {}
+    for name, fn in (("fwd_gemm_w4a4", lin.gemm_fwd), ("fwd_gemm_w4a16", fwd_a16),
+                     ("bwd_w4g4", lin.gemm_bwd_and_grads), ("bwd_g16", bwd_g16)):
+        us = timed(fn)
+        res[name] = {"us": round(us, 2), "TFLOPs": round(flops / us / 1e6, 1)}
+    res["fwd_gemm_w4a16"]["frac_bf16_peak"] = round(res["fwd_gemm_w4a16"]["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+    res["step_us"] = {tag: round(timed(step(a16, g16)), 2)
+                      for tag, a16, g16 in (("W4A4G4", False, False), ("W4A16G4", True, False),
+                                            ("W4A4G16", False, True), ("W4A16G16", True, True))}
+    return res
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fwd_mlp_up.traffic.txt")
 GEMM_SRCS = [os.path.join(ROOT, "bit_quantized_lora_amd", "csrc", f) for f in ("gemm_w4a4.hip", "gemm_tile.h")]
 
@@ -366,6 +429,7 @@ def main():
     gemm_b2b_ms = g0.elapsed_time(g1) / args.steps
 
     mlp_fusion = time_mlp_fc1_fusion(lin, args.steps)
+    precision = time_precision_variants(lin, args.steps)
     quant = time_quantizer(args.quant_reps)
     if args.calibration_copy:
         calibration_copy()
@@ -404,6 +468,7 @@ def main():
         "quantizer": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in quant.items()},
         "mlp_fc1_fusion_us": mlp_fusion,
+        "precision_variants": precision,
         "quant_GBps": round(quant["dY"]["GBps"], 1),
         "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),
     }

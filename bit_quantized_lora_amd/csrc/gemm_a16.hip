@@ -73,9 +73,10 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
-// E8M0 byte -> the float 2^(byte - 127) (byte 0: the subnormal 2^-127)
+// E8M0 byte -> the float 2^(byte - 127) (byte 0: the subnormal 2^-127); the
+// byte 0x100 stands for a scale of zero (masked elements past the end of K)
 __device__ __forceinline__ float e8m0_value(uint32_t b) {
-  return __builtin_bit_cast(float, b ? b << 23 : 0x00400000u);
+  return __builtin_bit_cast(float, b == 0x100u ? 0u : (b ? b << 23 : 0x00400000u));
 }
 
 // 8 E2M1 codes (one dword, element e in nibble e) times scale -> 8 bf16
@@ -96,7 +97,7 @@ struct AFrag {
 };
 struct BFrag {
   v2i codes[H_TNI];   // dword s: the 8 codes of k-step s
-  float sc[H_TNI];
+  uint32_t sb[H_TNI];  // E8M0 scale byte (converted where used, off the read's critical path)
 };
 
 __device__ __forceinline__ void read_a(AFrag& f, const uint8_t* st, int s, int wm, int l32, int lh) {
@@ -114,14 +115,24 @@ __device__ __forceinline__ void read_b(BFrag& f, const uint8_t* st, int kt, int 
     f.codes[j] = *reinterpret_cast<const v2i*>(st + H_A_ST + row * 16 + 8 * lh);
     const int blk = row >> 4;
     const int pos = (blk * srs4 + 2 * kt) & 3;
-    f.sc[j] = e8m0_value(st[H_A_ST + H_B_ST + 8 * blk + pos + lh]);
+    f.sb[j] = st[H_A_ST + H_B_ST + 8 * blk + pos + lh];
   }
 }
 
 template <int S>
 __device__ __forceinline__ void dequant_b(v8bf (&bv)[H_TNI], const BFrag& f) {
 #pragma unroll
-  for (int j = 0; j < H_TNI; ++j) bv[j] = dequant8((uint32_t)f.codes[j][S], f.sc[j]);
+  for (int j = 0; j < H_TNI; ++j) bv[j] = dequant8((uint32_t)f.codes[j][S], e8m0_value(f.sb[j]));
+}
+
+// keeps values computed before a following wait / barrier (asm operand)
+__device__ __forceinline__ void pin_b(const v8bf (&bv)[H_TNI]) {
+#pragma unroll
+  for (int j = 0; j < H_TNI; ++j) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" ::"v"(bv[j]));
+#endif
+  }
 }
 
 template <int I0, int I1>
@@ -262,23 +273,24 @@ gemm_a16_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
 #pragma unroll
         for (int i = 0; i < H_TMI; ++i) c0.a[i] = p1.a[i] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < H_TNI; ++j) bf.sc[j] = 0.0f;
+        for (int j = 0; j < H_TNI; ++j) bf.sb[j] = 0x100u;
       }
       dequant_b<0>(b0, bf);
       dequant_b<1>(b1, bf);
       __builtin_amdgcn_sched_barrier(0);
       mma_rows<0, H_TMI>(acc, c0, b0);
       pin_acc(acc);
+      pin_b(b1);
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + 1 < nkt) {
-        compiler_fence();
-        wait_stages(min(H_NS - 3, nkt - kt - 2));
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
-        const uint8_t* nx = smem + __builtin_amdgcn_readfirstlane(((kt + 1) % H_NS) * H_STAGE);
-        read_a(c0, nx, 0, wm, l32, lh);
-        read_b(bf, nx, kt + 1, srs4, wn, l32, lh);
-      }
+      // (also in the last iteration, where the reads fetch an unused buffer: no
+      // branch around them, so the LDS counter stays straight-line for the MFMAs)
+      compiler_fence();
+      wait_stages(max(0, min(H_NS - 3, nkt - kt - 2)));
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      const uint8_t* nx = smem + __builtin_amdgcn_readfirstlane(((kt + 1) % H_NS) * H_STAGE);
+      read_a(c0, nx, 0, wm, l32, lh);
+      read_b(bf, nx, kt + 1, srs4, wn, l32, lh);
       __builtin_amdgcn_sched_barrier(0);
       mma_rows<0, H_TMI / 2>(acc, p1, b1);
       pin_acc(acc);
