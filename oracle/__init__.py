@@ -15,7 +15,12 @@ for Diffusion Models"):
 * backward dX = GEMM_4bit(Q(G), Q(R)^T) + G L_stab^T + G (A B)^T (section
   3.2, Eq. 3) and dB = (X A)^T G, dA = X^T (G B^T) (section 3.2);
 * the offline split W ~= R + L1 L2 (section 3.1, Eq. 1) is checked, not
-  produced, here.
+  produced, here;
+* the other quantization granularities of section 4.3 ("Impact of
+  Quantization Granularity", Table 5): 1 x g groups along rows (g = 16, and
+  g = 32, the group the gfx950 block-scaled instruction takes), and the
+  backward's re-quantization of the transposed weight that group scales
+  force (section 3.2).
 
 Everything is evaluated in fp64 on exactly dequantized values.  Every
 function is pinned by a ``-m "not gpu"`` test against brute force, exact

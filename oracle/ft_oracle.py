@@ -37,7 +37,8 @@ __all__ = [
     "block_amax", "scale_pow2_exponent", "scale_f32", "quantize_block16",
     "pack_rm", "pack_cm", "unpack_rm", "dequantize", "scale_values",
     "linear_fwd", "linear_bwd", "gelu", "gelu_grad", "svd_split_check",
-    "rel_frob", "BLOCK",
+    "rel_frob", "BLOCK", "quantize_pow2", "dequantize_pow2", "quantize_groups",
+    "requantize_transposed", "rel_mse",
     "e3m2_decode", "OP_GROUP", "operand_merge", "operand_values", "operand_shape",
 ]
 
@@ -350,6 +351,64 @@ def operand_values(op, op_scales, rows: int, cols: int) -> np.ndarray:
     v = e3m2_decode(c6).reshape(rows, 32 * P)
     s = np.exp2(np.asarray(op_scales).astype(np.float64) - 127.0)  # [rows/16, 2P]
     return v * np.repeat(np.repeat(s, BLOCK, 0), BLOCK, 1)
+
+
+# --------------------------------------------------------------------------
+# Other quantization granularities (section 4.3 "Impact of Quantization
+# Granularity", Table 5: group-wise 1x16 against the 16x16 blocks; section
+# 3.2: group scales along a row end up along the reduction axis of the
+# transposed product)
+# --------------------------------------------------------------------------
+# Reading: a 1 x g group is g consecutive elements of one row (the reduction
+# axis of the forward product), with the same element rule (E2M1,
+# round-to-nearest-even, sign of the input) and the same pow2 scale rule as the
+# 16x16 blocks.  g = 16 is the paper's group-wise setting; g = 32 is the group
+# length the gfx950 block-scaled matrix instruction takes per scale.  The
+# transposed product of the backward reduces over R's rows, across R's groups,
+# so with group scales Q(R) is dequantized and quantized again in groups along
+# its columns: Q_g(deq(Q_g(R))^T).
+def quantize_pow2(x, bh: int, bw: int) -> Tuple[np.ndarray, np.ndarray]:
+    """pow2-rule Q(.) of an fp64 matrix over bh x bw blocks.
+
+    Returns (codes uint8 [rows, cols], scale bytes uint8 [rows/bh, cols/bw]);
+    E per block from the block maximum (scale_pow2_exponent), element ratio
+    x * 2^-E (exact), E2M1 round-to-nearest-even (e2m1_rne).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows, cols = x.shape
+    assert rows % bh == 0 and cols % bw == 0, "shape must be a multiple of the block"
+    xb = x.reshape(rows // bh, bh, cols // bw, bw)
+    E = scale_pow2_exponent(np.abs(xb).max(axis=(1, 3)))
+    v = xb * np.exp2(-E.astype(np.float64))[:, None, :, None]
+    return e2m1_rne(v).reshape(rows, cols), (E + 127).astype(np.uint8)
+
+
+def dequantize_pow2(codes, scales, bh: int, bw: int) -> np.ndarray:
+    """Exact fp64 value of a pow2-quantized matrix with bh x bw blocks."""
+    s = np.exp2(np.asarray(scales).astype(np.float64) - 127.0)
+    return e2m1_decode(codes) * np.repeat(np.repeat(s, bh, 0), bw, 1)
+
+
+def quantize_groups(bits, g: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Q(.) of a bf16 matrix in 1 x g groups along its rows: codes [rows, cols]
+    and scale bytes [rows, cols/g]."""
+    return quantize_pow2(bf16_to_f64(bits), 1, g)
+
+
+def requantize_transposed(codes, scales, g: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The backward's right operand under 1 x g groups: the values of Q_g(R)
+    transposed and quantized again in 1 x g groups, Q_g(deq(Q_g(R))^T).
+    codes [rows, cols], scales [rows, cols/g] of R -> codes [cols, rows],
+    scales [cols, rows/g]."""
+    return quantize_pow2(dequantize_pow2(codes, scales, 1, g).T, 1, g)
+
+
+def rel_mse(x, xhat) -> float:
+    """||x - xhat||^2 / ||x||^2 in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x - np.asarray(xhat, dtype=np.float64)
+    n = float(np.sum(x * x))
+    return float(np.sum(d * d)) / n if n > 0 else 0.0
 
 
 # --------------------------------------------------------------------------

@@ -567,3 +567,110 @@ def test_operand_of_the_transpose():
     op, osc = O.operand_merge(codes.T, scales.T)
     v = O.operand_values(op, osc, 160, 96)
     assert np.array_equal(v[:, :96], O.dequantize(codes, scales, "pow2").T)
+
+
+# ---------------------------------------------------------------- group granularities
+@pytest.mark.parametrize("g", [16, 32])
+def test_group_quantizer_elementwise_bruteforce(g):
+    """1 x g groups along each row: scale byte and every code re-derived by
+    exact rational brute force (section 4.3, Table 5's group-wise setting)."""
+    rng = np.random.default_rng(17 + g)
+    x = (rng.standard_normal((6, 96)) * np.exp2(rng.integers(-6, 6, (6, 96)))).astype(np.float32)
+    x[2, :g] = 0.0
+    x[3, g:2 * g] = -0.0
+    bits = synth.f32_to_bf16_bits(x)
+    codes, scales = O.quantize_groups(bits, g)
+    assert codes.shape == (6, 96) and scales.shape == (6, 96 // g)
+    xv = O.bf16_to_f64(bits)
+    for i in range(6):
+        for q in range(96 // g):
+            grp = xv[i, g * q:g * q + g]
+            E = _pow2_bruteforce(Fraction(float(np.abs(grp).max())))
+            assert scales[i, q] == E + 127
+            for j in range(g):
+                v = float(grp[j])
+                ratio = float(Fraction(v) / Fraction(2) ** E) if v != 0 else v
+                assert codes[i, g * q + j] == _rne_bruteforce(ratio), (i, q, j)
+
+
+def test_group_quantizer_reduces_to_16x16_blocks():
+    """When every row of a 16x16 block reaches the block's maximum, the 1 x 16
+    groups and the 16 x 16 blocks take the same scale and the same codes."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((32, 64)).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    xv = O.bf16_to_f64(bits).astype(np.float32)
+    for bi in range(2):
+        for bj in range(4):
+            blk = xv[16 * bi:16 * bi + 16, 16 * bj:16 * bj + 16]
+            m = np.abs(blk).max()
+            for r in range(16):
+                blk[r, (r * 5) % 16] = m if r % 2 else -m
+    bits = synth.f32_to_bf16_bits(xv)
+    cg, sg = O.quantize_groups(bits, 16)
+    cb, sb = O.quantize_block16(bits, "pow2")
+    assert np.array_equal(cg, cb)
+    assert np.array_equal(sg, np.repeat(sb, 16, axis=0))
+
+
+def _dequant_group_exact(codes, scales, g):
+    """Exact rational values of a group-quantized matrix from the code table."""
+    vals = {}
+    for bits, val in _read_golden("e2m1_table.txt"):
+        vals[int(bits, 2)] = Fraction(float(val))
+    rows, cols = codes.shape
+    return [[vals[int(codes[i, j])] * Fraction(2) ** (int(scales[i, j // g]) - 127) for j in range(cols)]
+            for i in range(rows)]
+
+
+@pytest.mark.parametrize("g", [16, 32])
+def test_requantize_transposed_bruteforce(g):
+    """Q_g(deq(Q_g(R))^T): the transpose of the exact dequantized values,
+    quantized again by brute force in groups along R's columns."""
+    rng = np.random.default_rng(31 + g)
+    R = (rng.standard_normal((2 * g, 64)) * np.exp2(rng.integers(-5, 5, (2 * g, 64)))).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(R)
+    c, s = O.quantize_groups(bits, g)
+    ct, st = O.requantize_transposed(c, s, g)
+    assert ct.shape == (64, 2 * g) and st.shape == (64, 2)
+    D = _dequant_group_exact(c, s, g)
+    for col in range(64):
+        for q in range(2):
+            grp = [D[g * q + r][col] for r in range(g)]
+            E = _pow2_bruteforce(max(abs(v) for v in grp))
+            assert st[col, q] == E + 127
+            for r in range(g):
+                v = grp[r]
+                code = int(c[g * q + r, col])
+                ratio = float(v / Fraction(2) ** E)
+                if v == 0:   # a zero keeps the sign bit of its code
+                    assert ct[col, g * q + r] == (code & 8)
+                else:
+                    assert ct[col, g * q + r] == _rne_bruteforce(ratio)
+
+
+def test_requantize_transposed_lossless_when_groups_share_the_maximum():
+    """If every group along the rows and along the columns holds a +-6 x 2^E
+    element (one common E) and all values are E2M1 values x 2^E, quantizing,
+    transposing and quantizing again loses nothing: the codes are transposed."""
+    rng = np.random.default_rng(41)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    v = grid[rng.integers(0, 8, (32, 64))] * rng.choice([-1.0, 1.0], (32, 64))
+    for i in range(32):
+        for j in range(4):
+            v[i, 16 * j + (i % 16)] = 6.0 if (i + j) % 2 else -6.0
+    v *= 2.0 ** -3
+    bits = synth.f32_to_bf16_bits(v.astype(np.float32))
+    c, s = O.quantize_groups(bits, 16)
+    assert np.all(s == 127 - 3)
+    ct, st = O.requantize_transposed(c, s, 16)
+    assert np.all(st == 127 - 3)
+    nz = (c.T & 7) != 0
+    assert np.array_equal(ct[nz], c.T[nz])
+    assert np.array_equal(O.dequantize_pow2(ct, st, 1, 16), O.bf16_to_f64(bits).T)
+
+
+def test_rel_mse_closed_form():
+    x = np.array([[3.0, 4.0]])
+    assert O.rel_mse(x, np.array([[3.0, 0.0]])) == 16.0 / 25.0
+    assert O.rel_mse(x, x) == 0.0
