@@ -47,6 +47,13 @@ _SIGS = {
     "ft_linear_bwd_g16": [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
                           c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p,
                           c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "ft_quant_group": [c_void_p, c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p],
+    "ft_requant_group_t": [c_void_p, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p],
+    "ft_linear_fwd_grp": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                          c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p],
+    "ft_linear_bwd_grp": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                          c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                          c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_gelu_fwd": [c_void_p, c_int64, c_void_p, c_void_p],
     "ft_gelu_bwd": [c_void_p, c_void_p, c_int64, c_void_p, c_void_p],
     "ft_status_str": [c_int32],

@@ -32,6 +32,11 @@ ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipSt
 // kernel for it); the caller then runs the separate kernels.
 ft_status launch_gemm_w4a4_gelu_quant(const GemmArgs& g, hipStream_t s);
 
+// The same product with scales per 1 x gs group along each row (gs 16 or 32):
+// sA [M][K / gs], sB [N][K / gs] bytes (sA_rs = sB_rs = K / gs).  Square tiles,
+// K a multiple of 128 (FT_ENOTSUP otherwise).
+ft_status launch_gemm_w4a4_groups(const GemmArgs& g, int gs, bool out_bf16, bool trans_b, hipStream_t s);
+
 // C[M x N] = A[M x K] deq(B)[N x K]^T + P [Wa; Wb] with a bf16 left operand:
 // g.A points to bf16 [M x K] with row pitch g.lda BYTES (g.sA unused); B, its
 // scales, P, W and C as for launch_gemm_w4a4.  K any multiple of 16.

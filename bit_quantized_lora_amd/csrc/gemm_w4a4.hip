@@ -57,13 +57,18 @@ constexpr int tc_max(int a, int b) { return a > b ? a : b; }
 // 192 x 384 tile (same operand bytes per FLOP) is taken when it fills the chip
 // in fewer partial rounds, e.g. 4608 x 12288 = 768 tiles = 3 full rounds on
 // 256 CUs where 256 x 256 gives 864 tiles = 3.4 rounds.
-template <int BM_, int BN_, int WM_, int TMI_, int NS_, int CHUNK_>
+// GS: scale granularity.  0: 16x16 blocks (the method's); 16 or 32: 1 x GS
+// groups along each row (section 4.3's group-wise setting, and the group the
+// block-scaled MFMA takes per scale), scale bytes [rows][K / GS].
+template <int BM_, int BN_, int WM_, int TMI_, int NS_, int CHUNK_, int GS_ = 0>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = 8 / WM_, TMI = TMI_;
   static constexpr int TNI = BN_ / (8 / WM_) / 32;
-  static constexpr int NS = NS_, CHUNK = CHUNK_;
+  static constexpr int NS = NS_, CHUNK = CHUNK_, GS = GS_;
   static constexpr int A_ST = BM * TC_BKB, B_ST = BN * TC_BKB;
-  static constexpr int SA_DW = BM / 16 * 2, SB_DW = BN / 16 * 2;      // scale dwords per stage
+  // scale dwords per stage: two per 16-row block, or 128 / GS bytes per row
+  static constexpr int DPR = GS ? 128 / GS / 4 : 0;                   // ... dwords per row (group modes)
+  static constexpr int SA_DW = GS ? BM * DPR : BM / 16 * 2, SB_DW = GS ? BN * DPR : BN / 16 * 2;
   static constexpr int STAGE = A_ST + B_ST + (SA_DW + SB_DW) * 4;
   static constexpr int N16 = (BM + BN) / 16;                          // 1-KiB DMAs per stage
   static constexpr int NQ = (N16 + 7) / 8;                            // ... per wave, at most
@@ -72,7 +77,10 @@ struct TileCfg {
   // same number DPS of DMA instructions per stage (compile-time wait counts).
   // Of the SW scale waves, the first WA fetch A's scale dwords, the others B's.
   static constexpr int FS = N16 % 8, SW = 8 - FS;
-  static constexpr int DPS = FS ? NQ : NQ + 1;
+  // group modes: the scale dwords take SQ whole 64-lane DMA instructions,
+  // spread evenly over the waves (A's first, then B's)
+  static constexpr int SQ = (SA_DW + SB_DW) / 64;
+  static constexpr int DPS = GS ? NQ + SQ / 8 : (FS ? NQ : NQ + 1);
   static constexpr int WA_RAW = (SW * SA_DW + (SA_DW + SB_DW) / 2) / (SA_DW + SB_DW);
   static constexpr int WA = WA_RAW < 1 ? 1 : (WA_RAW > SW - 1 ? SW - 1 : WA_RAW);
   static constexpr int LA = (SA_DW + WA - 1) / WA, LB = (SB_DW + (SW - WA) - 1) / (SW - WA);
@@ -80,17 +88,18 @@ struct TileCfg {
   static constexpr int SMEM = tc_max(tc_max(NS * STAGE, (NS - 1) * STAGE + CHUNK * W_PITCH),
                                      BM * (2 * BN + 64));                 // bf16 output tile image
   static_assert(BM == WM * 32 * TMI && BN == WN * 32 * TNI, "tile shape");
-  static_assert(SW >= 2 && LA <= 64 && LB <= 64, "scale DMA split");
+  static_assert(GS || (SW >= 2 && LA <= 64 && LB <= 64), "scale DMA split");
   // every scale wave has at least one dword to fetch
-  static_assert((WA - 1) * LA < SA_DW && (SW - WA - 1) * LB < SB_DW, "idle scale wave");
+  static_assert(GS || ((WA - 1) * LA < SA_DW && (SW - WA - 1) * LB < SB_DW), "idle scale wave");
+  static_assert(!GS || (FS == 0 && SA_DW % 64 == 0 && SB_DW % 64 == 0 && SQ % 8 == 0), "group-mode DMA split");
   static_assert(SMEM <= 160 * 1024, "LDS");
 };
 // CHUNK: ranks per low-rank pass; its W rows (pitch 2 BN + 32 bytes) go to the
 // last stage buffer (and the LDS beyond the ring where they need more)
 using CfgSquare = TileCfg<256, 256, 4, 2, 4, 48>;
 using CfgWide = TileCfg<192, 384, 2, 3, 4, 48>;
-template <int I> struct CfgOf { using type = CfgSquare; };
-template <> struct CfgOf<1> { using type = CfgWide; };
+template <int I, int GS = 0> struct CfgOf { using type = TileCfg<256, 256, 4, 2, 4, 48, GS>; };
+template <> struct CfgOf<1, 0> { using type = CfgWide; };
 }  // namespace ft
 
 namespace ft {
@@ -212,6 +221,49 @@ __device__ __forceinline__ void mma_kstep(AccT<TMI, TNI>& acc, const Part<TMI, T
   }
 }
 
+// Group modes (per-row scales, bytes [rows][K / GS]; in LDS one row after
+// another, DPR dwords each, A's rows then B's).  1 x 16: the lane's dword holds
+// the scales of its four 16-K blocks (k-steps 0-3), as in the 16x16 layout.
+// 1 x 32: part P's 16-byte read is the lane's 32-K group 2 lh + P, so the
+// lane's two bytes sit at 2 lh, 2 lh + 1 of its row's dword: shifted down, the
+// part selects byte P.
+template <int GS, int TMI, int TNI, int BMc, int BNc>
+__device__ __forceinline__ void read_scales_g(int (&sa)[TMI], int (&sb)[TNI], const uint8_t* st, int wm, int wn,
+                                              int l32, int lh) {
+  constexpr int RB = 128 / GS;                                   // scale bytes per row per stage
+  const uint8_t* SAs = st + (BMc + BNc) * BKB;
+  const uint8_t* SBs = SAs + BMc * RB;
+#pragma unroll
+  for (int i = 0; i < TMI; ++i) {
+    const int r = wm * 32 * TMI + 32 * i + l32;
+    if constexpr (GS == 16) sa[i] = *reinterpret_cast<const int*>(SAs + r * RB + 4 * lh);
+    else sa[i] = (int)(*reinterpret_cast<const uint32_t*>(SAs + r * RB) >> (16 * lh));
+  }
+#pragma unroll
+  for (int j = 0; j < TNI; ++j) {
+    const int r = wn * 32 * TNI + 32 * j + l32;
+    if constexpr (GS == 16) sb[j] = *reinterpret_cast<const int*>(SBs + r * RB + 4 * lh);
+    else sb[j] = (int)(*reinterpret_cast<const uint32_t*>(SBs + r * RB) >> (16 * lh));
+  }
+}
+
+// 1 x 32 groups: one MFMA per tile covers part P's 64 K (every K slot carries
+// data), rows I0 .. I1-1 of the wave's tiles.
+template <int P, int I0, int I1, int TMI, int TNI>
+__device__ __forceinline__ void mma_full(AccT<TMI, TNI>& acc, const Part<TMI, TNI>& f, const int (&sa)[TMI],
+                                         const int (&sb)[TNI]) {
+  const v4i z = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = I0; i < I1; ++i) {
+    const v8i aop = __builtin_shufflevector(f.a[i], z, 0, 1, 2, 3, 4, 4, 4, 4);
+#pragma unroll
+    for (int j = 0; j < TNI; ++j) {
+      const v8i bop = __builtin_shufflevector(f.b[j], z, 0, 1, 2, 3, 4, 4, 4, 4);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop, acc[i][j], 4, 4, P, sa[i], P, sb[j]);
+    }
+  }
+}
+
 template <int P, int TMI, int TNI>
 __device__ __forceinline__ void mma_part(AccT<TMI, TNI>& acc, const Part<TMI, TNI>& f, const int (&sa)[TMI],
                                          const int (&sb)[TNI]) {
@@ -321,10 +373,11 @@ __device__ __forceinline__ void store_gelu_quant_lds(AccT<TMI, TNI>& acc, const 
 
 // TRANS_B: backward instantiation (B = Q(R)^T); same code, separate name in profiles.
 // GELU_Q: MLP fusion epilogue (store_gelu_quant_lds; forward, bf16 Y)
-template <bool OUT_BF16, bool TRANS_B, int CFG, bool GELU_Q = false>   // CFG: 0 square tile, 1 wide tile
+// GS: scale granularity (TileCfg); the group modes use the square tile.
+template <bool OUT_BF16, bool TRANS_B, int CFG, bool GELU_Q = false, int GS = 0>   // CFG: 0 square tile, 1 wide tile
 __global__ void __launch_bounds__(PGT, 1)
 gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
-  using C = typename CfgOf<CFG>::type;
+  using C = typename CfgOf<CFG, GS>::type;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
   constexpr int BMc = C::BM, BNc = C::BN, NSc = C::NS;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -376,6 +429,11 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   const bool s_on = scale_w && lane < sl && sd < (scale_b ? C::SB_DW : C::SA_DW);
   const uint32_t offS = (uint32_t)((sd >> 1) * s_rs + 4 * (sd & 1));
   const int s_lds = C::A_ST + C::B_ST + 4 * ((scale_b ? C::SA_DW : 0) + sw * sl);
+  // group modes: the scale rows of the tile's A and B rows ([rows][K / GS] bytes)
+  const __amdgpu_buffer_rsrc_t rSA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.sA + m0 * g.sA_rs), 0, (int)(min<int64_t>(BMc, g.M - m0) * g.sA_rs), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rSB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.sB + n0 * g.sB_rs), 0, (int)(min<int64_t>(BNc, g.N - n0) * g.sB_rs), RSRC_FLAGS);
 
   auto issue = [&](int stage, int kt) {
     uint8_t* base = smem + stage * C::STAGE;
@@ -390,8 +448,22 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
                __builtin_amdgcn_readfirstlane(soff));
       }
     }
-    if (scale_w) {   // wave-uniform: the instruction counts even where no lane is active
-      if (s_on) dma4(rS, base + s_lds, offS + (uint32_t)kt * 8);
+    if constexpr (C::GS == 0) {
+      if (scale_w) {   // wave-uniform: the instruction counts even where no lane is active
+        if (s_on) dma4(rS, base + s_lds, offS + (uint32_t)kt * 8);
+      }
+    } else {
+      // scale DMA instruction t = wave + 8u covers scale dwords 64t .. 64t+63 of
+      // the stage (A's rows, then B's; each instruction within one of them)
+#pragma unroll
+      for (int u = 0; u < C::SQ / 8; ++u) {
+        const int t = wave + 8 * u;
+        const bool isb = t * 64 >= C::SA_DW;
+        const int d = t * 64 + lane - (isb ? C::SA_DW : 0);
+        const int row = d / C::DPR, part = d - (d / C::DPR) * C::DPR;
+        const uint32_t off = (uint32_t)(row * (isb ? g.sB_rs : g.sA_rs)) + (uint32_t)(kt * (128 / C::GS) + 4 * part);
+        dma4(isb ? rSB : rSA, base + C::A_ST + C::B_ST + 256 * t, off);
+      }
     }
   };
 
@@ -451,7 +523,8 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     const uint8_t* st = smem + __builtin_amdgcn_readfirstlane((kt % NSc) * C::STAGE);
     read_part<C::TMI, C::TNI, BMc, BNc>(p1, st, 1, wm, wn, l32, lh);
     __builtin_amdgcn_sched_barrier(0);
-    mma_part<0>(acc, c0, sa, sb);
+    if constexpr (C::GS == 32) mma_full<0, 0, C::TMI>(acc, c0, sa, sb);
+    else mma_part<0>(acc, c0, sa, sb);
     pin_acc(acc);
     __builtin_amdgcn_sched_barrier(0);
     if (steady || kt + 1 < nkt) {
@@ -466,17 +539,20 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
       }
       const uint8_t* nx = smem + __builtin_amdgcn_readfirstlane(((kt + 1) % NSc) * C::STAGE);
       read_part<C::TMI, C::TNI, BMc, BNc>(c0, nx, 0, wm, wn, l32, lh);
-      read_scales<C::TMI, C::TNI, BMc, BNc>(na, nb, nx, wm, wn, l32, lh);
+      if constexpr (C::GS) read_scales_g<C::GS, C::TMI, C::TNI, BMc, BNc>(na, nb, nx, wm, wn, l32, lh);
+      else read_scales<C::TMI, C::TNI, BMc, BNc>(na, nb, nx, wm, wn, l32, lh);
     }
     __builtin_amdgcn_sched_barrier(0);
-    mma_kstep<2>(acc, p1, sa, sb);
+    if constexpr (C::GS == 32) mma_full<1, 0, C::TMI / 2>(acc, p1, sa, sb);
+    else mma_kstep<2>(acc, p1, sa, sb);
     pin_acc(acc);
     __builtin_amdgcn_sched_barrier(0);
     // the next DMA between part 1's two k-steps: its LDS writes then overlap
     // MFMAs instead of the fragment reads just issued
     if (steady) issue((kt + NSc - 1) % NSc, kt + NSc - 1);
     __builtin_amdgcn_sched_barrier(0);
-    mma_kstep<3>(acc, p1, sa, sb);
+    if constexpr (C::GS == 32) mma_full<1, C::TMI / 2, C::TMI>(acc, p1, sa, sb);
+    else mma_kstep<3>(acc, p1, sa, sb);
 #pragma unroll
     for (int i = 0; i < C::TMI; ++i) sa[i] = na[i];
 #pragma unroll
@@ -488,7 +564,8 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
   __builtin_amdgcn_s_barrier();
   compiler_fence();
   read_part<C::TMI, C::TNI, BMc, BNc>(c0, smem, 0, wm, wn, l32, lh);
-  read_scales<C::TMI, C::TNI, BMc, BNc>(sa, sb, smem, wm, wn, l32, lh);
+  if constexpr (C::GS) read_scales_g<C::GS, C::TMI, C::TNI, BMc, BNc>(sa, sb, smem, wm, wn, l32, lh);
+  else read_scales<C::TMI, C::TNI, BMc, BNc>(sa, sb, smem, wm, wn, l32, lh);
   const int n_steady = max(0, nkt - (NSc - 1));
   int kt = 0;
   for (; kt < n_steady; ++kt) step(kt, true);
@@ -850,6 +927,32 @@ ft_status launch_gemm_w4a4_gelu_quant(const GemmArgs& g, hipStream_t s) {
     hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 1, true>), grid, block, 0, s, g, (int)tm, (int)tn, per_xcd);
   else
     hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 0, true>), grid, block, 0, s, g, (int)tm, (int)tn, per_xcd);
+  return launch_status();
+}
+
+ft_status launch_gemm_w4a4_groups(const GemmArgs& g, int gs, bool out_bf16, bool trans_b, hipStream_t s) {
+  if (g.M == 0 || g.N == 0) return FT_OK;
+  if (gs != 16 && gs != 32) return FT_EINVAL;
+  const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;
+  if (!(g.K > 0 && g.K % 128 == 0)) return FT_ENOTSUP;   // pipelined kernel only
+  if (BM * g.lda >= ((int64_t)1 << 31) || BN * g.ldb >= ((int64_t)1 << 31) ||
+      BM * g.sA_rs >= ((int64_t)1 << 31) || BN * g.sB_rs >= ((int64_t)1 << 31))
+    return FT_ESHAPE;
+  const int per_xcd = (int)((tiles + 7) / 8);
+  const dim3 grid((unsigned)(8 * per_xcd)), block(PGT);
+  const int tm = (int)tiles_m, tn = (int)tiles_n;
+#define FT_GEMM_G(OB, TB, G) \
+  hipLaunchKernelGGL((gemm_w4a4_kernel<OB, TB, 0, false, G>), grid, block, 0, s, g, tm, tn, per_xcd)
+  if (gs == 16) {
+    if (out_bf16) { if (trans_b) FT_GEMM_G(true, true, 16); else FT_GEMM_G(true, false, 16); }
+    else { if (trans_b) FT_GEMM_G(false, true, 16); else FT_GEMM_G(false, false, 16); }
+  } else {
+    if (out_bf16) { if (trans_b) FT_GEMM_G(true, true, 32); else FT_GEMM_G(true, false, 32); }
+    else { if (trans_b) FT_GEMM_G(false, true, 32); else FT_GEMM_G(false, false, 32); }
+  }
+#undef FT_GEMM_G
   return launch_status();
 }
 

@@ -333,3 +333,77 @@ extern "C" ft_status ft_linear_bwd_g16(int64_t M, int64_t N, int64_t K, const vo
   auto gemm = [&](hipStream_t s, bool) { return (M && K) ? launch_gemm_a16(g, out_bf16, true, s) : FT_OK; };
   return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
 }
+
+// Other quantization granularities (section 4.3 "Impact of Quantization
+// Granularity", Table 5): Eq. 2 and Eq. 3 with every 4-bit operand scaled per
+// 1 x group elements along its reduction axis (ft_quant_group); the backward's
+// right operand is the re-quantized transpose of Q(R) (ft_requant_group_t).
+extern "C" ft_status ft_linear_fwd_grp(int64_t M, int64_t N, int64_t K, int32_t group,
+                                       const uint8_t* xq_codes, const uint8_t* xq_scales,
+                                       const uint8_t* rq_codes, const uint8_t* rq_scales,
+                                       const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                                       void* Y, ft_out_dtype ydt, hipStream_t stream) {
+  using namespace ft;
+  if (ydt != FT_OUT_F32 && ydt != FT_OUT_BF16) return FT_EINVAL;
+  if (group != 16 && group != 32) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  if (M == 0 || N == 0) return FT_OK;
+  if (K % 128 != 0) return FT_ENOTSUP;
+  const int rho = rs + r;
+  if (!Y || !xq_codes || !xq_scales || !rq_codes || !rq_scales || (rho && !T) || (rs && !L2) || (r && !B))
+    return FT_EINVAL;
+  const void* ptrs[] = {Y, xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = xq_codes; g.lda = K / 2;
+  g.B = rq_codes; g.ldb = K / 2;
+  g.sA = xq_scales; g.sA_rs = K / group;
+  g.sB = rq_scales; g.sB_rs = K / group;
+  g.P = T;
+  g.Wa = static_cast<const uint16_t*>(L2); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(B); g.rb = r;
+  g.C = Y; g.ldc = N;
+  return launch_gemm_w4a4_groups(g, group, ydt == FT_OUT_BF16, false, stream);
+}
+
+extern "C" ft_status ft_linear_bwd_grp(int64_t M, int64_t N, int64_t K, int32_t group,
+                                       const uint8_t* gq_codes, const uint8_t* gq_scales,
+                                       const uint8_t* rtq_codes, const uint8_t* rtq_scales,
+                                       const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                                       const void* X, const void* G, const float* T,
+                                       void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  using namespace ft;
+  if (dxdt != FT_OUT_F32 && dxdt != FT_OUT_BF16) return FT_EINVAL;
+  if (group != 16 && group != 32) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
+  if (M && K && N % 128 != 0) return FT_ENOTSUP;
+  const int rho = rs + r;
+  const size_t need = ft_linear_bwd_workspace(M, N, K, r);
+  if (M && K && !dX) return FT_EINVAL;
+  if (M && N && K && (!gq_codes || !gq_scales || !rtq_codes || !rtq_scales)) return FT_EINVAL;
+  if (M && rho && !V) return FT_EINVAL;
+  if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
+  if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
+  if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
+  const void* ptrs[] = {gq_codes, gq_scales, rtq_codes, rtq_scales, V, L1t, At, X, G, T, dX, dAt, dB, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  GemmArgs g{};
+  g.M = M; g.N = K; g.K = N;
+  g.A = gq_codes; g.lda = N / 2;
+  g.B = rtq_codes; g.ldb = N / 2;
+  g.sA = gq_scales; g.sA_rs = N / group;
+  g.sB = rtq_scales; g.sB_rs = N / group;
+  g.P = V;
+  g.Wa = static_cast<const uint16_t*>(L1t); g.ra = rs;
+  g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
+  g.C = dX; g.ldc = K;
+  const bool out_bf16 = dxdt == FT_OUT_BF16;
+  auto gemm = [&](hipStream_t s, bool) {
+    return (M && K) ? launch_gemm_w4a4_groups(g, group, out_bf16, true, s) : FT_OK;
+  };
+  return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
+}

@@ -294,6 +294,69 @@ def linear_bwd_g16(G, rq_codes_cm, rq_scales_cm, V, L1t, At, X, T, M: int, N: in
     return dX, dAt, dB
 
 
+def quant_group(x: torch.Tensor, group: int, out=None):
+    """Q(x) in 1 x group groups along rows: (codes [rows, cols/2], scales [rows, cols/group])."""
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if out is None:
+        out = (torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((rows, cols // group), dtype=torch.uint8, device=x.device))
+    codes, scales = out
+    st = lib().ft_quant_group(x.data_ptr(), rows, cols, x.stride(0), group, codes.data_ptr(), scales.data_ptr(),
+                              _stream(x))
+    check("ft_quant_group", st)
+    return codes, scales
+
+
+def requant_group_t(codes: torch.Tensor, scales: torch.Tensor, rows: int, cols: int, group: int, out=None):
+    """Q(deq(Q(R))^T) in 1 x group groups: (codes_t [cols, rows/2], scales_t [cols, rows/group])."""
+    if out is None:
+        out = (torch.empty((cols, rows // 2), dtype=torch.uint8, device=codes.device),
+               torch.empty((cols, rows // group), dtype=torch.uint8, device=codes.device))
+    ct, st_ = out
+    st = lib().ft_requant_group_t(codes.data_ptr(), scales.data_ptr(), rows, cols, group, ct.data_ptr(),
+                                  st_.data_ptr(), _stream(codes))
+    check("ft_requant_group_t", st)
+    return ct, st_
+
+
+def linear_fwd_grp(group, xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
+                   out_dtype=torch.float32, out: Optional[torch.Tensor] = None):
+    """Eq. 2 with 1 x group scaled operands (ft_quant_group of X and R)."""
+    rs, r = L2.shape[0], B.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=T.device)
+    st = lib().ft_linear_fwd_grp(M, N, K, group, xq_codes.data_ptr(), xq_scales.data_ptr(), rq_codes.data_ptr(),
+                                 rq_scales.data_ptr(), T.data_ptr(), L2.data_ptr(), rs, B.data_ptr(), r,
+                                 out.data_ptr(), _OUT[out.dtype], _stream(T))
+    check("ft_linear_fwd_grp", st)
+    return out
+
+
+def linear_bwd_grp(group, gq_codes, gq_scales, rtq_codes, rtq_scales, V, L1t, At, X, G, T, M: int, N: int, K: int,
+                   out_dtype=torch.float32, workspace: Optional[torch.Tensor] = None,
+                   dX: Optional[torch.Tensor] = None, dAt: Optional[torch.Tensor] = None,
+                   dB: Optional[torch.Tensor] = None):
+    """Eq. 3 and the adapter gradients with 1 x group scaled operands (rtq: ft_requant_group_t of Q(R))."""
+    rs, r = L1t.shape[0], At.shape[0]
+    dev = V.device
+    if dX is None:
+        dX = torch.empty((M, K), dtype=out_dtype, device=dev)
+    if dAt is None:
+        dAt = torch.empty((r, K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((r, N), dtype=torch.float32, device=dev)
+    ws_bytes = linear_bwd_workspace(M, N, K, r)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    st = lib().ft_linear_bwd_grp(M, N, K, group, gq_codes.data_ptr(), gq_scales.data_ptr(), rtq_codes.data_ptr(),
+                                 rtq_scales.data_ptr(), V.data_ptr(), L1t.data_ptr(), rs, At.data_ptr(), r,
+                                 X.data_ptr(), G.data_ptr(), T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype],
+                                 dAt.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(V))
+    check("ft_linear_bwd_grp", st)
+    return dX, dAt, dB
+
+
 def gelu_fwd(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     _need(y, torch.bfloat16, "y")
     if out is None:

@@ -280,6 +280,53 @@ ft_status ft_linear_bwd_g16(int64_t M, int64_t N, int64_t K, const void* G,
                             void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
                             void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Other quantization granularities -- section 4.3 ("Impact of Quantization
+ * Granularity", Table 5) compares the 16x16 blocks with group-wise 1 x 16
+ * scales; 1 x 32 is the group one scale covers in gfx950's block-scaled matrix
+ * instruction.  Same element and scale rules as FT_SCALE_POW2 (E2M1 codes,
+ * scale 2^E with E = min{e : 6 * 2^e >= group max} clamped to [-127, 127],
+ * stored as the byte E + 127), over 1 x group elements along each row.
+ *
+ * ft_quant_group -- Q(x) in 1 x group groups (group 16 or 32).
+ *  x       bf16 [rows x cols], leading dimension ldx (elements, rows 16-byte aligned)
+ *  codes   out: row-major packed codes [rows x cols/2] (as ft_quant_block16 codes_rm)
+ *  scales  out: [rows x cols/group] bytes
+ *  cols must be a multiple of group (FT_ESHAPE).  Bit-exact function of x.
+ *
+ * ft_requant_group_t -- the backward's right operand under group scales
+ * (section 3.2: group scales of a row lie along the reduction axis once the
+ * matrix is transposed, so Q(R)^T cannot be read in place): the values of
+ * Q(R) = (codes, scales) [rows x cols] transposed and quantized again in
+ * 1 x group groups, Q(deq(Q(R))^T).
+ *  codes_t  out: row-major codes [cols x rows/2];  scales_t out: [cols x rows/group]
+ *  rows and cols must be multiples of group.  Exact (bit-exact function of the input).
+ *
+ * ft_linear_fwd_grp / ft_linear_bwd_grp -- Eq. 2 and Eq. 3 (and the adapter
+ * gradients) with group-scaled operands: xq / rq from ft_quant_group of X and R
+ * (scales [M x K/group], [N x K/group]); gq from ft_quant_group of G (scales
+ * [M x N/group]); rtq from ft_requant_group_t of Q(R) (codes [K x N/2],
+ * scales [K x N/group]).  Other arguments as ft_linear_fwd / ft_linear_bwd.
+ * The reduction length (K forward, N backward) must be a multiple of 128
+ * (FT_ENOTSUP otherwise).  With group 32 every 32-element fragment of the
+ * block-scaled MFMA carries data; with group 16 half of it does, as in the
+ * 16x16 path. */
+ft_status ft_quant_group(const void* x, int64_t rows, int64_t cols, int64_t ldx, int32_t group,
+                         uint8_t* codes, uint8_t* scales, hipStream_t stream);
+ft_status ft_requant_group_t(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                             int32_t group, uint8_t* codes_t, uint8_t* scales_t, hipStream_t stream);
+ft_status ft_linear_fwd_grp(int64_t M, int64_t N, int64_t K, int32_t group,
+                            const uint8_t* xq_codes, const uint8_t* xq_scales,
+                            const uint8_t* rq_codes, const uint8_t* rq_scales,
+                            const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                            void* Y, ft_out_dtype ydt, hipStream_t stream);
+ft_status ft_linear_bwd_grp(int64_t M, int64_t N, int64_t K, int32_t group,
+                            const uint8_t* gq_codes, const uint8_t* gq_scales,
+                            const uint8_t* rtq_codes, const uint8_t* rtq_scales,
+                            const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                            const void* X, const void* G, const float* T,
+                            void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* GELU between the two linears of an MLP (section 3.3 "MLP Fusion" names the
  * activation; the exact erf form x * Phi(x) is used).  h = GELU(y) in bf16;
  * dy = GELU'(y) * dh in bf16.  y, dh, h, dy are bf16 [n] (n a multiple of 8). */

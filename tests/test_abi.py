@@ -136,6 +136,28 @@ def test_precision_variant_argument_validation():
     assert lib.ft_linear_bwd_g16(*bad) == L.FT_EALIGN
 
 
+def test_group_granularity_argument_validation():
+    L = _lib(); lib = L.lib()
+    p = ctypes.c_void_p(16 * 1024)
+    assert lib.ft_quant_group(p, 16, 32, 32, 8, p, p, None) == L.FT_EINVAL            # group 8
+    assert lib.ft_quant_group(p, 16, 48, 48, 32, p, p, None) == L.FT_ESHAPE           # cols % 32
+    assert lib.ft_quant_group(p, 16, 32, 24, 16, p, p, None) == L.FT_ESHAPE           # ldx < cols
+    assert lib.ft_quant_group(p, 0, 32, 32, 16, None, None, None) == L.FT_OK
+    assert lib.ft_requant_group_t(p, p, 48, 64, 32, p, p, None) == L.FT_ESHAPE        # rows % 32
+    assert lib.ft_requant_group_t(p, p, 32, 64, 16, None, p, None) == L.FT_EINVAL
+    #      M   N    K    g  xq xs rq rs T  L2 rs  B  r   Y  ydt stream
+    fwd = [16, 128, 128, 16, p, p, p, p, p, p, 16, p, 16, p, 0, None]
+    bad = list(fwd); bad[2] = 144
+    assert lib.ft_linear_fwd_grp(*bad) == L.FT_ENOTSUP                                 # K % 128
+    bad = list(fwd); bad[3] = 64
+    assert lib.ft_linear_fwd_grp(*bad) == L.FT_EINVAL
+    bad = list(fwd); bad[5] = None
+    assert lib.ft_linear_fwd_grp(*bad) == L.FT_EINVAL
+    ws = int(lib.ft_linear_bwd_workspace(16, 128, 128, 16))
+    bwd = [16, 144, 128, 32, p, p, p, p, p, p, 16, p, 16, p, p, p, p, 0, p, p, p, ws, None]
+    assert lib.ft_linear_bwd_grp(*bwd) == L.FT_ENOTSUP                                 # N % 128
+
+
 def test_gelu_argument_validation():
     L = _lib(); lib = L.lib()
     p = ctypes.c_void_p(16 * 1024)
