@@ -95,7 +95,7 @@ class Linear:
             self.rq, self.rqc, self.rs_, self.rsct = ops.quant_block16(R, rm=True, cm=True, scales_cm=True)
             self.xq = (e((M, K // 2), u8), None, e((M // 16, K // 16), u8))
             self.gq = (e((M, N // 2), u8), None, e((M // 16, N // 16), u8))
-        del R
+        self.R = R
         self.T, self.V = e((M, rs + r), f32), e((M, rs + r), f32)
         self.Y, self.dX = e((M, N), bf), e((M, K), bf)
         self.dAt, self.dB = e((r, K), f32), e((r, N), f32)
@@ -308,6 +308,86 @@ def time_precision_variants(lin, reps):
     return res
 
 
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def _deq(codes, scales, bh, bw):
+    """fp64 values of packed row-major E2M1 codes with E8M0 scales over bh x bw
+    blocks (measurement helper: quantization error of the GPU quantizers)."""
+    import torch
+    lut = torch.tensor(_E2M1, dtype=torch.float64, device=codes.device)
+    c = codes.to(torch.int64)
+    vals = torch.stack([lut[c & 15], lut[c >> 4]], dim=-1).reshape(codes.shape[0], -1)
+    sc = torch.exp2(scales.to(torch.float64) - 127.0)
+    return vals * sc.repeat_interleave(bh, 0).repeat_interleave(bw, 1)
+
+
+def time_granularity(lin, reps):
+    """The quantization granularities of the paper's Table 5 on the benchmark
+    linear: relative quantization MSE of X, R, G and of the backward's operand
+    for R^T, and the time of each 4-bit step.  16x16: the method (Q(R)^T read in
+    place).  1 x g groups (g = 16, 32): forward GEMM, backward GEMM + adapter
+    gradients, and the re-quantization Q_g(deq(Q_g(R))^T) the transposed product
+    needs (a pass over R per step, or a second stored copy of the weight)."""
+    import torch
+    from bit_quantized_lora_amd import ops
+    if lin.path == "op":
+        return None
+    M, N, K = lin.M, lin.N, lin.K
+    s = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        e1.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+
+    def rel_mse(ref, deq):
+        ref = ref.to(torch.float64)
+        return float(((ref - deq) ** 2).sum() / (ref ** 2).sum())
+
+    X, R, G = lin.X, lin.R, lin.G
+    out = {}
+    xq, _, xs = ops.quant_block16(X)
+    gq, _, gs = ops.quant_block16(G)
+    out["16x16"] = {
+        "mse_X": rel_mse(X, _deq(xq, xs, 16, 16)), "mse_R": rel_mse(R, _deq(lin.rq, lin.rs_, 16, 16)),
+        "mse_G": rel_mse(G, _deq(gq, gs, 16, 16)),
+        "mse_Rt_operand": rel_mse(R.t(), _deq(lin.rqc, lin.rsct, 16, 16)),
+        "fwd_gemm_us": timed(lin.gemm_fwd), "bwd_us": timed(lin.gemm_bwd_and_grads), "requant_Rt_us": 0.0}
+    dX, dAt, dB = torch.empty_like(lin.dX), torch.empty_like(lin.dAt), torch.empty_like(lin.dB)
+    Y = torch.empty_like(lin.Y)
+    for g in (16, 32):
+        xq, xs = ops.quant_group(X, g)
+        rq, rsc = ops.quant_group(R, g)
+        gq, gs = ops.quant_group(G, g)
+        rtq, rts = ops.requant_group_t(rq, rsc, N, K, g)
+        direct_q, direct_s = ops.quant_group(R.t().contiguous(), g)
+        rec = {"mse_X": rel_mse(X, _deq(xq, xs, 1, g)), "mse_R": rel_mse(R, _deq(rq, rsc, 1, g)),
+               "mse_G": rel_mse(G, _deq(gq, gs, 1, g)),
+               "mse_Rt_operand": rel_mse(R.t(), _deq(rtq, rts, 1, g)),
+               "mse_Rt_if_quantized_from_R": rel_mse(R.t(), _deq(direct_q, direct_s, 1, g))}
+        rec["fwd_gemm_us"] = timed(lambda: ops.linear_fwd_grp(g, xq, xs, rq, rsc, lin.T, lin.L2, lin.B, M, N, K,
+                                                              out=Y))
+        rec["bwd_us"] = timed(lambda: ops.linear_bwd_grp(g, gq, gs, rtq, rts, lin.V, lin.L1t, lin.At, lin.X, lin.G,
+                                                         lin.T, M, N, K, workspace=lin.ws, dX=dX, dAt=dAt, dB=dB))
+        rec["requant_Rt_us"] = timed(lambda: ops.requant_group_t(rq, rsc, N, K, g, out=(rtq, rts)))
+        rec["quant_X_us"] = timed(lambda: ops.quant_group(X, g, out=(xq, xs)))
+        out[f"1x{g}"] = rec
+        del direct_q, direct_s
+    for v in out.values():
+        for k in list(v):
+            if k.startswith("mse"):
+                v[k] = float(f"{v[k]:.4e}")
+    return out
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_fwd_mlp_up.traffic.txt")
 GEMM_SRCS = [os.path.join(ROOT, "bit_quantized_lora_amd", "csrc", f) for f in ("gemm_w4a4.hip", "gemm_tile.h")]
 
@@ -430,6 +510,7 @@ def main():
 
     mlp_fusion = time_mlp_fc1_fusion(lin, args.steps)
     precision = time_precision_variants(lin, args.steps)
+    granularity = time_granularity(lin, args.steps)
     quant = time_quantizer(args.quant_reps)
     if args.calibration_copy:
         calibration_copy()
@@ -469,6 +550,7 @@ def main():
                       for k, v in quant.items()},
         "mlp_fc1_fusion_us": mlp_fusion,
         "precision_variants": precision,
+        "granularity": granularity,
         "quant_GBps": round(quant["dY"]["GBps"], 1),
         "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),
     }
