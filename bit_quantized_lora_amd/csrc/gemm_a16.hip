@@ -73,10 +73,9 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
-// E8M0 byte -> the float 2^(byte - 127) (byte 0: the subnormal 2^-127); the
-// byte 0x100 stands for a scale of zero (masked elements past the end of K)
+// E8M0 byte -> the float 2^(byte - 127) (byte 0: the subnormal 2^-127)
 __device__ __forceinline__ float e8m0_value(uint32_t b) {
-  return __builtin_bit_cast(float, b == 0x100u ? 0u : (b ? b << 23 : 0x00400000u));
+  return __builtin_bit_cast(float, b ? b << 23 : 0x00400000u);
 }
 
 // 8 E2M1 codes (one dword, element e in nibble e) times scale -> 8 bf16
@@ -269,11 +268,11 @@ gemm_a16_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     for (int kt = 0; kt < nkt; ++kt) {
       const uint8_t* st = smem + __builtin_amdgcn_readfirstlane((kt % H_NS) * H_STAGE);
       read_a(p1, st, 1, wm, l32, lh);
-      if (k_tail && kt == nkt - 1 && lh) {   // elements 16 .. 31 of the last stage are past K
-#pragma unroll
+      if (k_tail && kt == nkt - 1 && lh) {   // elements 16 .. 31 of the last stage are past K:
+#pragma unroll                                // zero codes and zero A (both, so no 0 * inf)
         for (int i = 0; i < H_TMI; ++i) c0.a[i] = p1.a[i] = v4i{0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < H_TNI; ++j) bf.sb[j] = 0x100u;
+        for (int j = 0; j < H_TNI; ++j) bf.codes[j] = v2i{0, 0};
       }
       dequant_b<0>(b0, bf);
       dequant_b<1>(b1, bf);
