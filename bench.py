@@ -543,6 +543,10 @@ def main():
                      "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                      "per_launch_flops": gemm_flops, "avg_launch_us": round(gemm_b2b_ms * 1e3, 2),
+                     # the codes path feeds one 16-K block per 32-K MFMA fragment, so its
+                     # instruction ceiling is half the FP4 peak
+                     "frac_of_half_fragment_ceiling": (round(achieved / (FP4_PEAK_TFLOPS / 2), 4)
+                                                       if args.path != "op" else None),
                      "avg_launch_us_in_step": round(gemm_ms * 1e3, 2)},
         "phases_us": {k: round(v, 2) for k, v in phases.items()},
         "host_enqueue_us_per_step": round(host_us, 1),
