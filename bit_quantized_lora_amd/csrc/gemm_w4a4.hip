@@ -933,6 +933,7 @@ ft_status launch_gemm_w4a4_gelu_quant(const GemmArgs& g, hipStream_t s) {
 ft_status launch_gemm_w4a4_groups(const GemmArgs& g, int gs, bool out_bf16, bool trans_b, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return FT_OK;
   if (gs != 16 && gs != 32) return FT_EINVAL;
+  if (g.K == 0) return launch_gemm_w4a4(g, out_bf16, trans_b, s);   // no scales read: the low-rank term only
   const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;

@@ -160,7 +160,7 @@ extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
   if (M && K && !dX) return FT_EINVAL;
   if (M && N && K && (!gq_codes || !gq_scales || !rq_codes_cm || !rq_scales_cm)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
-  if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
+  if ((rs && K && !L1t) || (r && ((K && (!At || !dAt)) || (N && !dB)))) return FT_EINVAL;
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   const void* ptrs[] = {gq_codes, rq_codes_cm, V, L1t, At, X, G, T, dX, dAt, dB, workspace};
@@ -243,7 +243,7 @@ extern "C" ft_status ft_linear_bwd_op(int64_t M, int64_t N, int64_t K, const uin
   if (M && K && !dX) return FT_EINVAL;
   if (M && N && K && (!g_op || !g_op_scales || !rt_op || !rt_op_scales)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
-  if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
+  if ((rs && K && !L1t) || (r && ((K && (!At || !dAt)) || (N && !dB)))) return FT_EINVAL;
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   const void* ptrs[] = {g_op, g_op_scales, rt_op, rt_op_scales, V, L1t, At, X, G, T, dX, dAt, dB, workspace};
@@ -312,7 +312,7 @@ extern "C" ft_status ft_linear_bwd_g16(int64_t M, int64_t N, int64_t K, const vo
   if (M && K && !dX) return FT_EINVAL;
   if (M && N && K && (!G || !rq_codes_cm || !rq_scales_cm)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
-  if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
+  if ((rs && K && !L1t) || (r && ((K && (!At || !dAt)) || (N && !dB)))) return FT_EINVAL;
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   const void* ptrs[] = {G, rq_codes_cm, rq_scales_cm, V, L1t, At, X, T, dX, dAt, dB, workspace};
@@ -350,7 +350,7 @@ extern "C" ft_status ft_linear_fwd_grp(int64_t M, int64_t N, int64_t K, int32_t 
   if (M == 0 || N == 0) return FT_OK;
   if (K % 128 != 0) return FT_ENOTSUP;
   const int rho = rs + r;
-  if (!Y || !xq_codes || !xq_scales || !rq_codes || !rq_scales || (rho && !T) || (rs && !L2) || (r && !B))
+  if (!Y || (K && (!xq_codes || !xq_scales || !rq_codes || !rq_scales)) || (rho && !T) || (rs && !L2) || (r && !B))
     return FT_EINVAL;
   const void* ptrs[] = {Y, xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B};
   for (const void* p : ptrs)
@@ -385,7 +385,7 @@ extern "C" ft_status ft_linear_bwd_grp(int64_t M, int64_t N, int64_t K, int32_t 
   if (M && K && !dX) return FT_EINVAL;
   if (M && N && K && (!gq_codes || !gq_scales || !rtq_codes || !rtq_scales)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
-  if ((rs && !L1t) || (r && (!At || !dAt || !dB))) return FT_EINVAL;
+  if ((rs && K && !L1t) || (r && ((K && (!At || !dAt)) || (N && !dB)))) return FT_EINVAL;
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   const void* ptrs[] = {gq_codes, gq_scales, rtq_codes, rtq_scales, V, L1t, At, X, G, T, dX, dAt, dB, workspace};
