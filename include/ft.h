@@ -35,9 +35,11 @@
  *  - Pointers must be 16-byte aligned; leading dimensions must keep every
  *    row 16-byte aligned (FT_EALIGN otherwise).
  *  - Every matrix dimension must be a multiple of 16 (the quantization block;
- *    FT_ESHAPE otherwise).  Zero-sized dimensions are accepted and enqueue
- *    nothing.  Ranks: rs (stabilizer) and r (LoRA) are multiples of 16 with
- *    0 <= rs + r <= 128.
+ *    FT_ESHAPE otherwise).  Zero-sized dimensions are accepted: an empty output
+ *    enqueues nothing, an empty reduction leaves the low-rank terms (K = 0
+ *    forward, N = 0 backward), and zero tokens (M = 0) give zero adapter
+ *    gradients.  Pointers to empty operands may be NULL.  Ranks: rs
+ *    (stabilizer) and r (LoRA) are multiples of 16 with 0 <= rs + r <= 128.
  */
 #ifndef FT_H_
 #define FT_H_
