@@ -28,6 +28,8 @@ _SIGS = {
     "ft_lowrank_workspace": [c_int64, c_int64, c_int32],
     "ft_quant_lowrank": [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "ft_gelu_quant_lowrank": [c_void_p, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_linear_fwd": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p],
     "ft_linear_fwd_gelu": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,

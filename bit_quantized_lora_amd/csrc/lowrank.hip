@@ -24,6 +24,13 @@
 // block s; a block is spread over the 16 lanes of one DPP row and the matching
 // 16 lanes of the other wave half, so its maximum is a 16-lane DPP reduction and
 // one permlane32 swap across the halves.
+//
+// ft_gelu_quant_lowrank puts the activation between an MLP's two linears in
+// front of that pass (FourTune section 3.3 "MLP Fusion": the intermediate is
+// not read back by a separate kernel): the first linear's output Y is read,
+// h = GELU(Y) is written out (the second linear's adapter gradient needs it)
+// and quantized and projected from the same registers, so the 4608 x 12288
+// intermediate crosses HBM once in each direction instead of three times.
 #include "ft_device.h"
 
 namespace ft {
@@ -85,12 +92,14 @@ int64_t num_splits(int64_t M, int64_t Kin) {
   return (nchunks + cps - 1) / cps;
 }
 
-template <int NCT, bool QUANT>  // NCT: 32-wide rank column tiles (0..4); QUANT: also write Q(in)
+// NCT: 32-wide rank column tiles (0..4); QUANT: also write Q(in); GELU: the
+// input is replaced by GELU(in) (written to hout [M x Kin]) before both
+template <int NCT, bool QUANT, bool GELU = false>
 __global__ void __launch_bounds__(LR_THREADS)
 lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t ld_in,
                const uint16_t* __restrict__ wa, int ra, const uint16_t* __restrict__ wb, int rb,
                int64_t cps, float* __restrict__ out, int64_t out_split_stride,
-               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ hout) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t s_w[];   // 2 buffers of rho rows
   const int wbuf_bytes = (ra + rb) * LR_WROW;
   const int lane = threadIdx.x & 63;
@@ -217,6 +226,23 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
     }
   };
 
+  // h = GELU(y) in place (fp32 math on the bf16 value, round to nearest even, as
+  // ft_gelu_fwd), stored right away so the write overlaps the quantizer's and
+  // the MFMAs' work
+  auto gelu_chunk = [&](v4i (&x)[8], int64_t c) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint32_t w[4] = {(uint32_t)x[s].x, (uint32_t)x[s].y, (uint32_t)x[s].z, (uint32_t)x[s].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = f32_to_bf16_rne(gelu_f(bf16lo_to_f32(w[k]))) | (f32_to_bf16_rne(gelu_f(bf16hi_to_f32(w[k]))) << 16);
+      x[s] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+      const int64_t k0 = c * LR_CHUNK + 16 * s;
+      if (arow_ok && k0 < Kin) *reinterpret_cast<v4i*>(hout + arow * Kin + k0 + 8 * lh) = x[s];
+    }
+  };
+
   v16f acc[NCT > 0 ? NCT : 1];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct] = v16f{};
@@ -235,6 +261,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       issue_w(buf ^ 1, c + 1);
       load_x(xn, c + 1);
     }
+    if constexpr (GELU) gelu_chunk(xc, c);
     if constexpr (QUANT) quantize_chunk(xc, c);
     const uint8_t* wbuf = s_w + buf * wbuf_bytes;
 #pragma unroll
@@ -293,7 +320,7 @@ namespace ft {
 namespace {
 ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, const void* wa, int32_t ra,
                        const void* wb, int32_t rb, float* out, uint8_t* codes, uint8_t* scales, void* workspace,
-                       size_t ws_bytes, hipStream_t stream) {
+                       size_t ws_bytes, hipStream_t stream, void* hout = nullptr) {
   if (!mult16(M) || !mult16(Kin) || ld_in < Kin) return FT_ESHAPE;
   if (ra < 0 || rb < 0 || (ra % 16) || (rb % 16) || ra + rb > 128) return FT_ESHAPE;
   const int rho = ra + rb;
@@ -303,6 +330,7 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   if ((Kin && !aligned16(in)) || (ld_in % 8) || (ra && !aligned16(wa)) || (rb && !aligned16(wb)) ||
       (rho && !aligned16(out)) || (quant && (!aligned16(codes) || !aligned16(scales))))
     return FT_EALIGN;
+  if (hout && !aligned16(hout)) return FT_EALIGN;
   if (Kin == 0) return rho ? fill_zero_f32(out, M * rho, stream) : FT_OK;  // empty reduction
   if ((int64_t)rho * Kin * 2 >= ((int64_t)1 << 31)) return FT_ESHAPE;
   const size_t need = rho ? ft_lowrank_workspace(M, Kin, rho) : 0;
@@ -317,10 +345,22 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   const uint16_t* b = static_cast<const uint16_t*>(wb);
   const int64_t stride = M * rho;
   const int nct = (rho + 31) / 32;
+  uint16_t* hp = static_cast<uint16_t*>(hout);
 #define FT_LR_LAUNCH(N, Q)                                                                                   \
   hipLaunchKernelGGL((lowrank_kernel<N, Q>), grid, dim3(LR_THREADS), (size_t)(2 * rho * LR_WROW), stream, ip, M, Kin, ld_in, a, ra, b, rb, \
-                     cps, dst, stride, codes, scales)
-  if (quant) {
+                     cps, dst, stride, codes, scales, hp)
+#define FT_LRG_LAUNCH(N)                                                                                     \
+  hipLaunchKernelGGL((lowrank_kernel<N, true, true>), grid, dim3(LR_THREADS), (size_t)(2 * rho * LR_WROW), stream, ip, M, Kin, ld_in, a, ra, \
+                     b, rb, cps, dst, stride, codes, scales, hp)
+  if (hout) {
+    switch (nct) {
+      case 0: FT_LRG_LAUNCH(0); break;
+      case 1: FT_LRG_LAUNCH(1); break;
+      case 2: FT_LRG_LAUNCH(2); break;
+      case 3: FT_LRG_LAUNCH(3); break;
+      default: FT_LRG_LAUNCH(4); break;
+    }
+  } else if (quant) {
     switch (nct) {
       case 0: FT_LR_LAUNCH(0, true); break;
       case 1: FT_LR_LAUNCH(1, true); break;
@@ -337,6 +377,7 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
     }
   }
 #undef FT_LR_LAUNCH
+#undef FT_LRG_LAUNCH
   if (launch_status() != FT_OK) return FT_EHIP;
   if (S > 1 && rho) {
     hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((stride + 255) / 256)), dim3(256), 0, stream,
@@ -360,4 +401,13 @@ extern "C" ft_status ft_quant_lowrank(const void* in, int64_t M, int64_t Kin, in
                                       hipStream_t stream) {
   if (!codes_rm) return FT_EINVAL;
   return ft::lowrank_impl(in, M, Kin, ld_in, wa, ra, wb, rb, out, codes_rm, scales, workspace, ws_bytes, stream);
+}
+
+extern "C" ft_status ft_gelu_quant_lowrank(const void* y, int64_t M, int64_t Kin, const void* wa, int32_t ra,
+                                           const void* wb, int32_t rb, void* h, float* out, uint8_t* codes_rm,
+                                           uint8_t* scales, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!codes_rm || !scales || (M && Kin && !h)) return FT_EINVAL;
+  if (Kin == 0 || M == 0) return ft::lowrank_impl(y, M, Kin, Kin, wa, ra, wb, rb, out, codes_rm, scales, workspace,
+                                                  ws_bytes, stream);
+  return ft::lowrank_impl(y, M, Kin, Kin, wa, ra, wb, rb, out, codes_rm, scales, workspace, ws_bytes, stream, h);
 }

@@ -157,6 +157,29 @@ def quant_lowrank(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, out: Op
     return out, codes, scales
 
 
+def gelu_quant_lowrank(y: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, out=None, workspace=None):
+    """h = GELU(y), Q(h) and [h wa^T | h wb^T] from one read of y:
+    returns (h, T, codes, scales)."""
+    _need(y, torch.bfloat16, "y")
+    M, Kin = y.shape
+    ra, rb = wa.shape[0], wb.shape[0]
+    dev = y.device
+    if out is None:
+        out = (torch.empty((M, Kin), dtype=torch.bfloat16, device=dev),
+               torch.empty((M, ra + rb), dtype=torch.float32, device=dev),
+               torch.empty((M, Kin // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M // 16, Kin // 16), dtype=torch.uint8, device=dev))
+    h, T, codes, scales = out
+    nb = lowrank_workspace(M, Kin, ra + rb)
+    if workspace is None or workspace.numel() < nb:
+        workspace = torch.empty((max(nb, 16),), dtype=torch.uint8, device=dev)
+    st = lib().ft_gelu_quant_lowrank(y.data_ptr(), M, Kin, wa.data_ptr(), ra, wb.data_ptr(), rb, h.data_ptr(),
+                                     T.data_ptr(), codes.data_ptr(), scales.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel(), _stream(y))
+    check("ft_gelu_quant_lowrank", st)
+    return h, T, codes, scales
+
+
 def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
                out_dtype=torch.float32, mode: str = "pow2", out: Optional[torch.Tensor] = None):
     """Y = deq(Xq) deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B."""

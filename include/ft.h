@@ -163,6 +163,24 @@ ft_status ft_quant_lowrank(const void* in, int64_t M, int64_t Kin, int64_t ld_in
                            uint8_t* codes_rm, uint8_t* scales, void* workspace, size_t ws_bytes,
                            hipStream_t stream);
 
+/* ft_gelu_quant_lowrank -- the MLP fusion of section 3.3 ("MLP Fusion": the
+ * activation and the second linear's input quantization go with a pass the
+ * intermediate already makes, so it is not read back by separate kernels),
+ * placed in the second linear's quantize + down-projection pass: from one read
+ * of the first linear's output y,
+ *
+ *   h      = GELU(y)                        (bf16, as ft_gelu_fwd)
+ *   Q(h)   codes_rm + scales                (as ft_quant_block16, FT_SCALE_POW2)
+ *   out    = [h wa^T | h wb^T]              (as ft_lowrank_fused; the second
+ *                                            linear's T with wa = L1t, wb = At)
+ *
+ *  y, h  bf16 [M x Kin], contiguous rows (leading dimension Kin)
+ *  Other arguments and the workspace as ft_quant_lowrank.  All three outputs
+ *  equal, bit for bit, ft_gelu_fwd followed by ft_quant_lowrank on h. */
+ft_status ft_gelu_quant_lowrank(const void* y, int64_t M, int64_t Kin, const void* wa, int32_t ra,
+                                const void* wb, int32_t rb, void* h, float* out, uint8_t* codes_rm,
+                                uint8_t* scales, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ft_linear_fwd -- Eq. 2 with the LoRA-fusion epilogue (section 3.3: the
  * backbone GEMM and the up-projections are accumulated in one kernel):
  *

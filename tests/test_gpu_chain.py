@@ -255,3 +255,77 @@ def test_mlp_pair_chain_fused_fc1_full_size():
     _check("fused dX_up", dX1, gu["dX"])
     _check("fused dA_up", dA1, gu["dA"])
     _check("fused dB_up", dB1, gu["dB"])
+
+
+@pytest.mark.parametrize("case", [
+    (4608, 12288, 32, 16),     # the MLP intermediate at full size, down-layer ranks
+    (48, 400, 16, 16),         # a ragged last chunk of the reduction
+    (272, 1040, 64, 64),       # two rank tiles, several splits
+    (16, 16, 0, 16),
+    (256, 384, 0, 0),          # no projection: GELU and Q(h) only
+], ids=lambda c: "x".join(map(str, c)))
+def test_gelu_quant_lowrank_matches_separate_kernels(case):
+    """The MLP fusion in the second linear's input pass: h, Q(h) and the
+    down-projection equal ft_gelu_fwd -> ft_quant_lowrank bit for bit."""
+    require_gpu()
+    import torch
+    from bit_quantized_lora_amd import ops
+    M, K, ra, rb = case
+    rng = np.random.default_rng(M + K + ra)
+    y = synth.f32_to_bf16_bits((rng.standard_t(3, (M, K)) * 2).astype(np.float32))
+    wa = synth.f32_to_bf16_bits(synth.make_tensor(rng, (ra, K), "normal", 0.02))
+    wb = synth.f32_to_bf16_bits(synth.make_tensor(rng, (rb, K), "normal", 0.01))
+    Y, Wa, Wb = dev_bf16(y), dev_bf16(wa), dev_bf16(wb)
+    say(f"[mlp-fusion pass] M={M} K={K} ra={ra} rb={rb}")
+    h, T, hc, hs = ops.gelu_quant_lowrank(Y, Wa, Wb)
+    Hs = ops.gelu_fwd(Y)
+    Ts, hcs, hss = ops.quant_lowrank(Hs, Wa, Wb)
+    torch.cuda.synchronize()
+    pairs = [("h", h.view(torch.int16), Hs.view(torch.int16)), ("codes", hc, hcs), ("scales", hs, hss)]
+    if ra + rb:
+        pairs.append(("T", T.view(torch.int32), Ts.view(torch.int32)))
+    for name, a, b in pairs:
+        diff = int(np.count_nonzero(host(a) != host(b)))
+        assert diff == 0, f"{name}: {diff} differing elements"
+
+
+def test_mlp_pair_chain_fused_pass_full_size():
+    """The MLP pair with GELU, Q(h) and the down layer's T from one pass over
+    Y_up (ft_gelu_quant_lowrank); every result against the oracle's chain."""
+    require_gpu()
+    import torch
+    from bit_quantized_lora_amd import ops
+    c = _config("c3")
+    up, down = c["c3-up"], c["c3-down"]
+    say("[chain] mlp-pair fused GELU + quantize + project pass")
+    Lu, Ld = GpuLayer(up), GpuLayer(down)
+    X, G2 = dev_bf16(up["X"]), dev_bf16(down["G"])
+    xq, _, xs = ops.quant_block16(X, rm=True, cm=False)
+    Y1, T1 = Lu.fwd_codes_given_q(X, xq, xs, torch.bfloat16)
+    h, T2, hc, hs = ops.gelu_quant_lowrank(Y1, Ld.L1t, Ld.At)
+    M = h.shape[0]
+    Y2 = ops.linear_fwd(hc, hs, Ld.rq, Ld.rs, T2, Ld.L2, Ld.B, M, Ld.N, Ld.K)
+    dh, dA2, dB2 = Ld.bwd(G2, h, T2, torch.bfloat16)
+    dY1 = ops.gelu_bwd(Y1, dh)
+    dX1, dA1, dB1 = Lu.bwd(dY1, X, T1, torch.float32)
+    torch.cuda.synchronize()
+
+    Lou, Lod = OracleLayer(up), OracleLayer(down)
+    y1 = O.f64_to_bf16_bits(Lou.fwd(up["X"]))
+    hb = O.f64_to_bf16_bits(O.gelu(O.bf16_to_f64(y1)))
+    y2 = Lod.fwd(hb)
+    gd = Lod.bwd(down["G"], hb)
+    dhb = O.f64_to_bf16_bits(gd["dX"])
+    dy1 = O.f64_to_bf16_bits(O.gelu_grad(O.bf16_to_f64(y1)) * O.bf16_to_f64(dhb))
+    gu = Lou.bwd(dy1, up["X"])
+
+    _check("pass Y_up (bf16)", Y1, y1, bf16=True)
+    _check("pass h = GELU(Y_up) (bf16)", h, hb, bf16=True)
+    _check("pass Y_down", Y2, y2)
+    _check("pass dX_down = dh (bf16)", dh, dhb, bf16=True)
+    _check("pass dA_down", dA2, gd["dA"])
+    _check("pass dB_down", dB2, gd["dB"])
+    _check("pass dY_up (bf16)", dY1, dy1, bf16=True)
+    _check("pass dX_up", dX1, gu["dX"])
+    _check("pass dA_up", dA1, gu["dA"])
+    _check("pass dB_up", dB1, gu["dB"])
