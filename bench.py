@@ -388,10 +388,27 @@ def time_granularity(lin, reps):
         rec["quant_X_us"] = timed(lambda: ops.quant_group(X, g, out=(xq, xs)))
         out[f"1x{g}"] = rec
         del direct_q, direct_s
+    flops = 2.0 * M * N * K
     for v in out.values():
         for k in list(v):
             if k.startswith("mse"):
                 v[k] = float(f"{v[k]:.4e}")
+        v["fwd_gemm_TFLOPs"] = round(flops / v["fwd_gemm_us"] / 1e6, 1)
+        v["fwd_gemm_frac_fp4_peak"] = round(flops / v["fwd_gemm_us"] / 1e6 / FP4_PEAK_TFLOPS, 4)
+    return out
+
+
+def lowrank_pass_rates(spec, phases):
+    """HBM roofline of the one-pass quantize + down-projection (in the step's
+    phase times, split sum included): algorithmic bytes = bf16 input read, E2M1
+    codes and E8M0 scales written, the fp32 projection written."""
+    M, K, N, rho = spec.M, spec.K, spec.N, spec.rs + spec.r
+    out = {}
+    for name, kin, key in (("X", K, "quant_lowrank_X"), ("G", N, "quant_lowrank_G")):
+        alg = 2 * M * kin + M * kin // 2 + M * kin // 256 + 4 * M * rho
+        us = phases[key]
+        out[name] = {"us": round(us, 2), "alg_MB": round(alg / 1e6, 1), "GBps": round(alg / us / 1e3, 1),
+                     "frac_hbm": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4)}
     return out
 
 
@@ -562,6 +579,7 @@ def main():
         "mlp_fc1_fusion_us": mlp_fusion,
         "precision_variants": precision,
         "granularity": granularity,
+        "quant_lowrank_pass": lowrank_pass_rates(spec, phases),
         "quant_GBps": round(quant["dY"]["GBps"], 1),
         "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),
     }
