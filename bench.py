@@ -517,6 +517,9 @@ def main():
     host_us = (time.perf_counter() - host_t0) / args.steps * 1e6
     torch.cuda.synchronize()
     phases = {n: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks])) * 1e3 for i, n in enumerate(names)}
+    step_us = np.array([m[0].elapsed_time(m[-1]) * 1e3 for m in marks])
+    step_pct = {"p10": round(float(np.percentile(step_us, 10)), 2), "p50": round(float(np.percentile(step_us, 50)), 2),
+                "p90": round(float(np.percentile(step_us, 90)), 2)}
 
     # forward GEMM alone, launched back to back (no event between launches, so
     # no cache write-back at an event marker is charged to the kernel): the
@@ -573,6 +576,7 @@ def main():
                                                        if args.path != "op" else None),
                      "avg_launch_us_in_step": round(gemm_ms * 1e3, 2)},
         "phases_us": {k: round(v, 2) for k, v in phases.items()},
+        "step_us_percentiles": step_pct,
         "host_enqueue_us_per_step": round(host_us, 1),
         "quantizer": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in quant.items()},
