@@ -162,12 +162,17 @@ lora_grad_kernel(const uint16_t* __restrict__ Phi, const uint16_t* __restrict__ 
     }
 }
 
+// out = sum over the splits of part[s], added in split order from 0.0f
+// (deterministic).  Each thread adds 4 consecutive values (n is a multiple of 4:
+// the rank and the column count are multiples of 16) with 16-byte loads, the
+// split loop unrolled so that its loads are in flight together.
 __global__ void sum_splits_kernel(const float* __restrict__ part, int splits, int64_t n, float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
-  float v = 0.0f;
-  for (int s = 0; s < splits; ++s) v += part[(int64_t)s * n + i];
-  out[i] = v;
+  v4f v = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+  for (int s = 0; s < splits; ++s) v += *reinterpret_cast<const v4f*>(part + (int64_t)s * n + i);
+  *reinterpret_cast<v4f*>(out + i) = v;
 }
 
 }  // namespace
@@ -183,6 +188,7 @@ size_t lora_grad_workspace(int64_t M, int64_t ncols, int r) {
 ft_status launch_lora_grad(const float* P, int64_t ldp, int poff, int r, const uint16_t* Q,
                            int64_t M, int64_t ncols, float* dW, void* ws, hipStream_t s) {
   if (r == 0 || ncols == 0) return FT_OK;
+  if (r % 16 || ncols % 16 || !aligned16(dW)) return FT_ESHAPE;   // the split sum's 16-byte accesses
   if (M == 0) return fill_zero_f32(dW, (int64_t)r * ncols, s);
   const int S = choose_splits(M, ncols);
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -207,7 +213,7 @@ ft_status launch_lora_grad(const float* P, int64_t ldp, int poff, int r, const u
   }
   if (launch_status() != FT_OK) return FT_EHIP;
   if (S > 1) {
-    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((stride + 255) / 256)), dim3(256), 0, s, part, S_used, stride, dW);
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((stride / 4 + 255) / 256)), dim3(256), 0, s, part, S_used, stride, dW);
     return launch_status();
   }
   return FT_OK;
