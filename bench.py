@@ -398,6 +398,28 @@ def time_granularity(lin, reps):
     return out
 
 
+def time_separate_passes(spec, d, steps, warmup, one_pass_us):
+    """The same linear step with the quantizer and the shared down-projection as
+    separate kernels (path "codes"), against the one-pass default: the layer-level
+    effect of folding Q(in) into the low-rank pass."""
+    import torch
+    lin = Linear(spec, d, "codes")
+    for _ in range(warmup):
+        lin.step()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        lin.step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del lin
+    return {"step_us_one_pass": round(one_pass_us, 2), "step_us_separate_passes": round(us, 2),
+            "speedup": round(us / one_pass_us, 3)}
+
+
 def lowrank_pass_rates(spec, phases):
     """HBM roofline of the one-pass quantize + down-projection (in the step's
     phase times, split sum included): algorithmic bytes = bf16 input read, E2M1
@@ -535,6 +557,7 @@ def main():
     torch.cuda.synchronize()
     gemm_b2b_ms = g0.elapsed_time(g1) / args.steps
 
+    separate = time_separate_passes(spec, d, args.steps, args.warmup, ms_step * 1e3) if args.path == "fused" else None
     mlp_fusion = time_mlp_fc1_fusion(lin, args.steps)
     precision = time_precision_variants(lin, args.steps)
     granularity = time_granularity(lin, args.steps)
@@ -584,6 +607,7 @@ def main():
         "precision_variants": precision,
         "granularity": granularity,
         "quant_lowrank_pass": lowrank_pass_rates(spec, phases),
+        "one_pass_vs_separate": separate,
         "quant_GBps": round(quant["dY"]["GBps"], 1),
         "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),
     }
