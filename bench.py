@@ -63,6 +63,26 @@ def make_inputs():
     return spec, d
 
 
+N_INPUT_SETS = 3   # X, G sets the timed steps rotate through (inputs of a step: 141 MB each)
+
+
+def extra_inputs(spec, d, n):
+    """n - 1 further (X, G) pairs drawn like the first (same distributions, the
+    same outlier columns of X), so that consecutive steps read different inputs
+    and the three sets (423 MB) exceed the 256 MB MALL, as new batches would."""
+    import synth
+    out = []
+    for i in range(1, n):
+        rng = np.random.default_rng(synth.CONFIG_SEED["c3"] + 1000 + i)
+        X = synth.make_tensor(rng, (spec.M, spec.K), spec.x_dist)
+        cols = d["x_outlier_cols"]
+        if len(cols):
+            X[:, cols] *= np.float32(spec.x_outlier_mult)
+        G = synth.make_tensor(rng, (spec.M, spec.N), "normal", spec.g_std)
+        out.append((synth.f32_to_bf16_bits(X), synth.f32_to_bf16_bits(G)))
+    return out
+
+
 class Linear:
     """Device buffers and the step of one triple-branch linear (all preallocated).
 
@@ -71,7 +91,7 @@ class Linear:
     low-rank passes.  path "op": the quantizer writes the pair-merged operands
     and the GEMMs read them (a full 32-K fragment per MFMA)."""
 
-    def __init__(self, spec, d, path="op"):
+    def __init__(self, spec, d, path="op", more_inputs=()):
         import torch
         from bit_quantized_lora_amd import ops
         self.ops, self.path = ops, path
@@ -80,6 +100,8 @@ class Linear:
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device="cuda")
         self.X, self.G = dev_bf16(d["X"]), dev_bf16(d["G"])
+        self.inputs = [(self.X, self.G)] + [(dev_bf16(x), dev_bf16(g)) for x, g in more_inputs]
+        self.k = 0
         self.L1t = dev_bf16(np.ascontiguousarray(d["L1"].T))
         self.At = dev_bf16(np.ascontiguousarray(d["A"].T))
         self.L2, self.B = dev_bf16(d["L2"]), dev_bf16(d["B"])
@@ -162,7 +184,13 @@ class Linear:
         self.quant_lowrank_g()
         self.gemm_bwd_and_grads()
 
+    def next_inputs(self):
+        """The next (X, G) set (host-side reference swap, no device work)."""
+        self.k = (self.k + 1) % len(self.inputs)
+        self.X, self.G = self.inputs[self.k]
+
     def step(self):
+        self.next_inputs()
         self.forward()
         self.backward()
 
@@ -398,12 +426,12 @@ def time_granularity(lin, reps):
     return out
 
 
-def time_separate_passes(spec, d, steps, warmup, one_pass_us):
+def time_separate_passes(spec, d, more, steps, warmup, one_pass_us):
     """The same linear step with the quantizer and the shared down-projection as
     separate kernels (path "codes"), against the one-pass default: the layer-level
     effect of folding Q(in) into the low-rank pass."""
     import torch
-    lin = Linear(spec, d, "codes")
+    lin = Linear(spec, d, "codes", more)
     for _ in range(warmup):
         lin.step()
     s = torch.cuda.current_stream()
@@ -501,7 +529,8 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     spec, d = make_inputs()
-    lin = Linear(spec, d, args.path)
+    more = extra_inputs(spec, d, N_INPUT_SETS)
+    lin = Linear(spec, d, args.path, more)
     M, K, N = spec.M, spec.K, spec.N
     s = torch.cuda.current_stream()
 
@@ -515,6 +544,7 @@ def main():
     torch.cuda.synchronize()
     t_start.record(s)
     for i in range(args.steps):
+        lin.next_inputs()
         lin.quant_lowrank_x()
         ev[i][0].record(s)
         lin.gemm_fwd()
@@ -532,6 +562,7 @@ def main():
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
     host_t0 = time.perf_counter()
     for k in range(args.steps):
+        lin.next_inputs()
         marks[k][0].record(s)
         for i, f in enumerate(fns):
             f()
@@ -557,7 +588,8 @@ def main():
     torch.cuda.synchronize()
     gemm_b2b_ms = g0.elapsed_time(g1) / args.steps
 
-    separate = time_separate_passes(spec, d, args.steps, args.warmup, ms_step * 1e3) if args.path == "fused" else None
+    separate = (time_separate_passes(spec, d, more, args.steps, args.warmup, ms_step * 1e3)
+                if args.path == "fused" else None)
     mlp_fusion = time_mlp_fc1_fusion(lin, args.steps)
     precision = time_precision_variants(lin, args.steps)
     granularity = time_granularity(lin, args.steps)
@@ -586,7 +618,8 @@ def main():
                    "gemm_operands": ("pair-merged FP6 E3M2 (two 16-K blocks per 32-K MFMA fragment)"
                                      if args.path == "op" else "E2M1 codes (one 16-K block per 32-K fragment)"),
                    "quantizer_and_lowrank": "one pass" if args.path == "fused" else "separate passes",
-                   "outputs": "bf16 Y and dX, fp32 dA and dB"},
+                   "outputs": "bf16 Y and dX, fp32 dA and dB",
+                   "input_sets": f"{N_INPUT_SETS} rotating (X, G) pairs, one per step"},
         "pct_fp4_peak_whole_linear": round(100.0 * value / FP4_PEAK_TFLOPS, 2),
         "roofline": {"kernel": ("gemm_m6_kernel" if args.path == "op" else "gemm_w4a4_kernel") + " (forward)",
                      "bound": "mfma",
