@@ -13,7 +13,7 @@ Q(R) is prepared once (R is frozen) and is not part of the step.  Inputs are
 resident in HBM before timing starts.  `value` is 4*M*N*K (the fwd + dX 4-bit
 GEMM work; the low-rank FLOPs are not counted) divided by the step time.
 
-Prints one JSON line.  --gpus N with N > 1 is refused: this build runs on one GPU.
+Prints one JSON line.  --gpus N with N > 1 is refused: the library runs the hot path on one GPU.
 """
 from __future__ import annotations
 
@@ -521,7 +521,7 @@ def cpu_baseline(spec, d, rows, reps):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": f"--gpus {args.gpus}: this build runs the hot path on one GPU only; "
+        print(json.dumps({"error": f"--gpus {args.gpus}: the library runs the hot path on one GPU only; "
                                    "multi-GPU runs are not supported"}))
         sys.exit(2)
     import torch

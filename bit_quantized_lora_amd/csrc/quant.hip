@@ -385,7 +385,7 @@ extern "C" const char* ft_status_str(ft_status s) {
     case FT_ESHAPE: return "bad shape (dimension not a multiple of 16, or ranks out of range)";
     case FT_EALIGN: return "misaligned pointer or leading dimension (16-byte alignment required)";
     case FT_EHIP: return "HIP launch failed";
-    case FT_ENOTSUP: return "not supported by this build";
+    case FT_ENOTSUP: return "not supported by this library";
     case FT_ESPACE: return "workspace too small";
   }
   return "unknown status";

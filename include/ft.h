@@ -58,7 +58,7 @@ typedef enum {
   FT_ESHAPE = 2,   /* a dimension not a multiple of 16, negative, or ranks out of range */
   FT_EALIGN = 3,   /* pointer or leading dimension breaks 16-byte alignment */
   FT_EHIP = 4,     /* a HIP launch failed (hipGetLastError after the launch) */
-  FT_ENOTSUP = 5,  /* valid request that this build does not implement */
+  FT_ENOTSUP = 5,  /* valid request that this library does not implement */
   FT_ESPACE = 6    /* workspace smaller than required */
 } ft_status;
 
