@@ -418,17 +418,112 @@ def test_input_gradient_finite_differences_straight_through():
 
 
 # ---------------------------------------------------------------- GELU
+# Phi(x) to 40+ significant digits, computed here from two textbook series in
+# decimal arithmetic (independent of scipy, which the oracle calls):
+#  * Maclaurin series of erf, Phi(x) = 1/2 + erf(x / sqrt 2) / 2, with enough
+#    working digits to survive the cancellation far in the lower tail;
+#  * Laplace's continued fraction for the Mills ratio, Phi(-x) = phi(x) R(x) with
+#    R(x) = 1/(x + 1/(x + 2/(x + 3/(x + ...)))), for x >= 5.
+# The two agree to 35 digits where both apply, which pins each of them.
+def _dec_pi(ctx):
+    from decimal import Decimal
+    def arctan_inv(n):   # arctan(1/n) by its Taylor series
+        x = Decimal(1) / n; x2 = x * x; t = x; s = x; k = 1
+        while True:
+            t *= -x2; k += 2
+            d = t / k
+            if abs(d) < Decimal(10) ** (-ctx.prec - 2):
+                return s
+            s += d
+    return 16 * arctan_inv(5) - 4 * arctan_inv(239)   # Machin
+
+
+def _phi_series(x: float, prec: int = 140):
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = prec
+        pi = _dec_pi(ctx)
+        z = Decimal(repr(x)) / Decimal(2).sqrt()
+        term, s, n = z, z, 0
+        while True:
+            n += 1
+            term *= -z * z / n
+            d = term / (2 * n + 1)
+            s += d
+            if n > 10 and abs(d) < Decimal(10) ** (-prec + 5):
+                break
+        erf = 2 * s / pi.sqrt()
+        return Decimal(1) / 2 + erf / 2
+
+
+def _phi_lower_cf(x: float, depth: int = 4000, prec: int = 60):
+    """Phi(-x) for x > 0 by the Mills-ratio continued fraction."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = prec
+        pi = _dec_pi(ctx)
+        X = Decimal(repr(x))
+        r = X
+        for k in range(depth, 0, -1):
+            r = X + k / r
+        dens = (-(X * X) / 2).exp() / (2 * pi).sqrt()
+        return dens / r
+
+
+def test_normal_cdf_references_agree():
+    from decimal import Decimal
+    for x in (5.0, 6.0, 8.0, 10.0, 12.0):
+        a = _phi_series(-x); b = _phi_lower_cf(x)
+        assert abs(a - b) <= Decimal(10) ** -35 * b, (x, a, b)
+    # textbook anchors: Phi(0) = 1/2, Phi(x) + Phi(-x) = 1
+    assert _phi_series(0.0) == Decimal(1) / 2
+    assert abs(_phi_series(1.3) + _phi_series(-1.3) - 1) < Decimal(10) ** -100
+
+
 def test_gelu_textbook_values_and_gradient():
+    # the printed table (to the digits it gives), then the series above to
+    # near fp64 relative accuracy over the whole range, the far lower tail included
     for x, phi in _read_golden("normal_cdf.txt"):
         x = float(x); phi = float(phi)
-        # relative accuracy, including the far lower tail
-        assert abs(O.gelu(np.array([x]))[0] - x * phi) <= 1e-13 * abs(x * phi) + 1e-300
+        assert abs(O.gelu(np.array([x]))[0] - x * phi) <= 1e-15 * max(abs(x), 1.0)
+    # fp64 tolerance from the conditioning of the tail: the argument x / sqrt 2
+    # carries a relative rounding error of about 2^-52, and d log Phi / d log x
+    # grows like x^2 in the lower tail, so the relative error of Phi(x) computed
+    # in fp64 is about (x^2 + 4) 2^-52 (a wrong term or constant is off by far more)
+    for x in (-12.0, -10.0, -8.0, -6.5, -5.0, -3.0, -1.0, -0.25, 0.0, 0.25, 1.0, 2.5, 4.0, 8.0):
+        ref = float(_phi_series(x))
+        got = O.gelu(np.array([x]))[0]
+        tol = (x * x + 4.0) * 2.0 ** -52
+        assert abs(got - x * ref) <= tol * abs(x * ref), (x, got, x * ref)
     xs = np.linspace(-6, 6, 241)
     h = 1e-6
     fd = (O.gelu(xs + h) - O.gelu(xs - h)) / (2 * h)
     assert np.max(np.abs(fd - O.gelu_grad(xs))) < 1e-8
     # GELU(x) - GELU(-x) = x
     assert np.max(np.abs(O.gelu(xs) - O.gelu(-xs) - xs)) < 1e-14
+
+
+# ---------------------------------------------------------------- comparison metric
+def test_rel_frob_closed_form():
+    """||a - b||_F / ||b||_F with b the reference: closed forms that a missing
+    square root, a norm of the other argument, or another matrix norm fail."""
+    b = np.array([[3.0, 4.0]])                                   # ||b|| = 5
+    assert O.rel_frob(np.array([[3.0, 4.5]]), b) == 0.1          # 0.5 / 5 (squared: 0.01)
+    assert O.rel_frob(np.array([[6.0, 8.0]]), b) == 1.0          # normalized by ||b||, not ||a|| (0.5)
+    assert O.rel_frob(b, np.array([[6.0, 8.0]])) == 0.5
+    assert O.rel_frob(np.zeros((1, 2)), b) == 1.0
+    # Frobenius, not spectral or max-entry: I + ones vs I gives sqrt(2)
+    # (spectral ratio 2, max-entry ratio 1)
+    eye = np.eye(2)
+    assert abs(O.rel_frob(eye + np.ones((2, 2)), eye) - math.sqrt(2.0)) <= 4.5e-16   # two roundings
+    # every element counts, in any layout
+    rng = np.random.default_rng(3)
+    ref = rng.standard_normal((7, 5)); err = rng.standard_normal((7, 5))
+    want = math.sqrt(sum(float(e) ** 2 for e in err.ravel())) / math.sqrt(sum(float(r) ** 2 for r in ref.ravel()))
+    assert abs(O.rel_frob(ref + err, ref) - want) <= 1e-14 * want
+    assert abs(O.rel_frob((ref + err).T, ref.T) - want) <= 1e-14 * want
+    # a zero reference: the absolute norm of the difference
+    assert O.rel_frob(b, np.zeros((1, 2))) == 5.0
 
 
 # ---------------------------------------------------------------- SVD split (Eq. 1)
