@@ -32,16 +32,21 @@ def _config(cfg):
 
 
 class GpuLayer:
-    """Device-side prepared layer: Q(R)'s pair-merged operands (R and R^T),
-    rank-major factors; the GEMMs run on the pair-merged operand path."""
+    """Device-side prepared layer: Q(R) (codes in both layouts, and the
+    pair-merged operands of R and R^T), rank-major factors.
 
-    def __init__(self, d):
+    path "op": the GEMMs read the pair-merged operands; the quantizer and the
+    down-projection run as separate passes.  path "fused": the default path of
+    the library -- one pass over X (G) writes Q(X) (Q(G)) and T (V), and the
+    GEMMs read E2M1 codes + block scales."""
+
+    def __init__(self, d, path="op"):
         from bit_quantized_lora_amd import ops
-        self.ops = ops
+        self.ops, self.path = ops, path
         self.N, self.K = d["R"].shape
         Rd = dev_bf16(d["R"])
         self.ro = ops.quant_block16_op(Rd, op_rm=True, op_cm=True)
-        self.rq, _, self.rs = ops.quant_block16(Rd, rm=True, cm=False)
+        self.rq, self.rqc, self.rs, self.rsct = ops.quant_block16(Rd, rm=True, cm=True, scales_cm=True)
         self.L1t = dev_bf16(np.ascontiguousarray(d["L1"].T))
         self.At = dev_bf16(np.ascontiguousarray(d["A"].T))
         self.L2, self.B = dev_bf16(d["L2"]), dev_bf16(d["B"])
@@ -49,6 +54,10 @@ class GpuLayer:
     def fwd(self, X, out_dtype):
         o = self.ops
         M = X.shape[0]
+        if self.path == "fused":
+            T, xq, xs = o.quant_lowrank(X, self.L1t, self.At)
+            Y = o.linear_fwd(xq, xs, self.rq, self.rs, T, self.L2, self.B, M, self.N, self.K, out_dtype=out_dtype)
+            return Y, T
         xo = o.quant_block16_op(X, op_rm=True)
         T = o.lowrank_fused(X, self.L1t, self.At)
         Y = o.linear_fwd_op(xo["op_rm"], xo["op_rm_scales"], self.ro["op_rm"], self.ro["op_rm_scales"], T, self.L2,
@@ -76,6 +85,10 @@ class GpuLayer:
     def bwd(self, G, X, T, out_dtype):
         o = self.ops
         M = G.shape[0]
+        if self.path == "fused":
+            V, gq, gs = o.quant_lowrank(G, self.L2, self.B)
+            return o.linear_bwd(gq, gs, self.rqc, self.rsct, V, self.L1t, self.At, X, G, T, M, self.N, self.K,
+                                out_dtype=out_dtype)
         go = o.quant_block16_op(G, op_rm=True)
         V = o.lowrank_fused(G, self.L2, self.B)
         dX, dAt, dB = o.linear_bwd_op(go["op_rm"], go["op_rm_scales"], self.ro["op_cm"], self.ro["op_cm_scales"], V,
@@ -113,11 +126,11 @@ def _check(label, got, ref, bf16=False):
     return e
 
 
-def _single(label, d):
+def _single(label, d, path="op"):
     """A standalone linear of the stack (fresh seeded input): fwd + bwd."""
     import torch
-    say(f"[chain] {label} M={d['X'].shape[0]} K={d['R'].shape[1]} N={d['R'].shape[0]}")
-    L, Lo = GpuLayer(d), OracleLayer(d)
+    say(f"[chain] {label} M={d['X'].shape[0]} K={d['R'].shape[1]} N={d['R'].shape[0]} path={path}")
+    L, Lo = GpuLayer(d, path), OracleLayer(d)
     X, G = dev_bf16(d["X"]), dev_bf16(d["G"])
     Y, T = L.fwd(X, torch.float32)
     dX, dAt, dB = L.bwd(G, X, T, torch.float32)
@@ -128,13 +141,13 @@ def _single(label, d):
     _check(f"{label} dB", dB, ref["dB"])
 
 
-def _mlp_chain(label, up, down):
+def _mlp_chain(label, up, down, path="op"):
     """up -> GELU -> down forward, then backward from down's seeded gradient."""
     import torch
     from bit_quantized_lora_amd import ops
     M = up["X"].shape[0]
-    say(f"[chain] {label} MLP chain M={M}")
-    Lu, Ld = GpuLayer(up), GpuLayer(down)
+    say(f"[chain] {label} MLP chain M={M} path={path}")
+    Lu, Ld = GpuLayer(up, path), GpuLayer(down, path)
     X, G2 = dev_bf16(up["X"]), dev_bf16(down["G"])
     Y1, T1 = Lu.fwd(X, torch.bfloat16)
     h = ops.gelu_fwd(Y1)
@@ -165,19 +178,24 @@ def _mlp_chain(label, up, down):
     _check(f"{label} dB_up", dB1, gu["dB"])
 
 
-def test_mlp_pair_chain_full_size():
+@pytest.mark.parametrize("path", ["fused", "op"])
+def test_mlp_pair_chain_full_size(path):
     require_gpu()
     c = _config("c3")
-    _mlp_chain("mlp-pair", c["c3-up"], c["c3-down"])
+    _mlp_chain("mlp-pair", c["c3-up"], c["c3-down"], path)
 
 
+@pytest.mark.parametrize("path", ["fused", "op"])
 @pytest.mark.parametrize("stream", ["txt", "img"])
-def test_block_stack_full_size(stream):
+def test_block_stack_full_size(stream, path):
+    """All four linears of a stream (qkv, proj, then up -> GELU -> down chained),
+    on the library's default one-pass codes path and on the pair-merged
+    operand path."""
     require_gpu()
     c = _config("c5")
-    _single(f"c5-{stream}-qkv", c[f"c5-{stream}-qkv"])
-    _single(f"c5-{stream}-proj", c[f"c5-{stream}-proj"])
-    _mlp_chain(f"c5-{stream}", c[f"c5-{stream}-up"], c[f"c5-{stream}-down"])
+    _single(f"c5-{stream}-qkv", c[f"c5-{stream}-qkv"], path)
+    _single(f"c5-{stream}-proj", c[f"c5-{stream}-proj"], path)
+    _mlp_chain(f"c5-{stream}", c[f"c5-{stream}-up"], c[f"c5-{stream}-down"], path)
 
 
 def _fused_fc1_matches_separate(M, K, N, rs, r, seed):
