@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--path", choices=["fused", "codes", "op"], default="fused",
                     help="fused: one pass quantizes and down-projects X (and G), GEMMs read E2M1 codes; "
                          "codes: separate quantizer and low-rank passes; op: pair-merged FP6 GEMM operands")
+    ap.add_argument("--prewarm-ms", type=float, default=250.0,
+                    help="GPU time of untimed steps before the counted warm-up (clocks settle)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-config block")
+    ap.add_argument("--config-reps", type=int, default=10)
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (counter calibration for profiles)")
     return ap.parse_args()
@@ -195,34 +199,45 @@ class Linear:
         self.backward()
 
 
-def time_quantizer(reps):
-    """Standalone quantizer over the QKV-config X [18432 x 3072] and dY [18432 x 9216]
-    (both code layouts), rotating input copies that exceed the 256 MB MALL."""
+def time_quantizer(reps, c4):
+    """Standalone quantizer (both code layouts, E8M0 scales) over the QKV config's
+    own X [18432 x 3072] and dY [18432 x 9216], rotating copies in distinct
+    buffers that together exceed the 256 MB MALL; beside it, in the same run, a
+    plain streaming kernel over the same buffers with the same 2 : 1 read : write
+    bytes (torch's int16 -> int8 conversion: 2 B read, 1 B written per element)."""
     import torch
     from bit_quantized_lora_amd import ops
     out = {}
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(1003)
-    for name, (rows, cols), ncopies in (("X", (18432, 3072), 3), ("dY", (18432, 9216), 2)):
-        xs = [torch.randn(rows, cols, device="cuda", dtype=torch.float32, generator=gen).to(torch.bfloat16)
-              for _ in range(ncopies)]
+    for name, bits, ncopies in (("X", c4["X"], 3), ("dY", c4["G"], 2)):
+        rows, cols = bits.shape
+        x0 = dev_bf16(bits)
+        xs = [x0] + [x0.clone() for _ in range(ncopies - 1)]
         bufs = [ops.quant_block16(x, rm=True, cm=True) for x in xs]
+        sink = [torch.empty((rows, cols), dtype=torch.int8, device="cuda") for _ in range(ncopies)]
         torch.cuda.synchronize()
         s = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for i in range(3):
-            ops.quant_block16(xs[i % ncopies], rm=True, cm=True, out=bufs[i % ncopies])
-        e0.record(s)
-        for i in range(reps):
-            ops.quant_block16(xs[i % ncopies], rm=True, cm=True, out=bufs[i % ncopies])
-        e1.record(s)
-        e1.synchronize()
-        sec = e0.elapsed_time(e1) / 1e3 / reps
+
+        def timed(fn):
+            for i in range(3):
+                fn(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for i in range(reps):
+                fn(i)
+            e1.record(s)
+            e1.synchronize()
+            return e0.elapsed_time(e1) / 1e3 / reps
+
+        sec = timed(lambda i: ops.quant_block16(xs[i % ncopies], rm=True, cm=True, out=bufs[i % ncopies]))
+        sec_stream = timed(lambda i: sink[i % ncopies].copy_(xs[i % ncopies].view(torch.int16)))
         elems = rows * cols
         alg_bytes = elems * 2 + elems // 2 * 2 + elems // 256   # bf16 in, two code layouts, E8M0 scales
         out[name] = {"shape": [rows, cols], "us": sec * 1e6, "GBps": alg_bytes / sec / 1e9,
-                     "bytes_per_elem": alg_bytes / elems}
-        del xs, bufs
+                     "bytes_per_elem": alg_bytes / elems,
+                     "streaming_ref_us": sec_stream * 1e6, "streaming_ref_GBps": 3 * elems / sec_stream / 1e9,
+                     "frac_of_streaming_ref": (alg_bytes / sec) / (3 * elems / sec_stream)}
+        del xs, bufs, sink, x0
+        torch.cuda.empty_cache()
     return out
 
 
@@ -491,6 +506,169 @@ def calibration_copy():
     torch.cuda.synchronize()
 
 
+def _layer(d):
+    """A prepared fused-path Linear for one linear of a config (a chained second
+    linear of a pair gets its X from the first linear's GELU at run time)."""
+    spec = d["spec"]
+    if "X" not in d:
+        d = dict(d)
+        d["X"] = np.zeros((spec.M, spec.K), np.uint16)
+    return Linear(spec, d, "fused")
+
+
+def _oracle_sample_s(d, rows):
+    """Seconds the oracle takes for one linear's fwd + bwd over its first `rows`
+    tokens (Q(R) prepared outside the timing), and the token count."""
+    import oracle as O
+    spec = d["spec"]
+    rows = min(rows, spec.M)
+    X = d["X"][:rows] if "X" in d else np.zeros((rows, spec.K), np.uint16)
+    G = d["G"][:rows]
+    f = {k: O.bf16_to_f64(d[k]) for k in ("L1", "L2", "A", "B")}
+    rc, rsc = O.quantize_block16(d["R"])
+    Rhat = O.dequantize(rc, rsc, "pow2")
+    t0 = time.perf_counter()
+    xc, xs = O.quantize_block16(X); gc, gs = O.quantize_block16(G)
+    Xf, Gf = O.bf16_to_f64(X), O.bf16_to_f64(G)
+    O.linear_fwd(O.dequantize(xc, xs, "pow2"), Rhat, Xf, f["L1"], f["L2"], f["A"], f["B"])
+    O.linear_bwd(O.dequantize(gc, gs, "pow2"), Rhat, Gf, Xf, f["L1"], f["L2"], f["A"], f["B"])
+    return time.perf_counter() - t0, rows
+
+
+def time_configs(reps, cache, oracle_rows=128):
+    """Per-config block: every config of the workload list on the fused path.
+
+    c1, c2, c4: one linear, fwd + bwd.  c3: the MLP pair chained (up -> GELU ->
+    down forward, then down, GELU and up backward).  c5: the double-stream
+    block's eight linears (per stream: qkv and proj on their own inputs, up ->
+    GELU -> down chained).  Reported: step time (median over `reps` steps),
+    4-bit GEMM work of the step per second and its fraction of the FP4 peak, each
+    linear's forward GEMM alone (launched back to back), the quantizer's rate on
+    the config's first input, and the oracle's time on a bounded sample of every
+    linear (the first `oracle_rows` tokens, scaled to the full token count)."""
+    import torch
+    import synth
+    from bit_quantized_lora_amd import ops
+    s = torch.cuda.current_stream()
+    out = {}
+    for cfg in ("c1", "c2", "c3", "c4", "c5"):
+        ds = cache[cfg] if cfg in cache else synth.config_linears(cfg)
+        lins = {d["spec"].name: _layer(d) for d in ds}
+        singles = [n for n in lins if not (n.endswith("-up") or n.endswith("-down"))]
+        pairs = [(n, n[:-3] + "-down") for n in lins if n.endswith("-up")]
+        bufs = {u: (torch.empty_like(lins[u].Y), torch.empty_like(lins[u].Y)) for u, _ in pairs}
+
+        def step():
+            for n in singles:
+                lins[n].forward()
+                lins[n].backward()
+            for u, dn in pairs:
+                up, down = lins[u], lins[dn]
+                h, dy = bufs[u]
+                up.forward()
+                ops.gelu_fwd(up.Y, out=h)
+                down.X = h
+                down.forward()
+                down.backward()
+                ops.gelu_bwd(up.Y, down.dX, out=dy)
+                up.G = dy
+                up.backward()
+
+        for _ in range(3):
+            step()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(s)
+        for i in range(reps):
+            step()
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
+        step_us = float(np.median([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]))
+        work = sum(4.0 * l.M * l.N * l.K for l in lins.values())
+        gemms = {}
+        for n, lin in lins.items():
+            for _ in range(2):
+                lin.gemm_fwd()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(s)
+            for _ in range(reps):
+                lin.gemm_fwd()
+            g1.record(s)
+            g1.synchronize()
+            us = g0.elapsed_time(g1) * 1e3 / reps
+            tf = 2.0 * lin.M * lin.N * lin.K / us / 1e6
+            gemms[n] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+        first = lins[ds[0]["spec"].name]
+        q = ops.quant_block16(first.X, rm=True, cm=True)
+        for _ in range(2):
+            ops.quant_block16(first.X, rm=True, cm=True, out=q)
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record(s)
+        for _ in range(reps):
+            ops.quant_block16(first.X, rm=True, cm=True, out=q)
+        q1.record(s)
+        q1.synchronize()
+        qus = q0.elapsed_time(q1) * 1e3 / reps
+        el = first.M * first.K
+        qbytes = el * 2 + el + el // 256
+        orc_s = 0.0
+        for d in ds:
+            t, rows = _oracle_sample_s(d, oracle_rows)
+            orc_s += t * d["spec"].M / rows
+        out[cfg] = {
+            "linears": len(lins), "step_us": round(step_us, 2),
+            "step_TFLOPs": round(work / step_us / 1e6, 1),
+            "step_frac_fp4_peak": round(work / step_us / 1e6 / FP4_PEAK_TFLOPS, 4),
+            "fwd_gemm": gemms,
+            "quantizer": {"shape": [first.M, first.K], "us": round(qus, 2), "GBps": round(qbytes / qus / 1e3, 1),
+                          "note": "repeated on one input (partly served from the MALL when it fits)"},
+            "oracle_s_full_est": round(orc_s, 2),
+            "oracle_sample": f"first {oracle_rows} tokens of each linear, scaled to the full token count",
+        }
+        del lins, bufs, q
+        torch.cuda.empty_cache()
+    return out
+
+
+def gpu_clock_mhz():
+    """Current and maximum graphics clock of GPU 0 in MHz (None when unavailable)."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        try:
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+            info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            return {"cur": info.get("clk"), "max": info.get("max_clk")}
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception:  # pragma: no cover - tool missing or no permission
+        return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def prewarm(fn, min_ms=250.0):
+    """Run `fn` (one step) until at least min_ms of GPU work has completed, so the
+    clocks have settled before the counted warm-up and the timed steps."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(8):
+            fn()
+        n += 8
+        torch.cuda.synchronize()
+    return {"steps": n, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
+
+
 def cpu_baseline(spec, d, rows, reps):
     """The oracle as it stands, `reps` passes over the first `rows` tokens of the same workload."""
     import oracle as O
@@ -513,9 +691,17 @@ def cpu_baseline(spec, d, rows, reps):
         O.linear_bwd(Ghat, Rhat, G, X, f["L1"], f["L2"], f["A"], f["B"])
     sec = time.perf_counter() - t0
     flops = 4.0 * rows * spec.N * spec.K * reps
+    # the oracle's quantizer alone (numpy elementwise work: one thread)
+    qs = d["X"][:1024]
+    q0 = time.perf_counter()
+    O.quantize_block16(qs)
+    qsec = time.perf_counter() - q0
     return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "quantizer_1thread_ns_per_elem": round(qsec / qs.size * 1e9, 2),
             "sample": f"fp64 numpy oracle, {reps} passes of fwd+bwd over {rows} of {spec.M} tokens "
-                      f"(K={spec.K}, N={spec.N}), Q(R) prepared outside the timing; {sec:.2f} s"}
+                      f"(K={spec.K}, N={spec.N}), Q(R) prepared outside the timing; {sec:.2f} s; "
+                      f"cores = the BLAS threads of its products"}
 
 
 def main():
@@ -534,12 +720,14 @@ def main():
     M, K, N = spec.M, spec.K, spec.N
     s = torch.cuda.current_stream()
 
+    # clocks settle over a fixed stretch of steps before the counted warm-up
+    warm = prewarm(lin.step, args.prewarm_ms)
+    clk_before = gpu_clock_mhz()
     for _ in range(args.warmup):
         lin.step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, no event inside it (an event marker
-    # between launches adds a cache write-back to the work it separates)
+    # timed region: exactly `steps` steps, no event inside it
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(s)
@@ -548,20 +736,22 @@ def main():
     t_end.record(s)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    clk_after = gpu_clock_mhz()
 
     # per-phase breakdown: events between the phases over `steps` further steps,
     # enqueued back to back so the GPU never waits for the host
     names = ["quant_lowrank_X", "fwd_gemm", "quant_lowrank_G", "bwd_gemm_and_adapter_grads"]
     fns = [lin.quant_lowrank_x, lin.gemm_fwd, lin.quant_lowrank_g, lin.gemm_bwd_and_grads]
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
+    nph = max(args.steps, 20)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(nph)]
     host_t0 = time.perf_counter()
-    for k in range(args.steps):
+    for k in range(nph):
         lin.next_inputs()
         marks[k][0].record(s)
         for i, f in enumerate(fns):
             f()
             marks[k][i + 1].record(s)
-    host_us = (time.perf_counter() - host_t0) / args.steps * 1e6
+    host_us = (time.perf_counter() - host_t0) / nph * 1e6
     torch.cuda.synchronize()
     phases = {n: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks])) * 1e3 for i, n in enumerate(names)}
     gemm_ms = phases["fwd_gemm"] / 1e3   # the forward GEMM between event markers inside the step
@@ -569,26 +759,30 @@ def main():
     step_pct = {"p10": round(float(np.percentile(step_us, 10)), 2), "p50": round(float(np.percentile(step_us, 50)), 2),
                 "p90": round(float(np.percentile(step_us, 90)), 2)}
 
-    # forward GEMM alone, launched back to back (no event between launches, so
-    # no cache write-back at an event marker is charged to the kernel): the
+    # forward GEMM alone, launched back to back (no event between launches): the
     # per-launch time used for the roofline
     for _ in range(3):
         lin.gemm_fwd()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     g0.record(s)
-    for _ in range(args.steps):
+    for _ in range(max(args.steps, 20)):
         lin.gemm_fwd()
     g1.record(s)
     torch.cuda.synchronize()
-    gemm_b2b_ms = g0.elapsed_time(g1) / args.steps
+    gemm_b2b_ms = g0.elapsed_time(g1) / max(args.steps, 20)
 
     separate = (time_separate_passes(spec, d, more, args.steps, args.warmup, ms_step * 1e3)
                 if args.path == "fused" else None)
     mlp_fusion = time_mlp_fc1_fusion(lin, args.steps)
     precision = time_precision_variants(lin, args.steps)
     granularity = time_granularity(lin, args.steps)
-    quant = time_quantizer(args.quant_reps)
+    del lin, more
+    torch.cuda.empty_cache()
+    import synth
+    cache = {"c4": synth.config_linears("c4")}
+    quant = time_quantizer(args.quant_reps, cache["c4"][0])
+    configs = None if args.no_configs else time_configs(args.config_reps, cache)
     if args.calibration_copy:
         calibration_copy()
     gemm_flops = 2.0 * M * N * K
@@ -626,16 +820,20 @@ def main():
                      "frac_of_half_fragment_ceiling": (round(achieved / (FP4_PEAK_TFLOPS / 2), 4)
                                                        if args.path != "op" else None),
                      "avg_launch_us_in_step": round(gemm_ms * 1e3, 2)},
+        "timed_vs_marker_p50": round(ms_step * 1e3 / step_pct["p50"], 4),
+        "prewarm": warm,
+        "gfx_clock_mhz": {"before_timed": clk_before, "after_timed": clk_after},
         "phases_us": {k: round(v, 2) for k, v in phases.items()},
         "step_us_percentiles": step_pct,
         "host_enqueue_us_per_step": round(host_us, 1),
-        "quantizer": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+        "quantizer": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in quant.items()},
         "mlp_fc1_fusion_us": mlp_fusion,
         "precision_variants": precision,
         "granularity": granularity,
         "quant_lowrank_pass": lowrank_pass_rates(spec, phases),
         "one_pass_vs_separate": separate,
+        "configs": configs,
         "quant_GBps": round(quant["dY"]["GBps"], 1),
         "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),
     }

@@ -21,18 +21,32 @@ ft_status adapter_grads(int64_t M, int64_t N, int64_t K, const float* V, int rs,
 // stream that forks from the caller's stream after the GEMM is enqueued and
 // joins it again before the call returns, so the memory-bound reductions use
 // the CUs the GEMM leaves idle (e.g. 216 tiles on 256 CUs) instead of
-// following it.  One side stream per device, created on first use (default
-// priority); the fork/join events are created per call, so concurrent calls on
-// different streams share nothing but the side stream's queue.
-hipStream_t side_stream() {
-  static std::mutex mu;
-  static hipStream_t streams[64] = {};
+// following it.  Per device, the library creates once (on first use) one side
+// stream (default priority) and one fork and one join event.  An event may be
+// recorded again as soon as a wait on it has been enqueued (the wait takes the
+// record that precedes it), so the pair is reused by every call; a mutex keeps
+// each record + wait pair of concurrent host threads together.
+struct SideCtx {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;
+};
+
+std::mutex side_mu;
+
+SideCtx* side_ctx() {
+  static SideCtx ctx[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess)
-    streams[dev] = nullptr;
-  return streams[dev];
+  SideCtx& c = ctx[dev];
+  if (!c.tried) {
+    c.tried = true;
+    if (hipStreamCreateWithFlags(&c.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&c.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c.join, hipEventDisableTiming) != hipSuccess)
+      c.stream = nullptr;   // no side stream: run everything on the caller's stream
+  }
+  return c.stream ? &c : nullptr;
 }
 
 // enqueue `gemm` on `stream` and the adapter gradients concurrently beside it
@@ -41,27 +55,21 @@ template <class F>
 ft_status gemm_with_adapter_grads(F gemm, int64_t M, int64_t N, int64_t K, const float* V, int rs, int r,
                                   const void* X, const void* G, const float* T, float* dAt, float* dB,
                                   void* workspace, hipStream_t stream) {
-  hipStream_t side = r ? side_stream() : nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  if (side && (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
-               hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess))
-    side = nullptr;
+  std::unique_lock<std::mutex> lock(side_mu);
+  SideCtx* side = r ? side_ctx() : nullptr;
   if (!side) {  // no side stream: one after the other on the caller's stream
-    if (fork) (void)hipEventDestroy(fork);
-    if (join) (void)hipEventDestroy(join);
+    lock.unlock();
     ft_status st = gemm(stream, false);
     if (st != FT_OK) return st;
     return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
   }
   ft_status st = FT_OK;
-  if (hipEventRecord(fork, stream) != hipSuccess) st = FT_EHIP;
+  if (hipEventRecord(side->fork, stream) != hipSuccess) st = FT_EHIP;
   if (st == FT_OK) st = gemm(stream, true);
-  if (st == FT_OK && hipStreamWaitEvent(side, fork, 0) != hipSuccess) st = FT_EHIP;
-  if (st == FT_OK) st = adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, side);
-  if (st == FT_OK && hipEventRecord(join, side) != hipSuccess) st = FT_EHIP;
-  if (st == FT_OK && hipStreamWaitEvent(stream, join, 0) != hipSuccess) st = FT_EHIP;
-  (void)hipEventDestroy(fork);
-  (void)hipEventDestroy(join);
+  if (st == FT_OK && hipStreamWaitEvent(side->stream, side->fork, 0) != hipSuccess) st = FT_EHIP;
+  if (st == FT_OK) st = adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, side->stream);
+  if (st == FT_OK && hipEventRecord(side->join, side->stream) != hipSuccess) st = FT_EHIP;
+  if (st == FT_OK && hipStreamWaitEvent(stream, side->join, 0) != hipSuccess) st = FT_EHIP;
   return st;
 }
 

@@ -7,6 +7,7 @@ method happens in Python.
 """
 from __future__ import annotations
 
+import math
 from typing import Optional, Tuple
 
 import torch
@@ -26,16 +27,20 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _need(t, dtype, name: str, shape=None, contiguous: bool = True, min_numel: int = 0) -> None:
+def _need(t, dtype, name: str, shape=None, contiguous: bool = True, min_numel: int = 0, used: bool = True) -> None:
     """Check a tensor before its pointer crosses the ABI: dtype, shape,
     contiguity and size (the device is checked by _same_device once every
     tensor of a call has passed these).  Raises ValueError on a mismatch."""
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name} must be a tensor, got {type(t).__name__}")
+    if not used and t.numel() == 0:
+        return   # an operand the call does not read (its product is empty) may be empty
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(int(s) for s in shape):
-        raise ValueError(f"{name} must have shape {tuple(int(s) for s in shape)}, got {tuple(t.shape)}")
+        # an empty operand (a zero-sized dimension) may come in any empty shape
+        if not (t.numel() == 0 and math.prod(int(s) for s in shape) == 0):
+            raise ValueError(f"{name} must have shape {tuple(int(s) for s in shape)}, got {tuple(t.shape)}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.numel() < min_numel:
@@ -292,12 +297,13 @@ def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: in
                out_dtype=torch.float32, mode: str = "pow2", out: Optional[torch.Tensor] = None):
     """Y = deq(Xq) deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B."""
     _mult16("linear_fwd", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     sdt = _sdt(mode)
     rs, r = _up_factors(L2, B, N)
-    _need(xq_codes, torch.uint8, "xq_codes", (M, K // 2))
-    _need(xq_scales, sdt, "xq_scales", (M // 16, K // 16))
-    _need(rq_codes, torch.uint8, "rq_codes", (N, K // 2))
-    _need(rq_scales, sdt, "rq_scales", (N // 16, K // 16))
+    _need(xq_codes, torch.uint8, "xq_codes", (M, K // 2), used=gemm)
+    _need(xq_scales, sdt, "xq_scales", (M // 16, K // 16), used=gemm)
+    _need(rq_codes, torch.uint8, "rq_codes", (N, K // 2), used=gemm)
+    _need(rq_scales, sdt, "rq_scales", (N // 16, K // 16), used=gemm)
     _need(T, torch.float32, "T", (M, rs + r))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=T.device)
@@ -317,12 +323,13 @@ def linear_fwd_gelu(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, 
     """First linear of an MLP with the fused epilogue: Y (bf16), H = GELU(Y) (bf16)
     and Q(H) (row-major codes, scales); returns (Y, H, h_codes, h_scales)."""
     _mult16("linear_fwd_gelu", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     sdt = _sdt(mode)
     rs, r = _up_factors(L2, B, N)
-    _need(xq_codes, torch.uint8, "xq_codes", (M, K // 2))
-    _need(xq_scales, sdt, "xq_scales", (M // 16, K // 16))
-    _need(rq_codes, torch.uint8, "rq_codes", (N, K // 2))
-    _need(rq_scales, sdt, "rq_scales", (N // 16, K // 16))
+    _need(xq_codes, torch.uint8, "xq_codes", (M, K // 2), used=gemm)
+    _need(xq_scales, sdt, "xq_scales", (M // 16, K // 16), used=gemm)
+    _need(rq_codes, torch.uint8, "rq_codes", (N, K // 2), used=gemm)
+    _need(rq_scales, sdt, "rq_scales", (N // 16, K // 16), used=gemm)
     _need(T, torch.float32, "T", (M, rs + r))
     dev = T.device
     if out is None:
@@ -377,12 +384,13 @@ def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G,
                dAt: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None):
     """dX, dAt, dB of Eq. 3 and section 3.2 (see include/ft.h)."""
     _mult16("linear_bwd", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     sdt = _sdt(mode)
     rs, r, dX, dAt, dB = _bwd_common(V, L1t, At, X, G, T, M, N, K, dX, dAt, dB, out_dtype)
-    _need(gq_codes, torch.uint8, "gq_codes", (M, N // 2))
-    _need(gq_scales, sdt, "gq_scales", (M // 16, N // 16))
-    _need(rq_codes_cm, torch.uint8, "rq_codes_cm", (K, N // 2))
-    _need(rq_scales_cm, sdt, "rq_scales_cm", (K // 16, N // 16))
+    _need(gq_codes, torch.uint8, "gq_codes", (M, N // 2), used=gemm)
+    _need(gq_scales, sdt, "gq_scales", (M // 16, N // 16), used=gemm)
+    _need(rq_codes_cm, torch.uint8, "rq_codes_cm", (K, N // 2), used=gemm)
+    _need(rq_scales_cm, sdt, "rq_scales_cm", (K // 16, N // 16), used=gemm)
     workspace = _ws(workspace, linear_bwd_workspace(M, N, K, r), V.device)
     _same_device(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G, T, dX, dAt, dB, workspace)
     st = lib().ft_linear_bwd(M, N, K, _MODES[mode], gq_codes.data_ptr(), gq_scales.data_ptr(),
@@ -398,13 +406,14 @@ def linear_fwd_op(x_op, x_op_scales, r_op, r_op_scales, T, L2, B, M: int, N: int
                   out_dtype=torch.float32, out: Optional[torch.Tensor] = None):
     """Y of Eq. 2 from pair-merged operands (ft_quant_block16_op op_rm of X and of R)."""
     _mult16("linear_fwd_op", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     rs, r = _up_factors(L2, B, N)
     (xa, xb), (xc, xd) = operand_shapes(M, K)
     (ra_, rb_), (rc, rd) = operand_shapes(N, K)
-    _need(x_op, torch.uint8, "x_op", (xa, xb))
-    _need(x_op_scales, torch.uint8, "x_op_scales", (xc, xd))
-    _need(r_op, torch.uint8, "r_op", (ra_, rb_))
-    _need(r_op_scales, torch.uint8, "r_op_scales", (rc, rd))
+    _need(x_op, torch.uint8, "x_op", (xa, xb), used=gemm)
+    _need(x_op_scales, torch.uint8, "x_op_scales", (xc, xd), used=gemm)
+    _need(r_op, torch.uint8, "r_op", (ra_, rb_), used=gemm)
+    _need(r_op_scales, torch.uint8, "r_op_scales", (rc, rd), used=gemm)
     _need(T, torch.float32, "T", (M, rs + r))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=T.device)
@@ -424,13 +433,14 @@ def linear_bwd_op(g_op, g_op_scales, rt_op, rt_op_scales, V, L1t, At, X, G, T, M
                   dB: Optional[torch.Tensor] = None):
     """dX, dAt, dB of Eq. 3 from pair-merged operands (op_rm of G, op_cm of R)."""
     _mult16("linear_bwd_op", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     rs, r, dX, dAt, dB = _bwd_common(V, L1t, At, X, G, T, M, N, K, dX, dAt, dB, out_dtype)
     (ga, gb), (gc, gd) = operand_shapes(M, N)
     (ta, tb), (tc, td) = operand_shapes(K, N)
-    _need(g_op, torch.uint8, "g_op", (ga, gb))
-    _need(g_op_scales, torch.uint8, "g_op_scales", (gc, gd))
-    _need(rt_op, torch.uint8, "rt_op", (ta, tb))
-    _need(rt_op_scales, torch.uint8, "rt_op_scales", (tc, td))
+    _need(g_op, torch.uint8, "g_op", (ga, gb), used=gemm)
+    _need(g_op_scales, torch.uint8, "g_op_scales", (gc, gd), used=gemm)
+    _need(rt_op, torch.uint8, "rt_op", (ta, tb), used=gemm)
+    _need(rt_op_scales, torch.uint8, "rt_op_scales", (tc, td), used=gemm)
     workspace = _ws(workspace, linear_bwd_workspace(M, N, K, r), V.device)
     _same_device(g_op, g_op_scales, rt_op, rt_op_scales, V, L1t, At, X, G, T, dX, dAt, dB, workspace)
     st = lib().ft_linear_bwd_op(M, N, K, g_op.data_ptr(), g_op_scales.data_ptr(), rt_op.data_ptr(),
@@ -446,10 +456,11 @@ def linear_fwd_a16(X, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
                    out_dtype=torch.float32, out: Optional[torch.Tensor] = None):
     """W4A16 forward: Y = X deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B (X bf16, unquantized)."""
     _mult16("linear_fwd_a16", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     rs, r = _up_factors(L2, B, N)
     _need(X, torch.bfloat16, "X", (M, K))
-    _need(rq_codes, torch.uint8, "rq_codes", (N, K // 2))
-    _need(rq_scales, torch.uint8, "rq_scales", (N // 16, K // 16))
+    _need(rq_codes, torch.uint8, "rq_codes", (N, K // 2), used=gemm)
+    _need(rq_scales, torch.uint8, "rq_scales", (N // 16, K // 16), used=gemm)
     _need(T, torch.float32, "T", (M, rs + r))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=X.device)
@@ -469,9 +480,10 @@ def linear_bwd_g16(G, rq_codes_cm, rq_scales_cm, V, L1t, At, X, T, M: int, N: in
                    dB: Optional[torch.Tensor] = None):
     """G16 backward: dX = G deq(Rq) + V [L1^T; A^T] (G bf16, unquantized) and dAt, dB."""
     _mult16("linear_bwd_g16", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     rs, r, dX, dAt, dB = _bwd_common(V, L1t, At, X, G, T, M, N, K, dX, dAt, dB, out_dtype)
-    _need(rq_codes_cm, torch.uint8, "rq_codes_cm", (K, N // 2))
-    _need(rq_scales_cm, torch.uint8, "rq_scales_cm", (K // 16, N // 16))
+    _need(rq_codes_cm, torch.uint8, "rq_codes_cm", (K, N // 2), used=gemm)
+    _need(rq_scales_cm, torch.uint8, "rq_scales_cm", (K // 16, N // 16), used=gemm)
     workspace = _ws(workspace, linear_bwd_workspace(M, N, K, r), G.device)
     _same_device(G, rq_codes_cm, rq_scales_cm, V, L1t, At, X, T, dX, dAt, dB, workspace)
     st = lib().ft_linear_bwd_g16(M, N, K, G.data_ptr(), rq_codes_cm.data_ptr(), rq_scales_cm.data_ptr(),
@@ -534,11 +546,12 @@ def linear_fwd_grp(group, xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M:
     """Eq. 2 with 1 x group scaled operands (ft_quant_group of X and R)."""
     _group(group)
     _mult16("linear_fwd_grp", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     rs, r = _up_factors(L2, B, N)
-    _need(xq_codes, torch.uint8, "xq_codes", (M, K // 2))
-    _need(xq_scales, torch.uint8, "xq_scales", (M, K // group))
-    _need(rq_codes, torch.uint8, "rq_codes", (N, K // 2))
-    _need(rq_scales, torch.uint8, "rq_scales", (N, K // group))
+    _need(xq_codes, torch.uint8, "xq_codes", (M, K // 2), used=gemm)
+    _need(xq_scales, torch.uint8, "xq_scales", (M, K // group), used=gemm)
+    _need(rq_codes, torch.uint8, "rq_codes", (N, K // 2), used=gemm)
+    _need(rq_scales, torch.uint8, "rq_scales", (N, K // group), used=gemm)
     _need(T, torch.float32, "T", (M, rs + r))
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=T.device)
@@ -559,11 +572,12 @@ def linear_bwd_grp(group, gq_codes, gq_scales, rtq_codes, rtq_scales, V, L1t, At
     """Eq. 3 and the adapter gradients with 1 x group scaled operands (rtq: ft_requant_group_t of Q(R))."""
     _group(group)
     _mult16("linear_bwd_grp", M, N, K)
+    gemm = M > 0 and N > 0 and K > 0
     rs, r, dX, dAt, dB = _bwd_common(V, L1t, At, X, G, T, M, N, K, dX, dAt, dB, out_dtype)
-    _need(gq_codes, torch.uint8, "gq_codes", (M, N // 2))
-    _need(gq_scales, torch.uint8, "gq_scales", (M, N // group))
-    _need(rtq_codes, torch.uint8, "rtq_codes", (K, N // 2))
-    _need(rtq_scales, torch.uint8, "rtq_scales", (K, N // group))
+    _need(gq_codes, torch.uint8, "gq_codes", (M, N // 2), used=gemm)
+    _need(gq_scales, torch.uint8, "gq_scales", (M, N // group), used=gemm)
+    _need(rtq_codes, torch.uint8, "rtq_codes", (K, N // 2), used=gemm)
+    _need(rtq_scales, torch.uint8, "rtq_scales", (K, N // group), used=gemm)
     workspace = _ws(workspace, linear_bwd_workspace(M, N, K, r), V.device)
     _same_device(gq_codes, gq_scales, rtq_codes, rtq_scales, V, L1t, At, X, G, T, dX, dAt, dB, workspace)
     st = lib().ft_linear_bwd_grp(M, N, K, group, gq_codes.data_ptr(), gq_scales.data_ptr(), rtq_codes.data_ptr(),

@@ -165,3 +165,4 @@ def test_gelu_argument_validation():
     assert lib.ft_gelu_bwd(p, p, 12, p, None) == L.FT_ESHAPE
     assert lib.ft_gelu_fwd(p, 0, p, None) == L.FT_OK
     assert lib.ft_gelu_fwd(None, 16, p, None) == L.FT_EINVAL
+

@@ -142,3 +142,13 @@ def test_group_and_gelu_bindings_reject_bad_buffers():
         ops.gelu_fwd(x, out=z((M, K - 8), bf))
     with pytest.raises(ValueError, match="dh"):
         ops.gelu_bwd(x, z((M, K), f32))
+
+
+def test_empty_operands_may_come_in_any_empty_shape():
+    """A zero-sized dimension makes an operand empty; its tensor's shape is then free
+    (the library takes NULL for it), so the checks pass and only the device check
+    remains on the CPU."""
+    e8 = z((0,), u8)
+    with pytest.raises(ValueError, match="device tensor"):
+        ops.linear_fwd(e8, e8, e8, e8, z((M, RS + R), f32), z((RS, N), bf), z((R, N), bf), M, N, 0,
+                       out=z((M, N), f32))
