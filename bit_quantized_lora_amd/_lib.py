@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libft.so")
 FT_OK, FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EHIP, FT_ENOTSUP, FT_ESPACE = range(7)
 FT_SCALE_POW2, FT_SCALE_F32 = 0, 1
 FT_OUT_F32, FT_OUT_BF16 = 0, 1
+FT_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # name -> argtypes (restype is ft_status = int unless stated)
 _SIGS = {
@@ -39,6 +40,9 @@ _SIGS = {
                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_linear_bwd_workspace": [c_int64, c_int64, c_int64, c_int32],
+    "ft_linear_bwd_noalloc": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_int32, c_void_p, c_void_p, c_void_p],
     "ft_linear_fwd_op": [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
                          c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p],
     "ft_linear_bwd_op": [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -151,14 +151,17 @@ extern "C" size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32
   return align256(lora_grad_workspace(M, K, r)) + align256(lora_grad_workspace(M, N, r));
 }
 
-extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
-                                   const uint8_t* gq_codes, const void* gq_scales,
-                                   const uint8_t* rq_codes_cm, const void* rq_scales_cm,
-                                   const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
-                                   const void* X, const void* G, const float* T,
-                                   void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
-                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
-  using namespace ft;
+namespace ft {
+namespace {
+// ft_linear_bwd with its workspace given; side: the adapter gradients may run on
+// the library's side stream (otherwise after the GEMM on the caller's stream)
+ft_status linear_bwd_impl(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                          const uint8_t* gq_codes, const void* gq_scales,
+                          const uint8_t* rq_codes_cm, const void* rq_scales_cm,
+                          const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                          const void* X, const void* G, const float* T,
+                          void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                          void* workspace, size_t ws_bytes, hipStream_t stream, bool side) {
   if (mode != FT_SCALE_POW2 && mode != FT_SCALE_F32) return FT_EINVAL;
   if (dxdt != FT_OUT_F32 && dxdt != FT_OUT_BF16) return FT_EINVAL;
   if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
@@ -191,7 +194,71 @@ extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
   auto gemm = [&](hipStream_t s, bool beside) {
     return (M && K) ? launch_gemm_w4a4(g, out_bf16, true, s, beside) : FT_OK;
   };
+  if (!side) {
+    ft_status st = gemm(stream, false);
+    if (st != FT_OK) return st;
+    return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
+  }
   return gemm_with_adapter_grads(gemm, M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
+}
+
+// Scratch of ft_linear_bwd_noalloc: a file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// is looked up once per device with hipGetSymbolAddress and only that address
+// is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[FT_NOALLOC_SCRATCH_BYTES];
+
+// the device address of `scratch` on the current device (nullptr on failure)
+void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+}  // namespace
+}  // namespace ft
+
+extern "C" ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                                   const uint8_t* gq_codes, const void* gq_scales,
+                                   const uint8_t* rq_codes_cm, const void* rq_scales_cm,
+                                   const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                                   const void* X, const void* G, const float* T,
+                                   void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return ft::linear_bwd_impl(M, N, K, mode, gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, rs, At, r, X,
+                             G, T, dX, dxdt, dAt, dB, workspace, ws_bytes, stream, true);
+}
+
+extern "C" ft_status ft_linear_bwd_noalloc(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                                           const uint8_t* gq_codes, const void* gq_scales,
+                                           const uint8_t* rq_codes_cm, const void* rq_scales_cm,
+                                           const float* V, const void* L1t, int32_t rs, const void* At,
+                                           int32_t r, const void* X, const void* G, const float* T,
+                                           void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
+                                           hipStream_t stream) {
+  using namespace ft;
+  if (M < 0 || N < 0 || K < 0 || r < 0) return FT_ESHAPE;
+  const size_t need = ft_linear_bwd_workspace(M, N, K, r);
+  if (need > FT_NOALLOC_SCRATCH_BYTES) return FT_ESPACE;
+  void* ws = nullptr;
+  if (need) {
+    // validate everything else before touching the device
+    const ft_status pre = linear_bwd_impl(M, N, K, mode, gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t,
+                                          rs, At, r, X, G, T, dX, dxdt, dAt, dB, nullptr, 0, stream, false);
+    if (pre != FT_EINVAL) return pre;   // the missing workspace is the only complaint expected here
+    ws = scratch_ptr();
+    if (!ws) return FT_EHIP;
+  }
+  return linear_bwd_impl(M, N, K, mode, gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, rs, At, r, X, G,
+                         T, dX, dxdt, dAt, dB, ws, need, stream, false);
 }
 
 namespace ft {

@@ -226,6 +226,28 @@ ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
 
 size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
 
+/* ft_linear_bwd_noalloc -- ft_linear_bwd for callers that cannot allocate device
+ * memory (code under stream capture, tight loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, the same kernels and
+ * the same results bit for bit.  The reduction partials live in a fixed scratch
+ * area of FT_NOALLOC_SCRATCH_BYTES that the library keeps per GPU (a device
+ * array, resident until the process ends; its address is looked up on the first
+ * call on each device).  The call allocates nothing and creates no stream or
+ * event: the adapter gradients run after the dX GEMM on the given stream.
+ *  - FT_ESPACE when ft_linear_bwd_workspace(M, N, K, r) exceeds
+ *    FT_NOALLOC_SCRATCH_BYTES (every config of the method needs at most 27 MiB).
+ *  - Every call on a GPU shares that GPU's scratch: calls that overlap in time
+ *    on one GPU (different streams, or host threads) race and must not be
+ *    issued.  Nothing in the scratch needs to start at zero; it keeps the last
+ *    call's partials. */
+#define FT_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ft_status ft_linear_bwd_noalloc(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                                const uint8_t* gq_codes, const void* gq_scales,
+                                const uint8_t* rq_codes_cm, const void* rq_scales_cm,
+                                const float* V, const void* L1t, int32_t rs, const void* At, int32_t r,
+                                const void* X, const void* G, const float* T,
+                                void* dX, ft_out_dtype dxdt, float* dAt, float* dB, hipStream_t stream);
+
 /* ft_linear_fwd_op / ft_linear_bwd_op -- the same Eq. 2 and Eq. 3 (and adapter
  * gradients) with the 4-bit operands given as pair-merged operands
  * (ft_quant_block16_op), FT_SCALE_POW2 only.  Results equal those of

@@ -166,3 +166,16 @@ def test_gelu_argument_validation():
     assert lib.ft_gelu_fwd(p, 0, p, None) == L.FT_OK
     assert lib.ft_gelu_fwd(None, 16, p, None) == L.FT_EINVAL
 
+
+def test_noalloc_backward_rejects_requests_beyond_its_scratch():
+    """ft_linear_bwd_noalloc refuses a backward whose reduction partials exceed its
+    fixed scratch, before touching the device."""
+    L = _lib(); lib = L.lib()
+    M, N, K, r = 1 << 20, 1 << 14, 1 << 12, 64
+    assert lib.ft_linear_bwd_workspace(M, N, K, r) > L.FT_NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(16 * 1024)   # never dereferenced
+    st = lib.ft_linear_bwd_noalloc(M, N, K, 0, p, p, p, p, p, p, 64, p, r, p, p, p, p, 0, p, p, None)
+    assert st == L.FT_ESPACE
+    # every config of the method fits
+    for (M, N, K, r) in ((18432, 9216, 3072, 64), (4608, 12288, 3072, 16), (4096, 3072, 12288, 32)):
+        assert lib.ft_linear_bwd_workspace(M, N, K, r) <= L.FT_NOALLOC_SCRATCH_BYTES
