@@ -127,9 +127,29 @@ class Linear:
         self.dAt, self.dB = e((r, K), f32), e((r, N), f32)
         self.ws = e((max(ops.linear_bwd_workspace(M, N, K, r), 16),), u8)
         self.ws_lr = e((max(ops.lowrank_workspace(M, K, rs + r), ops.lowrank_workspace(M, N, rs + r), 16),), u8)
+        # the step's library calls, checked once per input set and issued as prepared
+        # calls (no per-step Python checks); a layer whose X or G is replaced (a
+        # chained layer) falls back to the ordinary calls
+        self.p_fwd = self.p_qx = self.p_qg = self.p_bwd = None
+        if path != "op":
+            self.p_fwd = ops.linear_fwd(self.xq[0], self.xq[2], self.rq, self.rs_, self.T, self.L2, self.B, M, N, K,
+                                        out=self.Y, prepare=True)
+            self.p_bwd = [ops.linear_bwd(self.gq[0], self.gq[2], self.rqc, self.rsct, self.V, self.L1t, self.At,
+                                         x, g, self.T, M, N, K, workspace=self.ws, dX=self.dX, dAt=self.dAt,
+                                         dB=self.dB, prepare=True) for x, g in self.inputs]
+        if path == "fused":
+            self.p_qx = [ops.quant_lowrank(x, self.L1t, self.At, out=self.T, codes=self.xq[0], scales=self.xq[2],
+                                           workspace=self.ws_lr, prepare=True) for x, _ in self.inputs]
+            self.p_qg = [ops.quant_lowrank(g, self.L2, self.B, out=self.V, codes=self.gq[0], scales=self.gq[2],
+                                           workspace=self.ws_lr, prepare=True) for _, g in self.inputs]
+
+    def _own_inputs(self):
+        return self.X is self.inputs[self.k][0] and self.G is self.inputs[self.k][1]
 
     def quant_lowrank_x(self):
-        if self.path == "fused":
+        if self.path == "fused" and self.X is self.inputs[self.k][0]:
+            self.p_qx[self.k]()
+        elif self.path == "fused":
             self.ops.quant_lowrank(self.X, self.L1t, self.At, out=self.T, codes=self.xq[0], scales=self.xq[2],
                                    workspace=self.ws_lr)
         else:
@@ -137,7 +157,9 @@ class Linear:
             self.lowrank_x()
 
     def quant_lowrank_g(self):
-        if self.path == "fused":
+        if self.path == "fused" and self.G is self.inputs[self.k][1]:
+            self.p_qg[self.k]()
+        elif self.path == "fused":
             self.ops.quant_lowrank(self.G, self.L2, self.B, out=self.V, codes=self.gq[0], scales=self.gq[2],
                                    workspace=self.ws_lr)
         else:
@@ -159,7 +181,7 @@ class Linear:
             o.linear_fwd_op(self.xo["op_rm"], self.xo["op_rm_scales"], self.ro["op_rm"], self.ro["op_rm_scales"],
                             self.T, self.L2, self.B, M, N, K, out=self.Y)
         else:
-            o.linear_fwd(self.xq[0], self.xq[2], self.rq, self.rs_, self.T, self.L2, self.B, M, N, K, out=self.Y)
+            self.p_fwd()
 
     def quant_g(self):
         if self.path == "op":
@@ -176,6 +198,8 @@ class Linear:
             o.linear_bwd_op(self.go["op_rm"], self.go["op_rm_scales"], self.ro["op_cm"], self.ro["op_cm_scales"],
                             self.V, self.L1t, self.At, self.X, self.G, self.T, M, N, K, workspace=self.ws,
                             dX=self.dX, dAt=self.dAt, dB=self.dB)
+        elif self._own_inputs():
+            self.p_bwd[self.k]()
         else:
             o.linear_bwd(self.gq[0], self.gq[2], self.rqc, self.rsct, self.V, self.L1t, self.At, self.X, self.G,
                          self.T, M, N, K, workspace=self.ws, dX=self.dX, dAt=self.dAt, dB=self.dB)
@@ -204,7 +228,7 @@ def time_quantizer(reps, c4):
     own X [18432 x 3072] and dY [18432 x 9216], rotating copies in distinct
     buffers that together exceed the 256 MB MALL; beside it, in the same run, a
     plain streaming kernel over the same buffers with the same 2 : 1 read : write
-    bytes (torch's int16 -> int8 conversion: 2 B read, 1 B written per element)."""
+    bytes (ft_stream_2to1: 2 B read, 1 B written per element)."""
     import torch
     from bit_quantized_lora_amd import ops
     out = {}
@@ -213,7 +237,7 @@ def time_quantizer(reps, c4):
         x0 = dev_bf16(bits)
         xs = [x0] + [x0.clone() for _ in range(ncopies - 1)]
         bufs = [ops.quant_block16(x, rm=True, cm=True) for x in xs]
-        sink = [torch.empty((rows, cols), dtype=torch.int8, device="cuda") for _ in range(ncopies)]
+        sink = [torch.empty((rows, cols), dtype=torch.uint8, device="cuda") for _ in range(ncopies)]
         torch.cuda.synchronize()
         s = torch.cuda.current_stream()
 
@@ -229,7 +253,7 @@ def time_quantizer(reps, c4):
             return e0.elapsed_time(e1) / 1e3 / reps
 
         sec = timed(lambda i: ops.quant_block16(xs[i % ncopies], rm=True, cm=True, out=bufs[i % ncopies]))
-        sec_stream = timed(lambda i: sink[i % ncopies].copy_(xs[i % ncopies].view(torch.int16)))
+        sec_stream = timed(lambda i: ops.stream_2to1(xs[i % ncopies], sink[i % ncopies]))
         elems = rows * cols
         alg_bytes = elems * 2 + elems // 2 * 2 + elems // 256   # bf16 in, two code layouts, E8M0 scales
         out[name] = {"shape": [rows, cols], "us": sec * 1e6, "GBps": alg_bytes / sec / 1e9,

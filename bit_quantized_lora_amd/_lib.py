@@ -62,6 +62,7 @@ _SIGS = {
                           c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_gelu_fwd": [c_void_p, c_int64, c_void_p, c_void_p],
     "ft_gelu_bwd": [c_void_p, c_void_p, c_int64, c_void_p, c_void_p],
+    "ft_stream_2to1": [c_void_p, c_int64, c_void_p, c_void_p],
     "ft_status_str": [c_int32],
 }
 _RESTYPES = {"ft_operand_bytes": c_size_t, "ft_operand_scale_bytes": c_size_t,

@@ -18,3 +18,40 @@ ft_status fill_zero_f32(float* p, int64_t n, hipStream_t s) {
 }
 
 }  // namespace ft
+
+namespace ft {
+namespace {
+// Streaming reference: per element, 2 bytes read and 1 written (the high byte of
+// each 16-bit input), the 2 : 1 read : write ratio of the block quantizer with
+// both code layouts.  Each thread moves 32 input bytes (two 16-byte loads, both
+// issued before either is used) and 16 output bytes per iteration.
+__global__ void __launch_bounds__(256) stream_2to1_kernel(const v4i* __restrict__ in, int64_t n32,
+                                                         v4i* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n32; i += stride) {
+    const v4i a = __builtin_nontemporal_load(in + 2 * i);
+    const v4i b = __builtin_nontemporal_load(in + 2 * i + 1);
+    // high byte of each of the 16 halfwords
+    const uint32_t w0 = __builtin_amdgcn_perm((uint32_t)a.y, (uint32_t)a.x, 0x07050301u);
+    const uint32_t w1 = __builtin_amdgcn_perm((uint32_t)a.w, (uint32_t)a.z, 0x07050301u);
+    const uint32_t w2 = __builtin_amdgcn_perm((uint32_t)b.y, (uint32_t)b.x, 0x07050301u);
+    const uint32_t w3 = __builtin_amdgcn_perm((uint32_t)b.w, (uint32_t)b.z, 0x07050301u);
+    __builtin_nontemporal_store(v4i{(int)w0, (int)w1, (int)w2, (int)w3}, out + i);
+  }
+}
+}  // namespace
+}  // namespace ft
+
+extern "C" ft_status ft_stream_2to1(const void* in, int64_t n, void* out, hipStream_t stream) {
+  using namespace ft;
+  if (n < 0 || n % 16) return FT_ESHAPE;
+  if (n == 0) return FT_OK;
+  if (!in || !out) return FT_EINVAL;
+  if (!aligned16(in) || !aligned16(out)) return FT_EALIGN;
+  const int64_t n32 = n / 16;                      // 16 elements (32 input bytes) per work item
+  int64_t blocks = (n32 + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;        // 16 workgroups of 4 waves per CU, grid-stride beyond
+  hipLaunchKernelGGL(stream_2to1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const v4i*>(in), n32, static_cast<v4i*>(out));
+  return launch_status();
+}

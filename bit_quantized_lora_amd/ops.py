@@ -81,6 +81,34 @@ def _ws(workspace, nbytes: int, dev, name: str = "workspace"):
     return workspace
 
 
+class Prepared:
+    """A library call whose tensors were checked once.  Calling the object issues
+    the same call on the same buffers, on the device's current stream, with no
+    further Python-side checks (for loops that run one step many times).  The
+    tensors it was prepared with are kept alive by the object and must keep their
+    shapes; their contents may change between calls."""
+
+    __slots__ = ("_fn", "_name", "_args", "_dev", "result", "_keep")
+
+    def __init__(self, name: str, args: tuple, dev, result, keep):
+        self._fn = getattr(lib(), name)
+        self._name, self._args, self._dev, self.result, self._keep = name, args, dev, result, keep
+
+    def __call__(self):
+        st = self._fn(*self._args, torch.cuda.current_stream(self._dev).cuda_stream)
+        if st != _lib.FT_OK:
+            raise _lib.FtError(self._name, st)
+        return self.result
+
+
+def _issue(name: str, args: tuple, dev, result, keep, prepare: bool):
+    if prepare:
+        return Prepared(name, args, dev, result, keep)
+    st = getattr(lib(), name)(*args, torch.cuda.current_stream(dev).cuda_stream)
+    check(name, st)
+    return result
+
+
 def quant_block16(x: torch.Tensor, mode: str = "pow2", rm: bool = True, cm: bool = False,
                   out: Optional[Tuple] = None, scales_cm: bool = False):
     """Q(x) for a bf16 [rows, cols] matrix -> (codes_rm, codes_cm, scales), plus
@@ -214,8 +242,9 @@ def lowrank_fused(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor,
 
 def quant_lowrank(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, out: Optional[torch.Tensor] = None,
                   codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
-    """(out, codes_rm, scales): [inp wa^T | inp wb^T] and Q(inp) in one read of inp."""
+                  workspace: Optional[torch.Tensor] = None, prepare: bool = False):
+    """(out, codes_rm, scales): [inp wa^T | inp wb^T] and Q(inp) in one read of inp.
+    With ``prepare`` the checked call is returned as a ``Prepared`` object instead."""
     _need_matrix(inp, "inp")
     M, Kin = inp.shape
     _mult16("quant_lowrank", M, Kin)
@@ -232,11 +261,10 @@ def quant_lowrank(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, out: Op
     _need(scales, torch.uint8, "scales", (M // 16, Kin // 16))
     workspace = _ws(workspace, lowrank_workspace(M, Kin, ra + rb), dev)
     _same_device(inp, wa, wb, out, codes, scales, workspace)
-    st = lib().ft_quant_lowrank(inp.data_ptr(), M, Kin, inp.stride(0), wa.data_ptr(), ra, wb.data_ptr(), rb,
-                                out.data_ptr(), codes.data_ptr(), scales.data_ptr(), workspace.data_ptr(),
-                                workspace.numel(), _stream(inp))
-    check("ft_quant_lowrank", st)
-    return out, codes, scales
+    args = (inp.data_ptr(), M, Kin, inp.stride(0), wa.data_ptr(), ra, wb.data_ptr(), rb, out.data_ptr(),
+            codes.data_ptr(), scales.data_ptr(), workspace.data_ptr(), workspace.numel())
+    return _issue("ft_quant_lowrank", args, inp.device, (out, codes, scales),
+                  (inp, wa, wb, out, codes, scales, workspace), prepare)
 
 
 def gelu_quant_lowrank(y: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, out=None, workspace=None):
@@ -294,8 +322,9 @@ def _sdt(mode: str):
 
 
 def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
-               out_dtype=torch.float32, mode: str = "pow2", out: Optional[torch.Tensor] = None):
-    """Y = deq(Xq) deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B."""
+               out_dtype=torch.float32, mode: str = "pow2", out: Optional[torch.Tensor] = None,
+               prepare: bool = False):
+    """Y = deq(Xq) deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B (``prepare``: return a ``Prepared`` call)."""
     _mult16("linear_fwd", M, N, K)
     gemm = M > 0 and N > 0 and K > 0
     sdt = _sdt(mode)
@@ -310,12 +339,10 @@ def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: in
     odt = _out_dtype(out, "out")
     _need(out, out.dtype, "out", (M, N))
     _same_device(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, out)
-    st = lib().ft_linear_fwd(M, N, K, _MODES[mode], xq_codes.data_ptr(), xq_scales.data_ptr(),
-                             rq_codes.data_ptr(), rq_scales.data_ptr(), T.data_ptr(),
-                             L2.data_ptr(), rs, B.data_ptr(), r, out.data_ptr(), odt,
-                             _stream(T))
-    check("ft_linear_fwd", st)
-    return out
+    args = (M, N, K, _MODES[mode], xq_codes.data_ptr(), xq_scales.data_ptr(), rq_codes.data_ptr(),
+            rq_scales.data_ptr(), T.data_ptr(), L2.data_ptr(), rs, B.data_ptr(), r, out.data_ptr(), odt)
+    return _issue("ft_linear_fwd", args, T.device, out, (xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, out),
+                  prepare)
 
 
 def linear_fwd_gelu(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
@@ -381,8 +408,8 @@ def _bwd_common(V, L1t, At, X, G, T, M, N, K, dX, dAt, dB, out_dtype, x_name="X"
 def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G, T,
                M: int, N: int, K: int, out_dtype=torch.float32, mode: str = "pow2",
                workspace: Optional[torch.Tensor] = None, dX: Optional[torch.Tensor] = None,
-               dAt: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None):
-    """dX, dAt, dB of Eq. 3 and section 3.2 (see include/ft.h)."""
+               dAt: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None, prepare: bool = False):
+    """dX, dAt, dB of Eq. 3 and section 3.2 (see include/ft.h; ``prepare``: return a ``Prepared`` call)."""
     _mult16("linear_bwd", M, N, K)
     gemm = M > 0 and N > 0 and K > 0
     sdt = _sdt(mode)
@@ -393,13 +420,13 @@ def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G,
     _need(rq_scales_cm, sdt, "rq_scales_cm", (K // 16, N // 16), used=gemm)
     workspace = _ws(workspace, linear_bwd_workspace(M, N, K, r), V.device)
     _same_device(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G, T, dX, dAt, dB, workspace)
-    st = lib().ft_linear_bwd(M, N, K, _MODES[mode], gq_codes.data_ptr(), gq_scales.data_ptr(),
-                             rq_codes_cm.data_ptr(), rq_scales_cm.data_ptr(), V.data_ptr(),
-                             L1t.data_ptr(), rs, At.data_ptr(), r, X.data_ptr(), G.data_ptr(),
-                             T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype], dAt.data_ptr(),
-                             dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(V))
-    check("ft_linear_bwd", st)
-    return dX, dAt, dB
+    args = (M, N, K, _MODES[mode], gq_codes.data_ptr(), gq_scales.data_ptr(), rq_codes_cm.data_ptr(),
+            rq_scales_cm.data_ptr(), V.data_ptr(), L1t.data_ptr(), rs, At.data_ptr(), r, X.data_ptr(), G.data_ptr(),
+            T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype], dAt.data_ptr(), dB.data_ptr(), workspace.data_ptr(),
+            workspace.numel())
+    return _issue("ft_linear_bwd", args, V.device, (dX, dAt, dB),
+                  (gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G, T, dX, dAt, dB, workspace),
+                  prepare)
 
 
 def linear_fwd_op(x_op, x_op_scales, r_op, r_op_scales, T, L2, B, M: int, N: int, K: int,
@@ -586,6 +613,18 @@ def linear_bwd_grp(group, gq_codes, gq_scales, rtq_codes, rtq_scales, V, L1t, At
                                  dAt.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(V))
     check("ft_linear_bwd_grp", st)
     return dX, dAt, dB
+
+
+def stream_2to1(x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """Measurement reference: out[i] = high byte of the 16-bit x[i] (2 bytes read,
+    1 written per element; see ft_stream_2to1)."""
+    if x.element_size() != 2:
+        raise ValueError("x must hold 16-bit elements")
+    _need(x, x.dtype, "x")
+    _need(out, torch.uint8, "out", min_numel=x.numel())
+    _same_device(x, out)
+    check("ft_stream_2to1", lib().ft_stream_2to1(x.data_ptr(), x.numel(), out.data_ptr(), _stream(x)))
+    return out
 
 
 def gelu_fwd(y: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -376,6 +376,14 @@ ft_status ft_linear_bwd_grp(int64_t M, int64_t N, int64_t K, int32_t group,
 ft_status ft_gelu_fwd(const void* y, int64_t n, void* h, hipStream_t stream);
 ft_status ft_gelu_bwd(const void* y, const void* dh, int64_t n, void* dy, hipStream_t stream);
 
+/* ft_stream_2to1 -- a measurement reference, not a step of the method: reads n
+ * 16-bit values and writes one byte per value (its high byte), the same 2 : 1
+ * read : write byte ratio as ft_quant_block16 with both code layouts, as plain
+ * streaming with 16-byte accesses.  Its rate is the same-run HBM ceiling the
+ * quantizer is compared with.  in [n] 16-bit, out [n] bytes; n a multiple of 16;
+ * pointers 16-byte aligned. */
+ft_status ft_stream_2to1(const void* in, int64_t n, void* out, hipStream_t stream);
+
 const char* ft_status_str(ft_status s);
 
 #ifdef __cplusplus

@@ -148,3 +148,18 @@ def test_operand_full_size_sampled():
             c, sc = O.quantize_block16(bits[:, 16 * s:16 * s + 16])
             op, osc = O.operand_merge(c.T, sc.T)
             assert np.array_equal(op_cm[16 * s:16 * s + 16], op) and np.array_equal(sc_cm[s], osc[0])
+
+
+def test_stream_reference_kernel():
+    """ft_stream_2to1 (the quantizer's same-run streaming reference) writes the high
+    byte of every 16-bit input."""
+    require_gpu()
+    import torch
+    from bit_quantized_lora_amd import ops
+    rng = np.random.default_rng(5)
+    for n in (16, 4096 + 16, 3 * 1024 * 1024):
+        x = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+        xt = torch.from_numpy(x.view(np.int16)).cuda()
+        out = torch.empty(n, dtype=torch.uint8, device="cuda")
+        ops.stream_2to1(xt, out)
+        assert np.array_equal(host(out), (x >> 8).astype(np.uint8))
