@@ -95,10 +95,10 @@ class Linear:
     low-rank passes.  path "op": the quantizer writes the pair-merged operands
     and the GEMMs read them (a full 32-K fragment per MFMA)."""
 
-    def __init__(self, spec, d, path="op", more_inputs=()):
+    def __init__(self, spec, d, path="op", more_inputs=(), fold_db=False):
         import torch
         from bit_quantized_lora_amd import ops
-        self.ops, self.path = ops, path
+        self.ops, self.path, self.fold_db = ops, path, fold_db and path == "fused"
         M, K, N, rs, r = spec.M, spec.K, spec.N, spec.rs, spec.r
         self.M, self.K, self.N = M, K, N
         u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
@@ -136,12 +136,18 @@ class Linear:
                                         out=self.Y, prepare=True)
             self.p_bwd = [ops.linear_bwd(self.gq[0], self.gq[2], self.rqc, self.rsct, self.V, self.L1t, self.At,
                                          x, g, self.T, M, N, K, workspace=self.ws, dX=self.dX, dAt=self.dAt,
-                                         dB=self.dB, prepare=True) for x, g in self.inputs]
+                                         dB=self.dB, prepare=True, skip_dB=self.fold_db) for x, g in self.inputs]
         if path == "fused":
             self.p_qx = [ops.quant_lowrank(x, self.L1t, self.At, out=self.T, codes=self.xq[0], scales=self.xq[2],
                                            workspace=self.ws_lr, prepare=True) for x, _ in self.inputs]
-            self.p_qg = [ops.quant_lowrank(g, self.L2, self.B, out=self.V, codes=self.gq[0], scales=self.gq[2],
-                                           workspace=self.ws_lr, prepare=True) for _, g in self.inputs]
+            if self.fold_db:   # dB = (X A)^T G taken in the pass over G
+                self.ws_db = e((ops.quant_lowrank_db_workspace(M, N, rs + r, r),), u8)
+                self.p_qg = [ops.quant_lowrank_db(g, self.L2, self.B, self.T, out=self.V, codes=self.gq[0],
+                                                  scales=self.gq[2], dB=self.dB, workspace=self.ws_db, prepare=True)
+                             for _, g in self.inputs]
+            else:
+                self.p_qg = [ops.quant_lowrank(g, self.L2, self.B, out=self.V, codes=self.gq[0], scales=self.gq[2],
+                                               workspace=self.ws_lr, prepare=True) for _, g in self.inputs]
 
     def _own_inputs(self):
         return self.X is self.inputs[self.k][0] and self.G is self.inputs[self.k][1]
@@ -487,6 +493,41 @@ def time_separate_passes(spec, d, more, steps, warmup, one_pass_us):
             "speedup": round(us / one_pass_us, 3)}
 
 
+def time_db_fold(spec, d, more, steps, warmup, default_us):
+    """The same linear step with dB = (X A)^T G folded into the backward's pass
+    over G (ft_quant_lowrank_db, then ft_linear_bwd without its dB pass) against
+    the default, where dB is a separate pass over G on the side stream beside the
+    dX GEMM."""
+    import torch
+    lin = Linear(spec, d, "fused", more, fold_db=True)
+    for _ in range(warmup):
+        lin.step()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        lin.step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    # the G pass alone, each way
+    ph = {}
+    for name, fn in (("g_pass_with_db", lin.quant_lowrank_g),):
+        for _ in range(3):
+            fn()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(s)
+        for _ in range(steps):
+            fn()
+        g1.record(s)
+        g1.synchronize()
+        ph[name] = round(g0.elapsed_time(g1) * 1e3 / steps, 2)
+    del lin
+    return {"step_us_default_side_stream_dB": round(default_us, 2), "step_us_dB_in_G_pass": round(us, 2),
+            "speedup": round(default_us / us, 3), **ph}
+
+
 def lowrank_pass_rates(spec, phases):
     """HBM roofline of the one-pass quantize + down-projection (in the step's
     phase times, split sum included): algorithmic bytes = bf16 input read, E2M1
@@ -798,6 +839,8 @@ def main():
 
     separate = (time_separate_passes(spec, d, more, args.steps, args.warmup, ms_step * 1e3)
                 if args.path == "fused" else None)
+    db_fold = (time_db_fold(spec, d, more, args.steps, args.warmup, ms_step * 1e3)
+               if args.path == "fused" else None)
     mlp_fusion = time_mlp_fc1_fusion(lin, args.steps)
     precision = time_precision_variants(lin, args.steps)
     granularity = time_granularity(lin, args.steps)
@@ -857,6 +900,7 @@ def main():
         "granularity": granularity,
         "quant_lowrank_pass": lowrank_pass_rates(spec, phases),
         "one_pass_vs_separate": separate,
+        "dB_in_G_pass_vs_side_stream": db_fold,
         "configs": configs,
         "quant_GBps": round(quant["dY"]["GBps"], 1),
         "quant_frac_hbm": round(quant["dY"]["GBps"] / HBM_PEAK_GBPS, 4),

@@ -29,6 +29,9 @@ _SIGS = {
     "ft_lowrank_workspace": [c_int64, c_int64, c_int32],
     "ft_quant_lowrank": [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "ft_quant_lowrank_db": [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
+                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
+    "ft_quant_lowrank_db_workspace": [c_int64, c_int64, c_int32, c_int32],
     "ft_gelu_quant_lowrank": [c_void_p, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_linear_fwd": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -65,7 +68,7 @@ _SIGS = {
     "ft_stream_2to1": [c_void_p, c_int64, c_void_p, c_void_p],
     "ft_status_str": [c_int32],
 }
-_RESTYPES = {"ft_operand_bytes": c_size_t, "ft_operand_scale_bytes": c_size_t,
+_RESTYPES = {"ft_operand_bytes": c_size_t, "ft_quant_lowrank_db_workspace": c_size_t, "ft_operand_scale_bytes": c_size_t,
              "ft_linear_bwd_workspace": c_size_t, "ft_lowrank_workspace": c_size_t, "ft_status_str": c_char_p}
 
 _lib = None

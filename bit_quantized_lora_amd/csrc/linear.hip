@@ -171,7 +171,7 @@ ft_status linear_bwd_impl(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
   if (M && K && !dX) return FT_EINVAL;
   if (M && N && K && (!gq_codes || !gq_scales || !rq_codes_cm || !rq_scales_cm)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
-  if ((rs && K && !L1t) || (r && ((K && (!At || !dAt)) || (N && !dB)))) return FT_EINVAL;
+  if ((rs && K && !L1t) || (r && K && (!At || !dAt))) return FT_EINVAL;   // dB may be NULL: not computed
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   const void* ptrs[] = {gq_codes, rq_codes_cm, V, L1t, At, X, G, T, dX, dAt, dB, workspace};
@@ -270,7 +270,7 @@ ft_status adapter_grads(int64_t M, int64_t N, int64_t K, const float* V, int rs,
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const size_t wa = align256(lora_grad_workspace(M, K, r));
   ft_status st = launch_lora_grad(V, rho, rs, r, static_cast<const uint16_t*>(X), M, K, dAt, ws, stream);
-  if (st != FT_OK) return st;
+  if (st != FT_OK || !dB) return st;   // dB NULL: taken in the G pass (ft_quant_lowrank_db)
   return launch_lora_grad(T, rho, rs, r, static_cast<const uint16_t*>(G), M, N, dB, ws + wa, stream);
 }
 }  // namespace
@@ -318,7 +318,7 @@ extern "C" ft_status ft_linear_bwd_op(int64_t M, int64_t N, int64_t K, const uin
   if (M && K && !dX) return FT_EINVAL;
   if (M && N && K && (!g_op || !g_op_scales || !rt_op || !rt_op_scales)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
-  if ((rs && K && !L1t) || (r && ((K && (!At || !dAt)) || (N && !dB)))) return FT_EINVAL;
+  if ((rs && K && !L1t) || (r && K && (!At || !dAt))) return FT_EINVAL;   // dB may be NULL: not computed
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   const void* ptrs[] = {g_op, g_op_scales, rt_op, rt_op_scales, V, L1t, At, X, G, T, dX, dAt, dB, workspace};
@@ -387,7 +387,7 @@ extern "C" ft_status ft_linear_bwd_g16(int64_t M, int64_t N, int64_t K, const vo
   if (M && K && !dX) return FT_EINVAL;
   if (M && N && K && (!G || !rq_codes_cm || !rq_scales_cm)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
-  if ((rs && K && !L1t) || (r && ((K && (!At || !dAt)) || (N && !dB)))) return FT_EINVAL;
+  if ((rs && K && !L1t) || (r && K && (!At || !dAt))) return FT_EINVAL;   // dB may be NULL: not computed
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   const void* ptrs[] = {G, rq_codes_cm, rq_scales_cm, V, L1t, At, X, T, dX, dAt, dB, workspace};
@@ -460,7 +460,7 @@ extern "C" ft_status ft_linear_bwd_grp(int64_t M, int64_t N, int64_t K, int32_t 
   if (M && K && !dX) return FT_EINVAL;
   if (M && N && K && (!gq_codes || !gq_scales || !rtq_codes || !rtq_scales)) return FT_EINVAL;
   if (M && rho && !V) return FT_EINVAL;
-  if ((rs && K && !L1t) || (r && ((K && (!At || !dAt)) || (N && !dB)))) return FT_EINVAL;
+  if ((rs && K && !L1t) || (r && K && (!At || !dAt))) return FT_EINVAL;   // dB may be NULL: not computed
   if (r && M && ((K && !X) || (N && !G) || !T)) return FT_EINVAL;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   const void* ptrs[] = {gq_codes, gq_scales, rtq_codes, rtq_scales, V, L1t, At, X, G, T, dX, dAt, dB, workspace};

@@ -25,6 +25,15 @@
 // 16 lanes of the other wave half, so its maximum is a 16-lane DPP reduction and
 // one permlane32 swap across the halves.
 //
+// ft_quant_lowrank_db also takes the LoRA gradient dB = (X A)^T G (section 3.2)
+// from the same registers in the backward's pass over G: the workgroup's
+// 128 x 128 chunk of G goes to LDS row-major and comes back token-major through
+// transposing reads (ds_read_b64_tr_b16), each wave multiplying (X A)^T of the
+// workgroup's 128 tokens (from the forward's T, split into bf16 hi + lo like the
+// GEMM epilogue's low-rank term) with 32 of the chunk's columns on bf16 MFMA.
+// Each row block writes its partial dB for its columns; a second pass adds the
+// row blocks in a fixed order.
+//
 // ft_gelu_quant_lowrank puts the activation between an MLP's two linears in
 // front of that pass (FourTune section 3.3 "MLP Fusion": the intermediate is
 // not read back by a separate kernel): the first linear's output Y is read,
@@ -63,6 +72,8 @@ __device__ __forceinline__ uint32_t from_other_half(uint32_t v, int lh) {
 }
 
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
 // largest magnitude (as bf16 bits; magnitude order = integer order) of 8 bf16
@@ -92,15 +103,28 @@ int64_t num_splits(int64_t M, int64_t Kin) {
   return (nchunks + cps - 1) / cps;
 }
 
+// dB partials of ft_quant_lowrank_db: the forward's T (fp32 [M x ldt], its LoRA
+// columns from toff), the adapter rank r (1..64), partials [row blocks][r][Kin]
+struct DbArgs {
+  const float* T;
+  int64_t ldt;
+  int toff, r;
+  float* part;
+};
+
+constexpr int DB_GPITCH = 2 * LR_CHUNK + 16;   // bytes per LDS row of the staged G chunk (conflict-free tr reads)
+
 // NCT: 32-wide rank column tiles (0..4); QUANT: also write Q(in); GELU: the
-// input is replaced by GELU(in) (written to hout [M x Kin]) before both
-template <int NCT, bool QUANT, bool GELU = false>
+// input is replaced by GELU(in) (written to hout [M x Kin]) before both; NDB:
+// 32-row tiles of the dB partials (0: none; 1 for r <= 32, 2 for r <= 64)
+template <int NCT, bool QUANT, bool GELU = false, int NDB = 0>
 __global__ void __launch_bounds__(LR_THREADS)
 lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t ld_in,
                const uint16_t* __restrict__ wa, int ra, const uint16_t* __restrict__ wb, int rb,
                int64_t cps, float* __restrict__ out, int64_t out_split_stride,
-               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ hout) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t s_w[];   // 2 buffers of rho rows
+               uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ hout,
+               DbArgs db) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t s_w[];   // 2 buffers of rho rows (+ dB staging)
   const int wbuf_bytes = (ra + rb) * LR_WROW;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -247,6 +271,69 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) acc[ct] = v16f{};
 
+  // dB: (X A)^T of this workgroup's 128 tokens as bf16 hi + lo planes [32 NDB][128]
+  // in LDS after the weight buffers, then the G chunk [128][128] (pitch DB_GPITCH)
+  uint8_t* s_t = s_w + 2 * wbuf_bytes;
+  uint8_t* s_g = s_t + 2 * 32 * NDB * LR_ROWS * 2;
+  if constexpr (NDB > 0) {
+    for (int e = threadIdx.x; e < 32 * NDB * LR_ROWS; e += LR_THREADS) {
+      const int j = e / LR_ROWS, m = e - j * LR_ROWS;
+      const int64_t row = row0 + m;
+      const float v = (j < db.r && row < M) ? db.T[row * db.ldt + db.toff + j] : 0.0f;
+      uint32_t h, l;
+      split_bf16(v, h, l);
+      reinterpret_cast<uint16_t*>(s_t)[e] = (uint16_t)h;
+      reinterpret_cast<uint16_t*>(s_t)[32 * NDB * LR_ROWS + e] = (uint16_t)l;
+    }
+  }
+
+  // dB partial of chunk c: wave w takes the chunk's columns 32 w .. 32 w + 31 and
+  // reduces over the workgroup's 128 tokens (8 k-steps of 16), A = (X A)^T hi and
+  // lo from LDS, B = the G tile read token-major by transposing LDS reads; the
+  // [r x 32] result goes to this row block's partial.  The tile was written by
+  // all four waves, so a barrier comes first; the next chunk's barrier keeps it
+  // intact until every wave has read it.
+  auto dbp_chunk = [&](int64_t c) {
+    if constexpr (NDB > 0) {
+      // every wave's LDS writes of the tile visible; the next chunk's loads stay in flight
+      compiler_fence();
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt and expcnt unconstrained
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      const int g16 = lane >> 4, s16 = lane & 15;
+      const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);
+      const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);
+      v16f dacc[NDB];
+#pragma unroll
+      for (int t = 0; t < NDB; ++t) dacc[t] = v16f{};
+#pragma unroll
+      for (int ks = 0; ks < LR_ROWS / 16; ++ks) {
+        const uint8_t* b0 = s_g + (16 * ks + tr_row) * DB_GPITCH + 2 * (32 * wave + tr_col);
+        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0));
+        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + 4 * DB_GPITCH));
+        const v2i l2 = __builtin_bit_cast(v2i, lo4), h2 = __builtin_bit_cast(v2i, hi4);
+        const v8bf bq = __builtin_bit_cast(v8bf, v4i{l2.x, l2.y, h2.x, h2.y});
+#pragma unroll
+        for (int t = 0; t < NDB; ++t) {
+          const int e = (32 * t + l32) * LR_ROWS + 16 * ks + 8 * lh;
+          const v4i ah = *reinterpret_cast<const v4i*>(s_t + 2 * e);
+          const v4i al = *reinterpret_cast<const v4i*>(s_t + 2 * (32 * NDB * LR_ROWS + e));
+          dacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah), bq, dacc[t], 0, 0, 0);
+          dacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al), bq, dacc[t], 0, 0, 0);
+        }
+      }
+      const int64_t col = c * LR_CHUNK + 32 * wave + l32;
+      float* prow = db.part + (int64_t)blockIdx.x * db.r * Kin;
+#pragma unroll
+      for (int t = 0; t < NDB; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = 32 * t + 8 * (i >> 2) + 4 * lh + (i & 3);
+          if (j < db.r && col < Kin) prow[(int64_t)j * Kin + col] = dacc[t][i];
+        }
+    }
+  };
+
   // one chunk: wait for its DMA and loads, free the other buffer, start the next
   // chunk's loads into xn, then quantize and project xc (the two register sets
   // alternate, so nothing is copied between chunks)
@@ -262,6 +349,11 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       load_x(xn, c + 1);
     }
     if constexpr (GELU) gelu_chunk(xc, c);
+    if constexpr (NDB > 0) {   // this wave's 32 rows of the chunk into the LDS tile, row-major
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        *reinterpret_cast<v4i*>(s_g + (32 * wave + l32) * DB_GPITCH + (16 * s + 8 * lh) * 2) = xc[s];
+    }
     if constexpr (QUANT) quantize_chunk(xc, c);
     const uint8_t* wbuf = s_w + buf * wbuf_bytes;
 #pragma unroll
@@ -274,6 +366,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
                                                           __builtin_bit_cast(v8bf, b), acc[ct], 0, 0, 0);
       }
     }
+    if constexpr (NDB > 0) dbp_chunk(c);
   };
   v4i xa[8], xb[8];
   if (c_begin < c_end) {
@@ -323,9 +416,12 @@ extern "C" size_t ft_lowrank_workspace(int64_t M, int64_t Kin, int32_t rho) {
 
 namespace ft {
 namespace {
+int64_t row_blocks(int64_t M) { return (M + LR_ROWS - 1) / LR_ROWS; }
+
 ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, const void* wa, int32_t ra,
                        const void* wb, int32_t rb, float* out, uint8_t* codes, uint8_t* scales, void* workspace,
-                       size_t ws_bytes, hipStream_t stream, void* hout = nullptr) {
+                       size_t ws_bytes, hipStream_t stream, void* hout = nullptr, const DbArgs* dbp = nullptr,
+                       float* dB = nullptr) {
   if (!mult16(M) || !mult16(Kin) || ld_in < Kin) return FT_ESHAPE;
   if (ra < 0 || rb < 0 || (ra % 16) || (rb % 16) || ra + rb > 128) return FT_ESHAPE;
   const int rho = ra + rb;
@@ -338,9 +434,16 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   if (hout && !aligned16(hout)) return FT_EALIGN;
   if (Kin == 0) return rho ? fill_zero_f32(out, M * rho, stream) : FT_OK;  // empty reduction
   if ((int64_t)rho * Kin * 2 >= ((int64_t)1 << 31)) return FT_ESHAPE;
-  const size_t need = rho ? ft_lowrank_workspace(M, Kin, rho) : 0;
+  const size_t need_v = rho ? ft_lowrank_workspace(M, Kin, rho) : 0;
+  const size_t off_db = (need_v + 255) & ~(size_t)255;
+  const size_t need = dbp ? off_db + (size_t)row_blocks(M) * dbp->r * Kin * sizeof(float) : need_v;
   if (need && (!workspace || ws_bytes < need)) return workspace ? FT_ESPACE : FT_EINVAL;
   if (need && !aligned16(workspace)) return FT_EALIGN;
+  DbArgs db{};
+  if (dbp) {
+    db = *dbp;
+    db.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_db);
+  }
   const int64_t cps = chunks_per_split(M, Kin);
   const int64_t S = num_splits(M, Kin);
   float* dst = (S > 1 && rho) ? static_cast<float*>(workspace) : out;
@@ -353,11 +456,28 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   uint16_t* hp = static_cast<uint16_t*>(hout);
 #define FT_LR_LAUNCH(N, Q)                                                                                   \
   hipLaunchKernelGGL((lowrank_kernel<N, Q>), grid, dim3(LR_THREADS), (size_t)(2 * rho * LR_WROW), stream, ip, M, Kin, ld_in, a, ra, b, rb, \
-                     cps, dst, stride, codes, scales, hp)
+                     cps, dst, stride, codes, scales, hp, db)
 #define FT_LRG_LAUNCH(N)                                                                                     \
   hipLaunchKernelGGL((lowrank_kernel<N, true, true>), grid, dim3(LR_THREADS), (size_t)(2 * rho * LR_WROW), stream, ip, M, Kin, ld_in, a, ra, \
-                     b, rb, cps, dst, stride, codes, scales, hp)
-  if (hout) {
+                     b, rb, cps, dst, stride, codes, scales, hp, db)
+  // dB partials: + (X A)^T hi/lo planes and the staged G chunk
+#define FT_LRD_LAUNCH(N, D)                                                                                  \
+  hipLaunchKernelGGL((lowrank_kernel<N, true, false, D>), grid, dim3(LR_THREADS),                          \
+                     (size_t)(2 * rho * LR_WROW + 2 * 32 * D * LR_ROWS * 2 + LR_ROWS * DB_GPITCH), stream, ip, M, Kin, \
+                     ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db)
+  if (dbp) {
+    const int ndb = (db.r + 31) / 32;
+#define FT_LRD_SWITCH(D)                        \
+    switch (nct) {                              \
+      case 0: FT_LRD_LAUNCH(0, D); break;       \
+      case 1: FT_LRD_LAUNCH(1, D); break;       \
+      case 2: FT_LRD_LAUNCH(2, D); break;       \
+      case 3: FT_LRD_LAUNCH(3, D); break;       \
+      default: FT_LRD_LAUNCH(4, D); break;      \
+    }
+    if (ndb == 1) { FT_LRD_SWITCH(1) } else { FT_LRD_SWITCH(2) }
+#undef FT_LRD_SWITCH
+  } else if (hout) {
     switch (nct) {
       case 0: FT_LRG_LAUNCH(0); break;
       case 1: FT_LRG_LAUNCH(1); break;
@@ -383,10 +503,17 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   }
 #undef FT_LR_LAUNCH
 #undef FT_LRG_LAUNCH
+#undef FT_LRD_LAUNCH
   if (launch_status() != FT_OK) return FT_EHIP;
   if (S > 1 && rho) {
     hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((stride / 4 + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float*>(workspace), S, stride, out);
+    if (launch_status() != FT_OK) return FT_EHIP;
+  }
+  if (dbp) {   // dB = the row blocks' partials added in row-block order
+    const int64_t n = (int64_t)db.r * Kin;
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const float*>(db.part), row_blocks(M), n, dB);
     return launch_status();
   }
   return FT_OK;
@@ -415,4 +542,32 @@ extern "C" ft_status ft_gelu_quant_lowrank(const void* y, int64_t M, int64_t Kin
   if (Kin == 0 || M == 0) return ft::lowrank_impl(y, M, Kin, Kin, wa, ra, wb, rb, out, codes_rm, scales, workspace,
                                                   ws_bytes, stream);
   return ft::lowrank_impl(y, M, Kin, Kin, wa, ra, wb, rb, out, codes_rm, scales, workspace, ws_bytes, stream, h);
+}
+
+extern "C" size_t ft_quant_lowrank_db_workspace(int64_t M, int64_t Kin, int32_t rho, int32_t r) {
+  using namespace ft;
+  if (M <= 0 || Kin <= 0 || rho < 0 || r < 0) return 0;
+  const size_t v = rho ? ft_lowrank_workspace(M, Kin, rho) : 0;
+  return ((v + 255) & ~(size_t)255) + (size_t)row_blocks(M) * r * Kin * sizeof(float);
+}
+
+extern "C" ft_status ft_quant_lowrank_db(const void* g, int64_t M, int64_t N, int64_t ld_g, const void* L2, int32_t rs,
+                                         const void* B, int32_t r, float* V, uint8_t* codes_rm, uint8_t* scales,
+                                         const float* T, float* dB, void* workspace, size_t ws_bytes,
+                                         hipStream_t stream) {
+  using namespace ft;
+  if (!codes_rm || !scales) return FT_EINVAL;
+  if (r < 0 || r > 64 || r % 16 || rs < 0 || rs % 16 || rs + r > 128) return FT_ESHAPE;
+  if (r == 0 || M == 0 || N == 0) {   // no adapter gradient to fold in (or an empty one)
+    if (r && N && dB) {
+      const ft_status z = fill_zero_f32(dB, (int64_t)r * N, stream);
+      if (z != FT_OK) return z;
+    }
+    return lowrank_impl(g, M, N, ld_g, L2, rs, B, r, V, codes_rm, scales, workspace, ws_bytes, stream);
+  }
+  if (!T || !dB) return FT_EINVAL;
+  if (!aligned16(T) || !aligned16(dB)) return FT_EALIGN;
+  DbArgs db{T, (int64_t)(rs + r), rs, r, nullptr};
+  return lowrank_impl(g, M, N, ld_g, L2, rs, B, r, V, codes_rm, scales, workspace, ws_bytes, stream, nullptr, &db,
+                      dB);
 }

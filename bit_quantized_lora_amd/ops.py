@@ -267,6 +267,42 @@ def quant_lowrank(inp: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, out: Op
                   (inp, wa, wb, out, codes, scales, workspace), prepare)
 
 
+def quant_lowrank_db_workspace(M: int, Kin: int, rho: int, r: int) -> int:
+    return int(lib().ft_quant_lowrank_db_workspace(M, Kin, rho, r))
+
+
+def quant_lowrank_db(g: torch.Tensor, L2: torch.Tensor, B: torch.Tensor, T: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, prepare: bool = False):
+    """(V, codes_rm, scales, dB): the backward's pass over G with dB = T[:, rs:]^T G
+    folded in (T: the forward's [M, rs + r]).  ``prepare``: return a ``Prepared`` call."""
+    _need_matrix(g, "g")
+    M, N = g.shape
+    _mult16("quant_lowrank_db", M, N)
+    rs, r = _factors(L2, B, N, names=("L2", "B"))
+    dev = g.device
+    if out is None:
+        out = torch.empty((M, rs + r), dtype=torch.float32, device=dev)
+    if codes is None:
+        codes = torch.empty((M, N // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((M // 16, N // 16), dtype=torch.uint8, device=dev)
+    if dB is None:
+        dB = torch.empty((r, N), dtype=torch.float32, device=dev)
+    _need(out, torch.float32, "out", (M, rs + r))
+    _need(codes, torch.uint8, "codes", (M, N // 2))
+    _need(scales, torch.uint8, "scales", (M // 16, N // 16))
+    _need(T, torch.float32, "T", (M, rs + r))
+    _need(dB, torch.float32, "dB", (r, N))
+    workspace = _ws(workspace, quant_lowrank_db_workspace(M, N, rs + r, r), dev)
+    _same_device(g, L2, B, T, out, codes, scales, dB, workspace)
+    args = (g.data_ptr(), M, N, g.stride(0), L2.data_ptr(), rs, B.data_ptr(), r, out.data_ptr(), codes.data_ptr(),
+            scales.data_ptr(), T.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel())
+    return _issue("ft_quant_lowrank_db", args, dev, (out, codes, scales, dB),
+                  (g, L2, B, T, out, codes, scales, dB, workspace), prepare)
+
+
 def gelu_quant_lowrank(y: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, out=None, workspace=None):
     """h = GELU(y), Q(h) and [h wa^T | h wb^T] from one read of y:
     returns (h, T, codes, scales)."""
@@ -408,8 +444,10 @@ def _bwd_common(V, L1t, At, X, G, T, M, N, K, dX, dAt, dB, out_dtype, x_name="X"
 def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G, T,
                M: int, N: int, K: int, out_dtype=torch.float32, mode: str = "pow2",
                workspace: Optional[torch.Tensor] = None, dX: Optional[torch.Tensor] = None,
-               dAt: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None, prepare: bool = False):
-    """dX, dAt, dB of Eq. 3 and section 3.2 (see include/ft.h; ``prepare``: return a ``Prepared`` call)."""
+               dAt: Optional[torch.Tensor] = None, dB: Optional[torch.Tensor] = None, prepare: bool = False,
+               skip_dB: bool = False):
+    """dX, dAt, dB of Eq. 3 and section 3.2 (see include/ft.h; ``prepare``: return a ``Prepared`` call).
+    ``skip_dB``: dB is not computed (it was taken in the pass over G by quant_lowrank_db); dB is returned as None."""
     _mult16("linear_bwd", M, N, K)
     gemm = M > 0 and N > 0 and K > 0
     sdt = _sdt(mode)
@@ -422,9 +460,9 @@ def linear_bwd(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G,
     _same_device(gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G, T, dX, dAt, dB, workspace)
     args = (M, N, K, _MODES[mode], gq_codes.data_ptr(), gq_scales.data_ptr(), rq_codes_cm.data_ptr(),
             rq_scales_cm.data_ptr(), V.data_ptr(), L1t.data_ptr(), rs, At.data_ptr(), r, X.data_ptr(), G.data_ptr(),
-            T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype], dAt.data_ptr(), dB.data_ptr(), workspace.data_ptr(),
-            workspace.numel())
-    return _issue("ft_linear_bwd", args, V.device, (dX, dAt, dB),
+            T.data_ptr(), dX.data_ptr(), _OUT[dX.dtype], dAt.data_ptr(), None if skip_dB else dB.data_ptr(),
+            workspace.data_ptr(), workspace.numel())
+    return _issue("ft_linear_bwd", args, V.device, (dX, dAt, None if skip_dB else dB),
                   (gq_codes, gq_scales, rq_codes_cm, rq_scales_cm, V, L1t, At, X, G, T, dX, dAt, dB, workspace),
                   prepare)
 

@@ -164,6 +164,27 @@ ft_status ft_quant_lowrank(const void* in, int64_t M, int64_t Kin, int64_t ld_in
                            uint8_t* codes_rm, uint8_t* scales, void* workspace, size_t ws_bytes,
                            hipStream_t stream);
 
+/* ft_quant_lowrank_db -- the backward's pass over G with the LoRA gradient
+ * folded in (section 3.3 "LoRA Fusion": every branch reads the same G; section
+ * 3.2: dB = (X A)^T G).  From one read of g = G [M x N]:
+ *
+ *   V      = [G L2^T | G B^T]           (as ft_quant_lowrank with wa = L2, wb = B)
+ *   Q(G)   codes_rm + scales            (as ft_quant_lowrank)
+ *   dB     = T[:, rs:rs+r]^T G          (T: the forward's [X L1 | X A], [M x (rs+r)])
+ *
+ *  g bf16 [M x N], leading dimension ld_g; L2 [rs x N], B [r x N] bf16; V float
+ *  [M x (rs+r)]; T float [M x (rs+r)]; dB float [r x N]; r <= 64.
+ *  workspace  at least ft_quant_lowrank_db_workspace(M, N, rs + r, r) bytes: the
+ *             V reduction's partials and one dB partial per 128-token block,
+ *             added in block order (deterministic).
+ * V, codes and scales equal ft_quant_lowrank's bit for bit; dB is the same sum
+ * as ft_linear_bwd's in another order (fp32, equal to within rounding).  Follow
+ * it with ft_linear_bwd(..., dB = NULL, ...). */
+ft_status ft_quant_lowrank_db(const void* g, int64_t M, int64_t N, int64_t ld_g, const void* L2, int32_t rs,
+                              const void* B, int32_t r, float* V, uint8_t* codes_rm, uint8_t* scales,
+                              const float* T, float* dB, void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t ft_quant_lowrank_db_workspace(int64_t M, int64_t N, int32_t rho, int32_t r);
+
 /* ft_gelu_quant_lowrank -- the MLP fusion of section 3.3 ("MLP Fusion": the
  * activation and the second linear's input quantization go with a pass the
  * intermediate already makes, so it is not read back by separate kernels),
@@ -213,7 +234,8 @@ ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
  *  V            float [M x (rs+r)] from ft_lowrank_fused(G, L2, B)
  *  L1t [rs x K], At [r x K] bf16
  *  X  bf16 [M x K], G bf16 [M x N] (unquantized), T float [M x (rs+r)] (forward)
- *  dX [M x K] float or bf16; dAt float [r x K]; dB float [r x N]
+ *  dX [M x K] float or bf16; dAt float [r x K]; dB float [r x N], or NULL to
+ *     skip dB (a caller that took it in the pass over G, ft_quant_lowrank_db)
  *  workspace  device scratch of at least ft_linear_bwd_workspace(M, N, K, r)
  *             bytes (partial sums of the reductions over M). */
 ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,

@@ -297,3 +297,30 @@ def test_op_path_with_unmerged_pairs_in_both_operands(shape):
     ref = _gpu_linear(d, path="codes")
     for k in ("Y", "dX", "dA", "dB"):
         assert O.rel_frob(host(gpu[k]), host(ref[k]).astype(np.float64)) < 1e-5
+
+
+@pytest.mark.parametrize("case", [(144, 400, 16, 16), (528, 1040, 32, 32), (272, 256, 0, 64), (4608, 12288, 32, 16),
+                                  (48, 128, 64, 64)], ids=lambda c: "x".join(map(str, c)))
+def test_quant_lowrank_db_folds_the_adapter_gradient(case):
+    """The backward's pass over G with dB = (X A)^T G folded in: V, codes and scales
+    bit-identical to ft_quant_lowrank; dB within fp32 rounding of the separate
+    adapter-gradient pass of ft_linear_bwd and of the oracle's fp64 product."""
+    require_gpu()
+    import torch
+    from bit_quantized_lora_amd import ops
+    M, N, rs, r = case
+    rng = np.random.default_rng(M + N + r)
+    G = synth.f32_to_bf16_bits(synth.make_tensor(rng, (M, N), "normal", 1e-3))
+    L2 = synth.f32_to_bf16_bits(synth.make_tensor(rng, (rs, N), "normal", 0.05))
+    B = synth.f32_to_bf16_bits(synth.make_tensor(rng, (r, N), "normal", 0.01))
+    T = synth.make_tensor(rng, (M, rs + r), "t3").astype(np.float32)
+    say(f"[quant-lowrank-db] M={M} N={N} rs={rs} r={r}")
+    g, l2, b = dev_bf16(G), dev_bf16(L2), dev_bf16(B)
+    t = torch.from_numpy(T).cuda()
+    V, codes, scales, dB = ops.quant_lowrank_db(g, l2, b, t)
+    V0, codes0, scales0 = ops.quant_lowrank(g, l2, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(V).view(np.uint32), host(V0).view(np.uint32))
+    assert np.array_equal(host(codes), host(codes0)) and np.array_equal(host(scales), host(scales0))
+    ref = T[:, rs:].astype(np.float64).T @ O.bf16_to_f64(G)
+    assert O.rel_frob(host(dB).astype(np.float64), ref) < 1e-5
