@@ -696,17 +696,21 @@ def time_configs(reps, cache, oracle_rows=128):
 
 
 def gpu_clock_mhz():
-    """Current and maximum graphics clock of GPU 0 in MHz (None when unavailable)."""
+    """Current and maximum graphics clock (MHz) of the GPU this process runs on,
+    found among the node's GPUs by its PCI address (None when unavailable)."""
     try:
         import amdsmi
+        import torch
+        p = torch.cuda.get_device_properties(torch.cuda.current_device())
+        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
         amdsmi.amdsmi_init()
         try:
-            h = amdsmi.amdsmi_get_processor_handles()[0]
+            h = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
             info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-            return {"cur": info.get("clk"), "max": info.get("max_clk")}
+            return {"cur": info.get("clk"), "max": info.get("max_clk"), "bdf": bdf}
         finally:
             amdsmi.amdsmi_shut_down()
-    except Exception:  # pragma: no cover - tool missing or no permission
+    except Exception:  # pragma: no cover - tool missing, no permission, or no match
         return None
 
 
@@ -787,21 +791,24 @@ def main():
 
     # clocks settle over a fixed stretch of steps before the counted warm-up
     warm = prewarm(lin.step, args.prewarm_ms)
-    clk_before = gpu_clock_mhz()
     for _ in range(args.warmup):
         lin.step()
     torch.cuda.synchronize()
 
-    # timed region: exactly `steps` steps, no event inside it
+    # timed region: exactly `steps` steps, no event inside it.  The graphics clock
+    # is read while the GPU works through them (after the last step is enqueued,
+    # before the synchronize), and the host's enqueue time is recorded.
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(s)
+    h0 = time.perf_counter()
     for i in range(args.steps):
         lin.step()
+    host_timed_us = (time.perf_counter() - h0) / args.steps * 1e6
     t_end.record(s)
+    clk_during = gpu_clock_mhz()
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    clk_after = gpu_clock_mhz()
 
     # per-phase breakdown: events between the phases over `steps` further steps,
     # enqueued back to back so the GPU never waits for the host
@@ -889,10 +896,11 @@ def main():
                      "avg_launch_us_in_step": round(gemm_ms * 1e3, 2)},
         "timed_vs_marker_p50": round(ms_step * 1e3 / step_pct["p50"], 4),
         "prewarm": warm,
-        "gfx_clock_mhz": {"before_timed": clk_before, "after_timed": clk_after},
+        "gfx_clock_mhz_during_timed": clk_during,
         "phases_us": {k: round(v, 2) for k, v in phases.items()},
         "step_us_percentiles": step_pct,
-        "host_enqueue_us_per_step": round(host_us, 1),
+        "host_enqueue_us_per_step": round(host_timed_us, 1),
+        "host_enqueue_us_per_step_with_phase_markers": round(host_us, 1),
         "quantizer": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in quant.items()},
         "mlp_fc1_fusion_us": mlp_fusion,

@@ -33,10 +33,11 @@
 namespace ft {
 namespace {
 
-constexpr int QT = 128;                 // tile edge (elements)
-constexpr int QTHREADS = 256;
-constexpr int RM_PITCH = QT / 2 + 8;    // bytes per LDS row-major code row (padded)
-constexpr int CM_PITCH = QT / 2 + 8;    // bytes per LDS column-major code row (padded)
+// Tile edge: 128 (4 waves) when the pair-merged operands are written (one
+// 128-wide operand group per tile), else 256 (8 waves): a 256-wide tile row of
+// codes is one whole 128-byte line in both code layouts, so no line is written
+// in halves by two workgroups.
+constexpr int QT = 128;                 // tile edge of the operand-writing instances (elements)
 constexpr int OP_GROUP_BYTES = 96;      // operand bytes per row per 128 reduction elements
 
 typedef float v2f_t __attribute__((ext_vector_type(2)));
@@ -116,8 +117,22 @@ __device__ __forceinline__ v6u merge_pair(const uint32_t (&w)[4], int e1, int e2
 }
 
 template <bool POW2, bool WRITE_RM, bool WRITE_CM, bool OP_RM, bool OP_CM>
-__global__ void __launch_bounds__(QTHREADS)
+struct QCfg {
+  static constexpr bool OPS = OP_RM || OP_CM;
+  static constexpr int T = OPS ? 128 : 256;                // tile edge
+  static constexpr int THREADS = OPS ? 256 : 512;        // as QThreads
+  static constexpr int PITCH = T / 2 + 16;                 // bytes per LDS code row (16-byte aligned, padded)
+  static constexpr int BPR = T / 16;                       // blocks per tile row
+};
+
+template <bool OPS>
+struct QThreads { static constexpr int value = OPS ? 256 : 512; };
+
+template <bool POW2, bool WRITE_RM, bool WRITE_CM, bool OP_RM, bool OP_CM>
+__global__ void __launch_bounds__(QThreads<OP_RM || OP_CM>::value)
 quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, QuantOut o) {
+  using Q = QCfg<POW2, WRITE_RM, WRITE_CM, OP_RM, OP_CM>;
+  constexpr int QT = Q::T, QTHREADS = Q::THREADS, RM_PITCH = Q::PITCH, CM_PITCH = Q::PITCH, BPR = Q::BPR;
   constexpr bool STAGE_RM = WRITE_RM || OP_RM, STAGE_CM = WRITE_CM || OP_CM, OPS = OP_RM || OP_CM;
   __shared__ __attribute__((aligned(16))) uint8_t s_rm[STAGE_RM ? QT * RM_PITCH : 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_cm[STAGE_CM ? QT * CM_PITCH : 16];
@@ -144,12 +159,12 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
 #pragma unroll
   for (int it = 0; it < NPASS; ++it) {
     const int b = it * (QTHREADS / 16) + (tid >> 4);   // block index in the tile
-    const int br = b >> 3, bc = b & 7;                 // 8x8 blocks per tile
+    const int br = b / BPR, bc = b % BPR;              // BPR x BPR blocks per tile
     seg[it][0] = seg[it][1] = v4i{0, 0, 0, 0};
-    if (br * 16 < trows && bc * 16 < tcols) {
+    if (br * 16 < trows && bc * 16 < tcols) {          // read once: streaming loads
       const uint16_t* src = x + (row0 + br * 16 + i) * ldx + col0 + bc * 16;
-      seg[it][0] = *reinterpret_cast<const v4i*>(src);
-      seg[it][1] = *reinterpret_cast<const v4i*>(src + 8);
+      seg[it][0] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src));
+      seg[it][1] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + 8));
     }
   }
 
@@ -157,7 +172,7 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
 #pragma unroll
   for (int it = 0; it < NPASS; ++it) {
     const int b = it * (QTHREADS / 16) + (tid >> 4);   // block index in the tile
-    const int br = b >> 3, bc = b & 7;                 // 8x8 blocks per tile
+    const int br = b / BPR, bc = b % BPR;
     const bool live = (br * 16 < trows) && (bc * 16 < tcols);  // uniform over the 16 lanes
     const v4i p0 = seg[it][0], p1 = seg[it][1];
     uint32_t d[8] = {(uint32_t)p0.x, (uint32_t)p0.y, (uint32_t)p0.z, (uint32_t)p0.w,
@@ -227,25 +242,33 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
   }
   __syncthreads();
 
-  // 3. LDS -> HBM, 8-byte stores; 8 lanes cover one 64-byte code row.
+  // 3. LDS -> HBM, 16-byte stores; QT / 32 lanes cover one code row of the tile
+  //    (a whole 128-byte line for the 256-wide tile).  A chunk of 32 codes whose
+  //    second half lies past the tile's ragged edge (an extent of 16 mod 32) is
+  //    stored as its first 8 bytes only.
+  constexpr int CPR = QT / 32;                          // 16-byte chunks per code row
   if constexpr (WRITE_RM) {
 #pragma unroll
-    for (int it = 0; it < (QT * QT / 2 / 8) / QTHREADS; ++it) {
-      int c = it * QTHREADS + tid;
-      int r = c >> 3, q = c & 7;
-      if (r < trows && q * 16 < tcols)
-        *reinterpret_cast<v2i*>(codes_rm + (row0 + r) * (cols / 2) + col0 / 2 + q * 8) =
-            *reinterpret_cast<const v2i*>(s_rm + r * RM_PITCH + q * 8);
+    for (int it = 0; it < (QT * CPR) / QTHREADS; ++it) {
+      const int c = it * QTHREADS + tid, r = c / CPR, q = c % CPR;
+      if (r < trows && q * 32 < tcols) {
+        const v4i v = *reinterpret_cast<const v4i*>(s_rm + r * RM_PITCH + q * 16);
+        uint8_t* dst = codes_rm + (row0 + r) * (cols / 2) + col0 / 2 + q * 16;
+        if (q * 32 + 32 <= tcols) __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));
+        else *reinterpret_cast<v2i*>(dst) = v2i{v.x, v.y};
+      }
     }
   }
   if constexpr (WRITE_CM) {
 #pragma unroll
-    for (int it = 0; it < (QT * QT / 2 / 8) / QTHREADS; ++it) {
-      int c = it * QTHREADS + tid;
-      int cl = c >> 3, q = c & 7;
-      if (cl < tcols && q * 16 < trows)
-        *reinterpret_cast<v2i*>(codes_cm + (col0 + cl) * (rows / 2) + row0 / 2 + q * 8) =
-            *reinterpret_cast<const v2i*>(s_cm + cl * CM_PITCH + q * 8);
+    for (int it = 0; it < (QT * CPR) / QTHREADS; ++it) {
+      const int c = it * QTHREADS + tid, cl = c / CPR, q = c % CPR;
+      if (cl < tcols && q * 32 < trows) {
+        const v4i v = *reinterpret_cast<const v4i*>(s_cm + cl * CM_PITCH + q * 16);
+        uint8_t* dst = codes_cm + (col0 + cl) * (rows / 2) + row0 / 2 + q * 16;
+        if (q * 32 + 32 <= trows) __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));
+        else *reinterpret_cast<v2i*>(dst) = v2i{v.x, v.y};
+      }
     }
   }
   // 4. pair-merged operands: item = (tile row or column, pair); 4 consecutive
@@ -298,8 +321,9 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
 
 template <bool POW2, bool RM, bool CM, bool ORM, bool OCM>
 ft_status launch4(const void* x, int64_t rows, int64_t cols, int64_t ldx, const QuantOut& o, hipStream_t s) {
-  dim3 grid((unsigned)((cols + QT - 1) / QT), (unsigned)((rows + QT - 1) / QT));
-  hipLaunchKernelGGL((quant_block16_kernel<POW2, RM, CM, ORM, OCM>), grid, dim3(QTHREADS), 0, s,
+  using Q = QCfg<POW2, RM, CM, ORM, OCM>;
+  dim3 grid((unsigned)((cols + Q::T - 1) / Q::T), (unsigned)((rows + Q::T - 1) / Q::T));
+  hipLaunchKernelGGL((quant_block16_kernel<POW2, RM, CM, ORM, OCM>), grid, dim3(Q::THREADS), 0, s,
                      static_cast<const uint16_t*>(x), rows, cols, ldx, o);
   return launch_status();
 }
