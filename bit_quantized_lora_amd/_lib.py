@@ -36,6 +36,11 @@ _SIGS = {
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_linear_fwd": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p],
+    "ft_linear_fwd_ws": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                         c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_size_t,
+                         c_void_p],
+    "ft_linear_fwd_workspace": [c_int64, c_int64, c_int64],
+    "ft_linear_plan": [c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p],
     "ft_linear_fwd_gelu": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_void_p],
@@ -69,7 +74,8 @@ _SIGS = {
     "ft_status_str": [c_int32],
 }
 _RESTYPES = {"ft_operand_bytes": c_size_t, "ft_quant_lowrank_db_workspace": c_size_t, "ft_operand_scale_bytes": c_size_t,
-             "ft_linear_bwd_workspace": c_size_t, "ft_lowrank_workspace": c_size_t, "ft_status_str": c_char_p}
+             "ft_linear_bwd_workspace": c_size_t, "ft_linear_fwd_workspace": c_size_t,
+             "ft_lowrank_workspace": c_size_t, "ft_status_str": c_char_p}
 
 _lib = None
 

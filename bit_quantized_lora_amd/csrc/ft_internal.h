@@ -22,10 +22,24 @@ struct GemmArgs {
   // MLP fusion epilogue only: H = GELU(C) bf16 (pitch ldc), Q(H) codes row-major
   // [M][N/2] and power-of-two scale bytes [M/16][N/16]
   void* H; uint8_t* hq; uint8_t* hs;
+  // split reduction (set by the launcher): split s of `splits` takes the
+  // 128-K stages [s nkt / splits, (s+1) nkt / splits) and writes its fp32
+  // partial tile to part[s][M][N]; the low-rank term belongs to split 0
+  float* part = nullptr; int splits = 1;
 };
 
-// beside: other kernels run concurrently on the device (tile choice leaves them CUs)
-ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s, bool beside = false);
+// beside: other kernels run concurrently on the device (tile choice leaves them CUs).
+// ws: device scratch of at least gemm_w4a4_workspace(M, N, K) bytes, or nullptr:
+// with it, a product too small to fill the CUs with whole tiles may split its
+// reduction (fp32 partial tiles in ws, summed in split order by a second
+// kernel); without it the reduction is never split.  The choice depends only on
+// the shape and the device's CU count.
+ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s, bool beside = false,
+                           void* ws = nullptr);
+size_t gemm_w4a4_workspace(int64_t M, int64_t N, int64_t K);
+// the tile (rows x columns) and split count launch_gemm_w4a4 takes for a shape
+ft_status gemm_w4a4_plan(int64_t M, int64_t N, int64_t K, bool beside, bool can_split, int* tile_m, int* tile_n,
+                         int* splits);
 
 // Forward GEMM (bf16 Y) with the MLP fusion epilogue: also H = GELU(Y) and Q(H)
 // (g.H, g.hq, g.hs).  FT_ENOTSUP when K is not a multiple of 128 (no pipelined

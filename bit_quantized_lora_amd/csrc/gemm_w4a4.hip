@@ -98,8 +98,14 @@ struct TileCfg {
 // last stage buffer (and the LDS beyond the ring where they need more)
 using CfgSquare = TileCfg<256, 256, 4, 2, 4, 48>;
 using CfgWide = TileCfg<192, 384, 2, 3, 4, 48>;
+// 128 x 128 tile (8 waves of 64 x 32) for products too small to give every CU a
+// 256 x 256 tile (few rows, e.g. the 512 text tokens of a FLUX block): four
+// times the tiles, two workgroups per CU (66 KiB of LDS each)
+using CfgSmall = TileCfg<128, 128, 2, 2, 4, 64>;
 template <int I, int GS = 0> struct CfgOf { using type = TileCfg<256, 256, 4, 2, 4, 48, GS>; };
 template <> struct CfgOf<1, 0> { using type = CfgWide; };
+template <> struct CfgOf<2, 0> { using type = CfgSmall; };
+constexpr int cfg_occ(int cfg) { return cfg == 2 ? 2 : 1; }   // workgroups per CU the kernel is built for
 }  // namespace ft
 
 namespace ft {
@@ -374,10 +380,14 @@ __device__ __forceinline__ void store_gelu_quant_lds(AccT<TMI, TNI>& acc, const 
 // TRANS_B: backward instantiation (B = Q(R)^T); same code, separate name in profiles.
 // GELU_Q: MLP fusion epilogue (store_gelu_quant_lds; forward, bf16 Y)
 // GS: scale granularity (TileCfg); the group modes use the square tile.
-template <bool OUT_BF16, bool TRANS_B, int CFG, bool GELU_Q = false, int GS = 0>   // CFG: 0 square tile, 1 wide tile
-__global__ void __launch_bounds__(PGT, 1)
-gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
+// SPLIT: split reduction (GemmArgs::splits, ::part): work item v = s * tiles + t
+// takes split s of tile t and stores its fp32 partial tile; split 0 alone adds
+// the low-rank term.
+template <bool OUT_BF16, bool TRANS_B, int CFG, bool GELU_Q = false, int GS = 0, bool SPLIT = false>
+__global__ void __launch_bounds__(PGT, cfg_occ(CFG))   // CFG: 0 square, 1 wide, 2 small tile
+gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
   using C = typename CfgOf<CFG, GS>::type;
+  static_assert(!(SPLIT && GELU_Q), "the MLP fusion epilogue needs the whole reduction");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
   constexpr int BMc = C::BM, BNc = C::BN, NSc = C::NS;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -387,15 +397,29 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
 
   // XCD-aware raster: hardware places workgroup b on XCD b % 8
   const int b = blockIdx.x;
-  const int v = (b & 7) * per_xcd + (b >> 3);
-  if (v >= tiles_m * tiles_n) return;
+  int v = (b & 7) * per_xcd + (b >> 3);
+  const int ntile = tiles_m * tiles_n;
+  if (v >= ntile * (SPLIT ? g_in.splits : 1)) return;
+  int sp = 0;                                                  // split of the reduction
+  if constexpr (SPLIT) {
+    sp = v / ntile;
+    v -= sp * ntile;
+  }
+  GemmArgs g = g_in;
+  if (sp) g.ra = g.rb = 0;                                     // the low-rank term: split 0 only
   const int grp = v / (GROUP_M * tiles_n);
   const int first_m = grp * GROUP_M;
   const int gm = min(GROUP_M, tiles_m - first_m);
   const int in_grp = v - grp * GROUP_M * tiles_n;
   const int64_t m0 = (int64_t)(first_m + in_grp % gm) * BMc;
   const int64_t n0 = (int64_t)(in_grp / gm) * BNc;
-  const int nkt = (int)(g.K / 128);
+  // stages [k0, k0 + nkt) of the reduction
+  const int nk_all = (int)(g.K / 128);
+  int k0 = 0, nkt = nk_all;
+  if constexpr (SPLIT) {
+    k0 = (int)((int64_t)sp * nk_all / g.splits);
+    nkt = (int)((int64_t)(sp + 1) * nk_all / g.splits) - k0;
+  }
 
   // buffer resources for this tile; rows past M / N fall outside the range and read 0
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
@@ -443,14 +467,14 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
       if (u < nq) {
         const bool isb = q >= BMc / 16;
         const int r0 = isb ? 16 * q - BMc : 16 * q;
-        const uint32_t soff = (uint32_t)(r0 * (isb ? g.ldb : g.lda)) + (uint32_t)kt * BKB;
+        const uint32_t soff = (uint32_t)(r0 * (isb ? g.ldb : g.lda)) + (uint32_t)(k0 + kt) * BKB;
         dma16s(isb ? rB : rA, base + (isb ? C::A_ST : 0) + r0 * BKB, isb ? vB : vA,
                __builtin_amdgcn_readfirstlane(soff));
       }
     }
     if constexpr (C::GS == 0) {
       if (scale_w) {   // wave-uniform: the instruction counts even where no lane is active
-        if (s_on) dma4(rS, base + s_lds, offS + (uint32_t)kt * 8);
+        if (s_on) dma4(rS, base + s_lds, offS + (uint32_t)(k0 + kt) * 8);
       }
     } else {
       // scale DMA instruction t = wave + 8u covers scale dwords 64t .. 64t+63 of
@@ -461,7 +485,8 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
         const bool isb = t * 64 >= C::SA_DW;
         const int d = t * 64 + lane - (isb ? C::SA_DW : 0);
         const int row = d / C::DPR, part = d - (d / C::DPR) * C::DPR;
-        const uint32_t off = (uint32_t)(row * (isb ? g.sB_rs : g.sA_rs)) + (uint32_t)(kt * (128 / C::GS) + 4 * part);
+        const uint32_t off =
+            (uint32_t)(row * (isb ? g.sB_rs : g.sA_rs)) + (uint32_t)((k0 + kt) * (128 / C::GS) + 4 * part);
         dma4(isb ? rSB : rSA, base + C::A_ST + C::B_ST + 256 * t, off);
       }
     }
@@ -578,7 +603,12 @@ gemm_w4a4_kernel(GemmArgs g, int tiles_m, int tiles_n, int per_xcd) {
     tail_lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, g, smem + ((nkt - 4) % NSc) * C::STAGE,
                                                     smem + ((nkt - 3) % NSc) * C::STAGE, lane, wm, wn, l32, lh);
   }
-  if constexpr (GELU_Q) {
+  if constexpr (SPLIT) {
+    GemmArgs gp = g;                                           // fp32 partial tile of split sp
+    gp.C = g.part + (int64_t)sp * g.M * g.N;
+    gp.ldc = g.N;
+    store_acc<false, C::TMI, C::TNI>(acc, gp, m0, n0, lane, wm, wn, l32, lh);
+  } else if constexpr (GELU_Q) {
     static_assert(OUT_BF16 && !TRANS_B, "MLP fusion epilogue: forward, bf16 output");
     compiler_fence();
     __builtin_amdgcn_s_barrier();   // every wave done reading the last stage
@@ -869,64 +899,181 @@ __global__ void __launch_bounds__(GT, 1) gemm_w4a4_generic_kernel(GemmArgs g) {
   epilogue_and_store<OUT_BF16, 4, 4, 4, 256, 64>(acc, g, smem, m0, n0, tid, wave, wm, wn, l32, lh);
 }
 
+// C = sum over s of part[s], in split order (fp32 adds, so the result does not
+// depend on which split finished first), stored fp32 or bf16 (nearest even).
+// Four consecutive columns per work item; N is a multiple of 16.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256) split_sum_kernel(const float* __restrict__ part, int splits, int64_t M,
+                                                        int64_t N, void* __restrict__ C, int64_t ldc) {
+  const int64_t nq = N / 4, total = M * nq, plane = M * N;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t m = i / nq, c = 4 * (i - m * nq);
+    const float* p = part + m * N + c;
+    v4f acc = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    for (int sp = 1; sp < splits; ++sp) {
+      const v4f x = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p + sp * plane));
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    if constexpr (OUT_BF16) {
+      const uint32_t lo = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+      const uint32_t hi = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+      *reinterpret_cast<v2i*>(static_cast<uint16_t*>(C) + m * ldc + c) = v2i{(int)lo, (int)hi};
+    } else {
+      *reinterpret_cast<v4f*>(static_cast<float*>(C) + m * ldc + c) = acc;
+    }
+  }
+}
+
+// Launch plan of the pipelined kernel.
+struct GemmPlan {
+  int cfg;          // 0: square 256 x 256 tiles, 1: wide 192 x 384, 2: small 128 x 128
+  int splits;       // reduction splits (1: none)
+  int64_t tm, tn;   // tile grid
+};
+
+// Cost model of the small-product choice, fitted to measured launches of these
+// kernels (512-4608 rows, K 3072-12288): time of one 128 x 128 x 128 MFMA
+// step of a workgroup on its CU with the big tiles (4 or 4.5 steps per stage)
+// and with the small tile (twice the operand bytes per MFMA), the fixed cost of
+// a work item (launch, pipeline fill, low-rank term, store), and that of a
+// split: the partial sums' round trip through memory and the second launch.
+constexpr double STEP_US = 0.294, SMALL_STEP_US = 0.42;
+constexpr double ITEM_US = 13.3, SMALL_ITEM_US = 9.3;
+constexpr double SPLIT_GBS = 5000.0;    // partial sums' read + write rate, GB/s
+constexpr double SPLIT_US = 4.5;
+constexpr int MAX_SPLITS = 8;
+constexpr int MIN_SPLIT_STAGES = 4;     // 128-K stages per split, at least
+
+bool pipelined_ok(const GemmArgs& g) {
+  return g.K > 0 && g.K % 128 == 0 && BN * g.lda < ((int64_t)1 << 31) && CfgWide::BN * g.ldb < ((int64_t)1 << 31);
+}
+
+// beside: see launch_gemm_w4a4.  can_split: a workspace for split partials exists.
+// splits > 1 only when can_split; the result depends on the shape, the CU
+// count and these two flags only.
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool beside, bool can_split) {
+  const int cus = num_cus();
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, tiles = tiles_m * tiles_n;
+  const int64_t wm_ = (M + CfgWide::BM - 1) / CfgWide::BM, wn_ = (N + CfgWide::BN - 1) / CfgWide::BN;
+  const int64_t wide = wm_ * wn_;
+  // Big tiles: the shape that fills the CUs in fewer partial rounds; but when
+  // other kernels run beside the GEMM and both shapes take one round, the one
+  // with fewer tiles, which leaves those kernels more CUs.
+  const bool use_wide = (beside && wide <= cus && tiles <= cus) ? wide < tiles
+                                                                : fill(wide, cus) > fill(tiles, cus) + 0.02;
+  GemmPlan p{use_wide ? 1 : 0, 1, use_wide ? wm_ : tiles_m, use_wide ? wn_ : tiles_n};
+  if (tiles >= cus) return p;                                  // every CU has a big tile already
+  // Fewer big tiles than CUs: compare with 128 x 128 tiles and split reductions
+  // by the busiest CU's time.
+  const int64_t nkt = K / 128;
+  auto rounds = [&](int64_t units) { return (double)((units + cus - 1) / cus); };
+  double best = rounds(p.tm * p.tn) * ((double)nkt * (use_wide ? 4.5 : 4.0) * STEP_US + ITEM_US);
+  const int64_t sm = (M + CfgSmall::BM - 1) / CfgSmall::BM, sn = (N + CfgSmall::BN - 1) / CfgSmall::BN;
+  for (int S = 1; S <= (can_split ? MAX_SPLITS : 1); ++S) {
+    if (S > 1 && nkt < (int64_t)S * MIN_SPLIT_STAGES) break;
+    const double t = rounds(sm * sn * S) * ((double)((nkt + S - 1) / S) * SMALL_STEP_US + SMALL_ITEM_US) +
+                     (S > 1 ? (double)(S + 1) * M * N * 4 / (SPLIT_GBS * 1e3) + SPLIT_US : 0.0);
+    if (t < best) {
+      best = t;
+      p = GemmPlan{2, S, sm, sn};
+    }
+  }
+  return p;
+}
+
 }  // namespace
 
-ft_status launch_gemm_w4a4(const GemmArgs& g, bool out_bf16, bool trans_b, hipStream_t s, bool beside) {
-  if (g.M == 0 || g.N == 0) return FT_OK;
-  const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+ft_status gemm_w4a4_plan(int64_t M, int64_t N, int64_t K, bool beside, bool can_split, int* tile_m, int* tile_n,
+                         int* splits) {
+  if (M < 0 || N < 0 || K < 0) return FT_ESHAPE;
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K; g.lda = K / 2; g.ldb = K / 2;
+  if (!pipelined_ok(g)) {                                      // generic kernel: square tiles, whole reduction
+    *tile_m = BM; *tile_n = BN; *splits = 1;
+    return FT_OK;
+  }
+  const GemmPlan p = plan_gemm(M, N, K, beside, can_split);
+  *tile_m = p.cfg == 2 ? CfgSmall::BM : p.cfg == 1 ? CfgWide::BM : BM;
+  *tile_n = p.cfg == 2 ? CfgSmall::BN : p.cfg == 1 ? CfgWide::BN : BN;
+  *splits = p.splits;
+  return FT_OK;
+}
+
+size_t gemm_w4a4_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128) return 0;
+  const GemmPlan p = plan_gemm(M, N, K, false, true);
+  const GemmPlan q = plan_gemm(M, N, K, true, true);
+  const int S = p.splits > q.splits ? p.splits : q.splits;
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+ft_status launch_gemm_w4a4(const GemmArgs& g_in, bool out_bf16, bool trans_b, hipStream_t s, bool beside,
+                           void* ws) {
+  if (g_in.M == 0 || g_in.N == 0) return FT_OK;
+  const int64_t tiles_m = (g_in.M + BM - 1) / BM, tiles_n = (g_in.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;
-  const bool pipelined = g.K > 0 && g.K % 128 == 0 && BN * g.lda < ((int64_t)1 << 31) &&
-                         CfgWide::BN * g.ldb < ((int64_t)1 << 31);
-  if (pipelined) {
-    const int cus = num_cus();
-    const int64_t wide = ((g.M + CfgWide::BM - 1) / CfgWide::BM) * ((g.N + CfgWide::BN - 1) / CfgWide::BN);
-    // Tile shape: the one that fills the CUs in fewer partial rounds; but when
-    // other kernels run beside the GEMM and both shapes take one round, the one
-    // with fewer tiles, which leaves those kernels more CUs.
-    const bool use_wide = (beside && wide <= cus && tiles <= cus) ? wide < tiles
-                                                                  : fill(wide, cus) > fill(tiles, cus) + 0.02;
-    const int64_t tm = use_wide ? (g.M + CfgWide::BM - 1) / CfgWide::BM : tiles_m;
-    const int64_t tn = use_wide ? (g.N + CfgWide::BN - 1) / CfgWide::BN : tiles_n;
-    const int per_xcd = (int)((tm * tn + 7) / 8);
+  if (pipelined_ok(g_in)) {
+    const GemmPlan p = plan_gemm(g_in.M, g_in.N, g_in.K, beside, ws != nullptr);
+    GemmArgs g = g_in;
+    g.splits = p.splits;
+    g.part = static_cast<float*>(ws);
+    const int per_xcd = (int)((p.tm * p.tn * p.splits + 7) / 8);
     const dim3 grid((unsigned)(8 * per_xcd)), block(PGT);
-#define FT_GEMM_LAUNCH(OB, TB, C) \
-  hipLaunchKernelGGL((gemm_w4a4_kernel<OB, TB, C>), grid, block, 0, s, g, (int)tm, (int)tn, per_xcd)
-    if (use_wide) {
-      if (out_bf16) { if (trans_b) FT_GEMM_LAUNCH(true, true, 1); else FT_GEMM_LAUNCH(true, false, 1); }
-      else { if (trans_b) FT_GEMM_LAUNCH(false, true, 1); else FT_GEMM_LAUNCH(false, false, 1); }
+    const int tm = (int)p.tm, tn = (int)p.tn;
+#define FT_GEMM_LAUNCH(OB, TB, C, SP) \
+  hipLaunchKernelGGL((gemm_w4a4_kernel<OB, TB, C, false, 0, SP>), grid, block, 0, s, g, tm, tn, per_xcd)
+    if (p.splits > 1) {   // fp32 partials, then their sum
+      if (trans_b) FT_GEMM_LAUNCH(false, true, 2, true); else FT_GEMM_LAUNCH(false, false, 2, true);
+      const ft_status st = launch_status();
+      if (st != FT_OK) return st;
+      const int64_t items = g.M * (g.N / 4);
+      int64_t blocks = (items + 255) / 256;
+      if (blocks > 16 * (int64_t)num_cus()) blocks = 16 * (int64_t)num_cus();
+      if (out_bf16)
+        hipLaunchKernelGGL((split_sum_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, g.part, p.splits, g.M,
+                           g.N, g.C, g.ldc);
+      else
+        hipLaunchKernelGGL((split_sum_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, g.part, p.splits,
+                           g.M, g.N, g.C, g.ldc);
+    } else if (p.cfg == 2) {
+      if (out_bf16) { if (trans_b) FT_GEMM_LAUNCH(true, true, 2, false); else FT_GEMM_LAUNCH(true, false, 2, false); }
+      else { if (trans_b) FT_GEMM_LAUNCH(false, true, 2, false); else FT_GEMM_LAUNCH(false, false, 2, false); }
+    } else if (p.cfg == 1) {
+      if (out_bf16) { if (trans_b) FT_GEMM_LAUNCH(true, true, 1, false); else FT_GEMM_LAUNCH(true, false, 1, false); }
+      else { if (trans_b) FT_GEMM_LAUNCH(false, true, 1, false); else FT_GEMM_LAUNCH(false, false, 1, false); }
     } else {
-      if (out_bf16) { if (trans_b) FT_GEMM_LAUNCH(true, true, 0); else FT_GEMM_LAUNCH(true, false, 0); }
-      else { if (trans_b) FT_GEMM_LAUNCH(false, true, 0); else FT_GEMM_LAUNCH(false, false, 0); }
+      if (out_bf16) { if (trans_b) FT_GEMM_LAUNCH(true, true, 0, false); else FT_GEMM_LAUNCH(true, false, 0, false); }
+      else { if (trans_b) FT_GEMM_LAUNCH(false, true, 0, false); else FT_GEMM_LAUNCH(false, false, 0, false); }
     }
 #undef FT_GEMM_LAUNCH
     return launch_status();
   }
   const dim3 grid((unsigned)tiles), block(GT);
-  if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g);
-  else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g);
+  if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g_in);
+  else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g_in);
   return launch_status();
 }
 
 ft_status launch_gemm_w4a4_gelu_quant(const GemmArgs& g, hipStream_t s) {
   if (g.M == 0 || g.N == 0) return FT_OK;
   const int64_t tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  const int64_t tiles = tiles_m * tiles_n;
-  if (tiles >= ((int64_t)1 << 28)) return FT_ESHAPE;
-  const bool pipelined = g.K > 0 && g.K % 128 == 0 && BN * g.lda < ((int64_t)1 << 31) &&
-                         CfgWide::BN * g.ldb < ((int64_t)1 << 31);
-  if (!pipelined) return FT_ENOTSUP;
-  const int cus = num_cus();
-  const int64_t wide = ((g.M + CfgWide::BM - 1) / CfgWide::BM) * ((g.N + CfgWide::BN - 1) / CfgWide::BN);
-  const bool use_wide = fill(wide, cus) > fill(tiles, cus) + 0.02;
-  const int64_t tm = use_wide ? (g.M + CfgWide::BM - 1) / CfgWide::BM : tiles_m;
-  const int64_t tn = use_wide ? (g.N + CfgWide::BN - 1) / CfgWide::BN : tiles_n;
-  const int per_xcd = (int)((tm * tn + 7) / 8);
+  if (tiles_m * tiles_n >= ((int64_t)1 << 28)) return FT_ESHAPE;
+  if (!pipelined_ok(g)) return FT_ENOTSUP;
+  const GemmPlan p = plan_gemm(g.M, g.N, g.K, false, false);
+  const int per_xcd = (int)((p.tm * p.tn + 7) / 8);
   const dim3 grid((unsigned)(8 * per_xcd)), block(PGT);
-  if (use_wide)
-    hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 1, true>), grid, block, 0, s, g, (int)tm, (int)tn, per_xcd);
+  const int tm = (int)p.tm, tn = (int)p.tn;
+  if (p.cfg == 2)
+    hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 2, true>), grid, block, 0, s, g, tm, tn, per_xcd);
+  else if (p.cfg == 1)
+    hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 1, true>), grid, block, 0, s, g, tm, tn, per_xcd);
   else
-    hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 0, true>), grid, block, 0, s, g, (int)tm, (int)tn, per_xcd);
+    hipLaunchKernelGGL((gemm_w4a4_kernel<true, false, 0, true>), grid, block, 0, s, g, tm, tn, per_xcd);
   return launch_status();
 }
 

@@ -76,12 +76,14 @@ ft_status gemm_with_adapter_grads(F gemm, int64_t M, int64_t N, int64_t K, const
 }  // namespace
 }  // namespace ft
 
-extern "C" ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
-                                   const uint8_t* xq_codes, const void* xq_scales,
-                                   const uint8_t* rq_codes, const void* rq_scales,
-                                   const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
-                                   void* Y, ft_out_dtype ydt, hipStream_t stream) {
-  using namespace ft;
+namespace ft {
+namespace {
+// ft_linear_fwd (with_ws false: no workspace, the reduction is never split) and
+// ft_linear_fwd_ws
+ft_status linear_fwd_impl(int64_t M, int64_t N, int64_t K, ft_scale_mode mode, const uint8_t* xq_codes,
+                          const void* xq_scales, const uint8_t* rq_codes, const void* rq_scales, const float* T,
+                          const void* L2, int32_t rs, const void* B, int32_t r, void* Y, ft_out_dtype ydt,
+                          bool with_ws, void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (mode != FT_SCALE_POW2 && mode != FT_SCALE_F32) return FT_EINVAL;
   if (ydt != FT_OUT_F32 && ydt != FT_OUT_BF16) return FT_EINVAL;
   if (!mult16(M) || !mult16(N) || !mult16(K) || !ranks_ok(rs, r)) return FT_ESHAPE;
@@ -94,6 +96,10 @@ extern "C" ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
   if (!aligned16(Y) || (K && (!aligned16(xq_codes) || !aligned16(rq_codes))) || (rho && !aligned16(T)) ||
       (rs && !aligned16(L2)) || (r && !aligned16(B)))
     return FT_EALIGN;
+  const size_t need = with_ws ? gemm_w4a4_workspace(M, N, K) : 0;
+  if (need && !workspace) return FT_EINVAL;
+  if (need && !aligned16(workspace)) return FT_EALIGN;
+  if (need && ws_bytes < need) return FT_ESPACE;
   GemmArgs g{};
   g.M = M; g.N = N; g.K = K;
   g.A = xq_codes; g.lda = K / 2;
@@ -104,7 +110,49 @@ extern "C" ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mod
   g.Wa = static_cast<const uint16_t*>(L2); g.ra = rs;
   g.Wb = static_cast<const uint16_t*>(B); g.rb = r;
   g.C = Y; g.ldc = N;
-  return launch_gemm_w4a4(g, ydt == FT_OUT_BF16, false, stream);
+  return launch_gemm_w4a4(g, ydt == FT_OUT_BF16, false, stream, false, need ? workspace : nullptr);
+}
+}  // namespace
+}  // namespace ft
+
+extern "C" ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                                   const uint8_t* xq_codes, const void* xq_scales,
+                                   const uint8_t* rq_codes, const void* rq_scales,
+                                   const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                                   void* Y, ft_out_dtype ydt, hipStream_t stream) {
+  return ft::linear_fwd_impl(M, N, K, mode, xq_codes, xq_scales, rq_codes, rq_scales, T, L2, rs, B, r, Y, ydt,
+                             false, nullptr, 0, stream);
+}
+
+extern "C" size_t ft_linear_fwd_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  return ft::gemm_w4a4_workspace(M, N, K);
+}
+
+extern "C" ft_status ft_linear_plan(int64_t M, int64_t N, int64_t K, int32_t backward, int32_t with_ws,
+                                    int32_t* plan) {
+  using namespace ft;
+  if (!plan) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K)) return FT_ESHAPE;
+  int tm = 0, tn = 0, sp = 1;
+  // the backward's dX GEMM: M x K output, reduction over N, planned as with the
+  // adapter gradients beside it
+  const ft_status st = backward ? gemm_w4a4_plan(M, K, N, true, with_ws != 0, &tm, &tn, &sp)
+                                : gemm_w4a4_plan(M, N, K, false, with_ws != 0, &tm, &tn, &sp);
+  plan[0] = tm;
+  plan[1] = tn;
+  plan[2] = sp;
+  return st;
+}
+
+extern "C" ft_status ft_linear_fwd_ws(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                                      const uint8_t* xq_codes, const void* xq_scales,
+                                      const uint8_t* rq_codes, const void* rq_scales,
+                                      const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                                      void* Y, ft_out_dtype ydt, void* workspace, size_t ws_bytes,
+                                      hipStream_t stream) {
+  return ft::linear_fwd_impl(M, N, K, mode, xq_codes, xq_scales, rq_codes, rq_scales, T, L2, rs, B, r, Y, ydt,
+                             true, workspace, ws_bytes, stream);
 }
 
 extern "C" ft_status ft_linear_fwd_gelu(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
@@ -145,10 +193,12 @@ extern "C" ft_status ft_linear_fwd_gelu(int64_t M, int64_t N, int64_t K, ft_scal
   return s2;
 }
 
+// [dA partials | dB partials | the dX GEMM's split partials]
 extern "C" size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r) {
   using namespace ft;
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
-  return align256(lora_grad_workspace(M, K, r)) + align256(lora_grad_workspace(M, N, r));
+  return align256(lora_grad_workspace(M, K, r)) + align256(lora_grad_workspace(M, N, r)) +
+         gemm_w4a4_workspace(M, K, N);
 }
 
 namespace ft {
@@ -191,11 +241,17 @@ ft_status linear_bwd_impl(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
   g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
   g.C = dX; g.ldc = K;
   const bool out_bf16 = dxdt == FT_OUT_BF16;
+  void* split_ws = nullptr;   // the last part of the workspace, when the GEMM splits its reduction
+  if (gemm_w4a4_workspace(M, K, N))
+    split_ws = static_cast<uint8_t*>(workspace) + align256(lora_grad_workspace(M, K, r)) +
+               align256(lora_grad_workspace(M, N, r));
   auto gemm = [&](hipStream_t s, bool beside) {
-    return (M && K) ? launch_gemm_w4a4(g, out_bf16, true, s, beside) : FT_OK;
+    return (M && K) ? launch_gemm_w4a4(g, out_bf16, true, s, beside, split_ws) : FT_OK;
   };
   if (!side) {
-    ft_status st = gemm(stream, false);
+    // the GEMM planned as when the adapter gradients run beside it, so that both
+    // ways run the same kernels and give the same results bit for bit
+    ft_status st = gemm(stream, true);
     if (st != FT_OK) return st;
     return adapter_grads(M, N, K, V, rs, r, X, G, T, dAt, dB, workspace, stream);
   }

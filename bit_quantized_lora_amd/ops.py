@@ -357,10 +357,27 @@ def _sdt(mode: str):
     return torch.uint8 if mode == "pow2" else torch.float32
 
 
+def linear_fwd_workspace(M: int, N: int, K: int) -> int:
+    return int(lib().ft_linear_fwd_workspace(M, N, K))
+
+
+def linear_plan(M: int, N: int, K: int, backward: bool = False, with_ws: bool = True):
+    """(tile rows, tile columns, reduction splits) of the 4-bit GEMM of
+    linear_fwd (backward False) or of linear_bwd's dX GEMM (backward True)."""
+    import ctypes
+    out = (ctypes.c_int32 * 3)()
+    check("ft_linear_plan", lib().ft_linear_plan(M, N, K, int(backward), int(with_ws), ctypes.addressof(out)))
+    return int(out[0]), int(out[1]), int(out[2])
+
+
 def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,
                out_dtype=torch.float32, mode: str = "pow2", out: Optional[torch.Tensor] = None,
-               prepare: bool = False):
-    """Y = deq(Xq) deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B (``prepare``: return a ``Prepared`` call)."""
+               prepare: bool = False, split: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Y = deq(Xq) deq(Rq)^T + T[:, :rs] L2 + T[:, rs:] B (``prepare``: return a ``Prepared`` call).
+
+    ``split``: shapes with too few output tiles for the GPU split their reduction
+    (ft_linear_fwd_ws, with ``workspace`` or a fresh one); False: ft_linear_fwd,
+    never split."""
     _mult16("linear_fwd", M, N, K)
     gemm = M > 0 and N > 0 and K > 0
     sdt = _sdt(mode)
@@ -374,11 +391,17 @@ def linear_fwd(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: in
         out = torch.empty((M, N), dtype=out_dtype, device=T.device)
     odt = _out_dtype(out, "out")
     _need(out, out.dtype, "out", (M, N))
-    _same_device(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, out)
+    need = linear_fwd_workspace(M, N, K) if split else 0
+    if need:
+        workspace = _ws(workspace, need, T.device)
+    _same_device(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, out, workspace if need else None)
     args = (M, N, K, _MODES[mode], xq_codes.data_ptr(), xq_scales.data_ptr(), rq_codes.data_ptr(),
             rq_scales.data_ptr(), T.data_ptr(), L2.data_ptr(), rs, B.data_ptr(), r, out.data_ptr(), odt)
-    return _issue("ft_linear_fwd", args, T.device, out, (xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, out),
-                  prepare)
+    keep = (xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, out)
+    if need:
+        return _issue("ft_linear_fwd_ws", args + (workspace.data_ptr(), workspace.numel()), T.device, out,
+                      keep + (workspace,), prepare)
+    return _issue("ft_linear_fwd", args, T.device, out, keep, prepare)
 
 
 def linear_fwd_gelu(xq_codes, xq_scales, rq_codes, rq_scales, T, L2, B, M: int, N: int, K: int,

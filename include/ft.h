@@ -221,6 +221,33 @@ ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
                         const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
                         void* Y, ft_out_dtype ydt, hipStream_t stream);
 
+/* ft_linear_fwd_ws -- ft_linear_fwd with a workspace, for products too small to
+ * give every compute unit a whole output tile (few tokens, e.g. the 512 text
+ * tokens of a FLUX block): their reduction over K may be split into fp32
+ * partial products in the workspace, which a second kernel adds in split order
+ * (deterministic: no atomics).  Y equals ft_linear_fwd's up to fp32 summation
+ * order.
+ *  workspace  device scratch of at least ft_linear_fwd_workspace(M, N, K)
+ *             bytes, 16-byte aligned; may be NULL when that is 0 (the shape
+ *             does not split; the call is then ft_linear_fwd).  FT_ESPACE when
+ *             ws_bytes is smaller.
+ * Other arguments as ft_linear_fwd.  The split depends only on the shape and the
+ * device's compute-unit count. */
+ft_status ft_linear_fwd_ws(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
+                           const uint8_t* xq_codes, const void* xq_scales,
+                           const uint8_t* rq_codes, const void* rq_scales,
+                           const float* T, const void* L2, int32_t rs, const void* B, int32_t r,
+                           void* Y, ft_out_dtype ydt, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+size_t ft_linear_fwd_workspace(int64_t M, int64_t N, int64_t K);
+
+/* ft_linear_plan -- how the 4-bit GEMM of a call is launched (for tests and
+ * profiling; nothing is run): plan[0] x plan[1] output tile per workgroup,
+ * plan[2] reduction splits.  backward 0: the GEMM of ft_linear_fwd (with_ws 0)
+ * or ft_linear_fwd_ws (with_ws 1); backward 1: the dX GEMM of ft_linear_bwd
+ * (with_ws 1; it always has its workspace).  M, N, K as in those calls. */
+ft_status ft_linear_plan(int64_t M, int64_t N, int64_t K, int32_t backward, int32_t with_ws, int32_t* plan);
+
 /* ft_linear_bwd -- Eq. 3 and the adapter gradients of section 3.2:
  *
  *   dX  = deq(Gq) deq(Rq) + V[:, 0:rs] L1t + V[:, rs:rs+r] At
@@ -237,7 +264,9 @@ ft_status ft_linear_fwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
  *  dX [M x K] float or bf16; dAt float [r x K]; dB float [r x N], or NULL to
  *     skip dB (a caller that took it in the pass over G, ft_quant_lowrank_db)
  *  workspace  device scratch of at least ft_linear_bwd_workspace(M, N, K, r)
- *             bytes (partial sums of the reductions over M). */
+ *             bytes (partial sums of the reductions over M, and, for few
+ *             tokens, of the dX GEMM's split reduction over N as in
+ *             ft_linear_fwd_ws). */
 ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
                         const uint8_t* gq_codes, const void* gq_scales,
                         const uint8_t* rq_codes_cm, const void* rq_scales_cm,

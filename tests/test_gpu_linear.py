@@ -251,16 +251,90 @@ def test_wide_tile_ragged_edges(path, K, rs, r):
 def test_square_tile_lowrank_after_main_loop():
     """256 x 256 tiles with rs + r = 32 and 8 stages: the low-rank term's W and P
     tiles fit the freed ring buffers, so it runs after the main loop; ragged last
-    tiles in M and N."""
+    tiles in M and N (17 x 13 tiles: enough rows that the forward keeps the
+    square tile)."""
     require_gpu()
-    M, K, N = 528, 1024, 784
+    from bit_quantized_lora_amd import ops
+    M, K, N = 4112, 1024, 3088
+    assert ops.linear_plan(M, N, K) == (256, 256, 1)
     rng = np.random.default_rng(528)
     spec = synth.LinearSpec("t", M, K, N, 16, 16, x_dist="t3")
     d = synth.make_linear(spec, rng)
     say(f"[linear] square-tile low-rank after the main loop M={M} K={K} N={N}")
     gpu = _gpu_linear(d, path="codes")
-    rows = np.arange(M)
+    rows = np.unique(np.concatenate([_sample_strips(M, rng, 8), np.arange(M - 48, M)]))
     _compare(gpu, _oracle_rows(d, rows), rows, "square-tile/tail")
+
+
+# Few tokens: the 512 text tokens of a FLUX block (configuration 5's text-stream
+# linears, whole), and ragged variants.  Fewer 256 x 256 tiles than compute
+# units, so the GEMMs take 128 x 128 tiles and, where the reduction is long,
+# split it (fp32 partial products summed in split order by a second kernel).
+SMALL_M = [
+    # (M, K, N, rs, r)
+    (512, 3072, 9216, 32, 32),      # qkv
+    (512, 3072, 3072, 32, 32),      # out-proj
+    (512, 3072, 12288, 32, 32),     # MLP up
+    (512, 12288, 3072, 32, 32),     # MLP down
+    (400, 3072, 1040, 16, 16),      # ragged last tiles in M and N
+    (272, 4224, 656, 32, 16),       # ragged, 33 stages (uneven splits)
+    (528, 5248, 1040, 16, 16),      # ragged, 41 stages
+]
+
+
+def _small_m_data(shape):
+    M, K, N, rs, r = shape
+    spec = synth.LinearSpec("t", M, K, N, rs, r, x_outlier_frac=0.01, x_outlier_mult=50.0)
+    return synth.make_linear(spec, np.random.default_rng(M + 3 * K + 7 * N))
+
+
+@pytest.mark.parametrize("shape", SMALL_M, ids=lambda s: "x".join(map(str, s)))
+def test_small_m_tiles_and_split_reduction(shape):
+    """Every element of Y, dX, dA, dB against the oracle; the forward without a
+    workspace (never split) agrees as well; a split forward repeated gives the
+    same bits."""
+    require_gpu()
+    import torch
+    from bit_quantized_lora_amd import ops
+    M, K, N, rs, r = shape
+    fwd, fwd_nows, bwd = ops.linear_plan(M, N, K), ops.linear_plan(M, N, K, with_ws=False), \
+        ops.linear_plan(M, N, K, backward=True)
+    say(f"[linear] few tokens {shape}: fwd plan {fwd} (no workspace {fwd_nows}), dX plan {bwd}")
+    assert fwd[:2] == (128, 128) and fwd_nows == (128, 128, 1)
+    d = _small_m_data(shape)
+    gpu = _gpu_linear(d)
+    rows = np.arange(M)
+    _compare(gpu, _oracle_rows(d, rows), rows, f"few-tokens{shape}")
+    # the same forward through ft_linear_fwd (no workspace, whole reduction per tile)
+    X, R = dev_bf16(d["X"]), dev_bf16(d["R"])
+    L1t, At = dev_bf16(np.ascontiguousarray(d["L1"].T)), dev_bf16(np.ascontiguousarray(d["A"].T))
+    L2, B = dev_bf16(d["L2"]), dev_bf16(d["B"])
+    xq, _, xs = ops.quant_block16(X)
+    rq, _, rsc = ops.quant_block16(R)
+    T = ops.lowrank_fused(X, L1t, At)
+    Y1 = ops.linear_fwd(xq, xs, rq, rsc, T, L2, B, M, N, K, split=False)
+    Y2 = ops.linear_fwd(xq, xs, rq, rsc, T, L2, B, M, N, K)
+    Y3 = ops.linear_fwd(xq, xs, rq, rsc, T, L2, B, M, N, K)
+    torch.cuda.synchronize()
+    ref = _oracle_rows(d, rows)["Y"]
+    e1 = O.rel_frob(host(Y1).astype(np.float64), ref)
+    say(f"[linear] few tokens {shape}: unsplit forward rel-Frobenius {e1:.2e}")
+    assert e1 <= BUDGET
+    assert np.array_equal(host(Y2).view(np.uint32), host(Y3).view(np.uint32)), "split forward not deterministic"
+    if fwd[2] == 1:
+        assert np.array_equal(host(Y1).view(np.uint32), host(Y2).view(np.uint32))
+
+
+def test_small_m_set_covers_split_paths():
+    """The few-token shapes above take both the split and the unsplit small-tile
+    GEMM, forward and backward (as planned for this device's compute units)."""
+    require_gpu()
+    from bit_quantized_lora_amd import ops
+    fwd = [ops.linear_plan(M, N, K) for M, K, N, _, _ in SMALL_M]
+    bwd = [ops.linear_plan(M, N, K, backward=True) for M, K, N, _, _ in SMALL_M]
+    say(f"[linear] few-token plans: fwd {fwd}, dX {bwd}")
+    assert any(p[2] > 1 for p in fwd) and any(p[2] == 1 for p in fwd)
+    assert any(p[2] > 1 for p in bwd) and any(p[:2] == (128, 128) and p[2] == 1 for p in bwd)
 
 
 @pytest.mark.parametrize("shape", [(272, 384, 512), (304, 1040, 400)], ids=lambda s: "x".join(map(str, s)))
