@@ -695,23 +695,44 @@ def time_configs(reps, cache, oracle_rows=128):
     return out
 
 
-def gpu_clock_mhz():
-    """Current and maximum graphics clock (MHz) of the GPU this process runs on,
-    found among the node's GPUs by its PCI address (None when unavailable)."""
-    try:
-        import amdsmi
-        import torch
-        p = torch.cuda.get_device_properties(torch.cuda.current_device())
-        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
-        amdsmi.amdsmi_init()
+class GpuClock:
+    """Graphics clock (MHz) of the GPU this process runs on, found among the
+    node's GPUs by its PCI address.  The library is opened and the GPU found at
+    construction, so that read() is a single query, quick enough to land while
+    the GPU is still working through enqueued steps.  read() gives None when the
+    tool is missing or the GPU cannot be matched."""
+
+    def __init__(self):
+        self.h, self.bdf, self.mod = None, None, None
         try:
-            h = amdsmi.amdsmi_get_processor_handle_from_bdf(bdf)
-            info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-            return {"cur": info.get("clk"), "max": info.get("max_clk"), "bdf": bdf}
-        finally:
-            amdsmi.amdsmi_shut_down()
-    except Exception:  # pragma: no cover - tool missing, no permission, or no match
-        return None
+            import amdsmi
+            import torch
+            p = torch.cuda.get_device_properties(torch.cuda.current_device())
+            self.bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+            amdsmi.amdsmi_init()
+            self.mod = amdsmi
+            self.h = amdsmi.amdsmi_get_processor_handle_from_bdf(self.bdf)
+        except Exception:  # pragma: no cover - tool missing, no permission, or no match
+            self.h = None
+
+    def read(self):
+        if self.h is None:
+            return None
+        try:
+            t0 = time.perf_counter()
+            info = self.mod.amdsmi_get_clock_info(self.h, self.mod.AmdSmiClkType.GFX)
+            return {"cur": info.get("clk"), "max": info.get("max_clk"), "bdf": self.bdf,
+                    "query_ms": round((time.perf_counter() - t0) * 1e3, 2)}
+        except Exception:  # pragma: no cover
+            return None
+
+    def close(self):
+        if self.mod is not None:
+            try:
+                self.mod.amdsmi_shut_down()
+            except Exception:  # pragma: no cover
+                pass
+            self.mod = None
 
 
 def cpu_model():
@@ -798,6 +819,7 @@ def main():
     # timed region: exactly `steps` steps, no event inside it.  The graphics clock
     # is read while the GPU works through them (after the last step is enqueued,
     # before the synchronize), and the host's enqueue time is recorded.
+    clock = GpuClock()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(s)
@@ -806,8 +828,9 @@ def main():
         lin.step()
     host_timed_us = (time.perf_counter() - h0) / args.steps * 1e6
     t_end.record(s)
-    clk_during = gpu_clock_mhz()
+    clk_during = clock.read()
     torch.cuda.synchronize()
+    clock.close()
     ms_step = t_start.elapsed_time(t_end) / args.steps
 
     # per-phase breakdown: events between the phases over `steps` further steps,

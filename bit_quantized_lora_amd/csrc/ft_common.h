@@ -34,12 +34,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// fp32 value split into two bf16 values hi + lo with hi = rne(f), lo = rne(f - hi).
-// hi + lo equals f to within 2^-16 relative (16 significant bits).
+// Two fp32 values split into bf16 hi + lo: hi = rne(f), lo = rne(f - hi), each
+// pair packed into a dword (element 0 in the low half).  hi + lo equals f to
+// within 2^-16 relative (16 significant bits).  The conversions are the
+// hardware's packed fp32 -> bf16 (round to nearest even: the same bits as
+// f32_to_bf16_rne for finite values), two values per instruction.
+typedef float v2f_ __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_ __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x2(float f0, float f1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_){f0, f1}, v2bf_));
+  const float h0 = __builtin_bit_cast(float, h << 16), h1 = __builtin_bit_cast(float, h & 0xffff0000u);
+  hi = h;
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_){f0 - h0, f1 - h1}, v2bf_));
+}
+// one value: hi, lo in the low 16 bits
 __device__ __forceinline__ void split_bf16(float f, uint32_t& hi, uint32_t& lo) {
-  hi = f32_to_bf16_rne(f);
-  float r = f - __builtin_bit_cast(float, hi << 16);
-  lo = f32_to_bf16_rne(r);
+  split_bf16x2(f, 0.0f, hi, lo);
+  hi &= 0xffffu;
+  lo &= 0xffffu;
 }
 
 // Zero n floats on the stream with a kernel (graph-capture friendly, no memset node).

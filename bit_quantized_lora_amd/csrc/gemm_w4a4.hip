@@ -20,28 +20,35 @@
 // power-of-two scales exactly, so the result is the exact dequantized product
 // accumulated in fp32.  Half of each MFMA's K slots carry data.
 //
-// Tiling: 256 x 256 output tile per workgroup.  Pipelined kernel: 8 waves in
-// 4 x 2 (two per SIMD, so one wave's LDS or barrier wait overlaps the other's
-// MFMAs), each 64 x 128 = 2 x 4 MFMA tiles of 32 x 32.  Generic kernel: 4 waves
-// of 128 x 128.  K advances 128 elements (64 code bytes per row, 8 blocks) per stage.
+// Kernels (all of them 8 waves, two per SIMD, so one wave's LDS or barrier wait
+// overlaps the other's MFMAs; K advances 128 elements = 64 code bytes per row,
+// 8 blocks, per stage):
 //
-// Pipelined kernel (reduction length a multiple of 128): a 4-stage LDS ring
-// filled by buffer_load ... lds (global -> LDS without registers).  Each DMA
-// instruction writes 1 KiB = 16 tile rows contiguously; the 16-byte-chunk XOR
-// swizzle that keeps the fragment reads conflict-free is applied by choosing
-// which global chunk each lane fetches.  Out-of-range rows read as zero (buffer
-// range check).  One barrier per stage; each wave waits only for its own DMA of
-// the stage about to be consumed (explicit vmcnt), keeping 2 stages in flight.
-// Tiles are mapped XCD-aware: consecutive workgroups land on different XCDs, so
-// the linear id is re-grouped such that each XCD works on a compact block of
-// output tiles (shared A/B panels in that XCD's L2).
+// Pipelined kernel, one workgroup per output tile (reduction length a multiple
+// of 128): a 4-stage LDS ring filled by buffer_load ... lds (global -> LDS
+// without registers).  Each DMA instruction writes 1 KiB = 16 tile rows
+// contiguously; the 16-byte-chunk XOR swizzle that keeps the fragment reads
+// conflict-free is applied by choosing which global chunk each lane fetches.
+// Out-of-range rows read as zero (buffer range check).  One barrier per stage;
+// each wave waits only for its own DMA of the stage about to be consumed
+// (explicit vmcnt), keeping 2 stages in flight.  Tiles are mapped XCD-aware:
+// consecutive workgroups land on different XCDs, so the linear id is re-grouped
+// such that each XCD works on a compact block of output tiles (shared A/B panels
+// in that XCD's L2).  Tile shapes: 256 x 256, 192 x 384 (when it fills the CUs
+// in fewer partial rounds), and 128 x 128 for products with fewer big tiles
+// than CUs, with an optional split of the reduction (fp32 partial tiles summed
+// in split order by a second kernel).
 //
-// Generic kernel (any multiple-of-16 reduction length): register-staged double
-// buffer with per-chunk bounds checks; used only when K % 128 != 0.
+// Generic kernel (any multiple-of-16 reduction length): 4 waves of 128 x 128,
+// register-staged double buffer with per-chunk bounds checks; used only when
+// K % 128 != 0.
 //
-// Epilogue (both kernels): W's 256-column slice is staged transposed in LDS; P
-// is split into bf16 hi + lo (hi + lo = P to 2^-16 relative) and multiplied on
-// bf16 MFMA 32x32x16, so the fp32 low-rank intermediate keeps ~16 bits.
+// Low-rank term: W's slice is staged transposed in LDS; P is split into bf16
+// hi + lo (hi + lo = P to 2^-16 relative) and multiplied on bf16 MFMA 32x32x16,
+// so the fp32 low-rank intermediate keeps ~16 bits.  The pipelined kernel adds
+// it before the 4-bit products, 16 ranks at a time, whatever the tile shape or
+// epilogue, so its launches sum each output in the same order (the generic
+// kernel adds it after them).
 #include "ft_common.h"
 #include "ft_device.h"
 #include "ft_internal.h"
@@ -501,20 +508,18 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
   // The low-rank up-projection P W goes into the accumulators first, in the
   // buffer of stage NS-1 (free until the first steady iteration).  The loads of
   // its first chunk are issued ahead of the pipeline fill and awaited by count
-  // (the fill's DMAs, all younger, may stay in flight), so both overlap.
-  // (Or, when its tiles fit the ring buffers the last stages free, after the
-  // main loop: see tail_issue_w.)
+  // (the fill's DMAs, all younger, may stay in flight), so both overlap.  (Every
+  // GEMM kernel adds the low-rank term before the 4-bit products, 16 ranks at a
+  // time, so all of them sum each output in the same order.)
   const int rho = g.ra + g.rb;
-  const bool tail_lr = rho > 0 && rho <= C::CHUNK && rho * 2 * BNc <= C::STAGE && BMc * rho * 4 <= C::STAGE &&
-                       nkt >= NSc && (BMc * rho) % 256 == 0;
   uint8_t* lr_smem = smem + (NSc - 1) * C::STAGE;
   PRegs<C::TMI, C::CHUNK> pr;
-  if (rho > 0 && !tail_lr)
+  if (rho > 0)
     lowrank_load<C::TMI, C::TNI, 8, BNc, C::CHUNK>(pr, g, lr_smem, 0, m0, n0, wave, lane, wm, l32, lh);
 #pragma unroll
   for (int s = 0; s < NSc - 1; ++s)
     if (s < nkt) issue(s, s);
-  if (rho > 0 && !tail_lr) {
+  if (rho > 0) {
     compiler_fence();
     if (nkt >= NSc - 1) FT_WAIT_VMCNT(C::DPS * (NSc - 1));
     else if (nkt == 2) FT_WAIT_VMCNT(C::DPS * 2);
@@ -558,10 +563,6 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
       else FT_WAIT_VMCNT(0);
       __builtin_amdgcn_s_barrier();
       compiler_fence();
-      if (!steady && tail_lr) {   // from here on the buffer of stage kt-1 is free
-        if (kt == nkt - 3) tail_issue_w<8, BNc>(g, smem + ((nkt - 4) % NSc) * C::STAGE, n0, wave, lane);
-        else if (kt == nkt - 2) tail_issue_p<8, BMc>(g, smem + ((nkt - 3) % NSc) * C::STAGE, m0, wave, lane);
-      }
       const uint8_t* nx = smem + __builtin_amdgcn_readfirstlane(((kt + 1) % NSc) * C::STAGE);
       read_part<C::TMI, C::TNI, BMc, BNc>(c0, nx, 0, wm, wn, l32, lh);
       if constexpr (C::GS) read_scales_g<C::GS, C::TMI, C::TNI, BMc, BNc>(na, nb, nx, wm, wn, l32, lh);
@@ -595,14 +596,6 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
   int kt = 0;
   for (; kt < n_steady; ++kt) step(kt, true);
   for (; kt < nkt; ++kt) step(kt, false);   // the last NS-1 stages: nothing more to fetch
-  if (tail_lr) {
-    compiler_fence();
-    FT_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
-    tail_lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, g, smem + ((nkt - 4) % NSc) * C::STAGE,
-                                                    smem + ((nkt - 3) % NSc) * C::STAGE, lane, wm, wn, l32, lh);
-  }
   if constexpr (SPLIT) {
     GemmArgs gp = g;                                           // fp32 partial tile of split sp
     gp.C = g.part + (int64_t)sp * g.M * g.N;

@@ -245,7 +245,8 @@ size_t ft_linear_fwd_workspace(int64_t M, int64_t N, int64_t K);
  * profiling; nothing is run): plan[0] x plan[1] output tile per workgroup,
  * plan[2] reduction splits.  backward 0: the GEMM of ft_linear_fwd (with_ws 0)
  * or ft_linear_fwd_ws (with_ws 1); backward 1: the dX GEMM of ft_linear_bwd
- * (with_ws 1; it always has its workspace).  M, N, K as in those calls. */
+ * (with_ws 1; it always has its workspace).  M, N, K as in those calls; plan
+ * holds 3 int32. */
 ft_status ft_linear_plan(int64_t M, int64_t N, int64_t K, int32_t backward, int32_t with_ws, int32_t* plan);
 
 /* ft_linear_bwd -- Eq. 3 and the adapter gradients of section 3.2:

@@ -234,9 +234,8 @@ def test_full_size_configs_sampled_rows(cfg, path):
 def test_wide_tile_ragged_edges(path, K, rs, r):
     """A shape for which the 192 x 384 workgroup tile fills the chip better than
     256 x 256 (so the forward GEMM takes it), with ragged last tiles in both M
-    and N; rows sampled across the tiles, including the last ones.  K = 384
-    (3 stages) puts the fused low-rank term before the main loop, K = 1024
-    (8 stages) after it, from tiles fetched during the last stages."""
+    and N; rows sampled across the tiles, including the last ones.  K = 384:
+    3 stages (fewer than the ring's depth), K = 1024: 8."""
     require_gpu()
     M, N = 4592, 12272
     rng = np.random.default_rng(4592 + K)
@@ -248,11 +247,9 @@ def test_wide_tile_ragged_edges(path, K, rs, r):
     _compare(gpu, _oracle_rows(d, rows), rows, f"wide-tile/K{K}/{path}")
 
 
-def test_square_tile_lowrank_after_main_loop():
-    """256 x 256 tiles with rs + r = 32 and 8 stages: the low-rank term's W and P
-    tiles fit the freed ring buffers, so it runs after the main loop; ragged last
-    tiles in M and N (17 x 13 tiles: enough rows that the forward keeps the
-    square tile)."""
+def test_square_tiles_one_round_ragged():
+    """256 x 256 tiles, one workgroup per tile (17 x 13 tiles: fewer than CUs, too
+    many rows for the 128 x 128 tile), ragged last tiles in M and N, 8 stages."""
     require_gpu()
     from bit_quantized_lora_amd import ops
     M, K, N = 4112, 1024, 3088
@@ -260,10 +257,39 @@ def test_square_tile_lowrank_after_main_loop():
     rng = np.random.default_rng(528)
     spec = synth.LinearSpec("t", M, K, N, 16, 16, x_dist="t3")
     d = synth.make_linear(spec, rng)
-    say(f"[linear] square-tile low-rank after the main loop M={M} K={K} N={N}")
+    say(f"[linear] square tiles, one round, M={M} K={K} N={N}")
     gpu = _gpu_linear(d, path="codes")
     rows = np.unique(np.concatenate([_sample_strips(M, rng, 8), np.arange(M - 48, M)]))
-    _compare(gpu, _oracle_rows(d, rows), rows, "square-tile/tail")
+    _compare(gpu, _oracle_rows(d, rows), rows, "square-tile/one-round")
+
+
+# Big tiles with few stages and many ranks: ragged last tiles in M and N, both
+# tile shapes, 3-4 stages, no low-rank term, the largest rank (8 chunks of 16
+# ranks), ranks from both factors, and the backward's transposed GEMM.
+BIG_EDGES = [
+    # (M, K, N, rs, r)
+    (4624, 384, 4624, 16, 0),
+    (4624, 384, 4624, 64, 64),
+    (4624, 512, 4624, 0, 0),
+    (4624, 512, 4624, 48, 16),
+    (4592, 384, 12272, 64, 64),
+    (4624, 4624, 512, 16, 16),     # the dX GEMM reduces over 512: pipelined, square tiles
+]
+
+
+@pytest.mark.parametrize("case", BIG_EDGES, ids=lambda c: "x".join(map(str, c)))
+def test_big_tile_edges(case):
+    require_gpu()
+    from bit_quantized_lora_amd import ops
+    M, K, N, rs, r = case
+    say(f"[linear] big tiles {case}: fwd plan {ops.linear_plan(M, N, K)}, dX plan "
+        f"{ops.linear_plan(M, N, K, backward=True)}")
+    rng = np.random.default_rng(M + K + N + rs)
+    spec = synth.LinearSpec("t", M, K, N, rs, r, x_outlier_frac=0.01, x_outlier_mult=50.0)
+    d = synth.make_linear(spec, rng)
+    gpu = _gpu_linear(d)
+    rows = np.unique(np.concatenate([_sample_strips(M, rng, 10), np.arange(M - 48, M)]))
+    _compare(gpu, _oracle_rows(d, rows), rows, f"big-tiles{case}")
 
 
 # Few tokens: the 512 text tokens of a FLUX block (configuration 5's text-stream
