@@ -270,7 +270,7 @@ __device__ __forceinline__ void store_acc_bf16_lds(AccT<TMI, TNI>& acc, const Ge
   for (int it = 0; it < PER; ++it) {
     const int e = tid + 64 * NWAVES * it, r = e / CH, c = e - (e / CH) * CH;
     const int64_t row = m0 + r, col = n0 + 8 * c;
-    if (row < g.M && col < g.N) *reinterpret_cast<v4i*>(C + row * g.ldc + col) = val[it];
+    if (row < g.M && col < g.N) __builtin_nontemporal_store(val[it], reinterpret_cast<v4i*>(C + row * g.ldc + col));
   }
 }
 
