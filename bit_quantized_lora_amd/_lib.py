@@ -48,6 +48,7 @@ _SIGS = {
                       c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                       c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_linear_bwd_workspace": [c_int64, c_int64, c_int64, c_int32],
+    "ft_linear_bwd_plan": [c_int64, c_int64, c_int64, c_int32, c_int32, c_void_p],
     "ft_linear_bwd_noalloc": [c_int64, c_int64, c_int64, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                               c_void_p, c_int32, c_void_p, c_void_p, c_void_p],

@@ -1,6 +1,7 @@
 // Internal launch interfaces shared between the ft entry points.
 #pragma once
 
+#include "adapter_tile.h"
 #include "ft_common.h"
 
 namespace ft {
@@ -26,6 +27,9 @@ struct GemmArgs {
   // 128-K stages [s nkt / splits, (s+1) nkt / splits) and writes its fp32
   // partial tile to part[s][M][N]; the low-rank term belongs to split 0
   float* part = nullptr; int splits = 1;
+  // backward only: the adapter gradients taken by extra workgroups of the launch
+  // (launch_gemm_w4a4_adapt fills the plan fields)
+  AdaptArgs ad{};
 };
 
 // beside: other kernels run concurrently on the device (tile choice leaves them CUs).
@@ -40,6 +44,20 @@ size_t gemm_w4a4_workspace(int64_t M, int64_t N, int64_t K);
 // the tile (rows x columns) and split count launch_gemm_w4a4 takes for a shape
 ft_status gemm_w4a4_plan(int64_t M, int64_t N, int64_t K, bool beside, bool can_split, int* tile_m, int* tile_n,
                          int* splits);
+
+// The backward's dX GEMM (trans_b) with the adapter gradients of g.ad (P, Q, out,
+// ncols, M, ldp, poff, r set by the caller; out[1] may be null) computed by
+// extra workgroups of the same launch, plus, when the plan splits reductions,
+// the kernels that add the split partials (all on stream s).  gemm_ws: as for
+// launch_gemm_w4a4 (the GEMM's split partials, or nullptr); adapt_ws: at least
+// gemm_w4a4_adapt_workspace bytes for the adapter's token-range partials.
+// FT_ENOTSUP for shapes it does not take (no pipelined kernel, r > 64, an empty
+// dimension): the caller then runs the GEMM and the adapter kernels separately.
+ft_status launch_gemm_w4a4_adapt(const GemmArgs& g, bool out_bf16, hipStream_t s, void* gemm_ws, void* adapt_ws);
+bool gemm_w4a4_adapt_ok(const GemmArgs& g);
+size_t gemm_w4a4_adapt_workspace(const GemmArgs& g, bool can_split);
+// adapter workgroups and token ranges the launch takes (nothing runs)
+void gemm_w4a4_adapt_plan(const GemmArgs& g, bool can_split, bool with_db, int* nwg, int* splits);
 
 // Forward GEMM (bf16 Y) with the MLP fusion epilogue: also H = GELU(Y) and Q(H)
 // (g.H, g.hq, g.hs).  FT_ENOTSUP when K is not a multiple of 128 (no pipelined

@@ -390,12 +390,25 @@ __device__ __forceinline__ void store_gelu_quant_lds(AccT<TMI, TNI>& acc, const 
 // SPLIT: split reduction (GemmArgs::splits, ::part): work item v = s * tiles + t
 // takes split s of tile t and stores its fp32 partial tile; split 0 alone adds
 // the low-rank term.
-template <bool OUT_BF16, bool TRANS_B, int CFG, bool GELU_Q = false, int GS = 0, bool SPLIT = false>
+// ANRT > 0: workgroups past the GEMM's 8 * per_xcd compute the adapter
+// gradients of g_in.ad (adapter_tile.h; r <= 32 ANRT) in chunks of AD_CH tokens
+// per wave.
+
+template <bool OUT_BF16, bool TRANS_B, int CFG, bool GELU_Q = false, int GS = 0, bool SPLIT = false,
+          int ANRT = 0>
 __global__ void __launch_bounds__(PGT, cfg_occ(CFG))   // CFG: 0 square, 1 wide, 2 small tile
 gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
   using C = typename CfgOf<CFG, GS>::type;
   static_assert(!(SPLIT && GELU_Q), "the MLP fusion epilogue needs the whole reduction");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
+  if constexpr (ANRT > 0) {
+    static_assert(ad_lds_bytes(AD_CH) <= C::SMEM && PGT == AD_WAVES * 64, "adapter workgroup");
+    const int wg = (int)blockIdx.x - 8 * per_xcd;
+    if (wg >= 0) {
+      adapter_run<AD_CH, ANRT>(g_in.ad, wg, smem);
+      return;
+    }
+  }
   constexpr int BMc = C::BM, BNc = C::BN, NSc = C::NS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
@@ -921,6 +934,28 @@ __global__ void __launch_bounds__(256) split_sum_kernel(const float* __restrict_
   }
 }
 
+// dA^T and dB from the adapter workgroups' token-range partials: part[s] holds
+// [r x ncols0 | r x ncols1] fp32, added in range order.  Four consecutive
+// values per work item (both sizes are multiples of 16).
+__global__ void __launch_bounds__(256) adapter_sum_kernel(const float* __restrict__ part, int splits, int64_t n0,
+                                                          float* __restrict__ out0, int64_t n1,
+                                                          float* __restrict__ out1) {
+  const int64_t n = n0 + n1;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
+    v4f acc = *reinterpret_cast<const v4f*>(part + i);
+    for (int sp = 1; sp < splits; ++sp) {
+      const v4f x = *reinterpret_cast<const v4f*>(part + sp * n + i);
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    if (i < n0) *reinterpret_cast<v4f*>(out0 + i) = acc;
+    else *reinterpret_cast<v4f*>(out1 + (i - n0)) = acc;
+  }
+}
+
 // Launch plan of the pipelined kernel.
 struct GemmPlan {
   int cfg;          // 0: square 256 x 256 tiles, 1: wide 192 x 384, 2: small 128 x 128
@@ -978,6 +1013,54 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool beside, bool can_split)
   return p;
 }
 
+// Adapter workgroups of the backward GEMM launch: as many as the GEMM's last
+// round leaves slots free (they start at once, beside it), or one per slot when
+// it leaves fewer than an eighth (they follow it).  A unit is one 64-column strip
+// over one token range; the range count S minimizes the busiest workgroup's
+// rows (AD_ROW_US per 128-byte row on one CU, measured order of magnitude) plus,
+// for S > 1, the partials' round trip and the second launch.
+constexpr double AD_ROW_US = 0.005;
+constexpr double AD_SUM_US = 4.5;
+constexpr int AD_MAX_SPLITS = 16;
+constexpr int64_t AD_MIN_SPLIT_ROWS = 512;   // tokens per range when S > 1 (one 64-token chunk per wave)
+
+struct AdaptPlan {
+  int nwg, splits, units, strips0, strips1;
+  int64_t rows_per_split;
+};
+
+AdaptPlan plan_adapt(const GemmArgs& g, bool can_split, bool with_db) {
+  const GemmPlan gp = plan_gemm(g.M, g.N, g.K, true, can_split);
+  const int64_t slots = (int64_t)num_cus() * cfg_occ(gp.cfg);
+  const int64_t W = gp.tm * gp.tn * gp.splits;
+  const int64_t free_slots = (W + slots - 1) / slots * slots - W;
+  const int64_t na = free_slots >= slots / 8 ? free_slots : slots;
+  AdaptPlan best{};
+  best.strips0 = (int)((g.ad.ncols[0] + AD_COLS - 1) / AD_COLS);
+  best.strips1 = with_db ? (int)((g.ad.ncols[1] + AD_COLS - 1) / AD_COLS) : 0;
+  const int64_t strips = best.strips0 + best.strips1;
+  const int64_t n = (int64_t)g.ad.r * (g.ad.ncols[0] + (with_db ? g.ad.ncols[1] : 0));
+  double best_t = 1e300;
+  for (int S = 1; S <= AD_MAX_SPLITS; ++S) {
+    const int64_t rps = ((g.M + S - 1) / S + 63) / 64 * 64;
+    if (S > 1 && rps < AD_MIN_SPLIT_ROWS) break;
+    if ((g.M + rps - 1) / rps != S) continue;   // S whole 64-token ranges do not come out
+    const int64_t units = strips * S;
+    const int64_t nwg = units < na ? units : na;
+    // a split must save more than a tenth to be taken (the model is coarse)
+    const double t = (double)((units + nwg - 1) / nwg) * (double)rps * AD_ROW_US * (S > 1 ? 1.1 : 1.0) +
+                     (S > 1 ? AD_SUM_US + (double)(S + 1) * n * 4 / 5e6 : 0.0);
+    if (t < best_t) {
+      best_t = t;
+      best.nwg = (int)nwg;
+      best.splits = S;
+      best.units = (int)units;
+      best.rows_per_split = rps;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 ft_status gemm_w4a4_plan(int64_t M, int64_t N, int64_t K, bool beside, bool can_split, int* tile_m, int* tile_n,
@@ -1004,6 +1087,22 @@ size_t gemm_w4a4_workspace(int64_t M, int64_t N, int64_t K) {
   return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+namespace {
+// C from the split partials g.part (the second kernel of a split launch)
+ft_status launch_split_sum(const GemmArgs& g, int splits, bool out_bf16, hipStream_t s) {
+  const int64_t items = g.M * (g.N / 4);
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > 16 * (int64_t)num_cus()) blocks = 16 * (int64_t)num_cus();
+  if (out_bf16)
+    hipLaunchKernelGGL((split_sum_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, g.part, splits, g.M, g.N,
+                       g.C, g.ldc);
+  else
+    hipLaunchKernelGGL((split_sum_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, g.part, splits, g.M, g.N,
+                       g.C, g.ldc);
+  return launch_status();
+}
+}  // namespace
+
 ft_status launch_gemm_w4a4(const GemmArgs& g_in, bool out_bf16, bool trans_b, hipStream_t s, bool beside,
                            void* ws) {
   if (g_in.M == 0 || g_in.N == 0) return FT_OK;
@@ -1024,15 +1123,7 @@ ft_status launch_gemm_w4a4(const GemmArgs& g_in, bool out_bf16, bool trans_b, hi
       if (trans_b) FT_GEMM_LAUNCH(false, true, 2, true); else FT_GEMM_LAUNCH(false, false, 2, true);
       const ft_status st = launch_status();
       if (st != FT_OK) return st;
-      const int64_t items = g.M * (g.N / 4);
-      int64_t blocks = (items + 255) / 256;
-      if (blocks > 16 * (int64_t)num_cus()) blocks = 16 * (int64_t)num_cus();
-      if (out_bf16)
-        hipLaunchKernelGGL((split_sum_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, g.part, p.splits, g.M,
-                           g.N, g.C, g.ldc);
-      else
-        hipLaunchKernelGGL((split_sum_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, g.part, p.splits,
-                           g.M, g.N, g.C, g.ldc);
+      return launch_split_sum(g, p.splits, out_bf16, s);
     } else if (p.cfg == 2) {
       if (out_bf16) { if (trans_b) FT_GEMM_LAUNCH(true, true, 2, false); else FT_GEMM_LAUNCH(true, false, 2, false); }
       else { if (trans_b) FT_GEMM_LAUNCH(false, true, 2, false); else FT_GEMM_LAUNCH(false, false, 2, false); }
@@ -1050,6 +1141,91 @@ ft_status launch_gemm_w4a4(const GemmArgs& g_in, bool out_bf16, bool trans_b, hi
   if (out_bf16) hipLaunchKernelGGL((gemm_w4a4_generic_kernel<true>), grid, block, 0, s, g_in);
   else hipLaunchKernelGGL((gemm_w4a4_generic_kernel<false>), grid, block, 0, s, g_in);
   return launch_status();
+}
+
+bool gemm_w4a4_adapt_ok(const GemmArgs& g) {   // the shape (the launch checks the pointers)
+  if (!(g.M > 0 && g.N > 0 && pipelined_ok(g) && g.ad.r > 0 && g.ad.r <= AD_MAX_R && g.ad.r % 16 == 0 &&
+        g.ad.ncols[0] == g.N && g.ad.ncols[1] == g.K && g.ad.M == g.M && g.ad.ldp >= g.ad.poff + g.ad.r &&
+        (g.M + BM - 1) / BM * ((g.N + BN - 1) / BN) < ((int64_t)1 << 28)))
+    return false;
+  // the adapter's 32-bit buffer offsets cover a token range of Q and of P (P's
+  // row bound taken at the largest rs + r, so that the choice does not depend on rs)
+  const int64_t ncmax = g.ad.ncols[0] > g.ad.ncols[1] ? g.ad.ncols[0] : g.ad.ncols[1];
+  if (g.M * ncmax * 2 >= ((int64_t)1 << 31) || g.M * 128 * 4 >= ((int64_t)1 << 31)) return false;
+  // two rank tiles only beside the big tiles (the small tile keeps two workgroups per CU)
+  if (g.ad.r > 32 && (plan_gemm(g.M, g.N, g.K, true, false).cfg == 2 || plan_gemm(g.M, g.N, g.K, true, true).cfg == 2))
+    return false;
+  return true;
+}
+
+size_t gemm_w4a4_adapt_workspace(const GemmArgs& g, bool can_split) {
+  if (!gemm_w4a4_adapt_ok(g)) return 0;
+  size_t b = 0;
+  for (int with_db = 0; with_db < 2; ++with_db) {   // with and without dB (a caller may leave it out)
+    const AdaptPlan ap = plan_adapt(g, can_split, with_db != 0);
+    const size_t n = (size_t)g.ad.r * (size_t)(g.ad.ncols[0] + (with_db ? g.ad.ncols[1] : 0));
+    if (ap.splits > 1 && (size_t)ap.splits * n * sizeof(float) > b) b = (size_t)ap.splits * n * sizeof(float);
+  }
+  return b;
+}
+
+void gemm_w4a4_adapt_plan(const GemmArgs& g, bool can_split, bool with_db, int* nwg, int* splits) {
+  *nwg = 0;
+  *splits = 1;
+  if (!gemm_w4a4_adapt_ok(g)) return;
+  const AdaptPlan ap = plan_adapt(g, can_split, with_db);
+  *nwg = ap.nwg;
+  *splits = ap.splits;
+}
+
+ft_status launch_gemm_w4a4_adapt(const GemmArgs& g_in, bool out_bf16, hipStream_t s, void* gemm_ws, void* adapt_ws) {
+  if (!gemm_w4a4_adapt_ok(g_in)) return FT_ENOTSUP;
+  if (!g_in.ad.P[0] || !g_in.ad.Q[0] || !g_in.ad.out[0] || (g_in.ad.out[1] && (!g_in.ad.P[1] || !g_in.ad.Q[1])))
+    return FT_EINVAL;
+  const GemmPlan p = plan_gemm(g_in.M, g_in.N, g_in.K, true, gemm_ws != nullptr);
+  const AdaptPlan ap = plan_adapt(g_in, gemm_ws != nullptr, g_in.ad.out[1] != nullptr);
+  if (ap.splits > 1 && !adapt_ws) return FT_EINVAL;
+  GemmArgs g = g_in;
+  g.splits = p.splits;
+  g.part = static_cast<float*>(gemm_ws);
+  g.ad.strips[0] = ap.strips0;
+  g.ad.strips[1] = ap.strips1;
+  g.ad.splits = ap.splits;
+  g.ad.rows_per_split = ap.rows_per_split;
+  g.ad.units = ap.units;
+  g.ad.nwg = ap.nwg;
+  g.ad.part = static_cast<float*>(adapt_ws);
+  const int per_xcd = (int)((p.tm * p.tn * p.splits + 7) / 8);
+  const dim3 grid((unsigned)(8 * per_xcd + ap.nwg)), block(PGT);
+  const int tm = (int)p.tm, tn = (int)p.tn;
+#define FT_GEMM_LAUNCH_AD(OB, C, SP, NRT) \
+  hipLaunchKernelGGL((gemm_w4a4_kernel<OB, true, C, false, 0, SP, NRT>), grid, block, 0, s, g, tm, tn, per_xcd)
+  const bool two = g.ad.r > 32;   // never with the small tile (gemm_w4a4_adapt_ok)
+  if (p.splits > 1) FT_GEMM_LAUNCH_AD(false, 2, true, 1);
+  else if (p.cfg == 2) { if (out_bf16) FT_GEMM_LAUNCH_AD(true, 2, false, 1); else FT_GEMM_LAUNCH_AD(false, 2, false, 1); }
+  else if (p.cfg == 1) {
+    if (two) { if (out_bf16) FT_GEMM_LAUNCH_AD(true, 1, false, 2); else FT_GEMM_LAUNCH_AD(false, 1, false, 2); }
+    else { if (out_bf16) FT_GEMM_LAUNCH_AD(true, 1, false, 1); else FT_GEMM_LAUNCH_AD(false, 1, false, 1); }
+  } else {
+    if (two) { if (out_bf16) FT_GEMM_LAUNCH_AD(true, 0, false, 2); else FT_GEMM_LAUNCH_AD(false, 0, false, 2); }
+    else { if (out_bf16) FT_GEMM_LAUNCH_AD(true, 0, false, 1); else FT_GEMM_LAUNCH_AD(false, 0, false, 1); }
+  }
+#undef FT_GEMM_LAUNCH_AD
+  ft_status st = launch_status();
+  if (st != FT_OK) return st;
+  if (p.splits > 1) {
+    st = launch_split_sum(g, p.splits, out_bf16, s);
+    if (st != FT_OK) return st;
+  }
+  if (ap.splits > 1) {
+    const int64_t n0 = (int64_t)g.ad.r * g.ad.ncols[0], n1 = g.ad.out[1] ? (int64_t)g.ad.r * g.ad.ncols[1] : 0;
+    int64_t blocks = ((n0 + n1) / 4 + 255) / 256;
+    if (blocks > 16 * (int64_t)num_cus()) blocks = 16 * (int64_t)num_cus();
+    hipLaunchKernelGGL(adapter_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g.ad.part, ap.splits, n0,
+                       g.ad.out[0], n1, g.ad.out[1]);
+    st = launch_status();
+  }
+  return st;
 }
 
 ft_status launch_gemm_w4a4_gelu_quant(const GemmArgs& g, hipStream_t s) {

@@ -17,11 +17,12 @@ int64_t op_groups(int64_t k) { return (k + 127) / 128; }
 ft_status adapter_grads(int64_t M, int64_t N, int64_t K, const float* V, int rs, int r, const void* X,
                         const void* G, const float* T, float* dAt, float* dB, void* workspace, hipStream_t stream);
 
-// The adapter gradients do not depend on the dX GEMM.  They run on a second
-// stream that forks from the caller's stream after the GEMM is enqueued and
-// joins it again before the call returns, so the memory-bound reductions use
-// the CUs the GEMM leaves idle (e.g. 216 tiles on 256 CUs) instead of
-// following it.  Per device, the library creates once (on first use) one side
+// The adapter gradients do not depend on the dX GEMM.  Where the GEMM kernel
+// takes them in its own launch (launch_gemm_w4a4_adapt: r <= 64, K a multiple
+// of 128) they run on the CUs its last round leaves free.  Otherwise they run
+// on a second stream that forks from the caller's stream after the GEMM is
+// enqueued and joins it again before the call returns, so the memory-bound
+// reductions still use the CUs the GEMM leaves idle instead of following it.  Per device, the library creates once (on first use) one side
 // stream (default priority) and one fork and one join event.  An event may be
 // recorded again as soon as a wait on it has been enqueued (the wait takes the
 // record that precedes it), so the pair is reused by every call; a mutex keeps
@@ -193,12 +194,54 @@ extern "C" ft_status ft_linear_fwd_gelu(int64_t M, int64_t N, int64_t K, ft_scal
   return s2;
 }
 
-// [dA partials | dB partials | the dX GEMM's split partials]
+namespace ft {
+namespace {
+// The dX GEMM of the backward: M x K output, reduction over N.  With the
+// adapter gradients in the same launch (bwd_gemm_args(...).ad set), the
+// backward's workspace is [adapter token-range partials | the GEMM's split
+// partials]; otherwise [dA partials | dB partials | the GEMM's split partials].
+GemmArgs bwd_shape(int64_t M, int64_t N, int64_t K, int rs, int r) {
+  GemmArgs g{};
+  g.M = M; g.N = K; g.K = N;
+  g.lda = N / 2; g.ldb = N / 2;
+  g.ad.M = M; g.ad.ldp = rs + r; g.ad.poff = rs; g.ad.r = r;
+  g.ad.ncols[0] = K; g.ad.ncols[1] = N;
+  return g;
+}
+size_t bwd_adapt_bytes(const GemmArgs& g) {
+  return align256(gemm_w4a4_adapt_workspace(g, gemm_w4a4_workspace(g.M, g.N, g.K) > 0));
+}
+}  // namespace
+}  // namespace ft
+
+// One size for every backward entry point: the larger of the two layouts (the
+// _op, _g16 and _grp backwards always take the separate adapter kernels).
 extern "C" size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r) {
   using namespace ft;
   if (M < 0 || N < 0 || K < 0 || r < 0) return 0;
-  return align256(lora_grad_workspace(M, K, r)) + align256(lora_grad_workspace(M, N, r)) +
-         gemm_w4a4_workspace(M, K, N);
+  const size_t sep = align256(lora_grad_workspace(M, K, r)) + align256(lora_grad_workspace(M, N, r)) +
+                     gemm_w4a4_workspace(M, K, N);
+  const GemmArgs g = bwd_shape(M, N, K, 0, r);   // the plan does not depend on rs
+  const size_t one = gemm_w4a4_adapt_ok(g) ? bwd_adapt_bytes(g) + gemm_w4a4_workspace(M, K, N) : 0;
+  return sep > one ? sep : one;
+}
+
+extern "C" ft_status ft_linear_bwd_plan(int64_t M, int64_t N, int64_t K, int32_t r, int32_t with_db,
+                                        int32_t* plan) {
+  using namespace ft;
+  if (!plan) return FT_EINVAL;
+  if (!mult16(M) || !mult16(N) || !mult16(K) || r < 0 || r % 16 || r > 128) return FT_ESHAPE;
+  const GemmArgs g = bwd_shape(M, N, K, 0, r);
+  const bool split = gemm_w4a4_workspace(M, K, N) > 0;
+  int tm = 0, tn = 0, sp = 1, nwg = 0, asp = 1;
+  const ft_status st = gemm_w4a4_plan(M, K, N, true, split, &tm, &tn, &sp);
+  gemm_w4a4_adapt_plan(g, split, with_db != 0, &nwg, &asp);
+  plan[0] = tm;
+  plan[1] = tn;
+  plan[2] = sp;
+  plan[3] = nwg;
+  plan[4] = asp;
+  return st;
 }
 
 namespace ft {
@@ -241,6 +284,17 @@ ft_status linear_bwd_impl(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
   g.Wb = static_cast<const uint16_t*>(At); g.rb = r;
   g.C = dX; g.ldc = K;
   const bool out_bf16 = dxdt == FT_OUT_BF16;
+  // the adapter gradients in the GEMM's launch (one kernel on the caller's stream)
+  GemmArgs ga = bwd_shape(M, N, K, rs, r);
+  if (gemm_w4a4_adapt_ok(ga)) {
+    g.ad = ga.ad;
+    g.ad.P[0] = V; g.ad.Q[0] = static_cast<const uint16_t*>(X); g.ad.out[0] = dAt;
+    if (dB) { g.ad.P[1] = T; g.ad.Q[1] = static_cast<const uint16_t*>(G); g.ad.out[1] = dB; }
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    const size_t a_bytes = bwd_adapt_bytes(ga);
+    void* gemm_ws = gemm_w4a4_workspace(M, K, N) ? w + a_bytes : nullptr;
+    return launch_gemm_w4a4_adapt(g, out_bf16, stream, gemm_ws, a_bytes ? w : nullptr);
+  }
   void* split_ws = nullptr;   // the last part of the workspace, when the GEMM splits its reduction
   if (gemm_w4a4_workspace(M, K, N))
     split_ws = static_cast<uint8_t*>(workspace) + align256(lora_grad_workspace(M, K, r)) +

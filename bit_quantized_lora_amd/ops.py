@@ -440,6 +440,15 @@ def linear_bwd_workspace(M: int, N: int, K: int, r: int) -> int:
     return int(lib().ft_linear_bwd_workspace(M, N, K, r))
 
 
+def linear_bwd_plan(M: int, N: int, K: int, r: int, with_db: bool = True):
+    """(tile_m, tile_n, gemm_splits, adapter_workgroups, adapter_splits) of
+    ft_linear_bwd (adapter_workgroups 0: the adapter gradients on the side stream)."""
+    import ctypes
+    out = (ctypes.c_int32 * 5)()
+    check("ft_linear_bwd_plan", lib().ft_linear_bwd_plan(M, N, K, r, int(with_db), ctypes.addressof(out)))
+    return tuple(int(v) for v in out)
+
+
 def _bwd_common(V, L1t, At, X, G, T, M, N, K, dX, dAt, dB, out_dtype, x_name="X", g_name="G"):
     """Shared checks and output allocation of the backward calls: returns (rs, r, dX, dAt, dB)."""
     rs, r = _up_factors(L1t, At, K, names=("L1t", "At"))

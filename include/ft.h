@@ -267,7 +267,16 @@ ft_status ft_linear_plan(int64_t M, int64_t N, int64_t K, int32_t backward, int3
  *  workspace  device scratch of at least ft_linear_bwd_workspace(M, N, K, r)
  *             bytes (partial sums of the reductions over M, and, for few
  *             tokens, of the dX GEMM's split reduction over N as in
- *             ft_linear_fwd_ws). */
+ *             ft_linear_fwd_ws).
+ * For r <= 64 (r <= 32 where the dX GEMM takes 128 x 128 tiles) and K a
+ * multiple of 128 the adapter gradients are computed by extra workgroups of the
+ * dX GEMM's own launch: the call enqueues that kernel (plus, where reductions
+ * are split, the kernels that add the partials) on `stream` only.  Otherwise
+ * they run on a second stream the library creates once per device (default
+ * priority) that forks from and joins `stream` through two events.  Either way
+ * the results are complete in `stream`'s order when the call's work is; they
+ * depend only on the shape and the device's compute-unit count
+ * (ft_linear_bwd_plan). */
 ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
                         const uint8_t* gq_codes, const void* gq_scales,
                         const uint8_t* rq_codes_cm, const void* rq_scales_cm,
@@ -276,7 +285,17 @@ ft_status ft_linear_bwd(int64_t M, int64_t N, int64_t K, ft_scale_mode mode,
                         void* dX, ft_out_dtype dxdt, float* dAt, float* dB,
                         void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of workspace for ft_linear_bwd and for the _op, _g16 and _grp backwards
+ * (one size serves them all). */
 size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/* ft_linear_bwd_plan -- how ft_linear_bwd launches (for tests and profiling;
+ * nothing is run).  plan holds 5 int32: plan[0] x plan[1] the dX GEMM's output
+ * tile, plan[2] its reduction splits, plan[3] the adapter-gradient workgroups in
+ * the same launch (0: the adapter gradients run as separate kernels on the
+ * side stream), plan[4] the token ranges those workgroups split the reductions
+ * over M into.  with_db 0: the plan of a call with dB = NULL. */
+ft_status ft_linear_bwd_plan(int64_t M, int64_t N, int64_t K, int32_t r, int32_t with_db, int32_t* plan);
 
 /* ft_linear_bwd_noalloc -- ft_linear_bwd for callers that cannot allocate device
  * memory (code under stream capture, tight loops, harnesses that forbid
@@ -285,7 +304,8 @@ size_t ft_linear_bwd_workspace(int64_t M, int64_t N, int64_t K, int32_t r);
  * area of FT_NOALLOC_SCRATCH_BYTES that the library keeps per GPU (a device
  * array, resident until the process ends; its address is looked up on the first
  * call on each device).  The call allocates nothing and creates no stream or
- * event: the adapter gradients run after the dX GEMM on the given stream.
+ * event: where ft_linear_bwd would use its side stream, the adapter gradients
+ * run after the dX GEMM on the given stream.
  *  - FT_ESPACE when ft_linear_bwd_workspace(M, N, K, r) exceeds
  *    FT_NOALLOC_SCRATCH_BYTES (every config of the method needs at most 27 MiB).
  *  - Every call on a GPU shares that GPU's scratch: calls that overlap in time

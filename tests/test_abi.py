@@ -80,9 +80,10 @@ def test_linear_argument_validation():
     assert lib.ft_linear_fwd(16, 16, 16, 0, p, p, p, p, p, p, 16, p, 16, p, 5, None) == L.FT_EINVAL
     assert lib.ft_linear_fwd(16, 16, 16, 0, None, p, p, p, p, p, 16, p, 16, p, 0, None) == L.FT_EINVAL
     assert lib.ft_linear_fwd(0, 16, 16, 0, None, None, None, None, None, None, 16, None, 16, None, 0, None) == L.FT_OK
-    ws = lib.ft_linear_bwd_workspace(4608, 12288, 3072, 16)
+    # 512 tokens: the dX GEMM splits its reduction, so the backward needs a workspace
+    ws = lib.ft_linear_bwd_workspace(512, 9216, 3072, 32)
     assert ws > 0
-    args = [4608, 12288, 3072, 0, p, p, p, p, p, p, 32, p, 16, p, p, p, p, 0, p, p]
+    args = [512, 9216, 3072, 0, p, p, p, p, p, p, 32, p, 32, p, p, p, p, 0, p, p]
     assert lib.ft_linear_bwd(*args, p, 16, None) == L.FT_ESPACE
     assert lib.ft_linear_bwd(*args, None, 0, None) == L.FT_EINVAL
 
@@ -179,3 +180,19 @@ def test_noalloc_backward_rejects_requests_beyond_its_scratch():
     # every config of the method fits
     for (M, N, K, r) in ((18432, 9216, 3072, 64), (4608, 12288, 3072, 16), (4096, 3072, 12288, 32)):
         assert lib.ft_linear_bwd_workspace(M, N, K, r) <= L.FT_NOALLOC_SCRATCH_BYTES
+
+
+def test_backward_plan_query():
+    """ft_linear_bwd_plan validates its arguments and describes a launch: the
+    dX GEMM's tile and splits, the adapter workgroups of the same launch and
+    their token ranges (no GPU needed: the plan uses the CU count, 256 without
+    a device)."""
+    L = _lib(); lib = L.lib()
+    plan = (ctypes.c_int32 * 5)()
+    assert lib.ft_linear_bwd_plan(4608, 12288, 3072, 16, 1, None) == L.FT_EINVAL
+    assert lib.ft_linear_bwd_plan(4608, 12288, 3000, 16, 1, ctypes.addressof(plan)) == L.FT_ESHAPE
+    assert lib.ft_linear_bwd_plan(4608, 12288, 3072, 24, 1, ctypes.addressof(plan)) == L.FT_ESHAPE
+    assert lib.ft_linear_bwd_plan(4608, 12288, 3072, 16, 1, ctypes.addressof(plan)) == L.FT_OK
+    assert plan[3] > 0 and plan[4] >= 1                      # adapter workgroups in the GEMM launch
+    assert lib.ft_linear_bwd_plan(4608, 12288, 3072, 96, 1, ctypes.addressof(plan)) == L.FT_OK
+    assert plan[3] == 0                                      # r > 64: side stream
