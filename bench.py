@@ -637,7 +637,8 @@ def time_configs(reps, cache, oracle_rows=128):
     block's eight linears (per stream: qkv and proj on their own inputs, up ->
     GELU -> down chained).  Reported: step time (median over `reps` steps),
     4-bit GEMM work of the step per second and its fraction of the FP4 peak, each
-    linear's forward GEMM alone (launched back to back), the quantizer's rate on
+    linear's forward GEMM and its backward call (dX GEMM with the adapter
+    gradients) alone, launched back to back, the quantizer's rate on
     the config's first input, and the oracle's time on a bounded sample of every
     linear (the first `oracle_rows` tokens, scaled to the full token count)."""
     import torch
@@ -691,6 +692,19 @@ def time_configs(reps, cache, oracle_rows=128):
             us = g0.elapsed_time(g1) * 1e3 / reps
             tf = 2.0 * lin.M * lin.N * lin.K / us / 1e6
             gemms[n] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+        bwds = {}   # ft_linear_bwd alone: the dX GEMM with the adapter gradients (TFLOP/s of the dX GEMM's 2MNK)
+        for n, lin in lins.items():
+            for _ in range(2):
+                lin.gemm_bwd_and_grads()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record(s)
+            for _ in range(reps):
+                lin.gemm_bwd_and_grads()
+            g1.record(s)
+            g1.synchronize()
+            us = g0.elapsed_time(g1) * 1e3 / reps
+            tf = 2.0 * lin.M * lin.N * lin.K / us / 1e6
+            bwds[n] = {"us": round(us, 2), "TFLOPs": round(tf, 1), "frac_fp4_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
         first = lins[ds[0]["spec"].name]
         q = ops.quant_block16(first.X, rm=True, cm=True)
         for _ in range(2):
@@ -713,6 +727,7 @@ def time_configs(reps, cache, oracle_rows=128):
             "step_TFLOPs": round(work / step_us / 1e6, 1),
             "step_frac_fp4_peak": round(work / step_us / 1e6 / FP4_PEAK_TFLOPS, 4),
             "fwd_gemm": gemms,
+            "bwd_dX_gemm_with_adapter_grads": bwds,
             "quantizer": {"shape": [first.M, first.K], "us": round(qus, 2), "GBps": round(qbytes / qus / 1e3, 1),
                           "note": "repeated on one input (partly served from the MALL when it fits)"},
             "oracle_s_full_est": round(orc_s, 2),
