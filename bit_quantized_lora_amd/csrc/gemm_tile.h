@@ -196,6 +196,90 @@ __device__ __forceinline__ void lowrank_into_acc(AccT<TMI, TNI>& acc, const Gemm
   }
 }
 
+// Low-rank term after the main loop, for ranks that fit one pass (rho <= CHUNK)
+// and tiles that fit one ring buffer each: W [rho x BNc] and P [BMc x rho] are
+// fetched by DMA during the last stages into ring buffers those stages no
+// longer need, so their loads overlap the main loop's last MFMAs, and the
+// products follow the last k-step.  LDS layouts, 16-byte chunks XOR-swizzled
+// against bank conflicts: W row j (pitch 2 BNc) keeps chunk c at c ^ (2 (j & 3)),
+// so the 4 rows of a transposing read fall in distinct banks; P row r (rho / 4
+// chunks) keeps chunk c at r (rho / 4) + (c ^ ((r >> 1) & 3)), so 8 consecutive
+// rows of a 16-byte read do.
+template <int NWAVES, int BNc>
+__device__ __forceinline__ void tail_issue_w(const GemmArgs& g, uint8_t* dst, int64_t n0, int wave, int lane) {
+  const int rho = g.ra + g.rb;
+  const __amdgpu_buffer_rsrc_t rWa =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wa, 0, (int)((int64_t)g.ra * g.N * 2), RSRC_FLAGS);
+  const __amdgpu_buffer_rsrc_t rWb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.Wb, 0, (int)((int64_t)g.rb * g.N * 2), RSRC_FLAGS);
+  for (int j = wave; j < rho; j += NWAVES) {
+    const bool in_a = j < g.ra;
+    const int jj = in_a ? j : j - g.ra;
+    const int c = lane ^ (2 * (j & 3));                          // the chunk this lane fetches
+    const int64_t n = n0 + 8 * c;
+    const uint32_t off = (lane < BNc / 8 && n < g.N) ? (uint32_t)(((int64_t)jj * g.N + n) * 2) : 0x80000000u;
+    if (lane < BNc / 8) {
+      if (in_a) dma16(rWa, dst + j * 2 * BNc, off);
+      else dma16(rWb, dst + j * 2 * BNc, off);
+    }
+  }
+}
+
+template <int NWAVES, int BMc>
+__device__ __forceinline__ void tail_issue_p(const GemmArgs& g, uint8_t* dst, int64_t m0, int wave, int lane) {
+  const int rho = g.ra + g.rb, cpr = rho / 4;
+  const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.P + m0 * rho), 0, (int)(min<int64_t>(BMc, g.M - m0) * rho * 4), RSRC_FLAGS);
+  const int nq = BMc * cpr / 64;                                 // 1-KiB DMAs (BMc * rho % 256 == 0)
+  for (int q = wave; q < nq; q += NWAVES) {
+    const int pos = 64 * q + lane, r = pos / cpr, cs = pos - r * cpr;
+    const int c = cs ^ ((r >> 1) & 3);
+    dma16(rP, dst + 1024 * q, (uint32_t)((r * cpr + c) * 16));
+  }
+}
+
+// acc += (P_hi + P_lo) W from the tiles tail_issue_w / tail_issue_p staged
+template <int TMI, int TNI, int BNc, int CHUNK>
+__device__ __forceinline__ void tail_lowrank_mma(AccT<TMI, TNI>& acc, const GemmArgs& g, const uint8_t* wbuf,
+                                                 const uint8_t* pbuf, int lane, int wm, int wn, int l32, int lh) {
+  const int rho = g.ra + g.rb, cpr = rho / 4;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);             // + 16 ks (+ 4 for the second read)
+  const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn 32 TNI + 32 j
+#pragma unroll
+  for (int ks = 0; ks < CHUNK / 16; ++ks) {
+    if (16 * ks < rho) {
+      v8bf wf[TNI];
+#pragma unroll
+      for (int j = 0; j < TNI; ++j) {
+        const int row = 16 * ks + tr_row, col = wn * 32 * TNI + 32 * j + tr_col;
+        const uint8_t* b0 = wbuf + row * 2 * BNc + (((col >> 3) ^ (2 * (row & 3))) << 4) + 2 * (col & 7);
+        const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0));
+        const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + 4 * 2 * BNc));
+        const v2i l2 = __builtin_bit_cast(v2i, lo4), h2 = __builtin_bit_cast(v2i, hi4);
+        wf[j] = __builtin_bit_cast(v8bf, v4i{l2.x, l2.y, h2.x, h2.y});
+      }
+#pragma unroll
+      for (int i = 0; i < TMI; ++i) {
+        const int r = wm * 32 * TMI + 32 * i + l32, c0 = 4 * ks + 2 * lh;
+        const v4f p0 = *reinterpret_cast<const v4f*>(pbuf + 16 * (r * cpr + (c0 ^ ((r >> 1) & 3))));
+        const v4f p1 = *reinterpret_cast<const v4f*>(pbuf + 16 * (r * cpr + ((c0 + 1) ^ ((r >> 1) & 3))));
+        const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16x2(pv[2 * e], pv[2 * e + 1], h[e], l[e]);
+        const v8bf phi = __builtin_bit_cast(v8bf, v4i{(int)h[0], (int)h[1], (int)h[2], (int)h[3]});
+        const v8bf plo = __builtin_bit_cast(v8bf, v4i{(int)l[0], (int)l[1], (int)l[2], (int)l[3]});
+#pragma unroll
+        for (int j = 0; j < TNI; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(phi, wf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(plo, wf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+}
+
 template <bool OUT_BF16, int TMI, int TNI>
 __device__ __forceinline__ void store_acc(AccT<TMI, TNI>& acc, const GemmArgs& g, int64_t m0, int64_t n0, int lane,
                                           int wm, int wn, int l32, int lh) {
