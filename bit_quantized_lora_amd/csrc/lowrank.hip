@@ -5,22 +5,26 @@
 // (forward: in = X, wa = L1^T, wb = A^T; backward: in = G, wa = L2, wb = B).
 //
 // HBM-bound (arithmetic intensity = rank FLOP/byte): the input is read exactly
-// once.  A workgroup owns 128 rows (4 waves x 32) and a contiguous range of
-// 128-column chunks of the reduction; the split over the reduction gives the
-// launch enough workgroups to keep every CU streaming.  Per chunk, the weight
-// slice [rank x 128] is copied to LDS once (buffer_load ... lds, 16-byte-chunk
-// XOR swizzle against bank conflicts) and shared by the 4 waves, while each wave
-// prefetches its own 32 input rows of the next chunk into registers.  Products
-// run on bf16 MFMA 32x32x16 with fp32 accumulation.  Each split writes its
-// partial sums to the workspace and a second pass adds the splits in a fixed
-// order, so the result is deterministic.
+// once.  A workgroup of 4 waves owns 64 rows and a contiguous range of
+// 256-column chunks of the reduction: two row groups of 32, each split into two
+// 128-column halves (column groups), so every row is fetched in 512-byte runs.
+// (The dB variant keeps 128 rows x 128 columns: 4 row groups, one column
+// group.)  The split over the reduction gives the launch enough workgroups to
+// keep every CU streaming.  Per chunk, the weight slices [rank x 128] are
+// copied to LDS once (buffer_load ... lds, 16-byte-chunk XOR swizzle against
+// bank conflicts) and shared by the waves, while each wave prefetches its own
+// 32 x 128 input block of the next chunk into registers.  Products run on bf16
+// MFMA 32x32x16 with fp32 accumulation; the column groups' partial products are
+// added through LDS in column-group order.  Each split writes its partial sums
+// to the workspace and a second pass adds the splits in a fixed order, so the
+// result is deterministic.
 //
 // ft_quant_lowrank adds the 4-bit quantizer Q(in) (16x16 blocks, power-of-two
-// scales, row-major E2M1 codes) to the same pass: a 128-row x 128-column chunk
-// is exactly 8 x 8 quantization blocks, already in registers for the
+// scales, row-major E2M1 codes) to the same pass: a wave's 32 x 128 block is
+// exactly 2 x 8 quantization blocks, already in registers for the
 // down-projection, so the input is read from HBM once for both (the LoRA fusion
 // of FourTune section 3.3 extended to the quantizer, which reads the same input).
-// Lane (l32, lh) of wave w holds 8 values of row 32w + l32 in each 16-column
+// Lane (l32, lh) of a wave holds 8 values of its row group's row l32 in each 16-column
 // block s; a block is spread over the 16 lanes of one DPP row and the matching
 // 16 lanes of the other wave half, so its maximum is a 16-lane DPP reduction and
 // one permlane32 swap across the halves.
@@ -87,21 +91,36 @@ __device__ __forceinline__ uint32_t abs_max8(const v4i& v) {
   return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
-int64_t chunks_per_split(int64_t M, int64_t Kin) {
-  const int64_t nchunks = (Kin + LR_CHUNK - 1) / LR_CHUNK;
-  const int64_t rblocks = (M + LR_ROWS - 1) / LR_ROWS;
-  int64_t s = (512 + rblocks - 1) / rblocks;        // aim for ~2 workgroups per CU
+// wc: waves of a workgroup side by side along the reduction (1, 2 or 4): a
+// workgroup owns LR_ROWS / wc rows and chunks of LR_CHUNK * wc columns
+int64_t chunks_per_split(int64_t M, int64_t Kin, int wc = 1) {
+  const int64_t nchunks = (Kin + LR_CHUNK * wc - 1) / (LR_CHUNK * wc);
+  const int64_t rblocks = (M + LR_ROWS / wc - 1) / (LR_ROWS / wc);
+  if (wc == 1) {
+    int64_t s = (512 + rblocks - 1) / rblocks;        // aim for ~2 workgroups per CU
+    if (s > nchunks) s = nchunks;
+    if (s < 1) s = 1;
+    int64_t cps = (nchunks + s - 1) / s;
+    return cps < 4 ? (nchunks < 4 ? nchunks : 4) : cps;   // at least 4 chunks of work per split
+  }
+  // at most ~2 workgroups per CU, all resident at once
+  int64_t s = 512 / rblocks;
   if (s > nchunks) s = nchunks;
   if (s < 1) s = 1;
-  int64_t cps = (nchunks + s - 1) / s;
-  return cps < 4 ? (nchunks < 4 ? nchunks : 4) : cps;   // at least 4 chunks of work per split
+  return (nchunks + s - 1) / s;
 }
 
-int64_t num_splits(int64_t M, int64_t Kin) {
-  const int64_t nchunks = (Kin + LR_CHUNK - 1) / LR_CHUNK;
-  const int64_t cps = chunks_per_split(M, Kin);
+int64_t num_splits(int64_t M, int64_t Kin, int wc = 1) {
+  const int64_t nchunks = (Kin + LR_CHUNK * wc - 1) / (LR_CHUNK * wc);
+  const int64_t cps = chunks_per_split(M, Kin, wc);
   return (nchunks + cps - 1) / cps;
 }
+
+// the column-group width of the plain, quantizing and GELU passes (the dB
+// variant keeps 128-row blocks): wide chunks give each row a longer contiguous
+// run per request (512 bytes at wc 2), which the HBM serves faster than the
+// 256-byte runs of 128-column chunks
+constexpr int LR_WC = 2;
 
 // dB partials of ft_quant_lowrank_db: the forward's T (fp32 [M x ldt], its LoRA
 // columns from toff), the adapter rank r (1..64), partials [row blocks][r][Kin]
@@ -117,48 +136,58 @@ constexpr int DB_GPITCH = 2 * LR_CHUNK + 16;   // bytes per LDS row of the stage
 // NCT: 32-wide rank column tiles (0..4); QUANT: also write Q(in); GELU: the
 // input is replaced by GELU(in) (written to hout [M x Kin]) before both; NDB:
 // 32-row tiles of the dB partials (0: none; 1 for r <= 32, 2 for r <= 64)
-template <int NCT, bool QUANT, bool GELU = false, int NDB = 0>
+template <int NCT, bool QUANT, bool GELU = false, int NDB = 0, int WC = 1>
 __global__ void __launch_bounds__(LR_THREADS)
 lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t ld_in,
                const uint16_t* __restrict__ wa, int ra, const uint16_t* __restrict__ wb, int rb,
                int64_t cps, float* __restrict__ out, int64_t out_split_stride,
                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint16_t* __restrict__ hout,
                DbArgs db) {
+  // WC waves side by side along the reduction: wave (rg, cq) = (wave / WC,
+  // wave % WC) owns rows 32 rg .. of the workgroup's RB and columns
+  // 128 cq .. of each CC-column chunk; its partial projection is added to the
+  // other column groups' through LDS at the end, in cq order
+  static_assert(WC == 1 || NDB == 0, "the dB variant uses 128-row blocks");
+  constexpr int RB = LR_ROWS / WC, CC = LR_CHUNK * WC;
   extern __shared__ __attribute__((aligned(1024))) uint8_t s_w[];   // 2 buffers of rho rows (+ dB staging)
-  const int wbuf_bytes = (ra + rb) * LR_WROW;
+  const int wslice = (ra + rb) * LR_WROW;          // one 128-column slice of the weight chunk
+  const int wbuf_bytes = wslice * WC;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = wave / WC, cq = wave % WC;
   const int rho = ra + rb;
   const int l32 = lane & 31, lh = lane >> 5;
-  const int64_t row0 = (int64_t)blockIdx.x * LR_ROWS;
-  const int64_t nchunks = (Kin + LR_CHUNK - 1) / LR_CHUNK;
+  const int64_t row0 = (int64_t)blockIdx.x * RB;
+  const int64_t nchunks = (Kin + CC - 1) / CC;
   const int64_t c_begin = (int64_t)blockIdx.y * cps;
   const int64_t c_end = min(nchunks, c_begin + cps);
 
-  const int64_t arow = row0 + 32 * wave + l32;
+  const int64_t arow = row0 + 32 * rg + l32;
   const bool arow_ok = arow < M;
   // input rows of this workgroup through a buffer resource: a lane past M or past
   // the reduction gets an out-of-range offset and reads zeros (no branches)
   const __amdgpu_buffer_rsrc_t rIn = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(in + row0 * ld_in), 0, (int)(min<int64_t>(LR_ROWS, M - row0) * ld_in * 2), RSRC_FLAGS);
-  const uint32_t in_off = (uint32_t)(((32 * wave + l32) * ld_in + 8 * lh) * 2);
+      (void*)(in + row0 * ld_in), 0, (int)(min<int64_t>(RB, M - row0) * ld_in * 2), RSRC_FLAGS);
+  const uint32_t in_off = (uint32_t)(((32 * rg + l32) * ld_in + 8 * lh + 128 * cq) * 2);
 
   const __amdgpu_buffer_rsrc_t rWa =
       __builtin_amdgcn_make_buffer_rsrc((void*)wa, 0, (int)((int64_t)ra * Kin * 2), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rWb =
       __builtin_amdgcn_make_buffer_rsrc((void*)wb, 0, (int)((int64_t)rb * Kin * 2), RSRC_FLAGS);
 
-  // weight chunk c -> LDS buffer: DMA instruction i covers rank rows 4i .. 4i+3;
-  // lane l fills physical 16-byte chunk l & 15 of row 4i + l/16
+  // weight chunk c -> LDS buffer, one [rho x 128-column] slice after the other:
+  // DMA instruction i covers rank rows 4 (i / WC) .. +3 of slice i % WC; lane l
+  // fills physical 16-byte chunk l & 15 of row 4 (i / WC) + l / 16
   auto issue_w = [&](int buf, int64_t c) {
-    for (int i = wave; i < rho / 4; i += LR_THREADS / 64) {
-      const int row = 4 * i + (lane >> 4);
+    for (int i = wave; i < rho / 4 * WC; i += LR_THREADS / 64) {
+      const int ri = i / WC, cs = i - ri * WC;
+      const int row = 4 * ri + (lane >> 4);
       const int q = (lane & 15) ^ (row & 15);
-      const int64_t col = c * LR_CHUNK + 8 * q;
-      const bool in_a = 4 * i < ra;                   // ra is a multiple of 16: rows 4i..4i+3 share a matrix
+      const int64_t col = c * CC + 128 * cs + 8 * q;
+      const bool in_a = 4 * ri < ra;                  // ra is a multiple of 16: rows 4i..4i+3 share a matrix
       const int jj = in_a ? row : row - ra;
       const uint32_t off = col < Kin ? (uint32_t)(((int64_t)jj * Kin + col) * 2) : 0x80000000u;
-      uint8_t* dst = s_w + buf * wbuf_bytes + 4 * i * LR_WROW;
+      uint8_t* dst = s_w + buf * wbuf_bytes + cs * wslice + 4 * ri * LR_WROW;
       if (in_a) __builtin_amdgcn_raw_ptr_buffer_load_lds(rWa, (lds_void*)dst, 16, off, 0, 0, 0);
       else __builtin_amdgcn_raw_ptr_buffer_load_lds(rWb, (lds_void*)dst, 16, off, 0, 0, 0);
     }
@@ -166,8 +195,8 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
   auto load_x = [&](v4i (&a)[8], int64_t c) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int64_t k = c * LR_CHUNK + 16 * s;
-      const uint32_t off = (arow_ok && k < Kin) ? in_off + (uint32_t)(k * 2) : 0x80000000u;
+      const int64_t k = c * CC + 16 * s;              // + 128 cq (in in_off)
+      const uint32_t off = (arow_ok && k + 128 * cq < Kin) ? in_off + (uint32_t)(k * 2) : 0x80000000u;
       a[s] = __builtin_amdgcn_raw_buffer_load_b128(rIn, off, 0, 0);
     }
   };
@@ -216,7 +245,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       cw[s] = w;   // codes of columns 16s + 8lh .. +8 of this lane's row
     }
     if (!arow_ok) return;
-    const int64_t k0 = c * LR_CHUNK;
+    const int64_t k0 = c * CC + 128 * cq;
     uint8_t* crow = codes + arow * (Kin / 2) + k0 / 2;
     uint8_t* srow = scales + (arow / 16) * (Kin / 16) + k0 / 16;
     const bool sc_lane = lh == 0 && (l32 & 15) == 0;
@@ -262,7 +291,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       for (int k = 0; k < 4; ++k)
         o[k] = f32_to_bf16_rne(gelu_f(bf16lo_to_f32(w[k]))) | (f32_to_bf16_rne(gelu_f(bf16hi_to_f32(w[k]))) << 16);
       x[s] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-      const int64_t k0 = c * LR_CHUNK + 16 * s;
+      const int64_t k0 = c * CC + 128 * cq + 16 * s;
       if (arow_ok && k0 < Kin) *reinterpret_cast<v4i*>(hout + arow * Kin + k0 + 8 * lh) = x[s];
     }
   };
@@ -355,7 +384,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
         *reinterpret_cast<v4i*>(s_g + (32 * wave + l32) * DB_GPITCH + (16 * s + 8 * lh) * 2) = xc[s];
     }
     if constexpr (QUANT) quantize_chunk(xc, c);
-    const uint8_t* wbuf = s_w + buf * wbuf_bytes;
+    const uint8_t* wbuf = s_w + buf * wbuf_bytes + cq * wslice;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
@@ -379,13 +408,36 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
   }
 
   flush();
+  if constexpr (WC > 1 && NCT > 0) {
+    // the column groups' partial projections, added in cq order by the cq = 0 wave
+    compiler_fence();
+    __syncthreads();                                  // every wave done with the weight buffers
+    float* red = reinterpret_cast<float*>(s_w);       // [wave][NCT][16][64]
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((wave * NCT + ct) * 16 + r) * 64 + lane] = acc[ct][r];
+    __syncthreads();
+    if (cq == 0) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = acc[ct][r];
+#pragma unroll
+          for (int q = 1; q < WC; ++q) v += red[(((wave + q) * NCT + ct) * 16 + r) * 64 + lane];
+          acc[ct][r] = v;
+        }
+    }
+  }
   float* o = out + (int64_t)blockIdx.y * out_split_stride;
+  if (WC > 1 && cq != 0) return;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const int j = 32 * ct + l32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = row0 + 32 * wave + 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int64_t row = row0 + 32 * rg + 8 * (r >> 2) + 4 * lh + (r & 3);
       if (row < M && j < rho) o[row * rho + j] = acc[ct][r];
     }
   }
@@ -407,10 +459,14 @@ __global__ void sum_splits_kernel(const float* __restrict__ part, int64_t splits
 }  // namespace
 }  // namespace ft
 
+// split partials of either block shape (128-row blocks for the dB variant,
+// LR_WC column groups otherwise)
 extern "C" size_t ft_lowrank_workspace(int64_t M, int64_t Kin, int32_t rho) {
   using namespace ft;
   if (M <= 0 || Kin <= 0 || rho <= 0) return 0;
-  const int64_t S = num_splits(M, Kin);
+  int64_t S = num_splits(M, Kin, 1);
+  const int64_t S2 = num_splits(M, Kin, LR_WC);
+  if (S2 > S) S = S2;
   return S > 1 ? (size_t)(S * M * rho * sizeof(float)) : 0;
 }
 
@@ -444,10 +500,15 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
     db = *dbp;
     db.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_db);
   }
-  const int64_t cps = chunks_per_split(M, Kin);
-  const int64_t S = num_splits(M, Kin);
+  const int wc = dbp ? 1 : LR_WC;
+  const int64_t cps = chunks_per_split(M, Kin, wc);
+  const int64_t S = num_splits(M, Kin, wc);
   float* dst = (S > 1 && rho) ? static_cast<float*>(workspace) : out;
-  dim3 grid((unsigned)((M + LR_ROWS - 1) / LR_ROWS), (unsigned)S);
+  dim3 grid((unsigned)((M + LR_ROWS / wc - 1) / (LR_ROWS / wc)), (unsigned)S);
+  // LDS: two weight chunks of wc slices, and for wc > 1 the column groups' partial projections
+  const size_t lds_w = (size_t)2 * rho * LR_WROW * wc;
+  const size_t lds_red = wc > 1 ? (size_t)(LR_THREADS / 64) * ((rho + 31) / 32) * 16 * 64 * sizeof(float) : 0;
+  const size_t lds_wc = lds_w > lds_red ? lds_w : lds_red;
   const uint16_t* ip = static_cast<const uint16_t*>(in);
   const uint16_t* a = static_cast<const uint16_t*>(wa);
   const uint16_t* b = static_cast<const uint16_t*>(wb);
@@ -455,11 +516,11 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   const int nct = (rho + 31) / 32;
   uint16_t* hp = static_cast<uint16_t*>(hout);
 #define FT_LR_LAUNCH(N, Q)                                                                                   \
-  hipLaunchKernelGGL((lowrank_kernel<N, Q>), grid, dim3(LR_THREADS), (size_t)(2 * rho * LR_WROW), stream, ip, M, Kin, ld_in, a, ra, b, rb, \
-                     cps, dst, stride, codes, scales, hp, db)
+  hipLaunchKernelGGL((lowrank_kernel<N, Q, false, 0, LR_WC>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, \
+                     ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db)
 #define FT_LRG_LAUNCH(N)                                                                                     \
-  hipLaunchKernelGGL((lowrank_kernel<N, true, true>), grid, dim3(LR_THREADS), (size_t)(2 * rho * LR_WROW), stream, ip, M, Kin, ld_in, a, ra, \
-                     b, rb, cps, dst, stride, codes, scales, hp, db)
+  hipLaunchKernelGGL((lowrank_kernel<N, true, true, 0, LR_WC>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, \
+                     ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db)
   // dB partials: + (X A)^T hi/lo planes and the staged G chunk
 #define FT_LRD_LAUNCH(N, D)                                                                                  \
   hipLaunchKernelGGL((lowrank_kernel<N, true, false, D>), grid, dim3(LR_THREADS),                          \

@@ -402,9 +402,10 @@ def test_op_path_with_unmerged_pairs_in_both_operands(shape):
 @pytest.mark.parametrize("case", [(144, 400, 16, 16), (528, 1040, 32, 32), (272, 256, 0, 64), (4608, 12288, 32, 16),
                                   (48, 128, 64, 64)], ids=lambda c: "x".join(map(str, c)))
 def test_quant_lowrank_db_folds_the_adapter_gradient(case):
-    """The backward's pass over G with dB = (X A)^T G folded in: V, codes and scales
-    bit-identical to ft_quant_lowrank; dB within fp32 rounding of the separate
-    adapter-gradient pass of ft_linear_bwd and of the oracle's fp64 product."""
+    """The backward's pass over G with dB = (X A)^T G folded in: codes and scales
+    bit-identical to ft_quant_lowrank, V equal to it up to fp32 summation order
+    (this pass keeps 128-row blocks, ft_quant_lowrank adds two column groups per
+    64-row block), dB within fp32 rounding of the oracle's fp64 product."""
     require_gpu()
     import torch
     from bit_quantized_lora_amd import ops
@@ -420,7 +421,7 @@ def test_quant_lowrank_db_folds_the_adapter_gradient(case):
     V, codes, scales, dB = ops.quant_lowrank_db(g, l2, b, t)
     V0, codes0, scales0 = ops.quant_lowrank(g, l2, b)
     torch.cuda.synchronize()
-    assert np.array_equal(host(V).view(np.uint32), host(V0).view(np.uint32))
+    assert O.rel_frob(host(V).astype(np.float64), host(V0).astype(np.float64)) < 1e-6
     assert np.array_equal(host(codes), host(codes0)) and np.array_equal(host(scales), host(scales0))
     ref = T[:, rs:].astype(np.float64).T @ O.bf16_to_f64(G)
     assert O.rel_frob(host(dB).astype(np.float64), ref) < 1e-5
