@@ -8,8 +8,9 @@
 // once.  A workgroup of 4 waves owns 64 rows and a contiguous range of
 // 256-column chunks of the reduction: two row groups of 32, each split into two
 // 128-column halves (column groups), so every row is fetched in 512-byte runs.
-// (The dB variant keeps 128 rows x 128 columns: 4 row groups, one column
-// group.)  The split over the reduction gives the launch enough workgroups to
+// (The dB variant, and ranks above 64, whose weight buffers would then crowd
+// out the second workgroup per CU, keep 128 rows x 128 columns: 4 row groups,
+// one column group.)  The split over the reduction gives the launch enough workgroups to
 // keep every CU streaming.  Per chunk, the weight slices [rank x 128] are
 // copied to LDS once (buffer_load ... lds, 16-byte-chunk XOR swizzle against
 // bank conflicts) and shared by the waves, while each wave prefetches its own
@@ -459,8 +460,8 @@ __global__ void sum_splits_kernel(const float* __restrict__ part, int64_t splits
 }  // namespace
 }  // namespace ft
 
-// split partials of either block shape (128-row blocks for the dB variant,
-// LR_WC column groups otherwise)
+// split partials of either block shape (128-row blocks for the dB variant and
+// above 64 ranks, LR_WC column groups otherwise)
 extern "C" size_t ft_lowrank_workspace(int64_t M, int64_t Kin, int32_t rho) {
   using namespace ft;
   if (M <= 0 || Kin <= 0 || rho <= 0) return 0;
@@ -500,7 +501,9 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
     db = *dbp;
     db.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_db);
   }
-  const int wc = dbp ? 1 : LR_WC;
+  // column groups double the weight buffers: above 64 ranks (128 KB of LDS at
+  // rank 128) they would leave room for one workgroup per CU instead of two
+  const int wc = (dbp || rho > 64) ? 1 : LR_WC;
   const int64_t cps = chunks_per_split(M, Kin, wc);
   const int64_t S = num_splits(M, Kin, wc);
   float* dst = (S > 1 && rho) ? static_cast<float*>(workspace) : out;
@@ -516,11 +519,15 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   const int nct = (rho + 31) / 32;
   uint16_t* hp = static_cast<uint16_t*>(hout);
 #define FT_LR_LAUNCH(N, Q)                                                                                   \
-  hipLaunchKernelGGL((lowrank_kernel<N, Q, false, 0, LR_WC>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, \
-                     ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db)
+  if (wc > 1) hipLaunchKernelGGL((lowrank_kernel<N, Q, false, 0, LR_WC>), grid, dim3(LR_THREADS), lds_wc, stream, \
+                                 ip, M, Kin, ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db);     \
+  else hipLaunchKernelGGL((lowrank_kernel<N, Q>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, ld_in, a, ra, \
+                          b, rb, cps, dst, stride, codes, scales, hp, db)
 #define FT_LRG_LAUNCH(N)                                                                                     \
-  hipLaunchKernelGGL((lowrank_kernel<N, true, true, 0, LR_WC>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, \
-                     ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db)
+  if (wc > 1) hipLaunchKernelGGL((lowrank_kernel<N, true, true, 0, LR_WC>), grid, dim3(LR_THREADS), lds_wc, stream, \
+                                 ip, M, Kin, ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db);     \
+  else hipLaunchKernelGGL((lowrank_kernel<N, true, true>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, ld_in, \
+                          a, ra, b, rb, cps, dst, stride, codes, scales, hp, db)
   // dB partials: + (X A)^T hi/lo planes and the staged G chunk
 #define FT_LRD_LAUNCH(N, D)                                                                                  \
   hipLaunchKernelGGL((lowrank_kernel<N, true, false, D>), grid, dim3(LR_THREADS),                          \
