@@ -96,14 +96,16 @@ __device__ __forceinline__ void quad_transpose4(float (&v)[4], int t) {
 template <int TMI, int CHUNK>
 using PRegs = v4f[TMI][CHUNK / 16][2];
 
-// Loads of chunk jc (ranks jc .. jc+nr-1, nr = min(CHUNK, rho - jc)): W rows to LDS
-// (lanes 0 .. BNc/8-1: 16 bytes = 8 columns each), this wave's P rows to registers.
+// Loads of chunk jc (ranks jc .. jc+nr-1, nr = min(CHUNK, jend - jc); jend < 0:
+// all rho ranks): W rows to LDS (lanes 0 .. BNc/8-1: 16 bytes = 8 columns
+// each), this wave's P rows to registers.
 template <int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
 __device__ __forceinline__ void lowrank_load(PRegs<TMI, CHUNK>& p, const GemmArgs& g, uint8_t* smem, int jc,
-                                             int64_t m0, int64_t n0, int wave, int lane, int wm, int l32, int lh) {
+                                             int64_t m0, int64_t n0, int wave, int lane, int wm, int l32, int lh,
+                                             int jend = -1) {
   constexpr int W_PITCH = 2 * BNc + 32;
   const int rho = g.ra + g.rb;
-  const int nr = min(CHUNK, rho - jc);                           // multiple of 16
+  const int nr = min(CHUNK, (jend < 0 ? rho : jend) - jc);      // multiple of 16
   const __amdgpu_buffer_rsrc_t rWa =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.Wa, 0, (int)((int64_t)g.ra * g.N * 2), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rWb =
@@ -138,9 +140,9 @@ __device__ __forceinline__ void lowrank_load(PRegs<TMI, CHUNK>& p, const GemmArg
 // and visible to the workgroup)
 template <int TMI, int TNI, int BNc, int CHUNK>
 __device__ __forceinline__ void lowrank_mma(AccT<TMI, TNI>& acc, const PRegs<TMI, CHUNK>& p, const GemmArgs& g,
-                                            const uint8_t* smem, int jc, int lane, int wn) {
+                                            const uint8_t* smem, int jc, int lane, int wn, int jend = -1) {
   constexpr int W_PITCH = 2 * BNc + 32;
-  const int nr = min(CHUNK, g.ra + g.rb - jc);
+  const int nr = min(CHUNK, (jend < 0 ? g.ra + g.rb : jend) - jc);
   const int g16 = lane >> 4, s16 = lane & 15;
   const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);             // + 16 ks + 4 t
   const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn*32*TNI + 32 j
@@ -180,75 +182,78 @@ __device__ __forceinline__ void lowrank_mma(AccT<TMI, TNI>& acc, const PRegs<TMI
 template <int TMI, int TNI, int NWAVES, int BNc, int CHUNK>
 __device__ __forceinline__ void lowrank_into_acc(AccT<TMI, TNI>& acc, const GemmArgs& g, uint8_t* smem,
                                                  int64_t m0, int64_t n0, int tid, int wave, int wm, int wn,
-                                                 int l32, int lh, int jc0 = 0) {
+                                                 int l32, int lh, int jc0 = 0, int jend = -1) {
   const int lane = tid & 63;
-  for (int jc = jc0; jc < g.ra + g.rb; jc += CHUNK) {
+  const int je = jend < 0 ? g.ra + g.rb : jend;
+  for (int jc = jc0; jc < je; jc += CHUNK) {
     PRegs<TMI, CHUNK> p;
-    lowrank_load<TMI, TNI, NWAVES, BNc, CHUNK>(p, g, smem, jc, m0, n0, wave, lane, wm, l32, lh);
+    lowrank_load<TMI, TNI, NWAVES, BNc, CHUNK>(p, g, smem, jc, m0, n0, wave, lane, wm, l32, lh, je);
     compiler_fence();
     FT_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    lowrank_mma<TMI, TNI, BNc, CHUNK>(acc, p, g, smem, jc, lane, wn);
+    lowrank_mma<TMI, TNI, BNc, CHUNK>(acc, p, g, smem, jc, lane, wn, je);
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
   }
 }
 
-// Low-rank term after the main loop, for ranks that fit one pass (rho <= CHUNK)
-// and tiles that fit one ring buffer each: W [rho x BNc] and P [BMc x rho] are
-// fetched by DMA during the last stages into ring buffers those stages no
-// longer need, so their loads overlap the main loop's last MFMAs, and the
-// products follow the last k-step.  LDS layouts, 16-byte chunks XOR-swizzled
-// against bank conflicts: W row j (pitch 2 BNc) keeps chunk c at c ^ (2 (j & 3)),
-// so the 4 rows of a transposing read fall in distinct banks; P row r (rho / 4
-// chunks) keeps chunk c at r (rho / 4) + (c ^ ((r >> 1) & 3)), so 8 consecutive
-// rows of a 16-byte read do.
+// Low-rank term after the main loop for ranks j0 .. j0+nt-1 (nt <= CHUNK) whose
+// tiles fit one ring buffer each: W [nt x BNc] and P [BMc x nt] are fetched by
+// DMA during the last stages into ring buffers those stages no longer need, so
+// their loads overlap the main loop's last MFMAs, and the products follow the
+// last k-step.  LDS layouts, 16-byte chunks XOR-swizzled against bank conflicts:
+// W row j (pitch 2 BNc) keeps chunk c at c ^ (2 (j & 3)), so the 4 rows of a
+// transposing read fall in distinct banks; P row r (nt / 4 chunks) keeps chunk c
+// at r (nt / 4) + (c ^ ((r >> 1) & 3)), so 8 consecutive rows of a 16-byte read
+// do.
 template <int NWAVES, int BNc>
-__device__ __forceinline__ void tail_issue_w(const GemmArgs& g, uint8_t* dst, int64_t n0, int wave, int lane) {
-  const int rho = g.ra + g.rb;
+__device__ __forceinline__ void tail_issue_w(const GemmArgs& g, uint8_t* dst, int64_t n0, int wave, int lane, int j0,
+                                             int nt) {
   const __amdgpu_buffer_rsrc_t rWa =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.Wa, 0, (int)((int64_t)g.ra * g.N * 2), RSRC_FLAGS);
   const __amdgpu_buffer_rsrc_t rWb =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.Wb, 0, (int)((int64_t)g.rb * g.N * 2), RSRC_FLAGS);
-  for (int j = wave; j < rho; j += NWAVES) {
+  for (int jr = wave; jr < nt; jr += NWAVES) {
+    const int j = j0 + jr;                                       // rank; LDS row jr
     const bool in_a = j < g.ra;
     const int jj = in_a ? j : j - g.ra;
     const int c = lane ^ (2 * (j & 3));                          // the chunk this lane fetches
     const int64_t n = n0 + 8 * c;
     const uint32_t off = (lane < BNc / 8 && n < g.N) ? (uint32_t)(((int64_t)jj * g.N + n) * 2) : 0x80000000u;
     if (lane < BNc / 8) {
-      if (in_a) dma16(rWa, dst + j * 2 * BNc, off);
-      else dma16(rWb, dst + j * 2 * BNc, off);
+      if (in_a) dma16(rWa, dst + jr * 2 * BNc, off);
+      else dma16(rWb, dst + jr * 2 * BNc, off);
     }
   }
 }
 
 template <int NWAVES, int BMc>
-__device__ __forceinline__ void tail_issue_p(const GemmArgs& g, uint8_t* dst, int64_t m0, int wave, int lane) {
-  const int rho = g.ra + g.rb, cpr = rho / 4;
+__device__ __forceinline__ void tail_issue_p(const GemmArgs& g, uint8_t* dst, int64_t m0, int wave, int lane, int j0,
+                                             int nt) {
+  const int rho = g.ra + g.rb, cpr = nt / 4;
   const __amdgpu_buffer_rsrc_t rP = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.P + m0 * rho), 0, (int)(min<int64_t>(BMc, g.M - m0) * rho * 4), RSRC_FLAGS);
-  const int nq = BMc * cpr / 64;                                 // 1-KiB DMAs (BMc * rho % 256 == 0)
+  const int nq = BMc * cpr / 64;                                 // 1-KiB DMAs (BMc * nt % 256 == 0)
   for (int q = wave; q < nq; q += NWAVES) {
     const int pos = 64 * q + lane, r = pos / cpr, cs = pos - r * cpr;
     const int c = cs ^ ((r >> 1) & 3);
-    dma16(rP, dst + 1024 * q, (uint32_t)((r * cpr + c) * 16));
+    dma16(rP, dst + 1024 * q, (uint32_t)((r * rho + j0) * 4 + c * 16));
   }
 }
 
 // acc += (P_hi + P_lo) W from the tiles tail_issue_w / tail_issue_p staged
 template <int TMI, int TNI, int BNc, int CHUNK>
-__device__ __forceinline__ void tail_lowrank_mma(AccT<TMI, TNI>& acc, const GemmArgs& g, const uint8_t* wbuf,
-                                                 const uint8_t* pbuf, int lane, int wm, int wn, int l32, int lh) {
-  const int rho = g.ra + g.rb, cpr = rho / 4;
+__device__ __forceinline__ void tail_lowrank_mma(AccT<TMI, TNI>& acc, const uint8_t* wbuf, const uint8_t* pbuf,
+                                                 int nt, int lane, int wm, int wn, int l32, int lh) {
+  const int cpr = nt / 4;
   const int g16 = lane >> 4, s16 = lane & 15;
   const int tr_row = 8 * (g16 >> 1) + (s16 >> 2);             // + 16 ks (+ 4 for the second read)
   const int tr_col = 16 * (g16 & 1) + 4 * (s16 & 3);           // + wn 32 TNI + 32 j
 #pragma unroll
   for (int ks = 0; ks < CHUNK / 16; ++ks) {
-    if (16 * ks < rho) {
+    if (16 * ks < nt) {
       v8bf wf[TNI];
 #pragma unroll
       for (int j = 0; j < TNI; ++j) {

@@ -46,11 +46,12 @@
 // Low-rank term: W's slice is staged transposed in LDS; P is split into bf16
 // hi + lo (hi + lo = P to 2^-16 relative) and multiplied on bf16 MFMA 32x32x16,
 // so the fp32 low-rank intermediate keeps ~16 bits.  The pipelined kernel adds
-// it after the 4-bit products when its ranks fit one pass and its tiles fit the
-// ring buffers the last stages free (loaded during those stages), otherwise
-// before them, 16 ranks at a time.  The choice depends on the tile shape, the
-// ranks and the stage count only, not on the epilogue, so the launches of a
-// shape sum each output in the same order (the generic kernel adds it after).
+// its last ranks (up to one pass) after the 4-bit products when their tiles fit
+// the ring buffers the last stages free (loaded during those stages), and the
+// others before them, in passes of up to CHUNK ranks.  The split depends on the
+// tile shape, the ranks and the stage count only, not on the epilogue, so the
+// launches of a shape sum each output in the same order (the generic kernel
+// adds the whole term after the products).
 #include "ft_common.h"
 #include "ft_device.h"
 #include "ft_internal.h"
@@ -520,27 +521,30 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
 #pragma unroll
     for (int j = 0; j < C::TNI; ++j) acc[i][j] = v16f{};
 
-  // The low-rank up-projection P W.  When its ranks fit one pass and its W and P
-  // tiles fit one ring buffer each (and the reduction has at least NS stages),
-  // it follows the main loop: the tiles are fetched during the last stages into
-  // buffers those stages have freed (tail_issue_w).  Otherwise it goes into the
-  // accumulators first, in the buffer of stage NS-1 (free until the first
-  // steady iteration): the loads of its first chunk are issued ahead of the
-  // pipeline fill and awaited by count (the fill's DMAs, all younger, may stay
-  // in flight), so both overlap.  The choice depends only on the tile shape, the
-  // ranks and the stage count, so every kernel of a shape (plain, MLP-fusion
-  // epilogue, adapter workgroups) sums each output in the same order.
+  // The low-rank up-projection P W.  Its last nt ranks (all of them when they
+  // fit one pass, else the last CHUNK) follow the main loop when their W and P
+  // tiles fit one ring buffer each and the reduction has at least NS stages:
+  // the tiles are fetched during the last stages into buffers those stages have
+  // freed (tail_issue_w).  The other ranks go into the accumulators first, in
+  // the buffer of stage NS-1 (free until the first steady iteration): the loads
+  // of their first chunk are issued ahead of the pipeline fill and awaited by
+  // count (the fill's DMAs, all younger, may stay in flight), so both overlap;
+  // further chunks follow one by one.  The split depends only on the tile
+  // shape, the ranks and the stage count, so every kernel of a shape (plain,
+  // MLP-fusion epilogue, adapter workgroups) sums each output in the same order.
   const int rho = g.ra + g.rb;
-  const bool tail_lr = rho > 0 && rho <= C::CHUNK && rho * 2 * BNc <= C::STAGE && BMc * rho * 4 <= C::STAGE &&
-                       nkt >= NSc && (BMc * rho) % 256 == 0;
+  const int nt = rho <= C::CHUNK ? rho : C::CHUNK;
+  const bool tail_lr = rho > 0 && nt * 2 * BNc <= C::STAGE && BMc * nt * 4 <= C::STAGE && nkt >= NSc &&
+                       (BMc * nt) % 256 == 0;
+  const int rho_head = tail_lr ? rho - nt : rho;
   uint8_t* lr_smem = smem + (NSc - 1) * C::STAGE;
   PRegs<C::TMI, C::CHUNK> pr;
-  if (rho > 0 && !tail_lr)
-    lowrank_load<C::TMI, C::TNI, 8, BNc, C::CHUNK>(pr, g, lr_smem, 0, m0, n0, wave, lane, wm, l32, lh);
+  if (rho_head > 0)
+    lowrank_load<C::TMI, C::TNI, 8, BNc, C::CHUNK>(pr, g, lr_smem, 0, m0, n0, wave, lane, wm, l32, lh, rho_head);
 #pragma unroll
   for (int s = 0; s < NSc - 1; ++s)
     if (s < nkt) issue(s, s);
-  if (rho > 0 && !tail_lr) {
+  if (rho_head > 0) {
     compiler_fence();
     if (nkt >= NSc - 1) FT_WAIT_VMCNT(C::DPS * (NSc - 1));
     else if (nkt == 2) FT_WAIT_VMCNT(C::DPS * 2);
@@ -548,13 +552,13 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
     else FT_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, pr, g, lr_smem, 0, lane, wn);
+    lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, pr, g, lr_smem, 0, lane, wn, rho_head);
     compiler_fence();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    if (rho > C::CHUNK)
+    if (rho_head > C::CHUNK)
       lowrank_into_acc<C::TMI, C::TNI, 8, BNc, C::CHUNK>(acc, g, lr_smem, m0, n0, tid, wave, wm, wn, l32, lh,
-                                                         C::CHUNK);
+                                                         C::CHUNK, rho_head);
   }
 
   // Main loop, software-pipelined across the stage barrier.  Iteration kt reads
@@ -585,8 +589,9 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
       __builtin_amdgcn_s_barrier();
       compiler_fence();
       if (!steady && tail_lr) {   // from here on the buffer of stage kt-1 is free
-        if (kt == nkt - 3) tail_issue_w<8, BNc>(g, smem + ((nkt - 4) % NSc) * C::STAGE, n0, wave, lane);
-        else if (kt == nkt - 2) tail_issue_p<8, BMc>(g, smem + ((nkt - 3) % NSc) * C::STAGE, m0, wave, lane);
+        if (kt == nkt - 3) tail_issue_w<8, BNc>(g, smem + ((nkt - 4) % NSc) * C::STAGE, n0, wave, lane, rho_head, nt);
+        else if (kt == nkt - 2)
+          tail_issue_p<8, BMc>(g, smem + ((nkt - 3) % NSc) * C::STAGE, m0, wave, lane, rho_head, nt);
       }
       const uint8_t* nx = smem + __builtin_amdgcn_readfirstlane(((kt + 1) % NSc) * C::STAGE);
       read_part<C::TMI, C::TNI, BMc, BNc>(c0, nx, 0, wm, wn, l32, lh);
@@ -626,8 +631,8 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
     FT_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    tail_lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, g, smem + ((nkt - 4) % NSc) * C::STAGE,
-                                                    smem + ((nkt - 3) % NSc) * C::STAGE, lane, wm, wn, l32, lh);
+    tail_lowrank_mma<C::TMI, C::TNI, BNc, C::CHUNK>(acc, smem + ((nkt - 4) % NSc) * C::STAGE,
+                                                    smem + ((nkt - 3) % NSc) * C::STAGE, nt, lane, wm, wn, l32, lh);
   }
   if constexpr (SPLIT) {
     GemmArgs gp = g;                                           // fp32 partial tile of split sp
