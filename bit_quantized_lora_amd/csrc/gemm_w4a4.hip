@@ -116,6 +116,18 @@ template <int I, int GS = 0> struct CfgOf { using type = TileCfg<256, 256, 4, 2,
 template <> struct CfgOf<1, 0> { using type = CfgWide; };
 template <> struct CfgOf<2, 0> { using type = CfgSmall; };
 constexpr int cfg_occ(int cfg) { return cfg == 2 ? 2 : 1; }   // workgroups per CU the kernel is built for
+// Most low-rank ranks (a multiple of 16, at most one pass of `chunk`) whose W
+// rows [nt x bn] bf16 and P rows [bm x nt] fp32 each fit one ring buffer of
+// `stage` bytes, with P in whole 1-KiB DMAs: the ranks the pipelined kernel
+// adds after its main loop (256 x 256: 32, 192 x 384: 48, 128 x 128: 32)
+constexpr int tail_ranks_max(int bm, int bn, int stage, int chunk) {
+  int nt = chunk - chunk % 16;
+  while (nt > 0 && (nt * 2 * bn > stage || bm * nt * 4 > stage || (bm * nt) % 256 != 0)) nt -= 16;
+  return nt;
+}
+static_assert(tail_ranks_max(256, 256, CfgSquare::STAGE, CfgSquare::CHUNK) == 32, "square tail ranks");
+static_assert(tail_ranks_max(192, 384, CfgWide::STAGE, CfgWide::CHUNK) == 48, "wide tail ranks");
+static_assert(tail_ranks_max(128, 128, CfgSmall::STAGE, CfgSmall::CHUNK) == 32, "small tail ranks");
 }  // namespace ft
 
 namespace ft {
@@ -521,9 +533,9 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
 #pragma unroll
     for (int j = 0; j < C::TNI; ++j) acc[i][j] = v16f{};
 
-  // The low-rank up-projection P W.  Its last nt ranks (all of them when they
-  // fit one pass, else the last CHUNK) follow the main loop when their W and P
-  // tiles fit one ring buffer each and the reduction has at least NS stages:
+  // The low-rank up-projection P W.  Its last nt ranks (all of them, or as many
+  // as fit: NT_MAX, whose W and P tiles fit one ring buffer each) follow the
+  // main loop when the reduction has at least NS stages:
   // the tiles are fetched during the last stages into buffers those stages have
   // freed (tail_issue_w).  The other ranks go into the accumulators first, in
   // the buffer of stage NS-1 (free until the first steady iteration): the loads
@@ -532,10 +544,10 @@ gemm_w4a4_kernel(GemmArgs g_in, int tiles_m, int tiles_n, int per_xcd) {
   // further chunks follow one by one.  The split depends only on the tile
   // shape, the ranks and the stage count, so every kernel of a shape (plain,
   // MLP-fusion epilogue, adapter workgroups) sums each output in the same order.
+  constexpr int NT_MAX = tail_ranks_max(BMc, BNc, C::STAGE, C::CHUNK);
   const int rho = g.ra + g.rb;
-  const int nt = rho <= C::CHUNK ? rho : C::CHUNK;
-  const bool tail_lr = rho > 0 && nt * 2 * BNc <= C::STAGE && BMc * nt * 4 <= C::STAGE && nkt >= NSc &&
-                       (BMc * nt) % 256 == 0;
+  const int nt = rho <= NT_MAX ? rho : NT_MAX;
+  const bool tail_lr = rho > 0 && nt > 0 && nkt >= NSc && (BMc * nt) % 256 == 0;
   const int rho_head = tail_lr ? rho - nt : rho;
   uint8_t* lr_smem = smem + (NSc - 1) * C::STAGE;
   PRegs<C::TMI, C::CHUNK> pr;
