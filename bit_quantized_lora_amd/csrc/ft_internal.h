@@ -56,8 +56,10 @@ ft_status gemm_w4a4_plan(int64_t M, int64_t N, int64_t K, bool beside, bool can_
 ft_status launch_gemm_w4a4_adapt(const GemmArgs& g, bool out_bf16, hipStream_t s, void* gemm_ws, void* adapt_ws);
 bool gemm_w4a4_adapt_ok(const GemmArgs& g);
 size_t gemm_w4a4_adapt_workspace(const GemmArgs& g, bool can_split);
-// adapter workgroups and token ranges the launch takes (nothing runs)
-void gemm_w4a4_adapt_plan(const GemmArgs& g, bool can_split, bool with_db, int* nwg, int* splits);
+// the launch's GEMM tile and split count, adapter workgroups and token ranges
+// (nothing runs); false when gemm_w4a4_adapt_ok(g) does not hold
+bool gemm_w4a4_adapt_plan(const GemmArgs& g, bool can_split, bool with_db, int* tile_m, int* tile_n,
+                          int* gemm_splits, int* nwg, int* splits);
 
 // Forward GEMM (bf16 Y) with the MLP fusion epilogue: also H = GELU(Y) and Q(H)
 // (g.H, g.hq, g.hs).  FT_ENOTSUP when K is not a multiple of 128 (no pipelined

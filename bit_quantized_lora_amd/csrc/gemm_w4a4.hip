@@ -1017,45 +1017,12 @@ bool pipelined_ok(const GemmArgs& g) {
   return g.K > 0 && g.K % 128 == 0 && BN * g.lda < ((int64_t)1 << 31) && CfgWide::BN * g.ldb < ((int64_t)1 << 31);
 }
 
-// beside: see launch_gemm_w4a4.  can_split: a workspace for split partials exists.
-// splits > 1 only when can_split; the result depends on the shape, the CU
-// count and these two flags only.
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool beside, bool can_split) {
-  const int cus = num_cus();
-  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, tiles = tiles_m * tiles_n;
-  const int64_t wm_ = (M + CfgWide::BM - 1) / CfgWide::BM, wn_ = (N + CfgWide::BN - 1) / CfgWide::BN;
-  const int64_t wide = wm_ * wn_;
-  // Big tiles: the shape that fills the CUs in fewer partial rounds; but when
-  // other kernels run beside the GEMM and both shapes take one round, the one
-  // with fewer tiles, which leaves those kernels more CUs.
-  const bool use_wide = (beside && wide <= cus && tiles <= cus) ? wide < tiles
-                                                                : fill(wide, cus) > fill(tiles, cus) + 0.02;
-  GemmPlan p{use_wide ? 1 : 0, 1, use_wide ? wm_ : tiles_m, use_wide ? wn_ : tiles_n};
-  if (tiles >= cus) return p;                                  // every CU has a big tile already
-  // Fewer big tiles than CUs: compare with 128 x 128 tiles and split reductions
-  // by the busiest CU's time.
-  const int64_t nkt = K / 128;
-  auto rounds = [&](int64_t units) { return (double)((units + cus - 1) / cus); };
-  double best = rounds(p.tm * p.tn) * ((double)nkt * (use_wide ? 4.5 : 4.0) * STEP_US + ITEM_US);
-  const int64_t sm = (M + CfgSmall::BM - 1) / CfgSmall::BM, sn = (N + CfgSmall::BN - 1) / CfgSmall::BN;
-  for (int S = 1; S <= (can_split ? MAX_SPLITS : 1); ++S) {
-    if (S > 1 && nkt < (int64_t)S * MIN_SPLIT_STAGES) break;
-    const double t = rounds(sm * sn * S) * ((double)((nkt + S - 1) / S) * SMALL_STEP_US + SMALL_ITEM_US) +
-                     (S > 1 ? (double)(S + 1) * M * N * 4 / (SPLIT_GBS * 1e3) + SPLIT_US : 0.0);
-    if (t < best) {
-      best = t;
-      p = GemmPlan{2, S, sm, sn};
-    }
-  }
-  return p;
-}
-
-// Adapter workgroups of the backward GEMM launch: as many as the GEMM's last
-// round leaves slots free (they start at once, beside it), or one per slot when
-// it leaves fewer than an eighth (they follow it).  A unit is one 64-column strip
-// over one token range; the range count S minimizes the busiest workgroup's
-// rows (AD_ROW_US per 128-byte row on one CU, measured order of magnitude) plus,
-// for S > 1, the partials' round trip and the second launch.
+// Time of the adapter-gradient workgroups (AdaptArgs of g, dB when with_db) on
+// na slots: a unit is one 64-column strip over one token range; the range count
+// S minimizes the busiest workgroup's rows (AD_ROW_US per 128-byte row on one
+// CU, measured order of magnitude) plus, for S > 1, the partials' round trip
+// and the second launch.  *ap (if given) receives the units, ranges and
+// workgroups of the minimum.
 constexpr double AD_ROW_US = 0.005;
 constexpr double AD_SUM_US = 4.5;
 constexpr int AD_MAX_SPLITS = 16;
@@ -1066,12 +1033,7 @@ struct AdaptPlan {
   int64_t rows_per_split;
 };
 
-AdaptPlan plan_adapt(const GemmArgs& g, bool can_split, bool with_db) {
-  const GemmPlan gp = plan_gemm(g.M, g.N, g.K, true, can_split);
-  const int64_t slots = (int64_t)num_cus() * cfg_occ(gp.cfg);
-  const int64_t W = gp.tm * gp.tn * gp.splits;
-  const int64_t free_slots = (W + slots - 1) / slots * slots - W;
-  const int64_t na = free_slots >= slots / 8 ? free_slots : slots;
+double adapt_time(const GemmArgs& g, bool with_db, int64_t na, AdaptPlan* ap) {
   AdaptPlan best{};
   best.strips0 = (int)((g.ad.ncols[0] + AD_COLS - 1) / AD_COLS);
   best.strips1 = with_db ? (int)((g.ad.ncols[1] + AD_COLS - 1) / AD_COLS) : 0;
@@ -1095,7 +1057,76 @@ AdaptPlan plan_adapt(const GemmArgs& g, bool can_split, bool with_db) {
       best.rows_per_split = rps;
     }
   }
-  return best;
+  if (ap) *ap = best;
+  return best_t;
+}
+
+// Slots the adapter workgroups take beside a GEMM of W work items: those its
+// last round leaves free (they start with it), or, when that is under an
+// eighth, every slot (they follow it).
+int64_t adapt_slots(int64_t W, int64_t slots) {
+  const int64_t free_slots = (W + slots - 1) / slots * slots - W;
+  return free_slots >= slots / 8 ? free_slots : slots;
+}
+
+// beside: see launch_gemm_w4a4.  can_split: a workspace for split partials exists.
+// ad: the adapter gradients the same launch computes (launch_gemm_w4a4_adapt;
+// with_db: dB among them), or nullptr.  splits > 1 only when can_split; the
+// result depends on the shape, the CU count, these flags and ad's rank and
+// column counts only.
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool beside, bool can_split, const GemmArgs* ad = nullptr,
+                   bool with_db = true) {
+  const int cus = num_cus();
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, tiles = tiles_m * tiles_n;
+  const int64_t wm_ = (M + CfgWide::BM - 1) / CfgWide::BM, wn_ = (N + CfgWide::BN - 1) / CfgWide::BN;
+  const int64_t wide = wm_ * wn_;
+  const int64_t nkt = K / 128;
+  auto round_us = [&](bool w) { return (double)nkt * (w ? 4.5 : 4.0) * STEP_US + ITEM_US; };
+  // Big tiles: the shape that fills the CUs in fewer partial rounds.  When other
+  // kernels run beside the GEMM and both shapes take one round: with the adapter
+  // workgroups in the launch, the shape whose GEMM round or adapter work (on the
+  // slots it leaves) ends first; otherwise the one with fewer tiles, which
+  // leaves those kernels more CUs.
+  bool use_wide;
+  if (beside && wide <= cus && tiles <= cus) {
+    if (ad) {
+      auto end_us = [&](bool w) {
+        const int64_t na = adapt_slots(w ? wide : tiles, cus);
+        const double ta = adapt_time(*ad, with_db, na, nullptr);
+        return na == cus ? round_us(w) + ta : (round_us(w) > ta ? round_us(w) : ta);
+      };
+      use_wide = end_us(true) < end_us(false);
+    } else {
+      use_wide = wide < tiles;
+    }
+  } else {
+    use_wide = fill(wide, cus) > fill(tiles, cus) + 0.02;
+  }
+  GemmPlan p{use_wide ? 1 : 0, 1, use_wide ? wm_ : tiles_m, use_wide ? wn_ : tiles_n};
+  if (tiles >= cus) return p;                                  // every CU has a big tile already
+  // Fewer big tiles than CUs: compare with 128 x 128 tiles and split reductions
+  // by the busiest CU's time.
+  auto rounds = [&](int64_t units) { return (double)((units + cus - 1) / cus); };
+  double best = rounds(p.tm * p.tn) * round_us(use_wide);
+  const int64_t sm = (M + CfgSmall::BM - 1) / CfgSmall::BM, sn = (N + CfgSmall::BN - 1) / CfgSmall::BN;
+  for (int S = 1; S <= (can_split ? MAX_SPLITS : 1); ++S) {
+    if (S > 1 && nkt < (int64_t)S * MIN_SPLIT_STAGES) break;
+    const double t = rounds(sm * sn * S) * ((double)((nkt + S - 1) / S) * SMALL_STEP_US + SMALL_ITEM_US) +
+                     (S > 1 ? (double)(S + 1) * M * N * 4 / (SPLIT_GBS * 1e3) + SPLIT_US : 0.0);
+    if (t < best) {
+      best = t;
+      p = GemmPlan{2, S, sm, sn};
+    }
+  }
+  return p;
+}
+
+// Adapter workgroups of the backward GEMM launch (adapt_slots, adapt_time)
+AdaptPlan plan_adapt(const GemmArgs& g, bool can_split, bool with_db) {
+  const GemmPlan gp = plan_gemm(g.M, g.N, g.K, true, can_split, &g, with_db);
+  AdaptPlan ap{};
+  adapt_time(g, with_db, adapt_slots(gp.tm * gp.tn * gp.splits, (int64_t)num_cus() * cfg_occ(gp.cfg)), &ap);
+  return ap;
 }
 
 }  // namespace
@@ -1206,21 +1237,28 @@ size_t gemm_w4a4_adapt_workspace(const GemmArgs& g, bool can_split) {
   return b;
 }
 
-void gemm_w4a4_adapt_plan(const GemmArgs& g, bool can_split, bool with_db, int* nwg, int* splits) {
+bool gemm_w4a4_adapt_plan(const GemmArgs& g, bool can_split, bool with_db, int* tile_m, int* tile_n,
+                          int* gemm_splits, int* nwg, int* splits) {
   *nwg = 0;
   *splits = 1;
-  if (!gemm_w4a4_adapt_ok(g)) return;
+  if (!gemm_w4a4_adapt_ok(g)) return false;
+  const GemmPlan p = plan_gemm(g.M, g.N, g.K, true, can_split, &g, with_db);
   const AdaptPlan ap = plan_adapt(g, can_split, with_db);
+  *tile_m = p.cfg == 2 ? CfgSmall::BM : p.cfg == 1 ? CfgWide::BM : BM;
+  *tile_n = p.cfg == 2 ? CfgSmall::BN : p.cfg == 1 ? CfgWide::BN : BN;
+  *gemm_splits = p.splits;
   *nwg = ap.nwg;
   *splits = ap.splits;
+  return true;
 }
 
 ft_status launch_gemm_w4a4_adapt(const GemmArgs& g_in, bool out_bf16, hipStream_t s, void* gemm_ws, void* adapt_ws) {
   if (!gemm_w4a4_adapt_ok(g_in)) return FT_ENOTSUP;
   if (!g_in.ad.P[0] || !g_in.ad.Q[0] || !g_in.ad.out[0] || (g_in.ad.out[1] && (!g_in.ad.P[1] || !g_in.ad.Q[1])))
     return FT_EINVAL;
-  const GemmPlan p = plan_gemm(g_in.M, g_in.N, g_in.K, true, gemm_ws != nullptr);
-  const AdaptPlan ap = plan_adapt(g_in, gemm_ws != nullptr, g_in.ad.out[1] != nullptr);
+  const bool with_db = g_in.ad.out[1] != nullptr;
+  const GemmPlan p = plan_gemm(g_in.M, g_in.N, g_in.K, true, gemm_ws != nullptr, &g_in, with_db);
+  const AdaptPlan ap = plan_adapt(g_in, gemm_ws != nullptr, with_db);
   if (ap.splits > 1 && !adapt_ws) return FT_EINVAL;
   GemmArgs g = g_in;
   g.splits = p.splits;

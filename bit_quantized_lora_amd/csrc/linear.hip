@@ -137,7 +137,7 @@ extern "C" ft_status ft_linear_plan(int64_t M, int64_t N, int64_t K, int32_t bac
   if (!mult16(M) || !mult16(N) || !mult16(K)) return FT_ESHAPE;
   int tm = 0, tn = 0, sp = 1;
   // the backward's dX GEMM: M x K output, reduction over N, planned as with the
-  // adapter gradients beside it
+  // adapter gradients on the side stream beside it
   const ft_status st = backward ? gemm_w4a4_plan(M, K, N, true, with_ws != 0, &tm, &tn, &sp)
                                 : gemm_w4a4_plan(M, N, K, false, with_ws != 0, &tm, &tn, &sp);
   plan[0] = tm;
@@ -234,8 +234,9 @@ extern "C" ft_status ft_linear_bwd_plan(int64_t M, int64_t N, int64_t K, int32_t
   const GemmArgs g = bwd_shape(M, N, K, 0, r);
   const bool split = gemm_w4a4_workspace(M, K, N) > 0;
   int tm = 0, tn = 0, sp = 1, nwg = 0, asp = 1;
-  const ft_status st = gemm_w4a4_plan(M, K, N, true, split, &tm, &tn, &sp);
-  gemm_w4a4_adapt_plan(g, split, with_db != 0, &nwg, &asp);
+  ft_status st = FT_OK;
+  if (!gemm_w4a4_adapt_plan(g, split, with_db != 0, &tm, &tn, &sp, &nwg, &asp))
+    st = gemm_w4a4_plan(M, K, N, true, split, &tm, &tn, &sp);   // the GEMM beside the side stream
   plan[0] = tm;
   plan[1] = tn;
   plan[2] = sp;

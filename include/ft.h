@@ -244,9 +244,11 @@ size_t ft_linear_fwd_workspace(int64_t M, int64_t N, int64_t K);
 /* ft_linear_plan -- how the 4-bit GEMM of a call is launched (for tests and
  * profiling; nothing is run): plan[0] x plan[1] output tile per workgroup,
  * plan[2] reduction splits.  backward 0: the GEMM of ft_linear_fwd (with_ws 0)
- * or ft_linear_fwd_ws (with_ws 1); backward 1: the dX GEMM of ft_linear_bwd
- * (with_ws 1; it always has its workspace).  M, N, K as in those calls; plan
- * holds 3 int32. */
+ * or ft_linear_fwd_ws (with_ws 1); backward 1: the dX GEMM of a backward whose
+ * adapter gradients run as separate kernels beside it (the _op, _g16 and _grp
+ * backwards, and ranks ft_linear_bwd does not take into its launch; with_ws 1:
+ * they always have their workspace).  ft_linear_bwd_plan gives ft_linear_bwd's
+ * own launch.  M, N, K as in those calls; plan holds 3 int32. */
 ft_status ft_linear_plan(int64_t M, int64_t N, int64_t K, int32_t backward, int32_t with_ws, int32_t* plan);
 
 /* ft_linear_bwd -- Eq. 3 and the adapter gradients of section 3.2:

@@ -282,8 +282,8 @@ def test_big_tile_edges(case):
     require_gpu()
     from bit_quantized_lora_amd import ops
     M, K, N, rs, r = case
-    say(f"[linear] big tiles {case}: fwd plan {ops.linear_plan(M, N, K)}, dX plan "
-        f"{ops.linear_plan(M, N, K, backward=True)}")
+    say(f"[linear] big tiles {case}: fwd plan {ops.linear_plan(M, N, K)}, backward plan "
+        f"{ops.linear_bwd_plan(M, N, K, r)}")
     rng = np.random.default_rng(M + K + N + rs)
     spec = synth.LinearSpec("t", M, K, N, rs, r, x_outlier_frac=0.01, x_outlier_mult=50.0)
     d = synth.make_linear(spec, rng)
@@ -324,7 +324,7 @@ def test_small_m_tiles_and_split_reduction(shape):
     from bit_quantized_lora_amd import ops
     M, K, N, rs, r = shape
     fwd, fwd_nows, bwd = ops.linear_plan(M, N, K), ops.linear_plan(M, N, K, with_ws=False), \
-        ops.linear_plan(M, N, K, backward=True)
+        ops.linear_bwd_plan(M, N, K, r)
     say(f"[linear] few tokens {shape}: fwd plan {fwd} (no workspace {fwd_nows}), dX plan {bwd}")
     assert fwd[:2] == (128, 128) and fwd_nows == (128, 128, 1)
     d = _small_m_data(shape)
@@ -357,7 +357,7 @@ def test_small_m_set_covers_split_paths():
     require_gpu()
     from bit_quantized_lora_amd import ops
     fwd = [ops.linear_plan(M, N, K) for M, K, N, _, _ in SMALL_M]
-    bwd = [ops.linear_plan(M, N, K, backward=True) for M, K, N, _, _ in SMALL_M]
+    bwd = [ops.linear_bwd_plan(M, N, K, r)[:3] for M, K, N, _, r in SMALL_M]
     say(f"[linear] few-token plans: fwd {fwd}, dX {bwd}")
     assert any(p[2] > 1 for p in fwd) and any(p[2] == 1 for p in fwd)
     assert any(p[2] > 1 for p in bwd) and any(p[:2] == (128, 128) and p[2] == 1 for p in bwd)
