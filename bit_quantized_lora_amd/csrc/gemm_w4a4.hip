@@ -1010,6 +1010,10 @@ constexpr double STEP_US = 0.294, SMALL_STEP_US = 0.42;
 constexpr double ITEM_US = 13.3, SMALL_ITEM_US = 9.3;
 constexpr double SPLIT_GBS = 5000.0;    // partial sums' read + write rate, GB/s
 constexpr double SPLIT_US = 4.5;
+// The same for the backward's dX GEMM (Q(R) read transposed), whose big tiles
+// the planner weighs against the adapter workgroups beside them: fitted to the
+// dX launches of 4096-4608 rows, reductions 3072-12288, square and wide tiles.
+constexpr double DX_STEP_US = 0.323, DX_ITEM_US = 16.0;
 constexpr int MAX_SPLITS = 8;
 constexpr int MIN_SPLIT_STAGES = 4;     // 128-K stages per split, at least
 
@@ -1020,10 +1024,11 @@ bool pipelined_ok(const GemmArgs& g) {
 // Time of the adapter-gradient workgroups (AdaptArgs of g, dB when with_db) on
 // na slots: a unit is one 64-column strip over one token range; the range count
 // S minimizes the busiest workgroup's rows (AD_ROW_US per 128-byte row on one
-// CU, measured order of magnitude) plus, for S > 1, the partials' round trip
-// and the second launch.  *ap (if given) receives the units, ranges and
+// CU: about 20 GB/s per workgroup, as measured beside the dX GEMM in a training
+// step, with X and G streamed from HBM) plus, for S > 1, the partials' round
+// trip and the second launch.  *ap (if given) receives the units, ranges and
 // workgroups of the minimum.
-constexpr double AD_ROW_US = 0.005;
+constexpr double AD_ROW_US = 0.0065;
 constexpr double AD_SUM_US = 4.5;
 constexpr int AD_MAX_SPLITS = 16;
 constexpr int64_t AD_MIN_SPLIT_ROWS = 512;   // tokens per range when S > 1 (one 64-token chunk per wave)
@@ -1093,7 +1098,8 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, bool beside, bool can_split,
       auto end_us = [&](bool w) {
         const int64_t na = adapt_slots(w ? wide : tiles, cus);
         const double ta = adapt_time(*ad, with_db, na, nullptr);
-        return na == cus ? round_us(w) + ta : (round_us(w) > ta ? round_us(w) : ta);
+        const double tg = (double)nkt * (w ? 4.5 : 4.0) * DX_STEP_US + DX_ITEM_US;
+        return na == cus ? tg + ta : (tg > ta ? tg : ta);
       };
       use_wide = end_us(true) < end_us(false);
     } else {
