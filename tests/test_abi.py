@@ -196,3 +196,34 @@ def test_backward_plan_query():
     assert plan[3] > 0 and plan[4] >= 1                      # adapter workgroups in the GEMM launch
     assert lib.ft_linear_bwd_plan(4608, 12288, 3072, 96, 1, ctypes.addressof(plan)) == L.FT_OK
     assert plan[3] == 0                                      # r > 64: side stream
+
+
+def test_backward_workspace_covers_every_launch_plan():
+    """The one workspace size of the backward covers what ft_linear_bwd_plan
+    says the launch writes there, for shapes across the planner's branches
+    (one-round GEMMs with the adapter workgroups beside them, multi-round ones
+    with them after, the small tile with split reductions, ragged sizes) and
+    ranks of one and two rank tiles, with and without dB: the adapter
+    workgroups' token-range partials first (their largest size over both dB
+    settings, 256-byte aligned), then the dX GEMM's split partials."""
+    L = _lib(); lib = L.lib()
+    a256 = lambda n: (n + 255) // 256 * 256
+    plan = (ctypes.c_int32 * 5)()
+    checked = 0
+    for M in (256, 400, 512, 528, 4096, 4608, 16384, 18432):
+        for (N, K) in ((3072, 3072), (12288, 3072), (3072, 12288), (9216, 3072), (1040, 1152), (1024, 4096),
+                       (384, 4624)):
+            for r in (16, 32, 48, 64):
+                ws = lib.ft_linear_bwd_workspace(M, N, K, r)
+                plans = {}
+                for with_db in (1, 0):
+                    assert lib.ft_linear_bwd_plan(M, N, K, r, with_db, ctypes.addressof(plan)) == L.FT_OK
+                    plans[with_db] = tuple(plan)
+                adapt = [p[4] * r * (K + (N if db else 0)) * 4 if p[3] > 0 and p[4] > 1 else 0
+                         for db, p in plans.items()]
+                for db, p in plans.items():
+                    gemm = p[2] * M * K * 4 if p[2] > 1 else 0
+                    need = (a256(max(adapt)) if p[3] > 0 else 0) + gemm
+                    assert need <= ws, f"M={M} N={N} K={K} r={r} dB={db}: plan {p} needs {need} > {ws}"
+                    checked += 1
+    assert checked == 8 * 7 * 4 * 2
