@@ -5,14 +5,21 @@
 // the matrix and its transpose).  Scale = block amax / 6 (power-of-two rounded
 // up, or fp32), element code = round-to-nearest-even E2M1 of x / scale.
 //
-// One workgroup quantizes a 128x128 tile: the bf16 tile is read once from HBM
-// straight into registers (each lane owns one 16-element row segment of one
-// 16x16 block per pass, 16 lanes per block; a wave's 4 blocks are adjacent, so
-// its loads cover 16 rows x 128 contiguous bytes), reduces the block maximum
-// across its 16 lanes, converts with the hardware scaled E2M1 convert from bf16
-// (which rounds to nearest-even and saturates, matching the oracle bit for bit), and
-// transposes the 16x16 nibble block across the 16 lanes for the column-major
-// codes.  Both code layouts are staged in LDS and written with coalesced stores.
+// Two kernels.  The power-of-two instances that write codes only (the GEMM
+// operand Q(R), and X or G when quantized on their own) run quant_pow2_kernel:
+// 256x256 tiles whose loads cover whole 128-byte lines per instruction, a lane
+// holding half of one block (described at the kernel).  The fp32-scale
+// instances and the instances that also write the pair-merged operands run
+// quant_block16_kernel: the bf16 tile is read once from HBM straight into
+// registers (each lane owns one 16-element row segment of one 16x16 block per
+// pass, 16 lanes per block), the block maximum is reduced across its 16 lanes
+// with DPP exchanges, and the 16x16 nibble block is transposed across the 16
+// lanes for the column-major codes.  Both convert with the hardware scaled E2M1
+// convert from bf16 (which rounds to nearest-even and saturates, matching the
+// oracle bit for bit), stage both code layouts in LDS and write them with
+// coalesced 16-byte stores; power-of-two scale bytes are staged in LDS too and
+// written as one 16-byte run per block row (and block column of the
+// transposed grid) where the run is whole and aligned.
 //
 // Optionally the same tile also writes the pair-merged GEMM operand of Q(x)
 // (along columns) and of Q(x)^T (along rows): a value-preserving re-encoding in
@@ -50,10 +57,23 @@ struct QuantOut {
   uint8_t* op_rm; uint8_t* op_rm_scales; uint8_t* op_cm; uint8_t* op_cm_scales;
 };
 
-// Exchange with the lane whose index differs in bit MASK (MASK < 16).
+// Exchange with the lane whose index differs in bit MASK (MASK < 16), inside
+// each 16-lane DPP row: quad permutes for bits 0 and 1, a rotate by 8 for bit 3,
+// and for bit 2 a shift by 4 either way with the direction picked per lane.
+// Every source lane lies inside the row, so no lane reads a bound value.
 template <int MASK>
 __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
-  return (uint32_t)__shfl_xor((int)v, MASK, 64);
+  const int x = (int)v;
+  if constexpr (MASK == 1) return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
+  if constexpr (MASK == 2) return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
+  if constexpr (MASK == 8) return (uint32_t)__builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false);
+  if constexpr (MASK == 4) {
+    const int up = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0xF, false);   // row_shl:4, from lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(x, x, 0x114, 0xF, 0xF, false);   // row_shr:4, from lane - 4
+    return (uint32_t)((__lane_id() & 4) ? dn : up);
+  }
+  static_assert(MASK == 1 || MASK == 2 || MASK == 4 || MASK == 8, "lane masks inside a 16-lane row");
+  return v;
 }
 
 // Transpose a 16x16 block of nibbles held one row per lane (64 bits: positions
@@ -61,20 +81,17 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
 // swaps bit b of the lane index with bit b of the nibble position.
 __device__ __forceinline__ void transpose_nibbles16(uint32_t& w0, uint32_t& w1, int i) {
   {  // bit 3: dword halves
-    uint32_t send = (i & 8) ? w0 : w1;
-    uint32_t recv = xor_lane<8>(send);
-    if (i & 8) w0 = recv; else w1 = recv;
+    const bool hi = (i & 8) != 0;
+    const uint32_t recv = xor_lane<8>(hi ? w0 : w1);
+    w0 = hi ? recv : w0;
+    w1 = hi ? w1 : recv;
   }
 #define FT_NIB_STEP(BIT, SHIFT, M0)                                           \
   {                                                                           \
-    uint32_t r0 = xor_lane<BIT>(w0), r1 = xor_lane<BIT>(w1);                  \
-    if (i & BIT) {                                                            \
-      w0 = (w0 & ~(M0)) | ((r0 & ~(M0)) >> SHIFT);                            \
-      w1 = (w1 & ~(M0)) | ((r1 & ~(M0)) >> SHIFT);                            \
-    } else {                                                                  \
-      w0 = (w0 & (M0)) | ((r0 & (M0)) << SHIFT);                              \
-      w1 = (w1 & (M0)) | ((r1 & (M0)) << SHIFT);                              \
-    }                                                                         \
+    const uint32_t r0 = xor_lane<BIT>(w0), r1 = xor_lane<BIT>(w1);            \
+    const bool hi = (i & BIT) != 0;                                           \
+    w0 = hi ? ((w0 & ~(M0)) | ((r0 & ~(M0)) >> SHIFT)) : ((w0 & (M0)) | ((r0 & (M0)) << SHIFT)); \
+    w1 = hi ? ((w1 & ~(M0)) | ((r1 & ~(M0)) >> SHIFT)) : ((w1 & (M0)) | ((r1 & (M0)) << SHIFT)); \
   }
   FT_NIB_STEP(4, 16, 0x0000FFFFu)
   FT_NIB_STEP(2, 8, 0x00FF00FFu)
@@ -136,7 +153,7 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
   constexpr bool STAGE_RM = WRITE_RM || OP_RM, STAGE_CM = WRITE_CM || OP_CM, OPS = OP_RM || OP_CM;
   __shared__ __attribute__((aligned(16))) uint8_t s_rm[STAGE_RM ? QT * RM_PITCH : 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_cm[STAGE_CM ? QT * CM_PITCH : 16];
-  __shared__ uint8_t s_e[OPS ? 64 : 1];   // scale byte of each of the tile's 8 x 8 blocks
+  __shared__ __attribute__((aligned(16))) uint8_t s_e[POW2 ? BPR * BPR : 1];   // scale byte of each block
   __shared__ uint8_t s_z[OPS ? 64 : 1];   // 1 when every code of the block is +-0
   uint8_t* __restrict__ codes_rm = o.codes_rm;
   uint8_t* __restrict__ codes_cm = o.codes_cm;
@@ -196,21 +213,14 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
       FT_CVT(w0, 0, 0); FT_CVT(w0, 1, 1); FT_CVT(w0, 2, 2); FT_CVT(w0, 3, 3);
       FT_CVT(w1, 4, 0); FT_CVT(w1, 5, 1); FT_CVT(w1, 6, 2); FT_CVT(w1, 7, 3);
 #undef FT_CVT
-      if (live && i == 0) {
-        if (scales) static_cast<uint8_t*>(scales)[(row0 / 16 + br) * (cols / 16) + col0 / 16 + bc] = (uint8_t)(E + 127);
-        if (scales_cm)
-          static_cast<uint8_t*>(scales_cm)[(col0 / 16 + bc) * (rows / 16) + row0 / 16 + br] = (uint8_t)(E + 127);
-      }
+      if (i == 0) s_e[b] = (uint8_t)(E + 127);   // both scale grids are written from LDS below
       if constexpr (OPS) {
         uint32_t nz = (w0 | w1) & 0x77777777u;   // any non-zero magnitude in this row
         nz |= xor_lane<8>(nz);
         nz |= xor_lane<4>(nz);
         nz |= xor_lane<2>(nz);
         nz |= xor_lane<1>(nz);
-        if (i == 0) {
-          s_e[b] = (uint8_t)(E + 127);
-          s_z[b] = nz == 0 ? 1 : 0;
-        }
+        if (i == 0) s_z[b] = nz == 0 ? 1 : 0;
       }
     } else {
       const float amax = __builtin_bit_cast(float, m << 16);
@@ -241,6 +251,40 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
     }
   }
   __syncthreads();
+
+  // 3a. power-of-two scale bytes: lane r < BPR writes block row r of the grid,
+  //     lane 64 + c block column c of the transposed grid, each as one BPR-byte
+  //     store where the run is whole and aligned, else byte by byte.
+  if constexpr (POW2) {
+    const int nbr = trows / 16, nbc = tcols / 16;
+    const bool row_lane = scales && tid < nbr, col_lane = scales_cm && tid >= 64 && tid - 64 < nbc;
+    if (row_lane || col_lane) {
+      uint8_t* dst;
+      int n;
+      uint32_t wd[BPR / 4];
+      if (row_lane) {
+        const int r = tid;
+        dst = static_cast<uint8_t*>(scales) + (row0 / 16 + r) * (cols / 16) + col0 / 16;
+        n = nbc;
+#pragma unroll
+        for (int k = 0; k < BPR / 4; ++k) wd[k] = *reinterpret_cast<const uint32_t*>(s_e + r * BPR + 4 * k);
+      } else {
+        const int c = tid - 64;
+        dst = static_cast<uint8_t*>(scales_cm) + (col0 / 16 + c) * (rows / 16) + row0 / 16;
+        n = nbr;
+#pragma unroll
+        for (int k = 0; k < BPR / 4; ++k)
+          wd[k] = (uint32_t)s_e[(4 * k) * BPR + c] | ((uint32_t)s_e[(4 * k + 1) * BPR + c] << 8) |
+                  ((uint32_t)s_e[(4 * k + 2) * BPR + c] << 16) | ((uint32_t)s_e[(4 * k + 3) * BPR + c] << 24);
+      }
+      if (n == BPR && (reinterpret_cast<uintptr_t>(dst) & (BPR - 1)) == 0) {
+        if constexpr (BPR == 16) *reinterpret_cast<v4i*>(dst) = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+        else *reinterpret_cast<v2i*>(dst) = v2i{(int)wd[0], (int)wd[1]};
+      } else {
+        for (int k = 0; k < n; ++k) dst[k] = (uint8_t)(wd[k >> 2] >> (8 * (k & 3)));
+      }
+    }
+  }
 
   // 3. LDS -> HBM, 16-byte stores; QT / 32 lanes cover one code row of the tile
   //    (a whole 128-byte line for the 256-wide tile).  A chunk of 32 codes whose
@@ -319,6 +363,184 @@ quant_block16_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
   }
 }
 
+// 8x8 nibble transpose in registers: on entry a[r] nibble j is element (r, j),
+// on exit a[j] nibble r is.  Three exchange stages: the off-diagonal 4x4
+// quadrants (16-bit halves), then 2x2 sub-blocks (bytes), then single nibbles.
+__device__ __forceinline__ void transpose_nibbles8x8(uint32_t (&a)[8]) {
+#define FT_SWP(R, S, SH, M)                                \
+  {                                                        \
+    const uint32_t t = ((a[R] >> (SH)) ^ a[S]) & (M);      \
+    a[S] ^= t;                                             \
+    a[R] ^= t << (SH);                                     \
+  }
+  FT_SWP(0, 4, 16, 0x0000FFFFu) FT_SWP(1, 5, 16, 0x0000FFFFu) FT_SWP(2, 6, 16, 0x0000FFFFu) FT_SWP(3, 7, 16, 0x0000FFFFu)
+  FT_SWP(0, 2, 8, 0x00FF00FFu) FT_SWP(1, 3, 8, 0x00FF00FFu) FT_SWP(4, 6, 8, 0x00FF00FFu) FT_SWP(5, 7, 8, 0x00FF00FFu)
+  FT_SWP(0, 1, 4, 0x0F0F0F0Fu) FT_SWP(2, 3, 4, 0x0F0F0F0Fu) FT_SWP(4, 5, 4, 0x0F0F0F0Fu) FT_SWP(6, 7, 4, 0x0F0F0F0Fu)
+#undef FT_SWP
+}
+
+// The power-of-two, codes-only instances: a 256x256 tile per workgroup of 8
+// waves.  Wave w owns block rows 2w and 2w + 1; in pass p its lanes 0-31 read
+// row 16(2w) + p and lanes 32-63 row 16(2w + 1) + p, 16 bytes each, so every
+// load instruction covers two whole 512-byte row runs (whole 128-byte lines;
+// a layout in which each instruction touched half of each of its lines read
+// about a quarter slower).  A lane thus holds 16 rows x 8 columns, half of one
+// 16x16 block; the other half sits in the neighbouring lane, so the block
+// maximum is the lane's own maximum and one DPP exchange.  Codes of a row are
+// one dword (the hardware scaled convert from bf16); the column-major codes
+// come from two 8x8 nibble transposes in registers.  Both layouts are staged
+// in LDS at 128 bytes per code line (the column-major lines with their 16-byte
+// chunks XOR-swizzled by line, so a wave's staging writes spread over the
+// banks) and stored as whole 128-byte lines.
+constexpr int QP = 256;
+constexpr int QP_THREADS = 512;
+constexpr int QP_LINE = QP / 2;   // bytes per staged code line
+
+__device__ __forceinline__ int qp_cm_chunk(int line, int k) { return k ^ ((line >> 3) & 7); }
+
+template <bool WRITE_RM, bool WRITE_CM>
+__global__ void __launch_bounds__(QP_THREADS)
+quant_pow2_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, QuantOut o) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_rm[WRITE_RM ? QP * QP_LINE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_cm[WRITE_CM ? QP * QP_LINE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_e[16 * 16];   // scale byte of each block
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int q = lane & 31;                     // 16-byte piece of the tile row
+  const int br = 2 * w + (lane >> 5);          // block row
+  const int bc = q >> 1, hc = q & 1;           // block column, its left or right 8 columns
+  const int64_t row0 = (int64_t)blockIdx.y * QP;
+  const int64_t col0 = (int64_t)blockIdx.x * QP;
+  const int trows = (int)min<int64_t>(QP, rows - row0);   // multiple of 16
+  const int tcols = (int)min<int64_t>(QP, cols - col0);   // multiple of 16
+  const bool live = br * 16 < trows && bc * 16 < tcols;
+
+  // 1. all 16 passes' loads issued before any is used (streaming hints)
+  v4i seg[16];
+  const uint16_t* src = x + (row0 + br * 16) * ldx + col0 + q * 8;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    seg[p] = v4i{0, 0, 0, 0};
+    if (live) seg[p] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(src + p * ldx));
+  }
+
+  // 2. block maximum of |x| on the bf16 bit patterns, scale, codes
+  v2u16 pm = __builtin_bit_cast(v2u16, (uint32_t)seg[0].x & 0x7fff7fffu);
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    pm = __builtin_elementwise_max(pm, __builtin_bit_cast(v2u16, (uint32_t)seg[p].x & 0x7fff7fffu));
+    pm = __builtin_elementwise_max(pm, __builtin_bit_cast(v2u16, (uint32_t)seg[p].y & 0x7fff7fffu));
+    pm = __builtin_elementwise_max(pm, __builtin_bit_cast(v2u16, (uint32_t)seg[p].z & 0x7fff7fffu));
+    pm = __builtin_elementwise_max(pm, __builtin_bit_cast(v2u16, (uint32_t)seg[p].w & 0x7fff7fffu));
+  }
+  uint32_t m = max((uint32_t)pm.x, (uint32_t)pm.y);
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  const int E = pow2_exp_bf16(m);
+  const float sc = __builtin_bit_cast(float, (uint32_t)(E + 127) << 23);   // 2^E as the E8M0 operand
+  if (hc == 0) s_e[br * 16 + bc] = (uint8_t)(E + 127);
+
+  uint32_t rw[16];   // codes of this lane's 8 columns, one dword per row
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    uint32_t c = 0;
+#define FT_CVT(V, SEL) c = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(c, __builtin_bit_cast(v2bf, (uint32_t)(V)), sc, SEL)
+    FT_CVT(seg[p].x, 0); FT_CVT(seg[p].y, 1); FT_CVT(seg[p].z, 2); FT_CVT(seg[p].w, 3);
+#undef FT_CVT
+    rw[p] = c;
+  }
+  if constexpr (WRITE_RM) {
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+      *reinterpret_cast<uint32_t*>(s_rm + (br * 16 + p) * QP_LINE + bc * 8 + hc * 4) = rw[p];
+  }
+  if constexpr (WRITE_CM) {
+    uint32_t lo[8], hi[8];   // rows 0-7 and 8-15 of the block
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo[j] = rw[j];
+      hi[j] = rw[8 + j];
+    }
+    transpose_nibbles8x8(lo);
+    transpose_nibbles8x8(hi);
+    // column j of the lane is code line 8q + j of the tile; the block row's 16
+    // codes are bytes 8 br .. 8 br + 7 of that line (chunk br / 2, half br % 2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int line = 8 * q + j;
+      *reinterpret_cast<v2i*>(s_cm + line * QP_LINE + qp_cm_chunk(line, br >> 1) * 16 + (br & 1) * 8) =
+          v2i{(int)lo[j], (int)hi[j]};
+    }
+  }
+  __syncthreads();
+
+  // 3a. scale bytes: lane r < 16 writes block row r of the grid, lane 64 + c
+  //     block column c of the transposed grid, as one 16-byte store where the
+  //     run is whole and aligned, else byte by byte.
+  {
+    const int nbr = trows / 16, nbc = tcols / 16;
+    const bool row_lane = tid < nbr, col_lane = o.scales_cm && tid >= 64 && tid - 64 < nbc;
+    if (row_lane || col_lane) {
+      uint8_t* dst;
+      int n;
+      uint32_t wd[4];
+      if (row_lane) {
+        const int r = tid;
+        dst = static_cast<uint8_t*>(o.scales) + (row0 / 16 + r) * (cols / 16) + col0 / 16;
+        n = nbc;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) wd[k] = *reinterpret_cast<const uint32_t*>(s_e + r * 16 + 4 * k);
+      } else {
+        const int c = tid - 64;
+        dst = static_cast<uint8_t*>(o.scales_cm) + (col0 / 16 + c) * (rows / 16) + row0 / 16;
+        n = nbr;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          wd[k] = (uint32_t)s_e[(4 * k) * 16 + c] | ((uint32_t)s_e[(4 * k + 1) * 16 + c] << 8) |
+                  ((uint32_t)s_e[(4 * k + 2) * 16 + c] << 16) | ((uint32_t)s_e[(4 * k + 3) * 16 + c] << 24);
+      }
+      if (n == 16 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0)
+        *reinterpret_cast<v4i*>(dst) = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+      else
+        for (int k = 0; k < n; ++k) dst[k] = (uint8_t)(wd[k >> 2] >> (8 * (k & 3)));
+    }
+  }
+
+  // 3b. code lines LDS -> HBM, 16-byte stores, 8 lanes per 128-byte line.  A
+  //     chunk of 32 codes whose second half lies past a ragged tile edge is
+  //     stored as its first 8 bytes only.
+  if constexpr (WRITE_RM) {
+#pragma unroll
+    for (int it = 0; it < QP * 8 / QP_THREADS; ++it) {
+      const int c = it * QP_THREADS + tid, r = c >> 3, k = c & 7;
+      if (r < trows && k * 32 < tcols) {
+        const v4i v = *reinterpret_cast<const v4i*>(s_rm + r * QP_LINE + k * 16);
+        uint8_t* dst = o.codes_rm + (row0 + r) * (cols / 2) + col0 / 2 + k * 16;
+        if (k * 32 + 32 <= tcols) __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));
+        else *reinterpret_cast<v2i*>(dst) = v2i{v.x, v.y};
+      }
+    }
+  }
+  if constexpr (WRITE_CM) {
+#pragma unroll
+    for (int it = 0; it < QP * 8 / QP_THREADS; ++it) {
+      const int c = it * QP_THREADS + tid, line = c >> 3, k = c & 7;
+      if (line < tcols && k * 32 < trows) {
+        const v4i v = *reinterpret_cast<const v4i*>(s_cm + line * QP_LINE + qp_cm_chunk(line, k) * 16);
+        uint8_t* dst = o.codes_cm + (col0 + line) * (rows / 2) + row0 / 2 + k * 16;
+        if (k * 32 + 32 <= trows) __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(dst));
+        else *reinterpret_cast<v2i*>(dst) = v2i{v.x, v.y};
+      }
+    }
+  }
+}
+
+template <bool RM, bool CM>
+ft_status launch_qp(const void* x, int64_t rows, int64_t cols, int64_t ldx, const QuantOut& o, hipStream_t s) {
+  dim3 grid((unsigned)((cols + QP - 1) / QP), (unsigned)((rows + QP - 1) / QP));
+  hipLaunchKernelGGL((quant_pow2_kernel<RM, CM>), grid, dim3(QP_THREADS), 0, s, static_cast<const uint16_t*>(x),
+                     rows, cols, ldx, o);
+  return launch_status();
+}
+
 template <bool POW2, bool RM, bool CM, bool ORM, bool OCM>
 ft_status launch4(const void* x, int64_t rows, int64_t cols, int64_t ldx, const QuantOut& o, hipStream_t s) {
   using Q = QCfg<POW2, RM, CM, ORM, OCM>;
@@ -335,6 +557,7 @@ ft_status launch_ops(const void* x, int64_t rows, int64_t cols, int64_t ldx, con
     if (o.op_rm) return launch4<POW2, RM, CM, true, false>(x, rows, cols, ldx, o, s);
     if (o.op_cm) return launch4<POW2, RM, CM, false, true>(x, rows, cols, ldx, o, s);
   }
+  if constexpr (POW2 && (RM || CM)) return launch_qp<RM, CM>(x, rows, cols, ldx, o, s);
   if constexpr (RM || CM) return launch4<POW2, RM, CM, false, false>(x, rows, cols, ldx, o, s);
   return FT_EINVAL;
 }
