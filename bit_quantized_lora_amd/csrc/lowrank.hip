@@ -136,8 +136,10 @@ constexpr int DB_GPITCH = 2 * LR_CHUNK + 16;   // bytes per LDS row of the stage
 
 // NCT: 32-wide rank column tiles (0..4); QUANT: also write Q(in); GELU: the
 // input is replaced by GELU(in) (written to hout [M x Kin]) before both; NDB:
-// 32-row tiles of the dB partials (0: none; 1 for r <= 32, 2 for r <= 64)
-template <int NCT, bool QUANT, bool GELU = false, int NDB = 0, int WC = 1>
+// 32-row tiles of the dB partials (0: none; 1 for r <= 32, 2 for r <= 64);
+// LINES: the input is loaded in whole 128-byte lines and re-laid out through
+// LDS (below)
+template <int NCT, bool QUANT, bool GELU = false, int NDB = 0, int WC = 1, bool LINES = false>
 __global__ void __launch_bounds__(LR_THREADS)
 lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t ld_in,
                const uint16_t* __restrict__ wa, int ra, const uint16_t* __restrict__ wb, int rb,
@@ -149,6 +151,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
   // 128 cq .. of each CC-column chunk; its partial projection is added to the
   // other column groups' through LDS at the end, in cq order
   static_assert(WC == 1 || NDB == 0, "the dB variant uses 128-row blocks");
+  static_assert(!LINES || NDB == 0, "the dB variant stages its G chunk itself");
   constexpr int RB = LR_ROWS / WC, CC = LR_CHUNK * WC;
   extern __shared__ __attribute__((aligned(1024))) uint8_t s_w[];   // 2 buffers of rho rows (+ dB staging)
   const int wslice = (ra + rb) * LR_WROW;          // one 128-column slice of the weight chunk
@@ -193,13 +196,45 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       else __builtin_amdgcn_raw_ptr_buffer_load_lds(rWb, (lds_void*)dst, 16, off, 0, 0, 0);
     }
   };
+  // LINES: a wave's 32 x 128 block of a chunk is loaded in whole 128-byte lines
+  // (instruction s covers rows 4 s + lr of the block, lr = lane / 16, 16 lanes x
+  // 16 bytes per row); the fragment layout (32 rows x 32 bytes per instruction)
+  // reads the same bytes at about half the rate.  relayout() then moves the
+  // block through this wave's 8 KB of LDS staging into the MFMA fragment layout.
+  const int lr = lane >> 4, lp = lane & 15;
+  const uint32_t in_off_l = (uint32_t)(((32 * rg + lr) * ld_in + 8 * lp + 128 * cq) * 2);
   auto load_x = [&](v4i (&a)[8], int64_t c) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int64_t k = c * CC + 16 * s;              // + 128 cq (in in_off)
-      const uint32_t off = (arow_ok && k + 128 * cq < Kin) ? in_off + (uint32_t)(k * 2) : 0x80000000u;
-      a[s] = __builtin_amdgcn_raw_buffer_load_b128(rIn, off, 0, 0);
+      if constexpr (LINES) {
+        const int64_t k = c * CC + 128 * cq + 8 * lp;   // rows past M lie past the resource's range
+        const uint32_t off = k < Kin ? in_off_l + (uint32_t)((4 * s * ld_in + c * CC) * 2) : 0x80000000u;
+        a[s] = __builtin_amdgcn_raw_buffer_load_b128(rIn, off, 0, 0);
+      } else {
+        const int64_t k = c * CC + 16 * s;              // + 128 cq (in in_off)
+        const uint32_t off = (arow_ok && k + 128 * cq < Kin) ? in_off + (uint32_t)(k * 2) : 0x80000000u;
+        a[s] = __builtin_amdgcn_raw_buffer_load_b128(rIn, off, 0, 0);
+      }
     }
+  };
+  // whole-line layout -> fragment layout in place (lane (l32, lh) then holds row
+  // l32, columns 16 s + 8 lh .. + 8 in x[s]): 256 bytes per staged row, its
+  // 16-byte pieces XOR-swizzled by row so that the reads of 8 consecutive rows
+  // fall in distinct banks.  Only this wave reads what it wrote; its LDS reads
+  // are consumed before the next chunk's writes are issued.
+  uint8_t* const stg = s_w + 2 * wbuf_bytes + wave * 8192;
+  auto relayout = [&](v4i (&x)[8]) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int r = 4 * s + lr;
+      *reinterpret_cast<v4i*>(stg + r * 256 + ((lp ^ (r & 7)) << 4)) = x[s];
+    }
+    compiler_fence();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the block is in LDS
+    compiler_fence();
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      x[s] = *reinterpret_cast<const v4i*>(stg + l32 * 256 + (((2 * s + lh) ^ (l32 & 7)) << 4));
   };
 
   // Codes and scales of a full chunk wait in registers and are stored after the
@@ -292,8 +327,13 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       for (int k = 0; k < 4; ++k)
         o[k] = f32_to_bf16_rne(gelu_f(bf16lo_to_f32(w[k]))) | (f32_to_bf16_rne(gelu_f(bf16hi_to_f32(w[k]))) << 16);
       x[s] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-      const int64_t k0 = c * CC + 128 * cq + 16 * s;
-      if (arow_ok && k0 < Kin) *reinterpret_cast<v4i*>(hout + arow * Kin + k0 + 8 * lh) = x[s];
+      if constexpr (LINES) {   // whole-line layout: row 4 s + lr, 8 columns at 8 lp
+        const int64_t row = row0 + 32 * rg + 4 * s + lr, k0 = c * CC + 128 * cq + 8 * lp;
+        if (row < M && k0 < Kin) *reinterpret_cast<v4i*>(hout + row * Kin + k0) = x[s];
+      } else {
+        const int64_t k0 = c * CC + 128 * cq + 16 * s;
+        if (arow_ok && k0 < Kin) *reinterpret_cast<v4i*>(hout + arow * Kin + k0 + 8 * lh) = x[s];
+      }
     }
   };
 
@@ -384,6 +424,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       for (int s = 0; s < 8; ++s)
         *reinterpret_cast<v4i*>(s_g + (32 * wave + l32) * DB_GPITCH + (16 * s + 8 * lh) * 2) = xc[s];
     }
+    if constexpr (LINES) relayout(xc);
     if constexpr (QUANT) quantize_chunk(xc, c);
     const uint8_t* wbuf = s_w + buf * wbuf_bytes + cq * wslice;
 #pragma unroll
@@ -501,15 +542,27 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
     db = *dbp;
     db.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_db);
   }
-  // column groups double the weight buffers: above 64 ranks (128 KB of LDS at
-  // rank 128) they would leave room for one workgroup per CU instead of two
-  const int wc = (dbp || rho > 64) ? 1 : LR_WC;
+  // Column groups double the weight buffers, and whole-line loads add 32 KB of
+  // input staging: both are taken where two workgroups still fit a CU (column
+  // groups with whole-line loads up to rank 48, 128-row blocks with them up to
+  // rank 96); higher ranks and the dB variant keep 128-row blocks and the
+  // fragment-layout loads.
+  constexpr size_t kLdsPerWg = 80 * 1024, kStage = (size_t)(LR_THREADS / 64) * 8192;
+  const auto w_bytes = [&](int w) { return (size_t)2 * rho * LR_WROW * w; };
+  int wc = 1;
+  bool lines = false;
+  if (!dbp) {
+    if (w_bytes(LR_WC) + kStage <= kLdsPerWg) { wc = LR_WC; lines = true; }
+    else if (w_bytes(1) + kStage <= kLdsPerWg) { wc = 1; lines = true; }
+  }
   const int64_t cps = chunks_per_split(M, Kin, wc);
   const int64_t S = num_splits(M, Kin, wc);
   float* dst = (S > 1 && rho) ? static_cast<float*>(workspace) : out;
   dim3 grid((unsigned)((M + LR_ROWS / wc - 1) / (LR_ROWS / wc)), (unsigned)S);
   // LDS: two weight chunks of wc slices, and for wc > 1 the column groups' partial projections
-  const size_t lds_w = (size_t)2 * rho * LR_WROW * wc;
+  // (+ the input staging after the weight buffers with whole-line loads; the
+  // partial projections reuse the space after the last chunk)
+  const size_t lds_w = w_bytes(wc) + (lines ? kStage : 0);
   const size_t lds_red = wc > 1 ? (size_t)(LR_THREADS / 64) * ((rho + 31) / 32) * 16 * 64 * sizeof(float) : 0;
   const size_t lds_wc = lds_w > lds_red ? lds_w : lds_red;
   const uint16_t* ip = static_cast<const uint16_t*>(in);
@@ -518,16 +571,15 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   const int64_t stride = M * rho;
   const int nct = (rho + 31) / 32;
   uint16_t* hp = static_cast<uint16_t*>(hout);
-#define FT_LR_LAUNCH(N, Q)                                                                                   \
-  if (wc > 1) hipLaunchKernelGGL((lowrank_kernel<N, Q, false, 0, LR_WC>), grid, dim3(LR_THREADS), lds_wc, stream, \
-                                 ip, M, Kin, ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db);     \
-  else hipLaunchKernelGGL((lowrank_kernel<N, Q>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, ld_in, a, ra, \
-                          b, rb, cps, dst, stride, codes, scales, hp, db)
-#define FT_LRG_LAUNCH(N)                                                                                     \
-  if (wc > 1) hipLaunchKernelGGL((lowrank_kernel<N, true, true, 0, LR_WC>), grid, dim3(LR_THREADS), lds_wc, stream, \
-                                 ip, M, Kin, ld_in, a, ra, b, rb, cps, dst, stride, codes, scales, hp, db);     \
-  else hipLaunchKernelGGL((lowrank_kernel<N, true, true>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, ld_in, \
-                          a, ra, b, rb, cps, dst, stride, codes, scales, hp, db)
+#define FT_LR_ONE(N, Q, G, W, L)                                                                             \
+  hipLaunchKernelGGL((lowrank_kernel<N, Q, G, 0, W, L>), grid, dim3(LR_THREADS), lds_wc, stream, ip, M, Kin, ld_in, \
+                     a, ra, b, rb, cps, dst, stride, codes, scales, hp, db)
+#define FT_LR_ANY(N, Q, G)                          \
+  if (wc > 1 && lines) { FT_LR_ONE(N, Q, G, LR_WC, true); }  \
+  else if (lines) { FT_LR_ONE(N, Q, G, 1, true); }  \
+  else { FT_LR_ONE(N, Q, G, 1, false); }
+#define FT_LR_LAUNCH(N, Q) FT_LR_ANY(N, Q, false)
+#define FT_LRG_LAUNCH(N) FT_LR_ANY(N, true, true)
   // dB partials: + (X A)^T hi/lo planes and the staged G chunk
 #define FT_LRD_LAUNCH(N, D)                                                                                  \
   hipLaunchKernelGGL((lowrank_kernel<N, true, false, D>), grid, dim3(LR_THREADS),                          \
@@ -571,6 +623,8 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
   }
 #undef FT_LR_LAUNCH
 #undef FT_LRG_LAUNCH
+#undef FT_LR_ANY
+#undef FT_LR_ONE
 #undef FT_LRD_LAUNCH
   if (launch_status() != FT_OK) return FT_EHIP;
   if (S > 1 && rho) {

@@ -23,20 +23,27 @@ namespace ft {
 namespace {
 // Streaming reference: per element, 2 bytes read and 1 written (the high byte of
 // each 16-bit input), the 2 : 1 read : write ratio of the block quantizer with
-// both code layouts.  Each thread moves 32 input bytes (two 16-byte loads, both
-// issued before either is used) and 16 output bytes per iteration.
-__global__ void __launch_bounds__(256) stream_2to1_kernel(const v4i* __restrict__ in, int64_t n32,
-                                                         v4i* __restrict__ out) {
+// both code layouts.  Work item i reads 16 input bytes and writes 8; consecutive
+// lanes take consecutive items, so every load instruction covers 1 KB and every
+// store 512 bytes of whole 128-byte lines.  Each thread keeps two items in
+// flight (i and i + stride), both loads issued before either is used.
+__global__ void __launch_bounds__(256) stream_2to1_kernel(const v4i* __restrict__ in, int64_t n8,
+                                                         v2i* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n32; i += stride) {
-    const v4i a = __builtin_nontemporal_load(in + 2 * i);
-    const v4i b = __builtin_nontemporal_load(in + 2 * i + 1);
-    // high byte of each of the 16 halfwords
-    const uint32_t w0 = __builtin_amdgcn_perm((uint32_t)a.y, (uint32_t)a.x, 0x07050301u);
-    const uint32_t w1 = __builtin_amdgcn_perm((uint32_t)a.w, (uint32_t)a.z, 0x07050301u);
-    const uint32_t w2 = __builtin_amdgcn_perm((uint32_t)b.y, (uint32_t)b.x, 0x07050301u);
-    const uint32_t w3 = __builtin_amdgcn_perm((uint32_t)b.w, (uint32_t)b.z, 0x07050301u);
-    __builtin_nontemporal_store(v4i{(int)w0, (int)w1, (int)w2, (int)w3}, out + i);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += 2 * stride) {
+    const bool two = i + stride < n8;
+    const v4i a = __builtin_nontemporal_load(in + i);
+    v4i b = v4i{0, 0, 0, 0};
+    if (two) b = __builtin_nontemporal_load(in + i + stride);
+    // high byte of each of the 8 halfwords
+    const uint32_t a0 = __builtin_amdgcn_perm((uint32_t)a.y, (uint32_t)a.x, 0x07050301u);
+    const uint32_t a1 = __builtin_amdgcn_perm((uint32_t)a.w, (uint32_t)a.z, 0x07050301u);
+    __builtin_nontemporal_store(v2i{(int)a0, (int)a1}, out + i);
+    if (two) {
+      const uint32_t b0 = __builtin_amdgcn_perm((uint32_t)b.y, (uint32_t)b.x, 0x07050301u);
+      const uint32_t b1 = __builtin_amdgcn_perm((uint32_t)b.w, (uint32_t)b.z, 0x07050301u);
+      __builtin_nontemporal_store(v2i{(int)b0, (int)b1}, out + i + stride);
+    }
   }
 }
 }  // namespace
@@ -48,10 +55,10 @@ extern "C" ft_status ft_stream_2to1(const void* in, int64_t n, void* out, hipStr
   if (n == 0) return FT_OK;
   if (!in || !out) return FT_EINVAL;
   if (!aligned16(in) || !aligned16(out)) return FT_EALIGN;
-  const int64_t n32 = n / 16;                      // 16 elements (32 input bytes) per work item
-  int64_t blocks = (n32 + 255) / 256;
-  if (blocks > 256 * 16) blocks = 256 * 16;        // 16 workgroups of 4 waves per CU, grid-stride beyond
+  const int64_t n8 = n / 8;                        // 8 elements (16 input bytes) per work item
+  int64_t blocks = (n8 + 511) / 512;
+  if (blocks > 256 * 8) blocks = 256 * 8;          // 8 workgroups of 4 waves per CU, grid-stride beyond
   hipLaunchKernelGGL(stream_2to1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     static_cast<const v4i*>(in), n32, static_cast<v4i*>(out));
+                     static_cast<const v4i*>(in), n8, static_cast<v2i*>(out));
   return launch_status();
 }
