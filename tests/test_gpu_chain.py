@@ -298,6 +298,8 @@ def test_mlp_pair_chain_fused_fc1_full_size():
     (272, 1040, 64, 64),       # two rank tiles, several splits
     (16, 16, 0, 16),
     (256, 384, 0, 0),          # no projection: GELU and Q(h) only
+    (400, 1296, 48, 32),       # 128-row blocks with whole-line loads, ragged rows and reduction
+    (4096, 12288, 32, 32),     # the image-stream MLP intermediate of the FLUX block, rank 64
 ], ids=lambda c: "x".join(map(str, c)))
 def test_gelu_quant_lowrank_matches_separate_kernels(case):
     """The MLP fusion in the second linear's input pass: h, Q(h) and the

@@ -153,12 +153,18 @@ def test_lowrank_matches_oracle_products():
 
 
 @pytest.mark.parametrize("case", [(144, 400, 16, 16), (272, 128, 32, 16), (16, 16, 0, 16), (528, 1040, 64, 64),
-                                  (256, 384, 0, 0), (4608, 3072, 32, 16), (4608, 12288, 32, 16)],
+                                  (256, 384, 0, 0), (4608, 3072, 32, 16), (4608, 12288, 32, 16),
+                                  (400, 1296, 48, 32), (208, 560, 32, 32), (160, 272, 64, 32), (144, 400, 64, 48),
+                                  (4096, 3072, 32, 32)],
                          ids=lambda c: "x".join(map(str, c)))
 def test_quant_lowrank_one_pass(case):
     """Q(in) and the down-projection from one read of the input: codes and scales
     bit-exact with the oracle's quantizer, the projection bit-identical to
-    ft_lowrank_fused and within fp32 rounding of the oracle's product."""
+    ft_lowrank_fused and within fp32 rounding of the oracle's product.  The ranks
+    cover every launch layout: 64-row blocks with whole-line loads (rank <= 48),
+    128-row blocks with whole-line loads (49..96, the boundary 96 included) and
+    with fragment-layout loads (above 96), with row counts and reductions that
+    end inside a block and inside a chunk."""
     require_gpu()
     from bit_quantized_lora_amd import ops
     M, K, ra, rb = case
