@@ -209,7 +209,7 @@ lowrank_kernel(const uint16_t* __restrict__ in, int64_t M, int64_t Kin, int64_t 
       if constexpr (LINES) {
         const int64_t k = c * CC + 128 * cq + 8 * lp;   // rows past M lie past the resource's range
         const uint32_t off = k < Kin ? in_off_l + (uint32_t)((4 * s * ld_in + c * CC) * 2) : 0x80000000u;
-        a[s] = __builtin_amdgcn_raw_buffer_load_b128(rIn, off, 0, 0);
+        a[s] = __builtin_amdgcn_raw_buffer_load_b128(rIn, off, 0, 2);   // nt: streamed, read once
       } else {
         const int64_t k = c * CC + 16 * s;              // + 128 cq (in in_off)
         const uint32_t off = (arow_ok && k + 128 * cq < Kin) ? in_off + (uint32_t)(k * 2) : 0x80000000u;
