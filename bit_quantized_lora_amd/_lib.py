@@ -27,6 +27,7 @@ _SIGS = {
     "ft_lowrank_fused": [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                          c_void_p, c_size_t, c_void_p],
     "ft_lowrank_workspace": [c_int64, c_int64, c_int32],
+    "ft_lowrank_plan": [c_int64, c_int64, c_int32, c_void_p],
     "ft_quant_lowrank": [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,
                          c_void_p, c_void_p, c_void_p, c_size_t, c_void_p],
     "ft_quant_lowrank_db": [c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int32, c_void_p,

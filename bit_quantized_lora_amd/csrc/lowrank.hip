@@ -516,6 +516,38 @@ namespace ft {
 namespace {
 int64_t row_blocks(int64_t M) { return (M + LR_ROWS - 1) / LR_ROWS; }
 
+// The launch layout of a pass over in [M x Kin] projecting onto rho ranks (db: the
+// dB-fold variant).  Column groups double the weight buffers, and whole-line
+// loads add 32 KB of input staging: both are taken where two workgroups still
+// fit a CU (column groups with whole-line loads up to rank 48, 128-row blocks
+// with them up to rank 96); higher ranks and the dB variant keep 128-row blocks
+// and the fragment-layout loads.  LDS: two weight chunks of wc slices, the
+// staging after them, and for wc > 1 the column groups' partial projections,
+// which reuse the space after the last chunk.
+struct LrPlan {
+  int wc = 1;
+  bool lines = false;
+  int64_t cps = 0, splits = 0;
+  size_t lds = 0;
+};
+constexpr size_t kLdsPerWg = 80 * 1024, kStage = (size_t)(LR_THREADS / 64) * 8192;
+
+LrPlan lowrank_plan(int64_t M, int64_t Kin, int rho, bool db) {
+  LrPlan pl;
+  const auto w_bytes = [&](int w) { return (size_t)2 * rho * LR_WROW * w; };
+  if (!db) {
+    if (w_bytes(LR_WC) + kStage <= kLdsPerWg) { pl.wc = LR_WC; pl.lines = true; }
+    else if (w_bytes(1) + kStage <= kLdsPerWg) { pl.wc = 1; pl.lines = true; }
+  }
+  pl.cps = chunks_per_split(M, Kin, pl.wc);
+  pl.splits = num_splits(M, Kin, pl.wc);
+  const size_t lds_w = w_bytes(pl.wc) + (pl.lines ? kStage : 0);
+  const size_t lds_red =
+      pl.wc > 1 ? (size_t)(LR_THREADS / 64) * ((rho + 31) / 32) * 16 * 64 * sizeof(float) : 0;
+  pl.lds = lds_w > lds_red ? lds_w : lds_red;
+  return pl;
+}
+
 ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, const void* wa, int32_t ra,
                        const void* wb, int32_t rb, float* out, uint8_t* codes, uint8_t* scales, void* workspace,
                        size_t ws_bytes, hipStream_t stream, void* hout = nullptr, const DbArgs* dbp = nullptr,
@@ -542,29 +574,14 @@ ft_status lowrank_impl(const void* in, int64_t M, int64_t Kin, int64_t ld_in, co
     db = *dbp;
     db.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_db);
   }
-  // Column groups double the weight buffers, and whole-line loads add 32 KB of
-  // input staging: both are taken where two workgroups still fit a CU (column
-  // groups with whole-line loads up to rank 48, 128-row blocks with them up to
-  // rank 96); higher ranks and the dB variant keep 128-row blocks and the
-  // fragment-layout loads.
-  constexpr size_t kLdsPerWg = 80 * 1024, kStage = (size_t)(LR_THREADS / 64) * 8192;
-  const auto w_bytes = [&](int w) { return (size_t)2 * rho * LR_WROW * w; };
-  int wc = 1;
-  bool lines = false;
-  if (!dbp) {
-    if (w_bytes(LR_WC) + kStage <= kLdsPerWg) { wc = LR_WC; lines = true; }
-    else if (w_bytes(1) + kStage <= kLdsPerWg) { wc = 1; lines = true; }
-  }
-  const int64_t cps = chunks_per_split(M, Kin, wc);
-  const int64_t S = num_splits(M, Kin, wc);
+  const LrPlan pl = lowrank_plan(M, Kin, rho, dbp != nullptr);
+  const int wc = pl.wc;
+  const bool lines = pl.lines;
+  const int64_t cps = pl.cps;
+  const int64_t S = pl.splits;
   float* dst = (S > 1 && rho) ? static_cast<float*>(workspace) : out;
   dim3 grid((unsigned)((M + LR_ROWS / wc - 1) / (LR_ROWS / wc)), (unsigned)S);
-  // LDS: two weight chunks of wc slices, and for wc > 1 the column groups' partial projections
-  // (+ the input staging after the weight buffers with whole-line loads; the
-  // partial projections reuse the space after the last chunk)
-  const size_t lds_w = w_bytes(wc) + (lines ? kStage : 0);
-  const size_t lds_red = wc > 1 ? (size_t)(LR_THREADS / 64) * ((rho + 31) / 32) * 16 * 64 * sizeof(float) : 0;
-  const size_t lds_wc = lds_w > lds_red ? lds_w : lds_red;
+  const size_t lds_wc = pl.lds;
   const uint16_t* ip = static_cast<const uint16_t*>(in);
   const uint16_t* a = static_cast<const uint16_t*>(wa);
   const uint16_t* b = static_cast<const uint16_t*>(wb);
@@ -647,6 +664,23 @@ extern "C" ft_status ft_lowrank_fused(const void* in, int64_t M, int64_t Kin, in
                                       const void* wa, int32_t ra, const void* wb, int32_t rb,
                                       float* out, void* workspace, size_t ws_bytes, hipStream_t stream) {
   return ft::lowrank_impl(in, M, Kin, ld_in, wa, ra, wb, rb, out, nullptr, nullptr, workspace, ws_bytes, stream);
+}
+
+extern "C" ft_status ft_lowrank_plan(int64_t M, int64_t Kin, int32_t rho, int32_t* plan) {
+  using namespace ft;
+  if (!plan) return FT_EINVAL;
+  if (!mult16(M) || !mult16(Kin) || rho < 0 || rho % 16 || rho > 128) return FT_ESHAPE;
+  if (M == 0 || Kin == 0) {
+    for (int i = 0; i < 5; ++i) plan[i] = 0;
+    return FT_OK;
+  }
+  const LrPlan pl = lowrank_plan(M, Kin, rho, false);
+  plan[0] = LR_ROWS / pl.wc;
+  plan[1] = pl.lines ? 1 : 0;
+  plan[2] = (int32_t)pl.splits;
+  plan[3] = (int32_t)pl.cps;
+  plan[4] = (int32_t)pl.lds;
+  return FT_OK;
 }
 
 extern "C" ft_status ft_quant_lowrank(const void* in, int64_t M, int64_t Kin, int64_t ld_in,

@@ -153,6 +153,19 @@ ft_status ft_lowrank_fused(const void* in, int64_t M, int64_t Kin, int64_t ld_in
 
 size_t ft_lowrank_workspace(int64_t M, int64_t Kin, int32_t rho);
 
+/* ft_lowrank_plan -- how ft_lowrank_fused, ft_quant_lowrank and
+ * ft_gelu_quant_lowrank launch for in [M x Kin] and rho = ra + rb ranks (for
+ * tests and profiling; nothing is run).  plan holds 5 int32: plan[0] input rows
+ * per workgroup (64: two 128-column groups per 256-column chunk; 128: one
+ * 128-column chunk), plan[1] 1 when the input is loaded in whole 128-byte lines
+ * and re-laid out through LDS, 0 for loads in the MFMA fragment layout, plan[2]
+ * reduction splits (their partials go to the workspace when above 1), plan[3]
+ * chunks per split along the reduction (a chunk is 128 columns per column
+ * group: 256 columns at 64-row blocks, 128 at 128-row blocks), plan[4] LDS
+ * bytes per workgroup.  All zero for an empty input.  FT_ESHAPE for M or
+ * Kin not a multiple of 16, or rho not one of 0, 16, ..., 128. */
+ft_status ft_lowrank_plan(int64_t M, int64_t Kin, int32_t rho, int32_t* plan);
+
 /* ft_quant_lowrank -- ft_lowrank_fused and the quantizer Q(in) (FT_SCALE_POW2,
  * row-major codes) in one read of the input: the LoRA fusion of section 3.3
  * extended to the quantizer, which reads the same activations (forward: X) or

@@ -182,6 +182,45 @@ def test_noalloc_backward_rejects_requests_beyond_its_scratch():
         assert lib.ft_linear_bwd_workspace(M, N, K, r) <= L.FT_NOALLOC_SCRATCH_BYTES
 
 
+def test_lowrank_plan_layouts_fit_two_workgroups_per_cu():
+    """ft_lowrank_plan (the one-pass quantize + projection's launch) validates its
+    arguments, gives the step's two passes the 64-row, whole-line-load layout, and
+    for every rank keeps two workgroups per CU (at most 80 KB of LDS each, of a
+    CU's 160 KB), chooses whole-line loads exactly where their 32 KB of staging
+    still fits, covers the reduction with its splits, and stays within the
+    workspace ft_lowrank_workspace sizes (no GPU needed)."""
+    L = _lib(); lib = L.lib()
+    plan = (ctypes.c_int32 * 5)()
+    pp = ctypes.addressof(plan)
+    assert lib.ft_lowrank_plan(4608, 3072, 48, None) == L.FT_EINVAL
+    assert lib.ft_lowrank_plan(4600, 3072, 48, pp) == L.FT_ESHAPE
+    assert lib.ft_lowrank_plan(4608, 3072, 40, pp) == L.FT_ESHAPE
+    assert lib.ft_lowrank_plan(4608, 3072, 144, pp) == L.FT_ESHAPE
+    assert lib.ft_lowrank_plan(0, 3072, 48, pp) == L.FT_OK and list(plan) == [0] * 5
+    # the MLP-up step: X pass [4608 x 3072] and G pass [4608 x 12288] at rank 48
+    assert lib.ft_lowrank_plan(4608, 3072, 48, pp) == L.FT_OK
+    assert (plan[0], plan[1], plan[2], plan[3]) == (64, 1, 6, 2)
+    assert lib.ft_lowrank_plan(4608, 12288, 48, pp) == L.FT_OK
+    assert (plan[0], plan[1], plan[2], plan[3]) == (64, 1, 7, 7)
+    stage, weights = 4 * 8192, lambda rho, wc: 2 * rho * 256 * wc
+    for rho in range(0, 129, 16):
+        for M in (16, 400, 4096, 4608, 18432):
+            for K in (16, 1296, 3072, 12288):
+                assert lib.ft_lowrank_plan(M, K, rho, pp) == L.FT_OK
+                rows, lines, splits, cps, lds = list(plan)
+                wc = 2 if rows == 64 else 1
+                assert rows in (64, 128) and lds <= 80 * 1024, (rho, M, K, list(plan))
+                # whole-line loads wherever the staging fits, column groups first
+                fits2, fits1 = weights(rho, 2) + stage <= 80 * 1024, weights(rho, 1) + stage <= 80 * 1024
+                assert lines == int(fits2 or fits1) and (rows == 64) == fits2, (rho, list(plan))
+                assert lds >= weights(rho, wc) + (stage if lines else 0)
+                chunk = 128 * wc
+                nchunks = -(-K // chunk)
+                assert splits * cps >= nchunks > (splits - 1) * cps, (rho, M, K, list(plan))
+                if splits > 1 and rho:
+                    assert lib.ft_lowrank_workspace(M, K, rho) >= splits * M * rho * 4
+
+
 def test_backward_plan_query():
     """ft_linear_bwd_plan validates its arguments and describes a launch: the
     dX GEMM's tile and splits, the adapter workgroups of the same launch and
