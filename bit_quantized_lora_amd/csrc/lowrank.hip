@@ -8,9 +8,9 @@
 // once.  A workgroup of 4 waves owns 64 rows and a contiguous range of
 // 256-column chunks of the reduction: two row groups of 32, each split into two
 // 128-column halves (column groups), so every row is fetched in 512-byte runs.
-// (The dB variant, and ranks above 64, whose weight buffers would then crowd
-// out the second workgroup per CU, keep 128 rows x 128 columns: 4 row groups,
-// one column group.)  The split over the reduction gives the launch enough workgroups to
+// (The dB variant, and ranks above 48, whose weight buffers and input staging
+// would then crowd out the second workgroup per CU, keep 128 rows x 128
+// columns: 4 row groups, one column group; see lowrank_plan.)  The split over the reduction gives the launch enough workgroups to
 // keep every CU streaming.  Per chunk, the weight slices [rank x 128] are
 // copied to LDS once (buffer_load ... lds, 16-byte-chunk XOR swizzle against
 // bank conflicts) and shared by the waves, while each wave prefetches its own
@@ -502,7 +502,7 @@ __global__ void sum_splits_kernel(const float* __restrict__ part, int64_t splits
 }  // namespace ft
 
 // split partials of either block shape (128-row blocks for the dB variant and
-// above 64 ranks, LR_WC column groups otherwise)
+// above 48 ranks, LR_WC column groups otherwise)
 extern "C" size_t ft_lowrank_workspace(int64_t M, int64_t Kin, int32_t rho) {
   using namespace ft;
   if (M <= 0 || Kin <= 0 || rho <= 0) return 0;
